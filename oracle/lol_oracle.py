@@ -1,0 +1,310 @@
+"""Plain, slow CPU oracle of the Library-of-Layers routed-core forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module; only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+path (``runtime_routed_transformer_amd/csrc``); the two meet only in the
+seeded input generator, which holds none of the method's arithmetic.
+
+Sources (the four pages on the method):
+  [paper]  "Library of Layers (LoL): Adaptively Ordering Transformer Layers
+           at Runtime", arXiv HTML: Sec. 3.2.1 (strided window attention),
+           Sec. 3.2.2 (router), Appendix A (Algorithm 1, architecture and
+           loss-free balancing paragraphs, FiLM).
+  [blog]   "Library of Layers: a transformer that picks its own layer order"
+           (ai.satyajit.si): "The forward pass, term by term" and "How the
+           order is chosen" (the router in fp32, biased top-1).
+  [review] "Library of Layers: Routing Whole Transformer Blocks at Runtime"
+           (zhongzhuzhou.org): Eqs. (1)-(5), (7) and the reader's Algorithm 1.
+
+Arithmetic: everything in float64 (inputs are fp32 or bf16-exact fp32 values,
+upcast exactly), except the router's score-and-select step, which the blog's
+quoted code runs in fp32 (``self.c_fc(x.float())``) and which this oracle
+therefore also evaluates in fp32 so that both sides decide the argmax in the
+same precision.  Activations are never rounded to bf16.
+
+Readings of points the pages leave open (each also listed in the design doc):
+  * RMSNorm eps = 1e-6; Norm_s(x) = g_s * x / sqrt(mean(x^2) + eps) with a
+    per-expert gain g_s, followed by the depth FiLM gamma_{l,s}, beta_{l,s}
+    that is shared by all experts (review Eq. 7; paper App. A).
+  * RoPE: theta = 10000, rotate-half pairing (j, j + d_h/2), angle
+    pos * theta^(-2j/d_h), positions = token index in the document.
+  * Bias-free attention with scale 1/sqrt(d_h) and a causal mask confined
+    to the window; pre-norm block h = x + Attn(Norm(x)), y = h + MLP(Norm(h)).
+  * SwiGLU MLP silu(u W_g^T) * (u W_u^T) then W_d; GELU variant uses the
+    exact erf form with two matrices.
+  * Argmax ties go to the lowest expert index; margin = top-1 minus top-2 of
+    (a + b) in probability units (+inf when L = 1).
+  * Forcing: forced id >= 0 replaces the router's choice; the gate is the
+    forced gate if given and not NaN, else the router's unbiased a_rho.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+(worked values printed on the pages, closed forms, library routines on
+special cases, brute force and invariants).  The end-to-end values of a
+random forward are pinned only through those invariants; the pages print no
+numeric forward output.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import List, Optional, Tuple
+
+import numpy as np
+from scipy.special import erf
+
+
+# --------------------------------------------------------------------------
+# a1. Strided window partition
+#   [paper] Sec. 3.2.1 and Algorithm 1 (window preparation): the offset is
+#   delta_l = ((l-1) S) mod W and position i belongs to window
+#   floor((i + delta_l) / W).  [review] Eq. (2): no cyclic wrap, the modulo
+#   applies to the offset only.
+# --------------------------------------------------------------------------
+def window_offset(depth: int, W: int, S: int) -> int:
+    return ((depth - 1) * S) % W
+
+
+def window_ids(n: int, W: int, S: int, depth: int) -> np.ndarray:
+    """w_l(i) for i = 0..n-1 (depth is 1-based)."""
+    delta = window_offset(depth, W, S)
+    return (np.arange(n) + delta) // W
+
+
+def partition(n: int, W: int, S: int, depth: int) -> List[Tuple[int, int]]:
+    """Windows of depth ``depth`` as (first, last) inclusive, in ordinal order.
+
+    Built from the set definition I_k = {i : w_l(i) = k}: the ordinals are
+    consecutive from 0, so each I_k is a run of consecutive positions.
+    """
+    w = window_ids(n, W, S, depth)
+    out = []
+    for k in range(int(w[-1]) + 1):
+        members = np.nonzero(w == k)[0]
+        out.append((int(members[0]), int(members[-1])))
+    return out
+
+
+# --------------------------------------------------------------------------
+# a2, a3. Window means and the prefix router input
+#   [paper] Algorithm 1: mu_k = Mean(s_{I_k}); r_0 = (e^(l) + s_0) / 2 with a
+#   learned depth vector; r_k = (1/k) sum_{j<k} mu_j (mean of prior windows
+#   only).  [review] Eq. (4): equal weight per window, not per token.
+# --------------------------------------------------------------------------
+def window_means(s_row: np.ndarray, windows) -> np.ndarray:
+    return np.stack([s_row[a:b + 1].mean(axis=0) for a, b in windows])
+
+
+def router_inputs(s_row: np.ndarray, windows, e_depth: np.ndarray) -> np.ndarray:
+    mu = window_means(s_row, windows)
+    r = np.empty_like(mu)
+    r[0] = 0.5 * (e_depth + s_row[0])
+    for k in range(1, len(windows)):
+        r[k] = mu[:k].sum(axis=0) / k
+    return r
+
+
+# --------------------------------------------------------------------------
+# a4. Score and select
+#   [blog] "The forward pass, term by term", steps 3 and 4, and the quoted
+#   router code: logits = c_fc(x.float()) in fp32, softmax, biased top-1
+#   whose weight is the unbiased score.  [paper] App. A (loss-free
+#   balancing): rho = argmax_m (a_m + b_m), alpha = a_rho.  [review] Eq. (5).
+#   Training noise is off at inference ([review] reader's Algorithm 1 note).
+# --------------------------------------------------------------------------
+@dataclass
+class Route:
+    expert: int
+    gate: float      # alpha = a_rho (unbiased), or the forced gate
+    margin: float    # (a+b)_top1 - (a+b)_top2, +inf for a one-expert library
+    probs: np.ndarray  # a (fp32)
+
+
+def route(r: np.ndarray, w_r: np.ndarray, b_r: np.ndarray,
+          expert_bias: np.ndarray) -> Route:
+    r32 = np.asarray(r, np.float64).astype(np.float32)
+    # fp32 linear layer; the dot products are formed exactly in float64 and
+    # rounded once to fp32 (the correctly rounded fp32 result)
+    z = (w_r.astype(np.float64) @ r32.astype(np.float64)).astype(np.float32)
+    z = (z + b_r.astype(np.float32)).astype(np.float32)
+    ez = np.exp(z - z.max())                      # fp32 exp
+    a = (ez / ez.sum(dtype=np.float32)).astype(np.float32)
+    scores = (a + expert_bias.astype(np.float32)).astype(np.float32)
+    rho = int(np.argmax(scores))                  # first maximum = lowest index
+    if len(scores) > 1:
+        margin = float(scores[rho]) - float(np.max(np.delete(scores, rho)))
+    else:
+        margin = math.inf
+    return Route(rho, float(a[rho]), margin, a)
+
+
+# --------------------------------------------------------------------------
+# a6-a12. One library block on one window
+#   [paper] App. A: RoPE, RMSNorm, SwiGLU, bias-free attention; depth FiLM
+#   gamma_s * Norm_s(x) + beta_s in place of each norm.  [paper] Sec. 3.2.1:
+#   causal attention restricted to the window.  [review] Eq. (1) (scale
+#   1/sqrt(d_h)) and Eq. (7) (FiLM).  [blog] step 5: a full pre-norm
+#   residual block.
+# --------------------------------------------------------------------------
+@dataclass
+class BlockParams:
+    wq: np.ndarray    # [d][d]  (out, in)
+    wk: np.ndarray
+    wv: np.ndarray
+    wo: np.ndarray    # [d][d]
+    w_up: np.ndarray  # SwiGLU: W_u [f][d]; GELU: W_1 [f][d]
+    w_gate: Optional[np.ndarray]  # SwiGLU: W_g [f][d]; GELU: None
+    w_down: np.ndarray  # [d][f]
+    g_attn: np.ndarray
+    g_ffn: np.ndarray
+
+
+def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    return gain * x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half RoPE on x [len][H][d_h] at the given positions."""
+    if theta == 0.0:
+        return x
+    dh = x.shape[-1]
+    half = dh // 2
+    inv_freq = theta ** (-2.0 * np.arange(half) / dh)          # omega_j
+    ang = positions[:, None].astype(np.float64) * inv_freq[None, :]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def window_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """softmax(q k^T / sqrt(d_h)) v over keys j <= i, all inside one window.
+
+    q, k, v: [len][H][d_h] -> [len][H][d_h]
+    """
+    ln, H, dh = q.shape
+    out = np.empty_like(q)
+    allowed = np.tril(np.ones((ln, ln), dtype=bool))
+    for h in range(H):
+        sc = (q[:, h, :] @ k[:, h, :].T) / math.sqrt(dh)
+        sc = np.where(allowed, sc, -np.inf)
+        sc = sc - sc.max(axis=1, keepdims=True)
+        p = np.exp(sc)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, h, :]
+    return out
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def gelu_erf(x):
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def expert_block(x: np.ndarray, p: BlockParams, n_heads: int, positions: np.ndarray,
+                 film: Optional[Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]],
+                 eps: float, rope_theta: float) -> np.ndarray:
+    """E_m(x) for one window x [len][d] (float64); returns y [len][d]."""
+    ln, d = x.shape
+    dh = d // n_heads
+    u = rms_norm(x, p.g_attn, eps)
+    if film is not None:
+        u = film[0] * u + film[1]
+    q = (u @ p.wq.T).reshape(ln, n_heads, dh)
+    k = (u @ p.wk.T).reshape(ln, n_heads, dh)
+    v = (u @ p.wv.T).reshape(ln, n_heads, dh)
+    q = rope(q, positions, rope_theta)
+    k = rope(k, positions, rope_theta)
+    o = window_causal_attention(q, k, v).reshape(ln, d)
+    h = x + o @ p.wo.T
+    u2 = rms_norm(h, p.g_ffn, eps)
+    if film is not None:
+        u2 = film[2] * u2 + film[3]
+    if p.w_gate is not None:
+        mid = silu(u2 @ p.w_gate.T) * (u2 @ p.w_up.T)
+    else:
+        mid = gelu_erf(u2 @ p.w_up.T)
+    return h + mid @ p.w_down.T
+
+
+# --------------------------------------------------------------------------
+# The routed core: Algorithm 1 of [paper] App. A, routed-depth loop only
+# (the prelude output s^(0) is the input, the coda is not part of it).
+# Every window at depth l reads s^(l-1); the new states replace the old ones
+# only after all windows ([review] reader's Algorithm 1, lines 4 and 12).
+# --------------------------------------------------------------------------
+@dataclass
+class OracleResult:
+    s: np.ndarray              # s^(D) [B][n][d] float32
+    s64: np.ndarray            # s^(D) float64 (before the final rounding)
+    expert: np.ndarray         # [D][B][K_max] int32, -1 beyond K_l
+    gate: np.ndarray           # [D][B][K_max] float32, 0 beyond K_l
+    margin: np.ndarray         # [D][B][K_max] float32
+
+
+def expert_params(inp, m: int) -> BlockParams:
+    cfg = inp.cfg
+    d, f = cfg.d, cfg.d_ffn
+    f64 = lambda a: np.asarray(a, np.float64)
+    wqkv = f64(inp.wqkv[m])
+    if cfg.mlp == "swiglu":
+        w_gate, w_up = f64(inp.w_gu[m][:f]), f64(inp.w_gu[m][f:])
+    else:
+        w_gate, w_up = None, f64(inp.w_gu[m])
+    return BlockParams(wqkv[:d], wqkv[d:2 * d], wqkv[2 * d:], f64(inp.wo[m]),
+                       w_up, w_gate, f64(inp.w_down[m]),
+                       f64(inp.g_attn[m]), f64(inp.g_ffn[m]))
+
+
+def forward(inp, forced_expert: Optional[np.ndarray] = None,
+            forced_gate: Optional[np.ndarray] = None,
+            rows: Optional[List[int]] = None, n_tokens: Optional[int] = None) -> OracleResult:
+    """Run the routed core on ``inp`` (a ``CoreInputs``).
+
+    forced_expert / forced_gate: [D][B][K_max]; id -1 (or gate NaN) = free.
+    rows / n_tokens: optionally restrict to some batch rows and to the first
+    ``n_tokens`` positions of each (a document prefix; by the causality of the
+    core, outputs and routes inside the prefix equal those of the full run).
+    """
+    cfg = inp.cfg
+    rows = list(range(cfg.batch)) if rows is None else list(rows)
+    n = cfg.n if n_tokens is None else int(n_tokens)
+    D, L, K_max = cfg.D, cfg.L, cfg.k_max
+    params = [expert_params(inp, m) for m in range(L)]
+    w_r = np.asarray(inp.w_r, np.float32)
+    b_r = np.asarray(inp.b_r, np.float32)
+    bias = np.asarray(inp.expert_bias, np.float32)
+    s = np.asarray(inp.s0[rows, :n], np.float64).copy()
+    expert = np.full((D, len(rows), K_max), -1, np.int32)
+    gate = np.zeros((D, len(rows), K_max), np.float32)
+    margin = np.zeros((D, len(rows), K_max), np.float32)
+    for depth in range(1, D + 1):
+        windows = partition(n, cfg.W, cfg.S, depth)
+        if inp.film_gamma is not None:
+            fg = np.asarray(inp.film_gamma[depth - 1], np.float64)
+            fb = np.asarray(inp.film_beta[depth - 1], np.float64)
+            film = (fg[0], fb[0], fg[1], fb[1])
+        else:
+            film = None
+        s_next = s.copy()
+        for bi, b in enumerate(rows):
+            r = router_inputs(s[bi], windows, np.asarray(inp.e_depth[depth - 1], np.float64))
+            for k, (a0, a1) in enumerate(windows):
+                rt = route(r[k], w_r, b_r, bias)
+                rho, alpha = rt.expert, rt.gate
+                if forced_expert is not None and forced_expert[depth - 1, b, k] >= 0:
+                    rho = int(forced_expert[depth - 1, b, k])
+                    alpha = float(rt.probs[rho])
+                if forced_gate is not None and not np.isnan(forced_gate[depth - 1, b, k]):
+                    alpha = float(forced_gate[depth - 1, b, k])
+                x = s[bi, a0:a1 + 1]
+                y = expert_block(x, params[rho], cfg.n_heads, np.arange(a0, a1 + 1), film,
+                                 cfg.rms_eps, cfg.rope_theta)
+                s_next[bi, a0:a1 + 1] = x + np.float64(np.float32(alpha)) * (y - x)
+                expert[depth - 1, bi, k] = rho
+                gate[depth - 1, bi, k] = alpha
+                margin[depth - 1, bi, k] = rt.margin
+        s = s_next
+    return OracleResult(s.astype(np.float32), s, expert, gate, margin)

@@ -1,0 +1,195 @@
+"""Seeded synthetic workloads for the Library-of-Layers routed core.
+
+This module is the only code that both the CPU oracle (``oracle/``) and the
+HIP path see.  It draws inputs and nothing else: it holds none of the
+method's arithmetic (no partition, pooling, routing, norm, attention or MLP).
+
+Shapes follow the paper "Library of Layers (LoL): Adaptively Ordering
+Transformer Layers at Runtime" (arXiv HTML, Appendix A, architecture
+paragraph): bias-free attention, RMSNorm gains, SwiGLU MLP with three
+matrices; one exception is the tiny fp32 workload, which uses a two-matrix
+GELU MLP.  No dataset is used anywhere: the pages' corpora (FineWeb, math,
+sudoku and maze traces) are replaced by i.i.d. Gaussian hidden states of the
+same shapes.
+
+Weight layouts (all row-major, "[out][in]", so every GEMM operand is
+contiguous along the reduction dimension):
+
+  wqkv    [L][3d][d]   rows 0..d-1 = W_q, d..2d-1 = W_k, 2d..3d-1 = W_v
+  wo      [L][d][d]
+  w_gu    [L][2f][d]   SwiGLU: rows 0..f-1 = W_gate, f..2f-1 = W_up
+                       GELU:   [L][f][d] = W_1
+  w_down  [L][d][f]    (GELU: W_2)
+  g_attn, g_ffn [L][d] RMSNorm gains, fp32
+  film_gamma, film_beta [D][2][d] depth FiLM (index 0 = attention norm,
+                       1 = MLP norm), fp32, or None for "no FiLM"
+  w_r [L][d], b_r [L], e_depth [D][d], expert_bias [L]  router, fp32
+
+bf16 workloads round every block matrix to bf16 once (round to nearest even);
+``*_f32`` holds those rounded values exactly as fp32 for the oracle and
+``*_bf16`` the raw 16-bit patterns for the device.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+WEIGHT_STD = 0.02
+
+
+@dataclass(frozen=True)
+class CoreConfig:
+    name: str
+    batch: int
+    n: int
+    d: int
+    n_heads: int
+    d_ffn: int
+    L: int
+    D: int
+    W: int
+    S: int
+    mlp: str          # "swiglu" | "gelu"
+    dtype: str        # "fp32" | "bf16"
+    seed: int
+    film: bool = True
+    rope_theta: float = 10000.0
+    rms_eps: float = 1e-6
+    bias_mode: str = "zero"      # "zero" | "skewed" (large-library load skew)
+    path_mode: str = "free"      # "free" | "forced_seq" (one id sequence for all windows)
+
+    @property
+    def d_head(self) -> int:
+        return self.d // self.n_heads
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.n
+
+    @property
+    def k_max(self) -> int:
+        # enough window slots for any depth: ceil(n / W) + 1
+        return -(-self.n // self.W) + 1
+
+    def scaled(self, batch: int, n: int, name: Optional[str] = None) -> "CoreConfig":
+        return dataclasses.replace(self, batch=batch, n=n,
+                                   name=name or f"{self.name}@{batch}x{n}")
+
+    def with_(self, **kw) -> "CoreConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads.  Index 0 is the tiny fp32 case, 1 the small bf16 core,
+# 2 the mid bf16 core (the throughput workload), 3 the sparse large library
+# with skewed load, 4 the forced-path reuse extreme.
+CONFIGS = [
+    CoreConfig("tiny_fp32", batch=1, n=64, d=64, n_heads=2, d_ffn=256, L=3, D=3,
+               W=16, S=8, mlp="gelu", dtype="fp32", seed=0),
+    CoreConfig("small_bf16", batch=8, n=1024, d=512, n_heads=8, d_ffn=2048, L=4,
+               D=4, W=128, S=64, mlp="swiglu", dtype="bf16", seed=1),
+    CoreConfig("mid_bf16", batch=4, n=4096, d=1024, n_heads=16, d_ffn=4096, L=8,
+               D=8, W=256, S=128, mlp="swiglu", dtype="bf16", seed=2),
+    CoreConfig("sparse_bf16", batch=4, n=4096, d=1024, n_heads=16, d_ffn=4096,
+               L=32, D=6, W=256, S=128, mlp="swiglu", dtype="bf16", seed=3,
+               bias_mode="skewed"),
+    CoreConfig("forced_bf16", batch=16, n=2048, d=768, n_heads=12, d_ffn=3072,
+               L=2, D=12, W=64, S=32, mlp="swiglu", dtype="bf16", seed=4,
+               path_mode="forced_seq"),
+]
+CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even); returns fp32 values."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).copy()
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32)
+
+
+def bf16_bits(x_rounded: np.ndarray) -> np.ndarray:
+    """The upper 16 bits of already bf16-rounded fp32 values."""
+    u = np.ascontiguousarray(x_rounded, dtype=np.float32).view(np.uint32)
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+@dataclass
+class CoreInputs:
+    cfg: CoreConfig
+    s0: np.ndarray                 # [B][n][d] fp32
+    wqkv: np.ndarray               # fp32 values (bf16-exact in bf16 workloads)
+    wo: np.ndarray
+    w_gu: np.ndarray
+    w_down: np.ndarray
+    g_attn: np.ndarray             # [L][d]
+    g_ffn: np.ndarray
+    film_gamma: Optional[np.ndarray]   # [D][2][d] or None
+    film_beta: Optional[np.ndarray]
+    w_r: np.ndarray                # [L][d]
+    b_r: np.ndarray                # [L]
+    e_depth: np.ndarray            # [D][d]
+    expert_bias: np.ndarray        # [L]
+    forced_expert: Optional[np.ndarray]  # [D][B][K_max] int32, -1 = free, or None
+
+    def block_weights(self):
+        return self.wqkv, self.wo, self.w_gu, self.w_down
+
+    def device_weight(self, name: str) -> np.ndarray:
+        """The array the device receives for a block matrix (bf16 bits or fp32)."""
+        w = getattr(self, name)
+        return bf16_bits(w) if self.cfg.dtype == "bf16" else w
+
+
+def _normal(rng, shape, std):
+    return (rng.standard_normal(shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def generate(cfg: CoreConfig) -> CoreInputs:
+    """Draw every input of ``cfg`` from ``numpy.random.default_rng(cfg.seed)``.
+
+    Order of draws: s0; then per expert wqkv, wo, w_gu (or w_1), w_down
+    (or w_2), g_attn, g_ffn; then FiLM gamma, beta; then W_r and e_depth;
+    then, for the forced-sequence workload, the per-depth expert ids.
+    Projections, W_r and e_depth are N(0, 0.02^2); gains and FiLM gamma are
+    1 + N(0, 0.02^2); FiLM beta is N(0, 0.02^2); b_r = 0; expert_bias = 0
+    (the skewed workload's bias is calibrated afterwards by the test harness).
+    """
+    rng = np.random.default_rng(cfg.seed)
+    B, n, d, f, L, D = cfg.batch, cfg.n, cfg.d, cfg.d_ffn, cfg.L, cfg.D
+    if d % cfg.n_heads:
+        raise ValueError("d must be a multiple of n_heads")
+    s0 = rng.standard_normal((B, n, d), dtype=np.float32)
+    n_up = 2 * f if cfg.mlp == "swiglu" else f
+    wqkv = np.empty((L, 3 * d, d), np.float32)
+    wo = np.empty((L, d, d), np.float32)
+    w_gu = np.empty((L, n_up, d), np.float32)
+    w_down = np.empty((L, d, f), np.float32)
+    g_attn = np.empty((L, d), np.float32)
+    g_ffn = np.empty((L, d), np.float32)
+    for m in range(L):
+        wqkv[m] = _normal(rng, (3 * d, d), WEIGHT_STD)
+        wo[m] = _normal(rng, (d, d), WEIGHT_STD)
+        w_gu[m] = _normal(rng, (n_up, d), WEIGHT_STD)
+        w_down[m] = _normal(rng, (d, f), WEIGHT_STD)
+        g_attn[m] = 1.0 + _normal(rng, (d,), WEIGHT_STD)
+        g_ffn[m] = 1.0 + _normal(rng, (d,), WEIGHT_STD)
+    if cfg.film:
+        film_gamma = (1.0 + _normal(rng, (D, 2, d), WEIGHT_STD)).astype(np.float32)
+        film_beta = _normal(rng, (D, 2, d), WEIGHT_STD)
+    else:
+        film_gamma = film_beta = None
+    w_r = _normal(rng, (L, d), WEIGHT_STD)
+    e_depth = _normal(rng, (D, d), WEIGHT_STD)
+    b_r = np.zeros(L, np.float32)
+    expert_bias = np.zeros(L, np.float32)
+    forced = None
+    if cfg.path_mode == "forced_seq":
+        seq = rng.integers(0, L, size=D).astype(np.int32)
+        forced = np.broadcast_to(seq[:, None, None], (D, B, cfg.k_max)).astype(np.int32).copy()
+    if cfg.dtype == "bf16":
+        wqkv, wo, w_gu, w_down = (bf16_round(w) for w in (wqkv, wo, w_gu, w_down))
+    return CoreInputs(cfg, s0, wqkv, wo, w_gu, w_down, g_attn, g_ffn,
+                      film_gamma, film_beta, w_r, b_r, e_depth, expert_bias, forced)

@@ -1,0 +1,342 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test names the passage or identity it checks.  None of them retypes the
+oracle's own formula: they use worked values printed on the pages
+(``tests/golden``), a PyTorch library implementation of an ordinary causal
+block (``tests/torch_block.py``) on the special cases where the routed core
+reduces to it, brute force, and invariants.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from runtime_routed_transformer_amd.workloads import CONFIGS, CoreConfig, generate
+from tests import torch_block
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as fh:
+        return json.load(fh)
+
+
+def tiny(**kw):
+    base = CoreConfig("pin", batch=2, n=40, d=32, n_heads=2, d_ffn=64, L=3, D=3, W=12,
+                      S=5, mlp="swiglu", dtype="fp32", seed=11)
+    return base.with_(**kw)
+
+
+# ---------------------------------------------------------------- partition
+def test_partition_worked_example():
+    g = _gold("partition_examples.json")["small"]
+    for depth, wins in g["depths"].items():
+        got = oracle.partition(g["n"], g["W"], g["S"], int(depth))
+        assert [list(w) for w in got] == wins
+
+
+def test_partition_natural_language_counts():
+    g = _gold("partition_examples.json")["natural_language"]
+    for depth in range(1, 7):
+        lens = [b - a + 1 for a, b in oracle.partition(g["n"], g["W"], g["S"], depth)]
+        want = g["odd_depth_lengths"] if depth % 2 == 1 else g["even_depth_lengths"]
+        assert lens == want
+
+
+def _pairs(n, W, S, depth):
+    w = oracle.window_ids(n, W, S, depth)
+    i = np.arange(n)
+    # count (query i, key j) with j <= i in the same window, by brute force
+    return int(sum(np.count_nonzero((w[: q + 1] == w[q])) for q in i))
+
+
+def test_mask_pair_counts():
+    g = _gold("mask_and_reach.json")["pairs"]
+    assert _pairs(g["n"], g["W"], g["S"], 1) == g["aligned"]
+    assert _pairs(g["n"], g["W"], g["S"], 2) == g["shifted"]
+    assert _pairs(g["n"], g["n"], 0, 1) == g["full_causal"]
+
+
+def test_reachability_recurrence():
+    g = _gold("mask_and_reach.json")["reach"]
+    n, W, S = g["n"], g["W"], g["S"]
+    a = np.arange(n)
+    got = []
+    for depth in range(1, 4):
+        w = oracle.window_ids(n, W, S, depth)
+        a = np.array([min(a[j] for j in range(i + 1) if w[j] == w[i]) for i in range(n)])
+        got.append(int(a[g["token"]]))
+    assert got == g["earliest"]
+    # with S = 0 no position ever reaches across the first boundary
+    a = np.arange(n)
+    for depth in range(1, 6):
+        w = oracle.window_ids(n, W, 0, depth)
+        a = np.array([min(a[j] for j in range(i + 1) if w[j] == w[i]) for i in range(n)])
+    assert a[W] == W
+
+
+@pytest.mark.parametrize("n,W,S", [(1, 4, 2), (5, 8, 3), (37, 8, 3), (64, 16, 8), (100, 7, 12), (9, 9, 0)])
+def test_partition_covers_each_token_once(n, W, S):
+    for depth in range(1, 6):
+        wins = oracle.partition(n, W, S, depth)
+        flat = [i for a, b in wins for i in range(a, b + 1)]
+        assert flat == list(range(n))
+        assert all(b - a + 1 <= W for a, b in wins)
+        # the review's closed-form bounds (Eq. 2 paragraph) hold for every ordinal
+        delta = ((depth - 1) * S) % W
+        for k, (a, b) in enumerate(wins):
+            assert a == max(0, k * W - delta) and b == min(n - 1, (k + 1) * W - delta - 1)
+    # S and S + W give the same windows; S = 0 and S = W are fixed windows
+    for depth in range(1, 6):
+        assert oracle.partition(n, W, S, depth) == oracle.partition(n, W, S + W, depth)
+        assert oracle.partition(n, W, 0, depth) == oracle.partition(n, W, W, depth) == \
+            oracle.partition(n, W, 0, 1)
+
+
+# ---------------------------------------------------------------- router
+def test_prefix_coefficients_worked_example():
+    g = _gold("router_examples.json")["prefix"]
+    n = g["n"]
+    s = np.eye(n)                       # token i carries the unit vector e_i
+    wins = oracle.partition(n, g["W"], g["S"], g["depth"])
+    r = oracle.router_inputs(s, wins, np.zeros(n))
+    np.testing.assert_allclose(r[g["window"]], g["coefficients"], rtol=0, atol=1e-15)
+
+
+def test_prefix_inputs_brute_force():
+    rng = np.random.default_rng(5)
+    n, W, S, d = 53, 8, 3, 6
+    s = rng.standard_normal((n, d))
+    e = rng.standard_normal(d)
+    for depth in range(1, 5):
+        wins = oracle.partition(n, W, S, depth)
+        r = oracle.router_inputs(s, wins, e)
+        for k in range(len(wins)):
+            if k == 0:
+                want = (e + s[0]) / 2          # first-window rule
+            else:
+                # token weights: each earlier window shares 1/k equally
+                coef = np.zeros(n)
+                for a, b in wins[:k]:
+                    coef[a:b + 1] = 1.0 / (k * (b - a + 1))
+                want = coef @ s
+            np.testing.assert_allclose(r[k], want, rtol=1e-13, atol=1e-14)
+
+
+def test_first_window_rule_hand_values():
+    s = np.zeros((4, 2))
+    s[0] = [0.0, 4.0]
+    s[1:] = 100.0                        # later tokens must not matter
+    r = oracle.router_inputs(s, oracle.partition(4, 4, 0, 1), np.array([2.0, 0.0]))
+    np.testing.assert_array_equal(r[0], [1.0, 2.0])
+
+
+def _route_probs(p, b):
+    L = len(p)
+    # an identity-free way to feed given probabilities: W_r = 0, b_r = log p
+    return oracle.route(np.zeros(4), np.zeros((L, 4), np.float32),
+                        np.log(np.asarray(p, np.float64)).astype(np.float32),
+                        np.asarray(b, np.float32))
+
+
+def test_selection_worked_example():
+    g = _gold("router_examples.json")["selection"]
+    rt = _route_probs(g["p"], g["b"])
+    assert rt.expert == g["expert"]
+    assert abs(rt.gate - g["gate"]) < 1e-6
+    np.testing.assert_allclose(rt.probs, g["p"], rtol=1e-6)
+    assert abs(rt.margin - (0.48 - 0.45)) < 1e-6
+
+
+def test_selection_invariants():
+    rng = np.random.default_rng(3)
+    L, d = 5, 16
+    w_r = (rng.standard_normal((L, d)) * 0.5).astype(np.float32)
+    r = rng.standard_normal(d)
+    base = oracle.route(r, w_r, np.zeros(L, np.float32), np.zeros(L, np.float32))
+    assert base.margin > 1e-3
+    # a constant added to every balancing bias does not change the choice or gate
+    sh = oracle.route(r, w_r, np.zeros(L, np.float32), np.full(L, 0.3, np.float32))
+    assert sh.expert == base.expert and sh.gate == base.gate
+    # a constant added to every logit bias leaves softmax unchanged (up to fp32)
+    sl = oracle.route(r, w_r, np.full(L, 2.5, np.float32), np.zeros(L, np.float32))
+    assert sl.expert == base.expert and abs(sl.gate - base.gate) < 1e-6
+    # a large bias on one expert forces it; the gate stays that expert's own probability
+    for m in range(L):
+        b = np.zeros(L, np.float32)
+        b[m] = 10.0
+        fm = oracle.route(r, w_r, np.zeros(L, np.float32), b)
+        assert fm.expert == m and fm.gate == base.probs[m]
+    # ties go to the lowest index
+    tie = _route_probs([0.25, 0.25, 0.25, 0.25], [0, 0, 0, 0])
+    assert tie.expert == 0 and tie.margin == 0.0
+    # one expert: always chosen with gate 1
+    one = oracle.route(r, w_r[:1], np.zeros(1, np.float32), np.zeros(1, np.float32))
+    assert one.expert == 0 and one.gate == 1.0 and math.isinf(one.margin)
+
+
+def test_block_param_count():
+    g = _gold("router_examples.json")["block_params"]
+    cfg = CoreConfig("p", batch=1, n=2, d=g["d"], n_heads=16, d_ffn=g["f"], L=1, D=1,
+                     W=2, S=1, mlp="swiglu", dtype="fp32", seed=0, film=False)
+    inp = generate(cfg)
+    attn = inp.wqkv[0].size + inp.wo[0].size
+    mlp = inp.w_gu[0].size + inp.w_down[0].size
+    assert (attn, mlp, attn + mlp) == (g["attention"], g["mlp"], g["total"])
+
+
+# ---------------------------------------------------------------- block
+@pytest.mark.parametrize("mlp,film", [("swiglu", True), ("swiglu", False), ("gelu", True)])
+def test_single_block_equals_library_block(mlp, film):
+    """L=1, D=1, W=n: the routed core is one ordinary causal block."""
+    cfg = tiny(L=1, D=1, n=33, W=33, S=0, mlp=mlp, film=film)
+    inp = generate(cfg)
+    res = oracle.forward(inp)
+    for b in range(cfg.batch):
+        want = torch_block.block(
+            inp.s0[b], inp.wqkv[0], inp.wo[0], inp.w_gu[0], inp.w_down[0], inp.g_attn[0],
+            inp.g_ffn[0], cfg.n_heads, mlp,
+            film=None if not film else (inp.film_gamma[0], inp.film_beta[0]))
+        np.testing.assert_allclose(res.s64[b], want, rtol=0, atol=1e-11)
+    assert (res.expert[0, :, 0] == 0).all() and (res.gate[0, :, 0] == 1.0).all()
+    # the block really changed the states (a dropped update would pass above only by luck)
+    assert np.abs(res.s64 - inp.s0).max() > 1e-2
+
+
+def test_window_attention_equals_masked_full_attention():
+    """Window attention = full attention under the mask j<=i and w(i)=w(j),
+    at every depth (aligned and shifted windows, with half windows)."""
+    cfg = tiny(L=1, D=4, n=29, W=8, S=3, film=True)
+    inp = generate(cfg)
+    res = oracle.forward(inp)
+    for b in range(cfg.batch):
+        x = inp.s0[b].astype(np.float64)
+        for depth in range(1, cfg.D + 1):
+            w = oracle.window_ids(cfg.n, cfg.W, cfg.S, depth)
+            mask = (w[:, None] == w[None, :]) & np.tril(np.ones((cfg.n, cfg.n), bool))
+            x = torch_block.block(
+                x, inp.wqkv[0], inp.wo[0], inp.w_gu[0], inp.w_down[0], inp.g_attn[0],
+                inp.g_ffn[0], cfg.n_heads, "swiglu",
+                film=(inp.film_gamma[depth - 1], inp.film_beta[depth - 1]), mask=mask)
+        np.testing.assert_allclose(res.s64[b], x, rtol=0, atol=1e-11)
+
+
+def test_rope_positions_are_relative():
+    """Window-local and document positions give the same block output: the
+    rotary scores depend only on i - j (so a kernel may use either)."""
+    cfg = tiny(L=1, D=1, n=16, W=16, S=0)
+    inp = generate(cfg)
+    p = oracle.expert_params(inp, 0)
+    x = inp.s0[0].astype(np.float64)
+    y0 = oracle.expert_block(x, p, cfg.n_heads, np.arange(16), None, 1e-6, 1e4)
+    y1 = oracle.expert_block(x, p, cfg.n_heads, np.arange(16) + 3000, None, 1e-6, 1e4)
+    np.testing.assert_allclose(y0, y1, rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("film", [False, True])
+def test_forced_single_expert_is_looped_model(film):
+    """Forced ids all m with gate 1 on one window (W=n, S=0): D applications of E_m."""
+    cfg = tiny(L=3, D=4, n=24, W=24, S=0, film=film)
+    inp = generate(cfg)
+    m = 2
+    forced = np.full((cfg.D, cfg.batch, cfg.k_max), m, np.int32)
+    gate = np.ones((cfg.D, cfg.batch, cfg.k_max), np.float32)
+    res = oracle.forward(inp, forced_expert=forced, forced_gate=gate)
+    for b in range(cfg.batch):
+        x = inp.s0[b].astype(np.float64)
+        for depth in range(cfg.D):
+            x = torch_block.block(
+                x, inp.wqkv[m], inp.wo[m], inp.w_gu[m], inp.w_down[m], inp.g_attn[m],
+                inp.g_ffn[m], cfg.n_heads, "swiglu",
+                film=None if not film else (inp.film_gamma[depth], inp.film_beta[depth]))
+        np.testing.assert_allclose(res.s64[b], x, rtol=0, atol=1e-11)
+    assert (res.expert[:, :, 0] == m).all()
+
+
+# ---------------------------------------------------------------- whole-core invariants
+def test_stride_invariants():
+    inp = generate(tiny())
+    cfg = inp.cfg
+    a = oracle.forward(inp)
+    inp.cfg = cfg.with_(S=cfg.S + cfg.W)
+    b = oracle.forward(inp)
+    np.testing.assert_array_equal(a.s, b.s)
+    np.testing.assert_array_equal(a.expert, b.expert)
+    # with one depth the offset is 0 for every stride
+    outs = []
+    for S in (0, 1, 5, 7):
+        inp.cfg = cfg.with_(D=1, S=S)
+        outs.append(oracle.forward(inp).s)
+    for o in outs[1:]:
+        np.testing.assert_array_equal(outs[0], o)
+
+
+def test_causality_and_prefix_truncation():
+    """Outputs before p and routes of windows that end before p do not see
+    positions >= p (review, 'Deriving prefix-only routing')."""
+    inp = generate(tiny(n=48))
+    cfg = inp.cfg
+    base = oracle.forward(inp)
+    p = 23
+    pert = generate(cfg)
+    pert.s0 = inp.s0.copy()
+    pert.s0[:, p:] += np.random.default_rng(9).standard_normal(pert.s0[:, p:].shape).astype(np.float32)
+    got = oracle.forward(pert)
+    np.testing.assert_allclose(got.s64[:, :p], base.s64[:, :p], rtol=0, atol=1e-12)
+    assert np.abs(got.s64[:, p:] - base.s64[:, p:]).max() > 1e-3
+    for depth in range(1, cfg.D + 1):
+        for k, (a0, a1) in enumerate(oracle.partition(cfg.n, cfg.W, cfg.S, depth)):
+            if a1 < p:
+                assert (got.expert[depth - 1, :, k] == base.expert[depth - 1, :, k]).all()
+                np.testing.assert_array_equal(got.gate[depth - 1, :, k], base.gate[depth - 1, :, k])
+    # running only the prefix of a document gives the same outputs and routes
+    pre = oracle.forward(inp, rows=[1], n_tokens=p)
+    np.testing.assert_allclose(pre.s64[0], base.s64[1, :p], rtol=0, atol=1e-12)
+
+
+def test_gate_zero_is_identity_and_own_path_is_free_path():
+    inp = generate(tiny())
+    cfg = inp.cfg
+    zero = np.zeros((cfg.D, cfg.batch, cfg.k_max), np.float32)
+    res0 = oracle.forward(inp, forced_gate=zero)
+    np.testing.assert_array_equal(res0.s, inp.s0)
+    free = oracle.forward(inp)
+    again = oracle.forward(inp, forced_expert=free.expert)
+    np.testing.assert_array_equal(again.s, free.s)
+    np.testing.assert_array_equal(again.gate, free.gate)
+
+
+def test_batch_rows_are_independent():
+    inp = generate(tiny(batch=3))
+    full = oracle.forward(inp)
+    for b in range(3):
+        one = oracle.forward(inp, rows=[b])
+        np.testing.assert_array_equal(one.s[0], full.s[b])
+        np.testing.assert_array_equal(one.expert[:, 0], full.expert[:, b])
+
+
+def test_gate_scales_only_the_update():
+    """Algorithm 1 blend: s + alpha (E(s) - s); halving alpha halves the update
+    on a single depth (gate applied to E(s) - s, not to E(s))."""
+    inp = generate(tiny(D=1))
+    cfg = inp.cfg
+    g1 = np.full((1, cfg.batch, cfg.k_max), 0.5, np.float32)
+    g2 = np.full((1, cfg.batch, cfg.k_max), 0.25, np.float32)
+    u1 = oracle.forward(inp, forced_gate=g1).s64 - inp.s0
+    u2 = oracle.forward(inp, forced_gate=g2).s64 - inp.s0
+    np.testing.assert_allclose(u2 * 2.0, u1, rtol=1e-12, atol=1e-13)
+
+
+def test_path_layout_and_padding():
+    cfg = CONFIGS[0]
+    res = oracle.forward(generate(cfg))
+    for depth in range(1, cfg.D + 1):
+        K = len(oracle.partition(cfg.n, cfg.W, cfg.S, depth))
+        assert (res.expert[depth - 1, :, :K] >= 0).all()
+        assert (res.expert[depth - 1, :, K:] == -1).all()
+        assert (res.gate[depth - 1, :, K:] == 0).all()
+        assert (res.gate[depth - 1, :, :K] > 0).all()
