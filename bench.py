@@ -1,0 +1,136 @@
+"""Routed-core forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mid_bf16]
+
+One step = one whole routed-core forward (all D depths: windowing, router,
+bucketing, grouped GEMMs, window attention, gated blend) over one batch of
+synthetic inputs already resident in HBM.  Prints one JSON line with
+tokens/s, the roofline of the dominant kernel (measured with HIP events on
+the launch stream), the grouped GEMMs' MFMA utilisation, and the CPU
+oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "routed-core fwd tokens/sec on 1 MI355X; MFMA util % of bf16 peak"
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+
+
+def gemm_flops(cfg):
+    """Algorithmic FLOPs per launch (one depth) of each grouped GEMM kind."""
+    T, d, f = cfg.tokens, cfg.d, cfg.d_ffn
+    up = 2 * f if cfg.mlp == "swiglu" else f
+    return {"gemm_qkv": 2.0 * T * 3 * d * d, "gemm_o": 2.0 * T * d * d,
+            "gemm_gate_up": 2.0 * T * up * d, "gemm_down": 2.0 * T * d * f}
+
+
+def cpu_baseline(inp, seconds_hint=20.0):
+    """The oracle (unchanged) on one document of the workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    cfg = inp.cfg
+    n_tok = cfg.n
+    t0 = time.perf_counter()
+    oracle.forward(inp, forced_expert=inp.forced_expert, rows=[0], n_tokens=n_tok)
+    dt = time.perf_counter() - t0
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"document 0 of {cfg.name}: {n_tok} tokens x {cfg.D} depths, "
+                      f"numpy float64, {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mid_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--timing-steps", type=int, default=3)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the routed core shards over documents with no forward communication; "
+              "the multi-GPU path is not built)", file=sys.stderr)
+        return 2
+
+    import torch
+    from runtime_routed_transformer_amd import binding as B
+    from runtime_routed_transformer_amd.core import DeviceCore
+    from runtime_routed_transformer_amd.workloads import CONFIG_BY_NAME, generate
+
+    cfg = CONFIG_BY_NAME[args.workload]
+    inp = generate(cfg)
+    if cfg.bias_mode == "skewed":
+        from oracle.calibrate import apply_skew  # input preparation only
+        apply_skew(inp)
+    core = DeviceCore(inp, "cuda:0")
+    core.set_forcing(inp.forced_expert)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        core.forward(stream=stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        core.forward(stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tokens_per_s = cfg.tokens / (ms / 1e3)
+
+    # per-kernel durations: HIP events recorded by the library on the launch stream
+    B.lol_core_timing_collect()  # drop anything stale
+    B.lol_core_timing_enable(True)
+    for _ in range(args.timing_steps):
+        core.forward(stream=stream)
+    torch.cuda.synchronize()
+    B.lol_core_timing_enable(False)
+    kt = B.lol_core_timing_collect()
+    flops = gemm_flops(cfg)
+    per_kernel = {k: {"ms_avg": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items() if v[1]}
+    dominant = max(flops, key=lambda k: kt[k][0])
+    dom_ms = kt[dominant][0] / kt[dominant][1]
+    achieved = flops[dominant] / (dom_ms / 1e3) / 1e12
+    gemm_ms = sum(kt[k][0] for k in flops) / args.timing_steps
+    gemm_tflops = sum(flops.values()) * cfg.D / (gemm_ms / 1e3) / 1e12
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) states, N(0,0.02) weights)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "n": cfg.n, "d": cfg.d,
+                   "heads": cfg.n_heads, "d_ffn": cfg.d_ffn, "mlp": cfg.mlp, "L": cfg.L,
+                   "D": cfg.D, "W": cfg.W, "S": cfg.S, "film": cfg.film,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel_ms_avg": dom_ms,
+                     "flops_per_launch": flops[dominant]},
+        "mfma_util_pct": 100.0 * gemm_tflops / PEAK_BF16_TFLOPS,
+        "grouped_gemm_tflops": gemm_tflops,
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

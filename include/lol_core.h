@@ -1,0 +1,172 @@
+/*
+ * lol_core.h -- C ABI of the Library-of-Layers routed-core forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes: the routed core of Algorithm 1 in the paper "Library of
+ * Layers (LoL): Adaptively Ordering Transformer Layers at Runtime"
+ * (Appendix A), i.e. for every routed depth l = 1..D:
+ *   - windows of W tokens whose boundaries shift by ((l-1) S) mod W
+ *     (paper Sec. 3.2.1; review "Library of Layers: Routing Whole
+ *     Transformer Blocks at Runtime", Eq. 2);
+ *   - per window a router input built from earlier windows' means, or from
+ *     the first token and a depth vector for window 0 (paper Sec. 3.2.2;
+ *     review Eq. 4);
+ *   - a linear router in fp32, softmax, and a top-1 choice of one library
+ *     block by probability plus balancing bias, gated by the unbiased
+ *     probability (paper App. A, loss-free balancing; review Eq. 5; blog
+ *     "Library of Layers: a transformer that picks its own layer order",
+ *     "How the order is chosen");
+ *   - the chosen pre-norm block (RMSNorm with depth FiLM, bias-free QKV,
+ *     RoPE, attention causal inside the window, output projection, SwiGLU
+ *     or GELU MLP; paper App. A; review Eqs. 1 and 7);
+ *   - the gated residual blend s + alpha (E(s) - s) (Algorithm 1, blend
+ *     step; blog "The forward pass, term by term", step 5).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked DEVICE point to device memory of the current HIP
+ *     device; pointers marked HOST to host memory.  The caller owns every
+ *     buffer; the library allocates nothing inside lol_core_forward.
+ *   - lol_core_forward is asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL = the default stream).  Host-checkable errors are returned
+ *     before anything is launched.  No C++ exception crosses the ABI.
+ *   - Layouts are row-major.  Each batch row is one document.
+ *   - K_max = ceil(n / W) + 1 bounds the windows of any depth.
+ */
+#ifndef LOL_CORE_H
+#define LOL_CORE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOL_OK = 0,
+  LOL_EINVAL = 1,        /* a NULL required pointer or an invalid size/argument */
+  LOL_EUNSUPPORTED = 2,  /* valid for the method, outside what these kernels handle */
+  LOL_EWORKSPACE = 3,    /* workspace NULL or smaller than lol_core_workspace_size */
+  LOL_EHIP = 4           /* a HIP runtime call failed (launch, event, copy) */
+} lol_status;
+
+typedef enum { LOL_FP32 = 0, LOL_BF16 = 1 } lol_dtype;
+typedef enum { LOL_MLP_SWIGLU = 0, LOL_MLP_GELU = 1 } lol_mlp;
+
+/* Sizes and numeric settings of one routed core.
+ *   batch, n      documents and tokens per document (T = batch * n rows)
+ *   d, n_heads    model width and heads; d_head = d / n_heads must be 32 or 64
+ *   d_ffn         MLP hidden width f
+ *   L, D          library size (1..64) and routed depth (>= 1)
+ *   W, S          window size (>= 1) and per-depth boundary shift (>= 0)
+ *   mlp           lol_mlp: SwiGLU (three matrices) or exact-erf GELU (two)
+ *   dtype         lol_dtype of the block matrices and of the GEMM/attention
+ *                 operands; the residual stream, norms, softmax and router
+ *                 are fp32 in both modes
+ *   rms_eps       RMSNorm epsilon (> 0)
+ *   rope_theta    RoPE base (window-local positions, rotate-half pairs
+ *                 (j, j + d_head/2)); 0 disables RoPE
+ * Supported sizes: d % 64 == 0 and d_ffn % 64 == 0; in bf16 mode also
+ * d % 128 == 0 and d_ffn % 128 == 0. */
+typedef struct {
+  int32_t batch, n, d, n_heads, d_ffn, L, D, W, S;
+  int32_t mlp;
+  int32_t dtype;
+  float rms_eps;
+  float rope_theta;
+} lol_core_config;
+
+/* The shared library {E_1..E_L} (DEVICE).  Matrices are [out][in]:
+ *   wqkv   [L][3d][d]  rows W_q, then W_k, then W_v
+ *   wo     [L][d][d]
+ *   w_gu   SwiGLU [L][2f][d] (W_gate rows, then W_up rows); GELU [L][f][d]
+ *   w_down [L][d][f]
+ * element type = cfg.dtype (bf16 stored as raw 16-bit patterns).
+ *   g_attn, g_ffn          [L][d] fp32 RMSNorm gains of each expert
+ *   film_gamma, film_beta  [D][2][d] fp32 depth FiLM (index 0 = attention
+ *                          norm, 1 = MLP norm), shared by all experts; both
+ *                          NULL = no FiLM (gamma 1, beta 0). */
+typedef struct {
+  const void *wqkv, *wo, *w_gu, *w_down;
+  const float *g_attn, *g_ffn;
+  const float *film_gamma, *film_beta;
+} lol_library;
+
+/* The router (DEVICE, fp32), tied across depths:
+ *   w_r [L][d], b_r [L] (NULL = 0): logits z = W_r r + b_r
+ *   e_depth [D][d]: the learned vector of each depth used by window 0
+ *   expert_bias [L] (NULL = 0): balancing bias, used for the choice only */
+typedef struct {
+  const float *w_r, *b_r, *e_depth, *expert_bias;
+} lol_router;
+
+/* Per-window routing path (DEVICE), [D][batch][K_max], indexed by depth,
+ * document and window ordinal; slots k >= K_l hold expert -1, gate 0,
+ * margin 0.  expert: chosen library index; gate: alpha applied to the
+ * update; margin: (a+b)_top1 - (a+b)_top2 of the free router (+inf when
+ * L = 1).  Any member may be NULL (not written). */
+typedef struct {
+  int32_t *expert;
+  float *gate;
+  float *margin;
+} lol_path;
+
+/* ceil(n / W) + 1, or -1 for an invalid config.  HOST, pure. */
+int32_t lol_core_k_max(const lol_core_config *cfg);
+
+/* LOL_OK if the config is valid and supported, else the status that
+ * lol_core_forward would return for it.  HOST, pure. */
+lol_status lol_core_validate(const lol_core_config *cfg);
+
+/* Bytes of device workspace lol_core_forward needs for cfg (0 if invalid).
+ * HOST, pure. */
+size_t lol_core_workspace_size(const lol_core_config *cfg);
+
+/* The routed-core forward pass (Algorithm 1 of the paper, routed depths).
+ *   s0            DEVICE [batch][n][d] fp32, the prelude output s^(0)
+ *   lib, rt       library and router, as above
+ *   forced_expert DEVICE [D][batch][K_max] int32 or NULL; entry >= 0
+ *                 replaces the router's choice for that window (the router
+ *                 still runs), -1 leaves it free.  Ids >= L are treated as
+ *                 free and raise LOL_FLAG_BAD_FORCED_ID (lol_core_read_flags).
+ *   forced_gate   DEVICE [D][batch][K_max] fp32 or NULL; a non-NaN entry
+ *                 replaces alpha, NaN keeps the router's probability of the
+ *                 applied expert (the review's note on forcing a path:
+ *                 forcing supplies an expert id and a gate)
+ *   s_out         DEVICE [batch][n][d] fp32, receives s^(D); may equal s0
+ *   path          HOST struct of DEVICE pointers, or NULL
+ *   workspace     DEVICE scratch of workspace_bytes >= lol_core_workspace_size
+ *   stream        hipStream_t (as void*) the work is queued on
+ * Returns LOL_OK once the work is queued.  Inputs must stay unchanged and
+ * the workspace unused by others until the stream reaches the end of it. */
+lol_status lol_core_forward(const lol_core_config *cfg, const float *s0,
+                            const lol_library *lib, const lol_router *rt,
+                            const int32_t *forced_expert, const float *forced_gate,
+                            float *s_out, const lol_path *path,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device-side error flags of the last forward that used `workspace`. */
+#define LOL_FLAG_BAD_FORCED_ID 1u
+/* Copies the flag word to *flags (HOST) and clears it; synchronises
+ * `stream`. */
+lol_status lol_core_read_flags(void *workspace, uint32_t *flags, void *stream);
+
+/* Kernel-duration instrumentation, for measurement only.  While enabled,
+ * lol_core_forward records a HIP event pair on its stream around every
+ * kernel launch.  lol_core_timing_collect waits for those events and adds,
+ * per kernel kind, the summed milliseconds and the launch count to ms[k] and
+ * launches[k] (HOST arrays of LOL_KERNEL_KINDS), then forgets them. */
+#define LOL_KERNEL_KINDS 12
+lol_status lol_core_timing_enable(int32_t enable);
+lol_status lol_core_timing_collect(double *ms, int32_t *launches);
+/* Name of kernel kind k (0 <= k < LOL_KERNEL_KINDS), or NULL. */
+const char *lol_core_kernel_name(int32_t kind);
+
+/* Static description of a status code. */
+const char *lol_status_str(lol_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOL_CORE_H */

@@ -1,0 +1,136 @@
+"""ctypes binding of liblol_core (include/lol_core.h), names as in the C ABI.
+
+Argument marshalling only: every step of the routed core runs in the HIP
+kernels of ``csrc/``.  Loading fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_double, c_float, c_int32, c_size_t, c_uint32, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "liblol_core.so")
+
+LOL_OK, LOL_EINVAL, LOL_EUNSUPPORTED, LOL_EWORKSPACE, LOL_EHIP = range(5)
+LOL_FP32, LOL_BF16 = 0, 1
+LOL_MLP_SWIGLU, LOL_MLP_GELU = 0, 1
+LOL_FLAG_BAD_FORCED_ID = 1
+LOL_KERNEL_KINDS = 12
+
+# every function the header declares, with (restype, argtypes)
+_SIGNATURES = {}
+
+
+class LolError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+class lol_core_config(ctypes.Structure):
+    _fields_ = [(name, c_int32) for name in
+                ("batch", "n", "d", "n_heads", "d_ffn", "L", "D", "W", "S", "mlp", "dtype")] + \
+               [("rms_eps", c_float), ("rope_theta", c_float)]
+
+
+class lol_library(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in
+                ("wqkv", "wo", "w_gu", "w_down", "g_attn", "g_ffn", "film_gamma", "film_beta")]
+
+
+class lol_router(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in ("w_r", "b_r", "e_depth", "expert_bias")]
+
+
+class lol_path(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in ("expert", "gate", "margin")]
+
+
+_SIGNATURES.update({
+    "lol_core_k_max": (c_int32, [POINTER(lol_core_config)]),
+    "lol_core_validate": (c_int32, [POINTER(lol_core_config)]),
+    "lol_core_workspace_size": (c_size_t, [POINTER(lol_core_config)]),
+    "lol_core_forward": (c_int32, [POINTER(lol_core_config), c_void_p, POINTER(lol_library),
+                                   POINTER(lol_router), c_void_p, c_void_p, c_void_p,
+                                   POINTER(lol_path), c_void_p, c_size_t, c_void_p]),
+    "lol_core_read_flags": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
+    "lol_core_timing_enable": (c_int32, [c_int32]),
+    "lol_core_timing_collect": (c_int32, [POINTER(c_double), POINTER(c_int32)]),
+    "lol_core_kernel_name": (c_char_p, [c_int32]),
+    "lol_status_str": (c_char_p, [c_int32]),
+})
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblol_core.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m runtime_routed_transformer_amd.build_lib` "
+                "(there is no fallback implementation)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def exported_symbols():
+    return sorted(_SIGNATURES)
+
+
+def status_str(status: int) -> str:
+    return load().lol_status_str(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != LOL_OK:
+        raise LolError(status, what)
+
+
+def lol_core_k_max(cfg: lol_core_config) -> int:
+    return load().lol_core_k_max(ctypes.byref(cfg))
+
+
+def lol_core_validate(cfg: lol_core_config) -> int:
+    return load().lol_core_validate(ctypes.byref(cfg))
+
+
+def lol_core_workspace_size(cfg: lol_core_config) -> int:
+    return load().lol_core_workspace_size(ctypes.byref(cfg))
+
+
+def lol_core_forward(cfg, s0, lib, rt, forced_expert, forced_gate, s_out, path, workspace,
+                     workspace_bytes, stream) -> int:
+    """Pointers are ints (device addresses) or None; lib/rt/path are structs."""
+    return load().lol_core_forward(ctypes.byref(cfg), s0, ctypes.byref(lib), ctypes.byref(rt),
+                                   forced_expert, forced_gate, s_out,
+                                   ctypes.byref(path) if path is not None else None,
+                                   workspace, workspace_bytes, stream)
+
+
+def lol_core_read_flags(workspace, stream) -> int:
+    out = c_uint32(0)
+    _check(load().lol_core_read_flags(workspace, ctypes.byref(out), stream), "lol_core_read_flags")
+    return int(out.value)
+
+
+def lol_core_timing_enable(enable: bool) -> None:
+    _check(load().lol_core_timing_enable(1 if enable else 0), "lol_core_timing_enable")
+
+
+def lol_core_timing_collect():
+    ms = (c_double * LOL_KERNEL_KINDS)()
+    cnt = (c_int32 * LOL_KERNEL_KINDS)()
+    _check(load().lol_core_timing_collect(ms, cnt), "lol_core_timing_collect")
+    return {lol_core_kernel_name(k): (float(ms[k]), int(cnt[k])) for k in range(LOL_KERNEL_KINDS)}
+
+
+def lol_core_kernel_name(kind: int):
+    name = load().lol_core_kernel_name(kind)
+    return None if name is None else name.decode()

@@ -1,0 +1,100 @@
+"""Device-resident routed core: PyTorch holds device memory and streams, the
+HIP library (through ``binding``) does all of the computation."""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .workloads import CoreConfig, CoreInputs, bf16_bits
+
+
+def make_config(cfg: CoreConfig) -> B.lol_core_config:
+    return B.lol_core_config(
+        batch=cfg.batch, n=cfg.n, d=cfg.d, n_heads=cfg.n_heads, d_ffn=cfg.d_ffn, L=cfg.L,
+        D=cfg.D, W=cfg.W, S=cfg.S,
+        mlp=B.LOL_MLP_SWIGLU if cfg.mlp == "swiglu" else B.LOL_MLP_GELU,
+        dtype=B.LOL_BF16 if cfg.dtype == "bf16" else B.LOL_FP32,
+        rms_eps=cfg.rms_eps, rope_theta=cfg.rope_theta)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+class DeviceCore:
+    """Uploads one workload's inputs and runs ``lol_core_forward`` on them."""
+
+    def __init__(self, inp: CoreInputs, device: str = "cuda:0"):
+        self.inp = inp
+        self.cfg = inp.cfg
+        self.device = torch.device(device)
+        self.ccfg = make_config(self.cfg)
+        status = B.lol_core_validate(self.ccfg)
+        if status != B.LOL_OK:
+            raise B.LolError(status, f"config {self.cfg.name}")
+        dev = self.device
+
+        def f32(a):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+        def weight(a):
+            if self.cfg.dtype == "bf16":
+                return torch.from_numpy(bf16_bits(a).view(np.int16)).to(dev)
+            return f32(a)
+
+        self.s0 = f32(inp.s0)
+        self.w = {k: weight(getattr(inp, k)) for k in ("wqkv", "wo", "w_gu", "w_down")}
+        self.g_attn, self.g_ffn = f32(inp.g_attn), f32(inp.g_ffn)
+        self.film_gamma, self.film_beta = f32(inp.film_gamma), f32(inp.film_beta)
+        self.w_r, self.b_r = f32(inp.w_r), f32(inp.b_r)
+        self.e_depth, self.expert_bias = f32(inp.e_depth), f32(inp.expert_bias)
+        self.lib = B.lol_library(
+            wqkv=_ptr(self.w["wqkv"]), wo=_ptr(self.w["wo"]), w_gu=_ptr(self.w["w_gu"]),
+            w_down=_ptr(self.w["w_down"]), g_attn=_ptr(self.g_attn), g_ffn=_ptr(self.g_ffn),
+            film_gamma=_ptr(self.film_gamma), film_beta=_ptr(self.film_beta))
+        self.rt = B.lol_router(w_r=_ptr(self.w_r), b_r=_ptr(self.b_r), e_depth=_ptr(self.e_depth),
+                               expert_bias=_ptr(self.expert_bias))
+        self.k_max = B.lol_core_k_max(self.ccfg)
+        self.ws_bytes = B.lol_core_workspace_size(self.ccfg)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        shape = (self.cfg.D, self.cfg.batch, self.k_max)
+        self.path_expert = torch.empty(shape, dtype=torch.int32, device=dev)
+        self.path_gate = torch.empty(shape, dtype=torch.float32, device=dev)
+        self.path_margin = torch.empty(shape, dtype=torch.float32, device=dev)
+        self.path = B.lol_path(expert=_ptr(self.path_expert), gate=_ptr(self.path_gate),
+                               margin=_ptr(self.path_margin))
+        self.s_out = torch.empty_like(self.s0)
+        self.forced_expert = None
+        self.forced_gate = None
+
+    def set_forcing(self, forced_expert=None, forced_gate=None) -> None:
+        shape = (self.cfg.D, self.cfg.batch, self.k_max)
+        self.forced_expert = None if forced_expert is None else torch.from_numpy(
+            np.ascontiguousarray(np.broadcast_to(forced_expert, shape), np.int32)).to(self.device)
+        self.forced_gate = None if forced_gate is None else torch.from_numpy(
+            np.ascontiguousarray(np.broadcast_to(forced_gate, shape), np.float32)).to(self.device)
+
+    def forward(self, s_in: Optional[torch.Tensor] = None, s_out: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """Queue one forward on ``stream`` (default: torch's current stream)."""
+        s_in = self.s0 if s_in is None else s_in
+        s_out = self.s_out if s_out is None else s_out
+        st = (stream or torch.cuda.current_stream(self.device)).cuda_stream
+        status = B.lol_core_forward(self.ccfg, s_in.data_ptr(), self.lib, self.rt,
+                                    _ptr(self.forced_expert), _ptr(self.forced_gate),
+                                    s_out.data_ptr(), self.path, self.workspace.data_ptr(),
+                                    self.ws_bytes, st)
+        if status != B.LOL_OK:
+            raise B.LolError(status, "lol_core_forward")
+        return s_out
+
+    def flags(self, stream: Optional[torch.cuda.Stream] = None) -> int:
+        st = (stream or torch.cuda.current_stream(self.device)).cuda_stream
+        return B.lol_core_read_flags(self.workspace.data_ptr(), st)
+
+    def path_numpy(self):
+        return (self.path_expert.cpu().numpy(), self.path_gate.cpu().numpy(),
+                self.path_margin.cpu().numpy())

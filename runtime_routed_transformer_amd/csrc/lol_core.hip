@@ -1,0 +1,312 @@
+// Host side of liblol_core: argument validation, workspace layout, the
+// per-depth launch sequence of the routed core, flags and timing.
+//
+// The depth loop follows Algorithm 1 of the paper "Library of Layers (LoL)"
+// (App. A), routed depths only: partition, window means, router per window,
+// the chosen block on each window, gated blend.  All windows of a depth read
+// s^(l-1) and the blend writes each token exactly once, after every kernel
+// of the depth that reads s^(l-1) has run (review "Library of Layers:
+// Routing Whole Transformer Blocks at Runtime", reader's Algorithm 1, lines
+// 4 and 12), so the residual stream is updated in place.
+#include <math.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <vector>
+
+#include "lol_internal.h"
+
+namespace lol {
+int max_slots();
+
+namespace {
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+lol_status validate(const lol_core_config *c) {
+  if (!c) return LOL_EINVAL;
+  if (c->batch < 1 || c->n < 1 || c->d < 1 || c->n_heads < 1 || c->d_ffn < 1 || c->L < 1 ||
+      c->D < 1 || c->W < 1 || c->S < 0)
+    return LOL_EINVAL;
+  if (c->mlp != LOL_MLP_SWIGLU && c->mlp != LOL_MLP_GELU) return LOL_EINVAL;
+  if (c->dtype != LOL_FP32 && c->dtype != LOL_BF16) return LOL_EINVAL;
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta >= 0.f) || isinf(c->rope_theta)) return LOL_EINVAL;
+  if (c->d % c->n_heads != 0) return LOL_EINVAL;
+  const int dh = c->d / c->n_heads;
+  if (dh != 32 && dh != 64) return LOL_EUNSUPPORTED;
+  if (c->d % 64 != 0 || c->d_ffn % 64 != 0) return LOL_EUNSUPPORTED;
+  if (c->dtype == LOL_BF16 && (c->d % 128 != 0 || c->d_ffn % 128 != 0)) return LOL_EUNSUPPORTED;
+  if (c->L > kMaxExperts) return LOL_EUNSUPPORTED;
+  const long long kmax = (c->n + (long long)c->W - 1) / c->W + 1;
+  if ((long long)c->batch * kmax > max_slots()) return LOL_EUNSUPPORTED;
+  if ((long long)c->batch * c->n >= (1LL << 30)) return LOL_EUNSUPPORTED;  // int32 row ids
+  if (c->d > 16384) return LOL_EUNSUPPORTED;  // the router input is staged in 64 KiB of LDS
+  return LOL_OK;
+}
+
+Plan make_plan(const lol_core_config *c) {
+  Plan p;
+  p.cfg = *c;
+  p.K_max = (c->n + c->W - 1) / c->W + 1;
+  p.d_head = c->d / c->n_heads;
+  p.T = c->batch * c->n;
+  p.n_slots = c->batch * p.K_max;
+  p.act_bytes = c->dtype == LOL_BF16 ? 2 : 4;
+  return p;
+}
+
+// ---- timing instrumentation ----
+struct TimingRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct Launch {
+  hipStream_t st;
+  bool timing;
+  int kind;
+  hipEvent_t a = nullptr;
+  Launch(hipStream_t s, bool t, int k) : st(s), timing(t), kind(k) {
+    if (timing) {
+      std::lock_guard<std::mutex> lk(g_tmu);
+      a = take_event();
+      if (a) hipEventRecord(a, st);
+    }
+  }
+  hipError_t done(hipError_t err) {
+    if (timing && a) {
+      std::lock_guard<std::mutex> lk(g_tmu);
+      hipEvent_t b = take_event();
+      if (b) {
+        hipEventRecord(b, st);
+        g_recs.push_back({kind, a, b});
+      } else {
+        g_event_pool.push_back(a);
+      }
+    }
+    return err;
+  }
+};
+
+}  // namespace
+
+size_t workspace_layout(const Plan &p, char *base, Workspace *ws) {
+  const lol_core_config &c = p.cfg;
+  const size_t T = (size_t)p.T, d = (size_t)c.d, f = (size_t)c.d_ffn;
+  const size_t ns = (size_t)p.n_slots;
+  const int max_mtiles = (p.T + kTileM - 1) / kTileM + c.L;
+  size_t off = 0;
+  auto carve = [&](size_t bytes) -> char * {
+    char *ptr = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return ptr;
+  };
+  Workspace w;
+  w.flags = (uint32_t *)carve(16);
+  w.mu = (float *)carve(ns * d * 4);
+  w.win_exp = (int32_t *)carve(ns * 4);
+  w.win_gate = (float *)carve(ns * 4);
+  w.win_row0 = (int32_t *)carve(ns * 4);
+  w.ecount = (int32_t *)carve((size_t)(c.L + 1) * 4);
+  w.toff = (int32_t *)carve((size_t)(c.L + 1) * 4);
+  w.mtile = (int32_t *)carve((size_t)max_mtiles * 8);
+  w.row_tok = (int32_t *)carve(T * 4);
+  w.row_pos = (int32_t *)carve(T * 4);
+  w.row_exp = (int32_t *)carve(T * 4);
+  w.row_gate = (float *)carve(T * 4);
+  w.rope_cs = (float *)carve((size_t)c.W * (p.d_head / 2) * 2 * 4);
+  w.u = carve(T * d * p.act_bytes);
+  w.qkv = carve(T * 3 * d * p.act_bytes);
+  w.o = carve(T * d * p.act_bytes);
+  w.h = (float *)carve(T * d * 4);
+  w.hid = carve(T * f * p.act_bytes);
+  w.max_mtiles = max_mtiles;
+  if (ws) *ws = w;
+  return off;
+}
+
+}  // namespace lol
+
+using namespace lol;
+
+extern "C" {
+
+int32_t lol_core_k_max(const lol_core_config *cfg) {
+  if (validate(cfg) == LOL_EINVAL) return -1;
+  return (cfg->n + cfg->W - 1) / cfg->W + 1;
+}
+
+lol_status lol_core_validate(const lol_core_config *cfg) { return validate(cfg); }
+
+size_t lol_core_workspace_size(const lol_core_config *cfg) {
+  if (validate(cfg) != LOL_OK) return 0;
+  return workspace_layout(make_plan(cfg), nullptr, nullptr);
+}
+
+lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const lol_library *lib,
+                            const lol_router *rt, const int32_t *forced_expert,
+                            const float *forced_gate, float *s_out, const lol_path *path,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  const lol_status vs = validate(cfg);
+  if (vs != LOL_OK) return vs;
+  if (!s0 || !s_out || !lib || !rt) return LOL_EINVAL;
+  if (!lib->wqkv || !lib->wo || !lib->w_gu || !lib->w_down || !lib->g_attn || !lib->g_ffn)
+    return LOL_EINVAL;
+  if ((lib->film_gamma == nullptr) != (lib->film_beta == nullptr)) return LOL_EINVAL;
+  if (!rt->w_r || !rt->e_depth) return LOL_EINVAL;
+  const Plan p = make_plan(cfg);
+  const size_t need = workspace_layout(p, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return LOL_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return LOL_EINVAL;
+  Workspace ws;
+  workspace_layout(p, static_cast<char *>(workspace), &ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  bool timing;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    timing = g_timing;
+  }
+  const lol_core_config &c = p.cfg;
+  const size_t d = c.d, f = c.d_ffn;
+  const bool glu = c.mlp == LOL_MLP_SWIGLU;
+  hipError_t err;
+#define LOL_TRY(kind, call)                           \
+  do {                                                \
+    Launch _l(st, timing, kind);                      \
+    err = _l.done(call);                              \
+    if (err != hipSuccess) return LOL_EHIP;           \
+  } while (0)
+
+  if (s_out != s0)
+    LOL_TRY(KK_COPY, hipMemcpyAsync(s_out, s0, (size_t)p.T * d * sizeof(float),
+                                    hipMemcpyDeviceToDevice, st));
+  float *s = s_out;
+  LOL_TRY(KK_COPY, launch_setup(p, ws, st));
+  for (int l = 0; l < c.D; ++l) {
+    DepthGeom g;
+    g.depth = l;
+    g.delta = (int)(((long long)l * c.S) % c.W);
+    g.K = (c.n - 1 + g.delta) / c.W + 1;
+    LOL_TRY(KK_POOL, launch_pool(p, g, s, ws.mu, st));
+    LOL_TRY(KK_ROUTE, launch_route(p, g, s, ws, *rt, forced_expert, forced_gate, path, st));
+    LOL_TRY(KK_BUCKET, launch_bucket(p, g, ws, st));
+    LOL_TRY(KK_ROWMETA, launch_rowmeta(p, g, ws, st));
+    LOL_TRY(KK_NORM_ATTN, launch_norm(p, g, 0, s, *lib, ws, st));
+    GemmArgs a{};
+    a.A = ws.u;
+    a.Wt = lib->wqkv;
+    a.N = 3 * c.d;
+    a.K = c.d;
+    a.w_expert_stride = (long long)3 * d * d;
+    a.epi = EPI_STORE;
+    a.C = ws.qkv;
+    LOL_TRY(KK_GEMM_QKV, launch_gemm(p, ws, a, st));
+    LOL_TRY(KK_ATTN, launch_attention(p, g, ws, st));
+    a = GemmArgs{};
+    a.A = ws.o;
+    a.Wt = lib->wo;
+    a.N = c.d;
+    a.K = c.d;
+    a.w_expert_stride = (long long)d * d;
+    a.epi = EPI_RESID;
+    a.C = ws.h;
+    a.s = s;
+    LOL_TRY(KK_GEMM_O, launch_gemm(p, ws, a, st));
+    LOL_TRY(KK_NORM_FFN, launch_norm(p, g, 1, s, *lib, ws, st));
+    a = GemmArgs{};
+    a.A = ws.u;
+    a.Wt = lib->w_gu;
+    a.N = c.d_ffn;
+    a.K = c.d;
+    a.w_expert_stride = (long long)(glu ? 2 : 1) * f * d;
+    a.glu_offset = c.d_ffn;
+    a.epi = glu ? EPI_SWIGLU : EPI_GELU;
+    a.C = ws.hid;
+    LOL_TRY(KK_GEMM_GATE_UP, launch_gemm(p, ws, a, st));
+    a = GemmArgs{};
+    a.A = ws.hid;
+    a.Wt = lib->w_down;
+    a.N = c.d;
+    a.K = c.d_ffn;
+    a.w_expert_stride = (long long)d * f;
+    a.epi = EPI_BLEND;
+    a.s = s;
+    a.h = ws.h;
+    LOL_TRY(KK_GEMM_DOWN, launch_gemm(p, ws, a, st));
+  }
+#undef LOL_TRY
+  return LOL_OK;
+}
+
+lol_status lol_core_read_flags(void *workspace, uint32_t *flags, void *stream) {
+  if (!workspace || !flags) return LOL_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t *dflags = static_cast<uint32_t *>(workspace);  // flags are the first workspace word
+  if (hipMemcpyAsync(flags, dflags, sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return LOL_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return LOL_EHIP;
+  if (hipMemsetAsync(dflags, 0, sizeof(uint32_t), st) != hipSuccess) return LOL_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return LOL_EHIP;
+  return LOL_OK;
+}
+
+lol_status lol_core_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+  return LOL_OK;
+}
+
+lol_status lol_core_timing_collect(double *ms, int32_t *launches) {
+  if (!ms || !launches) return LOL_EINVAL;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  lol_status status = LOL_OK;
+  for (TimingRec &r : g_recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+      status = LOL_EHIP;
+    else {
+      ms[r.kind] += t;
+      launches[r.kind] += 1;
+    }
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return status;
+}
+
+const char *lol_core_kernel_name(int32_t kind) {
+  static const char *names[LOL_KERNEL_KINDS] = {
+      "copy_s0",  "pool",     "route",  "bucket", "rowmeta",      "norm_attn",
+      "gemm_qkv", "win_attn", "gemm_o", "norm_ffn", "gemm_gate_up", "gemm_down"};
+  if (kind < 0 || kind >= LOL_KERNEL_KINDS) return nullptr;
+  return names[kind];
+}
+
+const char *lol_status_str(lol_status status) {
+  switch (status) {
+    case LOL_OK: return "ok";
+    case LOL_EINVAL: return "invalid argument";
+    case LOL_EUNSUPPORTED: return "unsupported configuration";
+    case LOL_EWORKSPACE: return "workspace missing or too small";
+    case LOL_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Internal declarations shared by the HIP translation units of liblol_core.
+// Not part of the C ABI (that is include/lol_core.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lol_core.h"
+
+namespace lol {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+// Kernel kinds for the timing instrumentation (order = lol_core_kernel_name).
+enum KernelKind {
+  KK_COPY = 0,
+  KK_POOL,
+  KK_ROUTE,
+  KK_BUCKET,
+  KK_ROWMETA,
+  KK_NORM_ATTN,
+  KK_GEMM_QKV,
+  KK_ATTN,
+  KK_GEMM_O,
+  KK_NORM_FFN,
+  KK_GEMM_GATE_UP,
+  KK_GEMM_DOWN,
+};
+
+// Rows of one M tile of the grouped GEMMs (bucketing builds the tile table
+// for this height; every GEMM of the block uses it).
+constexpr int kTileM = 128;
+constexpr int kMaxExperts = 64;
+
+// Window geometry of one depth, computed on the host.
+struct DepthGeom {
+  int depth;      // 0-based depth index l-1
+  int delta;      // ((l-1) S) mod W
+  int K;          // windows per document at this depth
+};
+
+// Device buffers carved from the caller's workspace.
+struct Workspace {
+  uint32_t *flags;     // [4]
+  float *mu;           // [B*K_max][d]       window means
+  int32_t *win_exp;    // [B*K_max]          expert of each window slot (-1 = none)
+  float *win_gate;     // [B*K_max]
+  int32_t *win_row0;   // [B*K_max]          first grouped row of each window slot
+  int32_t *ecount;     // [L+1]              windows per expert (+ total)
+  int32_t *toff;       // [L+1]              grouped-row offset of each expert
+  int32_t *mtile;      // [max_mtiles][2]    (expert, first row) per M tile, expert -1 = idle
+  int32_t *row_tok;    // [T]                token (b*n + i) of each grouped row
+  int32_t *row_pos;    // [T]                window-local position
+  int32_t *row_exp;    // [T]
+  float *row_gate;     // [T]
+  float *rope_cs;      // [W][d_head/2][2]   cos, sin of p * theta^(-2j/d_head)
+  void *u;             // [T][d]   act       normed input of a GEMM
+  void *qkv;           // [T][3d]  act
+  void *o;             // [T][d]   act       attention output
+  float *h;            // [T][d]   fp32      after the attention sublayer
+  void *hid;           // [T][f]   act       MLP hidden
+  int max_mtiles;
+};
+
+struct Plan {
+  lol_core_config cfg;
+  int K_max, d_head, T, n_slots;
+  size_t act_bytes;    // 2 (bf16) or 4 (fp32)
+};
+
+size_t workspace_layout(const Plan &p, char *base, Workspace *ws);
+
+// ---- launchers (all asynchronous on `st`) ----
+hipError_t launch_pool(const Plan &p, const DepthGeom &g, const float *s, float *mu, hipStream_t st);
+hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const Workspace &ws,
+                        const lol_router &rt, const int32_t *forced_expert, const float *forced_gate,
+                        const lol_path *path, hipStream_t st);
+hipError_t launch_bucket(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st);
+hipError_t launch_rowmeta(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st);
+// clears the flag word and builds the RoPE table
+hipError_t launch_setup(const Plan &p, const Workspace &ws, hipStream_t st);
+// which = 0: u = FiLM(Norm_attn(s[row_tok])) ; which = 1: u = FiLM(Norm_ffn(h))
+hipError_t launch_norm(const Plan &p, const DepthGeom &g, int which, const float *s,
+                       const lol_library &lib, const Workspace &ws, hipStream_t st);
+hipError_t launch_attention(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st);
+
+enum GemmEpilogue {
+  EPI_STORE = 0,    // C (act) = acc
+  EPI_RESID = 1,    // h (fp32) = s[row_tok] + acc
+  EPI_SWIGLU = 2,   // hid (act) = silu(acc_gate) * acc_up
+  EPI_GELU = 3,     // hid (act) = gelu(acc)
+  EPI_BLEND = 4,    // s[row_tok] += gate * (h + acc - s[row_tok])
+};
+
+struct GemmArgs {
+  const void *A;        // [T][K] act, grouped rows
+  const void *Wt;       // [L][N_w][K] weights (act type)
+  int N;                // output columns of C (for SwiGLU: f)
+  int K;
+  long long w_expert_stride;  // elements between experts
+  int glu_offset;       // SwiGLU: row offset of W_up inside an expert (= f)
+  GemmEpilogue epi;
+  void *C;              // output (act or fp32 depending on epilogue)
+  float *s;             // residual stream (RESID, BLEND)
+  const float *h;       // BLEND
+};
+hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st);
+
+}  // namespace lol

@@ -1,0 +1,101 @@
+"""CPU checks of the C ABI: the built library loads, exports every function
+include/lol_core.h declares, and rejects invalid configurations and
+arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from runtime_routed_transformer_amd import binding as B
+from runtime_routed_transformer_amd.core import make_config
+from runtime_routed_transformer_amd.workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lol_core.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lol_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("liblol_core.so is not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert declared == B.exported_symbols()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        B._lib_saved = B._lib
+        try:
+            B._lib = None
+            B.load(str(tmp_path / "nope.so"))
+        finally:
+            B._lib = B._lib_saved
+
+
+def test_sizes_and_validation(lib):
+    for cfg in CONFIGS:
+        c = make_config(cfg)
+        assert B.lol_core_validate(c) == B.LOL_OK, cfg.name
+        assert B.lol_core_k_max(c) == -(-cfg.n // cfg.W) + 1
+        assert B.lol_core_workspace_size(c) > 0
+    base = CONFIGS[1]
+    bad = {
+        "W": 0, "S": -1, "n_heads": 3, "L": 0, "D": 0, "batch": 0, "n": 0, "d_ffn": 0,
+    }
+    for k, v in bad.items():
+        c = make_config(base)
+        setattr(c, k, v)
+        assert B.lol_core_validate(c) == B.LOL_EINVAL, k
+        assert B.lol_core_workspace_size(c) == 0
+    c = make_config(base); c.L = 65
+    assert B.lol_core_validate(c) == B.LOL_EUNSUPPORTED
+    c = make_config(base); c.n_heads = 4      # d_head 128
+    assert B.lol_core_validate(c) == B.LOL_EUNSUPPORTED
+    c = make_config(base); c.d_ffn = 192       # bf16 needs multiples of 128
+    assert B.lol_core_validate(c) == B.LOL_EUNSUPPORTED
+    c = make_config(base); c.mlp = 7
+    assert B.lol_core_validate(c) == B.LOL_EINVAL
+    c = make_config(base); c.rms_eps = 0.0
+    assert B.lol_core_validate(c) == B.LOL_EINVAL
+
+
+def test_forward_rejects_bad_arguments_before_launch(lib):
+    c = make_config(CONFIGS[0])
+    libw = B.lol_library(wqkv=16, wo=16, w_gu=16, w_down=16, g_attn=16, g_ffn=16)
+    rt = B.lol_router(w_r=16, e_depth=16)
+    ws = B.lol_core_workspace_size(c)
+    # NULL s0
+    assert B.lol_core_forward(c, None, libw, rt, None, None, 16, None, 256, ws, None) == B.LOL_EINVAL
+    # NULL weight
+    libn = B.lol_library(wqkv=None, wo=16, w_gu=16, w_down=16, g_attn=16, g_ffn=16)
+    assert B.lol_core_forward(c, 16, libn, rt, None, None, 16, None, 256, ws, None) == B.LOL_EINVAL
+    # FiLM half given
+    libf = B.lol_library(wqkv=16, wo=16, w_gu=16, w_down=16, g_attn=16, g_ffn=16, film_gamma=16)
+    assert B.lol_core_forward(c, 16, libf, rt, None, None, 16, None, 256, ws, None) == B.LOL_EINVAL
+    # workspace too small / missing
+    assert B.lol_core_forward(c, 16, libw, rt, None, None, 16, None, 256, ws - 1, None) == B.LOL_EWORKSPACE
+    assert B.lol_core_forward(c, 16, libw, rt, None, None, 16, None, None, ws, None) == B.LOL_EWORKSPACE
+    # invalid config
+    c.W = 0
+    assert B.lol_core_forward(c, 16, libw, rt, None, None, 16, None, 256, ws, None) == B.LOL_EINVAL
+
+
+def test_status_and_kernel_names(lib):
+    assert B.status_str(B.LOL_OK) == "ok"
+    assert "workspace" in B.status_str(B.LOL_EWORKSPACE)
+    names = [B.lol_core_kernel_name(k) for k in range(B.LOL_KERNEL_KINDS)]
+    assert all(names) and len(set(names)) == len(names)
+    assert B.lol_core_kernel_name(B.LOL_KERNEL_KINDS) is None

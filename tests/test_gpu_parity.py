@@ -1,0 +1,125 @@
+"""GPU parity: the HIP routed core (through the C ABI) against the CPU oracle.
+
+Sizes the oracle finishes in seconds but that still span several GEMM tiles,
+several windows per document and ragged tails (half windows, partial M
+tiles); then every workload at its full size in the launch configuration
+the benchmark times, compared on sampled documents and a document prefix
+(by the core's causality those outputs equal the full run's), and edge cases.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from runtime_routed_transformer_amd.workloads import CONFIGS, CoreConfig
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(rep):
+    print(rep, flush=True)
+    sys.stdout.flush()
+    assert rep.ok, str(rep)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from runtime_routed_transformer_amd import binding
+    binding.load()
+
+
+SCALED = [
+    CONFIGS[0],
+    CONFIGS[1].scaled(2, 384),
+    CONFIGS[2].scaled(2, 640),
+    CONFIGS[3].scaled(2, 640),
+    CONFIGS[4].scaled(3, 224),
+]
+
+
+@pytest.mark.parametrize("cfg", SCALED, ids=lambda c: c.name)
+def test_parity_scaled(cfg):
+    print(f"[parity] {cfg.name}", flush=True)
+    _report(parity.run(parity.prepare(cfg)))
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_parity_full_size_sampled(idx):
+    cfg = CONFIGS[idx]
+    print(f"[parity-full] {cfg.name}", flush=True)
+    inp = parity.prepare(cfg)
+    _report(parity.run(inp, rows=[0, cfg.batch - 1], n_tokens=min(cfg.n, 3 * cfg.W + cfg.W // 2)))
+
+
+EDGE = [
+    CoreConfig("edge_fp32_ragged", batch=2, n=37, d=64, n_heads=2, d_ffn=128, L=3, D=4, W=5, S=3,
+               mlp="swiglu", dtype="fp32", seed=21),
+    CoreConfig("edge_bf16_ragged", batch=2, n=150, d=128, n_heads=2, d_ffn=256, L=3, D=3, W=40,
+               S=13, mlp="swiglu", dtype="bf16", seed=22),
+    CoreConfig("edge_bf16_gelu_nofilm", batch=1, n=200, d=256, n_heads=4, d_ffn=512, L=2, D=2,
+               W=96, S=48, mlp="gelu", dtype="bf16", seed=23, film=False),
+    CoreConfig("edge_one_token", batch=1, n=1, d=128, n_heads=2, d_ffn=128, L=2, D=2, W=4, S=1,
+               mlp="swiglu", dtype="bf16", seed=24),
+    CoreConfig("edge_window_longer_than_doc", batch=3, n=50, d=128, n_heads=4, d_ffn=256, L=4,
+               D=3, W=64, S=40, mlp="swiglu", dtype="bf16", seed=25),
+    CoreConfig("edge_stride_zero_L1", batch=2, n=96, d=64, n_heads=1, d_ffn=64, L=1, D=3, W=32,
+               S=0, mlp="gelu", dtype="fp32", seed=26, rope_theta=0.0),
+    CoreConfig("edge_stride_ge_window", batch=2, n=100, d=128, n_heads=2, d_ffn=128, L=3, D=3,
+               W=16, S=37, mlp="swiglu", dtype="bf16", seed=27),
+    CoreConfig("edge_dh32_bf16", batch=2, n=130, d=128, n_heads=4, d_ffn=384, L=5, D=2, W=64,
+               S=32, mlp="swiglu", dtype="bf16", seed=28),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=lambda c: c.name)
+def test_parity_edge_cases(cfg):
+    print(f"[parity-edge] {cfg.name}", flush=True)
+    _report(parity.run(parity.prepare(cfg)))
+
+
+def test_gate_zero_identity_and_determinism_and_inplace():
+    import torch
+    from runtime_routed_transformer_amd.core import DeviceCore
+    cfg = CONFIGS[1].scaled(2, 256)
+    inp = parity.prepare(cfg)
+    core = DeviceCore(inp)
+    core.set_forcing(forced_gate=np.zeros((cfg.D, cfg.batch, core.k_max), np.float32))
+    out = core.forward().cpu().numpy()
+    np.testing.assert_array_equal(out, inp.s0)
+    core.set_forcing()
+    a = core.forward().clone()
+    b = core.forward().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "two runs differ"
+    s = core.s0.clone()
+    core.forward(s_in=s, s_out=s)
+    torch.cuda.synchronize()
+    assert torch.equal(s, a), "in-place run differs"
+
+
+def test_forced_own_path_and_bad_forced_id_flag():
+    import torch
+    from runtime_routed_transformer_amd import binding
+    from runtime_routed_transformer_amd.core import DeviceCore
+    cfg = CONFIGS[2].scaled(1, 512)
+    inp = parity.prepare(cfg)
+    core = DeviceCore(inp)
+    free = core.forward().clone()
+    pe, _, _ = core.path_numpy()
+    core.set_forcing(forced_expert=pe)
+    again = core.forward().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(free, again)
+    assert core.flags() == 0
+    bad = np.full_like(pe, -1)
+    bad[0, 0, 0] = cfg.L + 3
+    core.set_forcing(forced_expert=bad)
+    out = core.forward().clone()
+    assert core.flags() & binding.LOL_FLAG_BAD_FORCED_ID
+    assert torch.equal(out, free)    # the bad id was treated as free
+    assert core.flags() == 0         # reading clears the flag
