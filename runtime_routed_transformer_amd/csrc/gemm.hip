@@ -92,18 +92,21 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel: tile 128 (rows) x 128 (weight rows) x 64 (k), 4 waves in
-// a 2 x 2 grid, each wave 64 x 64 outputs as 2 x 2 blocks of 32 x 32.
+// bf16 MFMA kernel.  4 waves in a 2 x 2 grid; each wave owns TM x TN blocks of
+// 32 x 32 outputs, so the block tile is (64 TM) x (64 TN) and k advances by
+// BK = 64 per stage.  Stage k+1 is fetched from global memory into registers
+// while stage k is multiplied out of one of two LDS buffers; one barrier per
+// stage.
 // ---------------------------------------------------------------------------
-constexpr int BM = kTileM;  // 128
-constexpr int BN = 128;
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;  // padded LDS row (144 B): conflict-free 16-B fragment reads
 
-template <int EPI>
+template <int EPI, int TM, int TN>
 __global__ void __launch_bounds__(256) k_gemm_bf16(GemmParams P) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * LDK];
+  constexpr int BMt = 64 * TM, BNt = 64 * TN;
+  constexpr int AV = BMt / 32, BV = BNt / 32;  // 16-byte vectors per thread per stage
+  constexpr int STAGE = (BMt + BNt) * LDK;     // elements per LDS buffer
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   const int mt = blockIdx.x / P.n_tiles_n, nt = blockIdx.x % P.n_tiles_n;
   const int e = P.mtile[2 * mt];
   if (e < 0) return;
@@ -113,70 +116,84 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(GemmParams P) {
   const bf16_t *A = reinterpret_cast<const bf16_t *>(P.A);
   const bf16_t *Wt = reinterpret_cast<const bf16_t *>(P.Wt) + (size_t)e * P.w_stride;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int kv = tid & 7, r_base = tid >> 3;  // each thread: one 16-byte chunk of rows r_base + 32 i
 
-  // global -> register staging: 4 x 16 B of A and of B per thread per k-step
-  const bf16_t *a_src[4];
-  const bf16_t *b_src[4];
-  int lds_off[4];
+  const bf16_t *a_src[AV];
+  const bf16_t *b_src[BV];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = tid + i * 256, r = v >> 3, kv = v & 7;
-    const int arow = min(row0 + r, row_end - 1);
+  for (int i = 0; i < AV; ++i) {
+    const int arow = min(row0 + r_base + 32 * i, row_end - 1);
     a_src[i] = A + (size_t)arow * K + kv * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < BV; ++i) {
+    const int r = r_base + 32 * i;
     int wrow;
     if (EPI == EPI_SWIGLU) {
-      const int wc = r >> 6, within = r & 63;
-      const int hidden = nt * 64 + wc * 32 + (within & 31);
-      wrow = (within < 32 ? 0 : P.glu_offset) + hidden;
+      constexpr int WR = TN * 32, HALF = TN * 16;  // weight rows per wave column, gate half
+      const int wc = r / WR, within = r % WR;
+      const int hidden = nt * (BNt / 2) + wc * HALF + (within % HALF);
+      wrow = (within < HALF ? 0 : P.glu_offset) + hidden;
     } else {
-      wrow = nt * BN + r;
+      wrow = nt * BNt + r;
     }
     b_src[i] = Wt + (size_t)wrow * K + kv * 8;
-    lds_off[i] = r * LDK + kv * 8;
   }
-  uint4 ra[4], rb[4];
+  uint4 ra[AV], rb[BV];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = *reinterpret_cast<const uint4 *>(a_src[i]);
-    rb[i] = *reinterpret_cast<const uint4 *>(b_src[i]);
+  for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const uint4 *>(a_src[i]);
+#pragma unroll
+  for (int i = 0; i < BV; ++i) rb[i] = *reinterpret_cast<const uint4 *>(b_src[i]);
+  {
+    bf16_t *As = smem, *Bs = smem + BMt * LDK;
+#pragma unroll
+    for (int i = 0; i < AV; ++i) *reinterpret_cast<uint4 *>(&As[(r_base + 32 * i) * LDK + kv * 8]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BV; ++i) *reinterpret_cast<uint4 *>(&Bs[(r_base + 32 * i) * LDK + kv * 8]) = rb[i];
   }
+  __syncthreads();
+
   const int wm = wave >> 1, wn = wave & 1;
-  f32x16 acc[2][2];
+  f32x16 acc[TN][TM];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TN; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < TM; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
   const int frow = lane & 31, fk = (lane >> 5) * 8;
-  for (int k0 = 0; k0 < K; k0 += BK) {
+  const int nk = K / BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    // prefetch stage kt+1 (the last iteration re-reads the final stage, unused)
+    const int knext = min(kt + 1, nk - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4 *>(&As[lds_off[i]]) = ra[i];
-      *reinterpret_cast<uint4 *>(&Bs[lds_off[i]]) = rb[i];
-    }
-    __syncthreads();
-    if (k0 + BK < K) {
+    for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + knext);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + k0 + BK);
-        rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + k0 + BK);
-      }
-    }
+    for (int i = 0; i < BV; ++i) rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + knext);
+    const bf16_t *As = smem + cur * STAGE, *Bs = As + BMt * LDK;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 fw[2], fx[2];
+      bf16x8 fw[TN], fx[TM];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        fw[i] = *reinterpret_cast<const bf16x8 *>(&Bs[(wn * 64 + i * 32 + frow) * LDK + kk + fk]);
-        fx[i] = *reinterpret_cast<const bf16x8 *>(&As[(wm * 64 + i * 32 + frow) * LDK + kk + fk]);
-      }
+      for (int i = 0; i < TN; ++i)
+        fw[i] = *reinterpret_cast<const bf16x8 *>(&Bs[(wn * TN * 32 + i * 32 + frow) * LDK + kk + fk]);
 #pragma unroll
-      for (int in = 0; in < 2; ++in)
+      for (int i = 0; i < TM; ++i)
+        fx[i] = *reinterpret_cast<const bf16x8 *>(&As[(wm * TM * 32 + i * 32 + frow) * LDK + kk + fk]);
 #pragma unroll
-        for (int im = 0; im < 2; ++im)
+      for (int in = 0; in < TN; ++in)
+#pragma unroll
+        for (int im = 0; im < TM; ++im)
           acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[in], fx[im], acc[in][im], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      bf16_t *An = smem + (cur ^ 1) * STAGE, *Bn = An + BMt * LDK;
+#pragma unroll
+      for (int i = 0; i < AV; ++i) *reinterpret_cast<uint4 *>(&An[(r_base + 32 * i) * LDK + kv * 8]) = ra[i];
+#pragma unroll
+      for (int i = 0; i < BV; ++i) *reinterpret_cast<uint4 *>(&Bn[(r_base + 32 * i) * LDK + kv * 8]) = rb[i];
     }
     __syncthreads();
   }
@@ -184,24 +201,29 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(GemmParams P) {
   // lane holds C[m = im*32 + lane%32][n = in*32 + g*8 + 4*(lane/32) + j], g, j < 4
   const int cq = (lane >> 5) * 4;
 #pragma unroll
-  for (int im = 0; im < 2; ++im) {
-    const int row = row0 + wm * 64 + im * 32 + (lane & 31);
+  for (int im = 0; im < TM; ++im) {
+    const int row = row0 + wm * TM * 32 + im * 32 + (lane & 31);
     if (row >= row_end) continue;
     if (EPI == EPI_SWIGLU) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int hcol = nt * 64 + wn * 32 + g * 8 + cq;
-        float gv[4], uv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { gv[j] = acc[0][im][g * 4 + j]; uv[j] = acc[1][im][g * 4 + j]; }
-        store_glu4<bf16_t>(P, row, hcol, gv, uv);
-      }
-    } else {
-#pragma unroll
-      for (int in = 0; in < 2; ++in)
+      for (int in = 0; in < TN / 2; ++in)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = nt * BN + wn * 64 + in * 32 + g * 8 + cq;
+          const int hcol = nt * (BNt / 2) + wn * TN * 16 + in * 32 + g * 8 + cq;
+          float gv[4], uv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            gv[j] = acc[in][im][g * 4 + j];
+            uv[j] = acc[in + TN / 2][im][g * 4 + j];
+          }
+          store_glu4<bf16_t>(P, row, hcol, gv, uv);
+        }
+    } else {
+#pragma unroll
+      for (int in = 0; in < TN; ++in)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = nt * BNt + wn * TN * 32 + in * 32 + g * 8 + cq;
           epilogue4<EPI, bf16_t>(P, row, col, acc[in][im][g * 4], acc[in][im][g * 4 + 1],
                                  acc[in][im][g * 4 + 2], acc[in][im][g * 4 + 3]);
         }
@@ -213,6 +235,7 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(GemmParams P) {
 // fp32 kernel: tile 128 rows x 64 logical columns x 16 k; each thread
 // computes 8 rows x 4 columns (x2 for SwiGLU: gate and up).
 // ---------------------------------------------------------------------------
+constexpr int BM = kTileM;  // 128 rows per fp32 tile
 constexpr int FBN = 64;
 constexpr int FBK = 16;
 
@@ -308,9 +331,28 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.s = a.s;
   P.h = a.h;
   if (p.cfg.dtype == LOL_BF16) {
-    const int cols_per_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-    P.n_tiles_n = a.N / cols_per_tile;
-    hipLaunchKernelGGL(k_gemm_bf16<EPI>, dim3(ws.max_mtiles * P.n_tiles_n), dim3(256), 0, st, P);
+    // 256 x 256 tiles for the wide projections (QKV, gate/up); 256 x 128 for
+    // the d-wide ones (O, down), which otherwise leave CUs idle in the tail
+    const bool wide = (EPI == EPI_SWIGLU ? 2 * a.N : a.N) >= 2048;
+    if (wide && a.N % (EPI == EPI_SWIGLU ? 128 : 256) == 0) {
+      constexpr int TM = 4, TN = 4;
+      P.mtile = ws.mtile2;
+      P.n_tiles_n = (EPI == EPI_SWIGLU) ? a.N / (32 * TN) : a.N / (64 * TN);
+      const size_t smem = 2 * (size_t)(64 * TM + 64 * TN) * LDK * sizeof(bf16_t);
+      hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, TM, TN>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      hipLaunchKernelGGL((k_gemm_bf16<EPI, TM, TN>), dim3(ws.max_mtiles2 * P.n_tiles_n), dim3(256),
+                         smem, st, P);
+    } else {
+      constexpr int TM = 4, TN = 2;
+      P.mtile = ws.mtile2;
+      P.n_tiles_n = (EPI == EPI_SWIGLU) ? a.N / (32 * TN) : a.N / (64 * TN);
+      const size_t smem = 2 * (size_t)(64 * TM + 64 * TN) * LDK * sizeof(bf16_t);
+      hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, TM, TN>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      hipLaunchKernelGGL((k_gemm_bf16<EPI, TM, TN>), dim3(ws.max_mtiles2 * P.n_tiles_n), dim3(256),
+                         smem, st, P);
+    }
   } else {
     P.n_tiles_n = a.N / FBN;
     hipLaunchKernelGGL(k_gemm_f32<EPI>, dim3(ws.max_mtiles * P.n_tiles_n), dim3(256), 0, st, P);

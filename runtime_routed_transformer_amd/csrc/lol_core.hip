@@ -110,6 +110,7 @@ size_t workspace_layout(const Plan &p, char *base, Workspace *ws) {
   const size_t T = (size_t)p.T, d = (size_t)c.d, f = (size_t)c.d_ffn;
   const size_t ns = (size_t)p.n_slots;
   const int max_mtiles = (p.T + kTileM - 1) / kTileM + c.L;
+  const int max_mtiles2 = (p.T + kTileM2 - 1) / kTileM2 + c.L;
   size_t off = 0;
   auto carve = [&](size_t bytes) -> char * {
     char *ptr = base ? base + off : nullptr;
@@ -125,6 +126,7 @@ size_t workspace_layout(const Plan &p, char *base, Workspace *ws) {
   w.ecount = (int32_t *)carve((size_t)(c.L + 1) * 4);
   w.toff = (int32_t *)carve((size_t)(c.L + 1) * 4);
   w.mtile = (int32_t *)carve((size_t)max_mtiles * 8);
+  w.mtile2 = (int32_t *)carve((size_t)max_mtiles2 * 8);
   w.row_tok = (int32_t *)carve(T * 4);
   w.row_pos = (int32_t *)carve(T * 4);
   w.row_exp = (int32_t *)carve(T * 4);
@@ -136,6 +138,7 @@ size_t workspace_layout(const Plan &p, char *base, Workspace *ws) {
   w.h = (float *)carve(T * d * 4);
   w.hid = carve(T * f * p.act_bytes);
   w.max_mtiles = max_mtiles;
+  w.max_mtiles2 = max_mtiles2;
   if (ws) *ws = w;
   return off;
 }

@@ -27,9 +27,10 @@ enum KernelKind {
   KK_GEMM_DOWN,
 };
 
-// Rows of one M tile of the grouped GEMMs (bucketing builds the tile table
-// for this height; every GEMM of the block uses it).
+// Rows of one M tile of the grouped GEMMs.  Bucketing builds one tile table
+// per height: kTileM rows and kTileM2 rows.
 constexpr int kTileM = 128;
+constexpr int kTileM2 = 256;
 constexpr int kMaxExperts = 64;
 
 // Window geometry of one depth, computed on the host.
@@ -48,7 +49,8 @@ struct Workspace {
   int32_t *win_row0;   // [B*K_max]          first grouped row of each window slot
   int32_t *ecount;     // [L+1]              windows per expert (+ total)
   int32_t *toff;       // [L+1]              grouped-row offset of each expert
-  int32_t *mtile;      // [max_mtiles][2]    (expert, first row) per M tile, expert -1 = idle
+  int32_t *mtile;      // [max_mtiles][2]    (expert, first row) per kTileM-row tile, -1 = idle
+  int32_t *mtile2;     // [max_mtiles2][2]   the same for kTileM2-row tiles
   int32_t *row_tok;    // [T]                token (b*n + i) of each grouped row
   int32_t *row_pos;    // [T]                window-local position
   int32_t *row_exp;    // [T]
@@ -59,7 +61,7 @@ struct Workspace {
   void *o;             // [T][d]   act       attention output
   float *h;            // [T][d]   fp32      after the attention sublayer
   void *hid;           // [T][f]   act       MLP hidden
-  int max_mtiles;
+  int max_mtiles, max_mtiles2;
 };
 
 struct Plan {

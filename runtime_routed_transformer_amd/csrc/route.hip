@@ -151,13 +151,14 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t *__restrict__ win
                                                  int32_t *__restrict__ win_row0,
                                                  int32_t *__restrict__ ecount,
                                                  int32_t *__restrict__ toff_out,
-                                                 int32_t *__restrict__ mtile, int max_mtiles, int n,
+                                                 int32_t *__restrict__ mtile, int max_mtiles,
+                                                 int32_t *__restrict__ mtile2, int max_mtiles2, int n,
                                                  int W, int delta, int K, int K_max, int n_slots,
                                                  int L) {
   __shared__ int s_exp[kMaxSlots];
   __shared__ int s_len[kMaxSlots];
   __shared__ int cnt_w[kMaxExperts], cnt_t[kMaxExperts];
-  __shared__ int toff[kMaxExperts + 1], moff[kMaxExperts + 1];
+  __shared__ int toff[kMaxExperts + 1], moff[kMaxExperts + 1], moff2[kMaxExperts + 1];
   const int tid = threadIdx.x;
   for (int i = tid; i < kMaxExperts; i += blockDim.x) { cnt_w[i] = 0; cnt_t[i] = 0; }
   for (int slot = tid; slot < n_slots; slot += blockDim.x) {
@@ -176,16 +177,19 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t *__restrict__ win
   }
   __syncthreads();
   if (tid == 0) {
-    int t = 0, m = 0, w = 0;
+    int t = 0, m = 0, m2 = 0, w = 0;
     for (int e = 0; e < L; ++e) {
       toff[e] = t;
       moff[e] = m;
+      moff2[e] = m2;
       t += cnt_t[e];
       m += (cnt_t[e] + kTileM - 1) / kTileM;
+      m2 += (cnt_t[e] + kTileM2 - 1) / kTileM2;
       w += cnt_w[e];
     }
     toff[L] = t;
     moff[L] = m;
+    moff2[L] = m2;
     ecount[L] = w;
   }
   __syncthreads();
@@ -210,6 +214,16 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t *__restrict__ win
     }
     mtile[2 * i] = e;
     mtile[2 * i + 1] = row0;
+  }
+  for (int i = tid; i < max_mtiles2; i += blockDim.x) {
+    int e = -1, row0 = 0;
+    if (i < moff2[L]) {
+      e = 0;
+      while (moff2[e + 1] <= i) ++e;
+      row0 = toff[e] + (i - moff2[e]) * kTileM2;
+    }
+    mtile2[2 * i] = e;
+    mtile2[2 * i + 1] = row0;
   }
 }
 
@@ -276,7 +290,7 @@ hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const
 
 hipError_t launch_bucket(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {
   hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, st, ws.win_exp, ws.win_row0, ws.ecount,
-                     ws.toff, ws.mtile, ws.max_mtiles, p.cfg.n, p.cfg.W, g.delta, g.K, p.K_max,
+                     ws.toff, ws.mtile, ws.max_mtiles, ws.mtile2, ws.max_mtiles2, p.cfg.n, p.cfg.W, g.delta, g.K, p.K_max,
                      p.n_slots, p.cfg.L);
   return hipGetLastError();
 }
