@@ -156,6 +156,243 @@ __global__ void __launch_bounds__(64) k_attn_simt(const act_t *__restrict__ qkv,
   for (int c = 0; c < DH; ++c) st<act_t>(op + c, acc[c] * il);
 }
 
+// bf16 window-causal attention on MFMA (v_mfma_f32_32x32x16_bf16).
+// Block = (window, head, chunk of 256 queries), 4 waves.  Keys and values
+// stream through LDS in chunks of 256 keys (K row-major with RoPE applied,
+// V transposed).  Each wave owns query blocks of 32 (wave w takes blocks w
+// and 7-w of the chunk, which balances the causal triangle) and computes
+// S^T = K Q^T, so every lane holds one query's scores for 16 of 32 keys:
+// the online softmax needs one exchange with the lane 32 apart.  Then
+// O^T += V^T P^T, with the key order inside each 16-key MFMA step permuted
+// to match where the scores already sit in the lane.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+template <int DH>
+__global__ void __launch_bounds__(256) k_attn_mfma(const bf16_t *__restrict__ qkv,
+                                                   bf16_t *__restrict__ o,
+                                                   const int32_t *__restrict__ win_exp,
+                                                   const int32_t *__restrict__ win_row0,
+                                                   const float *__restrict__ rope_cs, int n, int d,
+                                                   int W, int delta, int K_max, float qscale,
+                                                   int use_rope) {
+  constexpr int CH = 256;           // keys / queries per chunk
+  constexpr int LDKR = DH + 8;      // K row stride (elements)
+  constexpr int LDV = CH + 4;       // V^T row stride: 2-bank reads hit 32 distinct bank pairs
+  constexpr int HALF = DH / 2;
+  constexpr int KS = DH / 16;       // MFMA k-steps over the head dimension
+  constexpr int DB = DH / 32;       // 32-wide output blocks over the head dimension
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[CH * LDKR];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[DH * LDV];
+  const int slot = blockIdx.x, h = blockIdx.y, qc = blockIdx.z;
+  if (win_exp[slot] < 0) return;
+  const int k = slot % K_max;
+  const int start = max(0, k * W - delta);
+  const int len = min(n - 1, (k + 1) * W - delta - 1) - start + 1;
+  const int q_begin = qc * CH;
+  if (q_begin >= len) return;
+  const int base = win_row0[slot];
+  const size_t ld3 = (size_t)3 * d;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hl = lane >> 5, col = lane & 31;
+
+  // ---- this wave's two query blocks: Q fragments (RoPE, scale) in registers
+  int qblk[2] = {wave, 7 - wave};
+  bf16x8_t qf[2][KS];
+  float m_run[2], l_run[2];
+  f32x16_t acc[2][DB];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int qpos = q_begin + qblk[b] * 32 + col;         // window-local query position
+    const int qrow = min(qpos, len - 1);
+    const bf16_t *qp = qkv + (size_t)(base + qrow) * ld3 + h * DH;
+    float x[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 raw = *reinterpret_cast<const uint4 *>(qp + ks * 16 + hl * 8);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[ks][2 * j] = __uint_as_float(w[j] << 16);
+        x[ks][2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+    if (use_rope) {
+      const float *cs = rope_cs + (size_t)qrow * HALF * 2;
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int dd = ks * 16 + hl * 8 + j;                // < HALF; partner dd + HALF
+          const float c0 = cs[2 * dd], s0 = cs[2 * dd + 1];
+          const float x1 = x[ks][j], x2 = x[ks + KS / 2][j];
+          x[ks][j] = x1 * c0 - x2 * s0;
+          x[ks + KS / 2][j] = x1 * s0 + x2 * c0;
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[b][ks][j] = (__bf16)(x[ks][j] * qscale);
+    m_run[b] = -INFINITY;
+    l_run[b] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][db][i] = 0.f;
+  }
+
+  for (int kc = 0; kc <= qc; ++kc) {
+    const int k_begin = kc * CH;
+    __syncthreads();
+    // ---- stage K (RoPE) row-major and V transposed; zero rows past the window
+    {
+      const int kpos = k_begin + tid;
+      float x[DH];
+      if (kpos < len) {
+        const bf16_t *kp = qkv + (size_t)(base + kpos) * ld3 + d + h * DH;
+#pragma unroll
+        for (int c = 0; c < DH; c += 8) {
+          const uint4 raw = *reinterpret_cast<const uint4 *>(kp + c);
+          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[c + 2 * j] = __uint_as_float(w[j] << 16);
+            x[c + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+          }
+        }
+        if (use_rope) {
+          const float *cs = rope_cs + (size_t)kpos * HALF * 2;
+#pragma unroll
+          for (int j = 0; j < HALF; ++j) {
+            const float c0 = cs[2 * j], s0 = cs[2 * j + 1];
+            const float x1 = x[j], x2 = x[j + HALF];
+            x[j] = x1 * c0 - x2 * s0;
+            x[j + HALF] = x1 * s0 + x2 * c0;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < DH; ++c) x[c] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < DH; c += 8) {
+        uint4 pk;
+        pk.x = (uint32_t)f2bf(x[c]) | ((uint32_t)f2bf(x[c + 1]) << 16);
+        pk.y = (uint32_t)f2bf(x[c + 2]) | ((uint32_t)f2bf(x[c + 3]) << 16);
+        pk.z = (uint32_t)f2bf(x[c + 4]) | ((uint32_t)f2bf(x[c + 5]) << 16);
+        pk.w = (uint32_t)f2bf(x[c + 6]) | ((uint32_t)f2bf(x[c + 7]) << 16);
+        *reinterpret_cast<uint4 *>(&Ks[tid * LDKR + c]) = pk;
+      }
+      // V^T: thread = (key pair, half of the head dims); packed 32-bit writes
+      const int pr = tid & 127, dh0 = (tid >> 7) * HALF;
+      const int k0 = k_begin + 2 * pr;
+      const bf16_t *v0 = qkv + (size_t)(base + min(k0, len - 1)) * ld3 + 2 * d + h * DH + dh0;
+      const bf16_t *v1 = qkv + (size_t)(base + min(k0 + 1, len - 1)) * ld3 + 2 * d + h * DH + dh0;
+      const bool ok0 = k0 < len, ok1 = k0 + 1 < len;
+#pragma unroll
+      for (int c = 0; c < HALF; c += 8) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(v0 + c);
+        const uint4 b = *reinterpret_cast<const uint4 *>(v1 + c);
+        const uint32_t wa[4] = {ok0 ? a.x : 0u, ok0 ? a.y : 0u, ok0 ? a.z : 0u, ok0 ? a.w : 0u};
+        const uint32_t wb[4] = {ok1 ? b.x : 0u, ok1 ? b.y : 0u, ok1 ? b.z : 0u, ok1 ? b.w : 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = (wa[j] & 0xFFFFu) | (wb[j] << 16);          // dim c+2j
+          const uint32_t hi = (wa[j] >> 16) | (wb[j] & 0xFFFF0000u);      // dim c+2j+1
+          *reinterpret_cast<uint32_t *>(&Vt[(dh0 + c + 2 * j) * LDV + 2 * pr]) = lo;
+          *reinterpret_cast<uint32_t *>(&Vt[(dh0 + c + 2 * j + 1) * LDV + 2 * pr]) = hi;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int q_lo = q_begin + qblk[b] * 32;            // first query of the block
+      if (q_lo >= len) continue;
+      const int q = q_lo + col;
+      // key blocks of this chunk that the query block can see
+      const int kb_end = (kc < qc) ? CH / 32 : qblk[b] + 1;
+      for (int kb = 0; kb < kb_end; ++kb) {
+        f32x16_t sc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8_t kf =
+              *reinterpret_cast<const bf16x8_t *>(&Ks[(kb * 32 + col) * LDKR + ks * 16 + hl * 8]);
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[b][ks], sc, 0, 0, 0);
+        }
+        // sc[i] = score(key = k_begin + kb*32 + (i/4)*8 + 4*hl + i%4, query q), log2 units
+        if (kc == qc && kb == qblk[b]) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k_begin + kb * 32 + (i >> 2) * 8 + 4 * hl + (i & 3);
+            if (key > q) sc[i] = -INFINITY;
+          }
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[b], mx);
+        const float corr = exp2f(m_run[b] - m_new);
+        float p[16], rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = exp2f(sc[i] - m_new);
+          rs += p[i];
+        }
+        rs += __shfl_xor(rs, 32, 64);
+        l_run[b] = l_run[b] * corr + rs;
+        m_run[b] = m_new;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[b][db][i] *= corr;
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+          bf16x8_t pb;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * step + j];
+          const int key0 = kb * 32 + 16 * step + 4 * hl;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16_t *vr = &Vt[(db * 32 + col) * LDV + key0];
+            const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 8);
+            bf16x8_t va;
+            const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              va[2 * j] = __builtin_bit_cast(__bf16, (bf16_t)(w[j] & 0xFFFFu));
+              va[2 * j + 1] = __builtin_bit_cast(__bf16, (bf16_t)(w[j] >> 16));
+            }
+            acc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[b][db], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // ---- O[q][d] = acc / l ; lane holds d = db*32 + (i/4)*8 + 4*hl + i%4 of query col
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int q = q_begin + qblk[b] * 32 + col;
+    if (q >= len) continue;
+    const float il = 1.0f / l_run[b];
+    bf16_t *op = o + (size_t)(base + q) * d + h * DH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(acc[b][db][4 * g] * il) | ((uint32_t)f2bf(acc[b][db][4 * g + 1] * il) << 16);
+        pk.y = (uint32_t)f2bf(acc[b][db][4 * g + 2] * il) | ((uint32_t)f2bf(acc[b][db][4 * g + 3] * il) << 16);
+        *reinterpret_cast<uint2 *>(op + db * 32 + g * 8 + 4 * hl) = pk;
+      }
+  }
+}
+
 template <typename act_t>
 hipError_t norm_typed(const Plan &p, int which, const float *s, const lol_library &lib,
                       const Workspace &ws, int depth, hipStream_t st) {
@@ -185,6 +422,18 @@ hipError_t attn_typed(const Plan &p, const DepthGeom &g, const Workspace &ws, hi
   return hipGetLastError();
 }
 
+template <int DH>
+hipError_t attn_mfma(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {
+  dim3 grid(p.n_slots, p.cfg.n_heads, (p.cfg.W + 255) / 256);
+  // scores come out in log2 units: softmax uses exp2
+  const float qscale = 1.4426950408889634f / sqrtf((float)DH);
+  hipLaunchKernelGGL((k_attn_mfma<DH>), grid, dim3(256), 0, st,
+                     reinterpret_cast<const bf16_t *>(ws.qkv), reinterpret_cast<bf16_t *>(ws.o),
+                     ws.win_exp, ws.win_row0, ws.rope_cs, p.cfg.n, p.cfg.d, p.cfg.W, g.delta,
+                     p.K_max, qscale, p.cfg.rope_theta != 0.f ? 1 : 0);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_norm(const Plan &p, const DepthGeom &g, int which, const float *s,
@@ -195,7 +444,7 @@ hipError_t launch_norm(const Plan &p, const DepthGeom &g, int which, const float
 
 hipError_t launch_attention(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {
   if (p.cfg.dtype == LOL_BF16)
-    return p.d_head == 64 ? attn_typed<bf16_t, 64>(p, g, ws, st) : attn_typed<bf16_t, 32>(p, g, ws, st);
+    return p.d_head == 64 ? attn_mfma<64>(p, g, ws, st) : attn_mfma<32>(p, g, ws, st);
   return p.d_head == 64 ? attn_typed<float, 64>(p, g, ws, st) : attn_typed<float, 32>(p, g, ws, st);
 }
 
