@@ -12,6 +12,7 @@ oracle's rate on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,8 +35,9 @@ def gemm_flops(cfg):
             "gemm_gate_up": 2.0 * T * up * d, "gemm_down": 2.0 * T * d * f}
 
 
-def cpu_baseline(inp, seconds_hint=20.0):
-    """The oracle (unchanged) on one document of the workload."""
+def cpu_baseline(inp, budget_s=12.0):
+    """The oracle, unchanged, on whole documents of the workload, one after
+    another until about ``budget_s`` seconds of CPU work are done."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -43,13 +45,53 @@ def cpu_baseline(inp, seconds_hint=20.0):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     cfg = inp.cfg
-    n_tok = cfg.n
-    t0 = time.perf_counter()
-    oracle.forward(inp, forced_expert=inp.forced_expert, rows=[0], n_tokens=n_tok)
+    done, t0 = 0, time.perf_counter()
+    while done < cfg.batch:
+        oracle.forward(inp, forced_expert=inp.forced_expert, rows=[done])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
     dt = time.perf_counter() - t0
-    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"document 0 of {cfg.name}: {n_tok} tokens x {cfg.D} depths, "
-                      f"numpy float64, {dt:.1f} s"}
+    return {"value": done * cfg.n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} documents of {cfg.name} ({done * cfg.n} tokens x "
+                      f"{cfg.D} depths), numpy float64, {dt:.1f} s"}
+
+
+# source files that define each kernel kind's code and launch shape
+KERNEL_SOURCES = {
+    "gemm_qkv": ("gemm.hip", "lol_internal.h"), "gemm_o": ("gemm.hip", "lol_internal.h"),
+    "gemm_gate_up": ("gemm.hip", "lol_internal.h"), "gemm_down": ("gemm.hip", "lol_internal.h"),
+    "win_attn": ("block.hip", "lol_internal.h"),
+}
+
+
+def kernel_sources_digest(kernel):
+    """sha256 over the HIP sources of ``kernel``, to tell whether stored
+    counters are stale."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "runtime_routed_transformer_amd", "csrc")
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 PMC
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel's reading), or
+    None if there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(blob)
+    except (IndexError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_digest(kernel):
+        return None
+    return float(rec["bytes_per_launch"])
 
 
 def main(argv=None):
@@ -84,30 +126,38 @@ def main(argv=None):
     for _ in range(args.warmup):
         core.forward(stream=stream)
     torch.cuda.synchronize()
+
+    # per-kernel breakdown: HIP events the library records on the launch
+    # stream around every kernel, over a few extra (untimed) steps
+    B.lol_core_timing_collect()  # drop anything stale
+    B.lol_core_timing_enable(B.LOL_TIMING_ALL)
+    for _ in range(args.timing_steps):
+        core.forward(stream=stream)
+    torch.cuda.synchronize()
+    B.lol_core_timing_enable(0)
+    kt = B.lol_core_timing_collect()
+    flops = gemm_flops(cfg)
+    per_kernel = {k: {"ms_avg": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items() if v[1]}
+    dominant = max(flops, key=lambda k: kt[k][0])
+    gemm_ms = sum(kt[k][0] for k in flops) / args.timing_steps
+    gemm_tflops = sum(flops.values()) * cfg.D / (gemm_ms / 1e3) / 1e12
+
+    # timed region: K whole forwards; events only around the dominant kernel
+    B.lol_core_timing_enable(1 << B.kernel_kind(dominant))
+    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(args.steps):
         core.forward(stream=stream)
     ev1.record(stream)
     torch.cuda.synchronize()
+    B.lol_core_timing_enable(0)
     ms = ev0.elapsed_time(ev1) / args.steps
     tokens_per_s = cfg.tokens / (ms / 1e3)
-
-    # per-kernel durations: HIP events recorded by the library on the launch stream
-    B.lol_core_timing_collect()  # drop anything stale
-    B.lol_core_timing_enable(True)
-    for _ in range(args.timing_steps):
-        core.forward(stream=stream)
-    torch.cuda.synchronize()
-    B.lol_core_timing_enable(False)
-    kt = B.lol_core_timing_collect()
-    flops = gemm_flops(cfg)
-    per_kernel = {k: {"ms_avg": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items() if v[1]}
-    dominant = max(flops, key=lambda k: kt[k][0])
-    dom_ms = kt[dominant][0] / kt[dominant][1]
+    dom_total, dom_n = B.lol_core_timing_collect()[dominant]
+    dom_ms = dom_total / dom_n
     achieved = flops[dominant] / (dom_ms / 1e3) / 1e12
-    gemm_ms = sum(kt[k][0] for k in flops) / args.timing_steps
-    gemm_tflops = sum(flops.values()) * cfg.D / (gemm_ms / 1e3) / 1e12
+    traffic = stored_traffic(dominant, cfg.name)
     result = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -119,8 +169,8 @@ def main(argv=None):
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel_ms_avg": dom_ms,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel_ms_avg": dom_ms, "kernel_launches_timed": dom_n,
                      "flops_per_launch": flops[dominant]},
         "mfma_util_pct": 100.0 * gemm_tflops / PEAK_BF16_TFLOPS,
         "grouped_gemm_tflops": gemm_tflops,

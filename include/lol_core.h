@@ -151,13 +151,17 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0,
  * `stream`. */
 lol_status lol_core_read_flags(void *workspace, uint32_t *flags, void *stream);
 
-/* Kernel-duration instrumentation, for measurement only.  While enabled,
+/* Kernel-duration instrumentation, for measurement only.
+ * lol_core_timing_enable(mask): while bit k of `mask` is set,
  * lol_core_forward records a HIP event pair on its stream around every
- * kernel launch.  lol_core_timing_collect waits for those events and adds,
- * per kernel kind, the summed milliseconds and the launch count to ms[k] and
- * launches[k] (HOST arrays of LOL_KERNEL_KINDS), then forgets them. */
+ * launch of kernel kind k (0 <= k < LOL_KERNEL_KINDS; mask 0 disables,
+ * LOL_TIMING_ALL enables every kind).  lol_core_timing_collect waits for
+ * those events and adds, per kind, the summed milliseconds and the launch
+ * count to ms[k] and launches[k] (HOST arrays of LOL_KERNEL_KINDS), then
+ * forgets them. */
 #define LOL_KERNEL_KINDS 12
-lol_status lol_core_timing_enable(int32_t enable);
+#define LOL_TIMING_ALL 0xFFFu
+lol_status lol_core_timing_enable(uint32_t mask);
 lol_status lol_core_timing_collect(double *ms, int32_t *launches);
 /* Name of kernel kind k (0 <= k < LOL_KERNEL_KINDS), or NULL. */
 const char *lol_core_kernel_name(int32_t kind);

@@ -23,7 +23,7 @@ quoted code runs in fp32 (``self.c_fc(x.float())``) and which this oracle
 therefore also evaluates in fp32 so that both sides decide the argmax in the
 same precision.  Activations are never rounded to bf16.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   * RMSNorm eps = 1e-6; Norm_s(x) = g_s * x / sqrt(mean(x^2) + eps) with a
     per-expert gain g_s, followed by the depth FiLM gamma_{l,s}, beta_{l,s}
     that is shared by all experts (review Eq. 7; paper App. A).
@@ -233,7 +233,8 @@ def expert_block(x: np.ndarray, p: BlockParams, n_heads: int, positions: np.ndar
 # The routed core: Algorithm 1 of [paper] App. A, routed-depth loop only
 # (the prelude output s^(0) is the input, the coda is not part of it).
 # Every window at depth l reads s^(l-1); the new states replace the old ones
-# only after all windows ([review] reader's Algorithm 1, lines 4 and 12).
+# only after all windows ([review] reader's Algorithm 1 and the note after
+# it: window means are taken from the unchanged depth input).
 # --------------------------------------------------------------------------
 @dataclass
 class OracleResult:

@@ -16,6 +16,7 @@ LOL_FP32, LOL_BF16 = 0, 1
 LOL_MLP_SWIGLU, LOL_MLP_GELU = 0, 1
 LOL_FLAG_BAD_FORCED_ID = 1
 LOL_KERNEL_KINDS = 12
+LOL_TIMING_ALL = (1 << LOL_KERNEL_KINDS) - 1
 
 # every function the header declares, with (restype, argtypes)
 _SIGNATURES = {}
@@ -54,7 +55,7 @@ _SIGNATURES.update({
                                    POINTER(lol_router), c_void_p, c_void_p, c_void_p,
                                    POINTER(lol_path), c_void_p, c_size_t, c_void_p]),
     "lol_core_read_flags": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
-    "lol_core_timing_enable": (c_int32, [c_int32]),
+    "lol_core_timing_enable": (c_int32, [c_uint32]),
     "lol_core_timing_collect": (c_int32, [POINTER(c_double), POINTER(c_int32)]),
     "lol_core_kernel_name": (c_char_p, [c_int32]),
     "lol_status_str": (c_char_p, [c_int32]),
@@ -120,8 +121,16 @@ def lol_core_read_flags(workspace, stream) -> int:
     return int(out.value)
 
 
-def lol_core_timing_enable(enable: bool) -> None:
-    _check(load().lol_core_timing_enable(1 if enable else 0), "lol_core_timing_enable")
+def lol_core_timing_enable(mask: int) -> None:
+    """Bit k of ``mask`` times kernel kind k; 0 disables, LOL_TIMING_ALL times all."""
+    _check(load().lol_core_timing_enable(int(mask)), "lol_core_timing_enable")
+
+
+def kernel_kind(name: str) -> int:
+    for k in range(LOL_KERNEL_KINDS):
+        if lol_core_kernel_name(k) == name:
+            return k
+    raise KeyError(name)
 
 
 def lol_core_timing_collect():

@@ -6,8 +6,10 @@
 // the chosen block on each window, gated blend.  All windows of a depth read
 // s^(l-1) and the blend writes each token exactly once, after every kernel
 // of the depth that reads s^(l-1) has run (review "Library of Layers:
-// Routing Whole Transformer Blocks at Runtime", reader's Algorithm 1, lines
-// 4 and 12), so the residual stream is updated in place.
+// Routing Whole Transformer Blocks at Runtime", reader's Algorithm 1 and the
+// note after it: means come from the unchanged depth input, the new states
+// replace the old ones after all windows), so the residual stream is
+// updated in place.
 #include <math.h>
 #include <stdio.h>
 
@@ -61,7 +63,7 @@ struct TimingRec {
   hipEvent_t a, b;
 };
 std::mutex g_tmu;
-bool g_timing = false;
+uint32_t g_timing = 0;  // bit k: time kernel kind k
 std::vector<TimingRec> g_recs;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -179,7 +181,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
   Workspace ws;
   workspace_layout(p, static_cast<char *>(workspace), &ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  bool timing;
+  uint32_t timing;
   {
     std::lock_guard<std::mutex> lk(g_tmu);
     timing = g_timing;
@@ -190,7 +192,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
   hipError_t err;
 #define LOL_TRY(kind, call)                           \
   do {                                                \
-    Launch _l(st, timing, kind);                      \
+    Launch _l(st, (timing >> (kind)) & 1u, kind);     \
     err = _l.done(call);                              \
     if (err != hipSuccess) return LOL_EHIP;           \
   } while (0)
@@ -268,9 +270,10 @@ lol_status lol_core_read_flags(void *workspace, uint32_t *flags, void *stream) {
   return LOL_OK;
 }
 
-lol_status lol_core_timing_enable(int32_t enable) {
+lol_status lol_core_timing_enable(uint32_t mask) {
+  if (mask & ~(uint32_t)LOL_TIMING_ALL) return LOL_EINVAL;
   std::lock_guard<std::mutex> lk(g_tmu);
-  g_timing = enable != 0;
+  g_timing = mask;
   return LOL_OK;
 }
 

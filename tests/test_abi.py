@@ -9,7 +9,7 @@ import pytest
 
 from runtime_routed_transformer_amd import binding as B
 from runtime_routed_transformer_amd.core import make_config
-from runtime_routed_transformer_amd.workloads import CONFIGS
+from runtime_routed_transformer_amd.workloads import CONFIG_BY_NAME, CONFIGS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lol_core.h")
@@ -51,7 +51,7 @@ def test_sizes_and_validation(lib):
         assert B.lol_core_validate(c) == B.LOL_OK, cfg.name
         assert B.lol_core_k_max(c) == -(-cfg.n // cfg.W) + 1
         assert B.lol_core_workspace_size(c) > 0
-    base = CONFIGS[1]
+    base = CONFIG_BY_NAME["small_bf16"]
     bad = {
         "W": 0, "S": -1, "n_heads": 3, "L": 0, "D": 0, "batch": 0, "n": 0, "d_ffn": 0,
     }
@@ -73,7 +73,7 @@ def test_sizes_and_validation(lib):
 
 
 def test_forward_rejects_bad_arguments_before_launch(lib):
-    c = make_config(CONFIGS[0])
+    c = make_config(CONFIG_BY_NAME["tiny_fp32"])
     libw = B.lol_library(wqkv=16, wo=16, w_gu=16, w_down=16, g_attn=16, g_ffn=16)
     rt = B.lol_router(w_r=16, e_depth=16)
     ws = B.lol_core_workspace_size(c)

@@ -12,7 +12,7 @@ import sys
 import numpy as np
 import pytest
 
-from runtime_routed_transformer_amd.workloads import CONFIGS, CoreConfig
+from runtime_routed_transformer_amd.workloads import CONFIG_BY_NAME, CoreConfig
 from tests import parity
 
 pytestmark = pytest.mark.gpu
@@ -34,11 +34,11 @@ def _gpu():
 
 
 SCALED = [
-    CONFIGS[0],
-    CONFIGS[1].scaled(2, 384),
-    CONFIGS[2].scaled(2, 640),
-    CONFIGS[3].scaled(2, 640),
-    CONFIGS[4].scaled(3, 224),
+    CONFIG_BY_NAME["tiny_fp32"],
+    CONFIG_BY_NAME["small_bf16"].scaled(2, 384),
+    CONFIG_BY_NAME["mid_bf16"].scaled(2, 640),
+    CONFIG_BY_NAME["sparse_bf16"].scaled(2, 640),
+    CONFIG_BY_NAME["forced_bf16"].scaled(3, 224),
 ]
 
 
@@ -48,9 +48,9 @@ def test_parity_scaled(cfg):
     _report(parity.run(parity.prepare(cfg)))
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4])
-def test_parity_full_size_sampled(idx):
-    cfg = CONFIGS[idx]
+@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "sparse_bf16", "forced_bf16"])
+def test_parity_full_size_sampled(name):
+    cfg = CONFIG_BY_NAME[name]
     print(f"[parity-full] {cfg.name}", flush=True)
     inp = parity.prepare(cfg)
     _report(parity.run(inp, rows=[0, cfg.batch - 1], n_tokens=min(cfg.n, 3 * cfg.W + cfg.W // 2)))
@@ -85,7 +85,7 @@ def test_parity_edge_cases(cfg):
 def test_gate_zero_identity_and_determinism_and_inplace():
     import torch
     from runtime_routed_transformer_amd.core import DeviceCore
-    cfg = CONFIGS[1].scaled(2, 256)
+    cfg = CONFIG_BY_NAME["small_bf16"].scaled(2, 256)
     inp = parity.prepare(cfg)
     core = DeviceCore(inp)
     core.set_forcing(forced_gate=np.zeros((cfg.D, cfg.batch, core.k_max), np.float32))
@@ -106,7 +106,7 @@ def test_forced_own_path_and_bad_forced_id_flag():
     import torch
     from runtime_routed_transformer_amd import binding
     from runtime_routed_transformer_amd.core import DeviceCore
-    cfg = CONFIGS[2].scaled(1, 512)
+    cfg = CONFIG_BY_NAME["mid_bf16"].scaled(1, 512)
     inp = parity.prepare(cfg)
     core = DeviceCore(inp)
     free = core.forward().clone()

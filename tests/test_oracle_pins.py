@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from runtime_routed_transformer_amd.workloads import CONFIGS, CoreConfig, generate
+from runtime_routed_transformer_amd.workloads import CONFIG_BY_NAME, CoreConfig, generate
 from tests import torch_block
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -332,7 +332,7 @@ def test_gate_scales_only_the_update():
 
 
 def test_path_layout_and_padding():
-    cfg = CONFIGS[0]
+    cfg = CONFIG_BY_NAME["tiny_fp32"]
     res = oracle.forward(generate(cfg))
     for depth in range(1, cfg.D + 1):
         K = len(oracle.partition(cfg.n, cfg.W, cfg.S, depth))
