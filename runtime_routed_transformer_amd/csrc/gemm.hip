@@ -43,6 +43,7 @@ struct GemmParams {
   int glu_offset;
   int n_tiles_n;
   const int32_t *mtile;
+  const int32_t *mcount;   // [0]: M tiles in use in mtile
   const int32_t *toff;
   const int32_t *row_tok;
   const float *row_gate;
@@ -92,22 +93,116 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel.  4 waves in a 2 x 2 grid; each wave owns TM x TN blocks of
-// 32 x 32 outputs, so the block tile is (64 TM) x (64 TN) and k advances by
-// BK = 64 per stage.  Stage k+1 is fetched from global memory into registers
-// while stage k is multiplied out of one of two LDS buffers; one barrier per
-// stage.
+// bf16 MFMA kernel.  A workgroup computes a 256 x 128 tile (rows x output
+// columns of W) with 4 waves in a 2 x 2 grid, each wave 128 x 64 = 4 x 2
+// blocks of v_mfma_f32_32x32x16_bf16.  Two workgroups share a CU (LDS 72
+// KiB, at most 256 registers per lane each), so one workgroup's barriers,
+// prologue and epilogue overlap the other's matrix work.
+//
+// Main loop: k advances by BK = 32 per stage through a ring of NSTAGE LDS
+// stages filled by direct global-to-LDS loads (16 bytes per lane, no
+// register staging).  Inside a stage the fragments of the second 16-k step
+// are read while the first step's MFMAs run, and the first step of the next
+// stage right after the stage barrier.
+//
+// LDS layout of one operand in one stage: rows of 32 k = 64 bytes, four
+// 16-byte chunks per row; logical chunk c of row r sits at chunk
+// c ^ swz(r), swz(r) = (r >> 2) & 3.  One load instruction fills 16
+// consecutive rows (1 KiB); the swizzle is applied on the global side (each
+// lane picks which chunk of its row to fetch).  A 128-bit LDS read is served
+// 16 lanes at a time over 64 four-byte banks; with this swizzle the 16 lanes
+// of an MFMA fragment read (16 consecutive rows, one logical chunk) cover
+// all 64 banks, and the hardware's bank-conflict counter reads zero for
+// every fragment read of the kernel (measured for each 32-row block and
+// chunk pair).
+//
+// Epilogue: each wave stages 32 rows of its results at a time in LDS (fp32,
+// XOR-swizzled 16-byte slots) and reads them back row-wise, so that every
+// global access of the epilogue (bf16 stores, residual reads and writes) is
+// a run of 8 consecutive columns per lane and whole rows per group of lanes.
+//
+// Tile order: tiles are numbered (m-tile, n-tile) in groups of GM m-tiles
+// (n-tile major inside a group) and dealt to the 8 XCDs in contiguous
+// ranges (workgroup i runs on XCD i mod 8), so that tiles sharing an A or B
+// slice run close together in time on one XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // padded LDS row (144 B): conflict-free 16-B fragment reads
+constexpr int TM = 4, TN = 2;           // 32 x 32 blocks per wave
+constexpr int BMT = 64 * TM, BNT = 64 * TN;
+constexpr int BK = 32;
+constexpr int NSTAGE = 3;
+constexpr int GM = 4;
+constexpr int STAGE_BYTES = (BMT + BNT) * BK * 2;
+constexpr int GEMM_LDS = NSTAGE * STAGE_BYTES;  // 72 KiB
+static_assert(BMT == kTileM2, "M tiles of the grouped GEMM are kTileM2 rows");
 
-template <int EPI, int TM, int TN>
-__global__ void __launch_bounds__(256) k_gemm_bf16(GemmParams P) {
-  constexpr int BMt = 64 * TM, BNt = 64 * TN;
-  constexpr int AV = BMt / 32, BV = BNt / 32;  // 16-byte vectors per thread per stage
-  constexpr int STAGE = (BMt + BNt) * LDK;     // elements per LDS buffer
-  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-  const int mt = blockIdx.x / P.n_tiles_n, nt = blockIdx.x % P.n_tiles_n;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void lds_dma16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)lds, 16, 0, 0);
+}
+
+// Stage barrier: wait until at most VM vector-memory operations (the
+// direct-to-LDS stage loads) and LG LDS operations of this wave are in flight,
+// then s_barrier.  Built from the compiler's own intrinsics so that its
+// wait-count tracking knows about them; the empty asm statements keep memory
+// accesses from being moved across, and the scheduling barriers keep the
+// MFMA blocks on their side.
+template <int VM, int LG>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(VM >= 0 && VM < 64 && LG >= 0 && LG < 16, "counter range");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LG << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Scheduling hint for "NR fragment reads (for the next step), then NM MFMAs
+// (on fragments already in registers)": every read first, so that each has
+// the whole MFMA block to arrive.
+template <int NR, int NM>
+__device__ __forceinline__ void reads_then_mfmas() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // the LDS reads
+  __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // the MFMAs
+}
+
+// silu(x) = x / (1 + e^-x) with the hardware exp2 and reciprocal (about one
+// ulp each, far below the bf16 rounding of the result).
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(256, 2) k_gemm_bf16(GemmParams P) {
+  constexpr int A_BYTES = BMT * BK * 2;
+  constexpr int AQ = BMT / 64, BQ = BNT / 64;  // 1-KiB load instructions per wave per stage
+  constexpr int NQ = AQ + BQ;
+  constexpr int NR = TM + TN;                  // fragment reads per 16-k step
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  // ---- tile of this workgroup (see "Tile order")
+  const int n_mt = P.mcount[0];
+  const int n_nt = P.n_tiles_n;
+  const int R = n_mt * n_nt;
+  const int per = (R + 7) >> 3;
+  const int idx = blockIdx.x >> 3;
+  const int t = (blockIdx.x & 7) * per + idx;
+  if (idx >= per || t >= R) return;
+  const int grp = t / (GM * n_nt), within = t - grp * (GM * n_nt);
+  const int gm = min(GM, n_mt - grp * GM);
+  const int mt = grp * GM + within % gm, nt = within / gm;
   const int e = P.mtile[2 * mt];
   if (e < 0) return;
   const int row0 = P.mtile[2 * mt + 1];
@@ -116,44 +211,49 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(GemmParams P) {
   const bf16_t *A = reinterpret_cast<const bf16_t *>(P.A);
   const bf16_t *Wt = reinterpret_cast<const bf16_t *>(P.Wt) + (size_t)e * P.w_stride;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int kv = tid & 7, r_base = tid >> 3;  // each thread: one 16-byte chunk of rows r_base + 32 i
 
-  const bf16_t *a_src[AV];
-  const bf16_t *b_src[BV];
+  // ---- per-lane global sources of this wave's load instructions
+  const int lrow = lane >> 2, lchunk = lane & 3;
+  const bf16_t *src[NQ];
 #pragma unroll
-  for (int i = 0; i < AV; ++i) {
-    const int arow = min(row0 + r_base + 32 * i, row_end - 1);
-    a_src[i] = A + (size_t)arow * K + kv * 8;
+  for (int i = 0; i < AQ; ++i) {
+    const int r = (wave + 4 * i) * 16 + lrow;              // row inside the A tile
+    const int arow = min(row0 + r, row_end - 1);
+    src[i] = A + (size_t)arow * K + ((lchunk ^ swz(r)) << 3);
   }
 #pragma unroll
-  for (int i = 0; i < BV; ++i) {
-    const int r = r_base + 32 * i;
+  for (int i = 0; i < BQ; ++i) {
+    const int r = (wave + 4 * i) * 16 + lrow;              // row inside the B tile
     int wrow;
     if (EPI == EPI_SWIGLU) {
-      constexpr int WR = TN * 32, HALF = TN * 16;  // weight rows per wave column, gate half
-      const int wc = r / WR, within = r % WR;
-      const int hidden = nt * (BNt / 2) + wc * HALF + (within % HALF);
-      wrow = (within < HALF ? 0 : P.glu_offset) + hidden;
+      // each wave column's 64 B rows: 32 gate rows, then the 32 up rows of
+      // the same hidden columns
+      const int wc = r >> 6, in_wc = r & 63;
+      const int hidden = nt * (BNT / 2) + wc * 32 + (in_wc & 31);
+      wrow = (in_wc < 32 ? 0 : P.glu_offset) + hidden;
     } else {
-      wrow = nt * BNt + r;
+      wrow = nt * BNT + r;
     }
-    b_src[i] = Wt + (size_t)wrow * K + kv * 8;
+    src[AQ + i] = Wt + (size_t)wrow * K + ((lchunk ^ swz(r)) << 3);
   }
-  uint4 ra[AV], rb[BV];
+  auto issue = [&](int stage, int slot) {
+    char *base = smem + slot * STAGE_BYTES;
+    const int koff = stage * BK;
 #pragma unroll
-  for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const uint4 *>(a_src[i]);
+    for (int i = 0; i < AQ; ++i) lds_dma16(src[i] + koff, base + (wave + 4 * i) * 1024);
 #pragma unroll
-  for (int i = 0; i < BV; ++i) rb[i] = *reinterpret_cast<const uint4 *>(b_src[i]);
-  {
-    bf16_t *As = smem, *Bs = smem + BMt * LDK;
-#pragma unroll
-    for (int i = 0; i < AV; ++i) *reinterpret_cast<uint4 *>(&As[(r_base + 32 * i) * LDK + kv * 8]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BV; ++i) *reinterpret_cast<uint4 *>(&Bs[(r_base + 32 * i) * LDK + kv * 8]) = rb[i];
-  }
-  __syncthreads();
+    for (int i = 0; i < BQ; ++i) lds_dma16(src[AQ + i] + koff, base + A_BYTES + (wave + 4 * i) * 1024);
+  };
 
+  // ---- fragment addresses: lane reads row (lane & 31) of each 32-row block
+  // at logical chunk 2 kk + (lane >> 5)
   const int wm = wave >> 1, wn = wave & 1;
+  const int frow = lane & 31;
+  const int sw = swz(frow);
+  const int coff0 = ((lane >> 5) ^ sw) << 4, coff1 = ((2 + (lane >> 5)) ^ sw) << 4;
+  const int a_frag = (wm * TM * 32 + frow) * 64;            // byte offset inside the A part
+  const int b_frag = A_BYTES + (wn * TN * 32 + frow) * 64;  // inside the B part
+
   f32x16 acc[TN][TM];
 #pragma unroll
   for (int a = 0; a < TN; ++a)
@@ -162,71 +262,146 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(GemmParams P) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-  const int frow = lane & 31, fk = (lane >> 5) * 8;
-  const int nk = K / BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    // prefetch stage kt+1 (the last iteration re-reads the final stage, unused)
-    const int knext = min(kt + 1, nk - 1) * BK;
+  bf16x8 fw0[TN], fx0[TM], fw1[TN], fx1[TM];
+  auto read_frags = [&](bf16x8 *fw, bf16x8 *fx, int slot, int coff) {
+    const char *base = smem + slot * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + knext);
+    for (int i = 0; i < TN; ++i)
+      fw[i] = *reinterpret_cast<const bf16x8 *>(base + b_frag + i * 32 * 64 + coff);
 #pragma unroll
-    for (int i = 0; i < BV; ++i) rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + knext);
-    const bf16_t *As = smem + cur * STAGE, *Bs = As + BMt * LDK;
+    for (int i = 0; i < TM; ++i)
+      fx[i] = *reinterpret_cast<const bf16x8 *>(base + a_frag + i * 32 * 64 + coff);
+  };
+  auto mfmas = [&](const bf16x8 *fw, const bf16x8 *fx) {
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 fw[TN], fx[TM];
+    for (int in = 0; in < TN; ++in)
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
-        fw[i] = *reinterpret_cast<const bf16x8 *>(&Bs[(wn * TN * 32 + i * 32 + frow) * LDK + kk + fk]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fx[i] = *reinterpret_cast<const bf16x8 *>(&As[(wm * TM * 32 + i * 32 + frow) * LDK + kk + fk]);
-#pragma unroll
-      for (int in = 0; in < TN; ++in)
-#pragma unroll
-        for (int im = 0; im < TM; ++im)
-          acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[in], fx[im], acc[in][im], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      bf16_t *An = smem + (cur ^ 1) * STAGE, *Bn = An + BMt * LDK;
-#pragma unroll
-      for (int i = 0; i < AV; ++i) *reinterpret_cast<uint4 *>(&An[(r_base + 32 * i) * LDK + kv * 8]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < BV; ++i) *reinterpret_cast<uint4 *>(&Bn[(r_base + 32 * i) * LDK + kv * 8]) = rb[i];
-    }
-    __syncthreads();
-  }
+      for (int im = 0; im < TM; ++im)
+        acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[in], fx[im], acc[in][im], 0, 0, 0);
+  };
 
-  // lane holds C[m = im*32 + lane%32][n = in*32 + g*8 + 4*(lane/32) + j], g, j < 4
-  const int cq = (lane >> 5) * 4;
+  // Order inside iteration kt (stage kt in slot kt % NSTAGE):
+  //   wait for the first-step fragments of stage kt (read one MFMA block
+  //   ago); read the second-step fragments; MFMAs of the first step;
+  //   barrier: stage kt+1 has landed and every fragment read of this wave
+  //   is done (they too had a whole MFMA block), so after it the slot of
+  //   stage kt-1 is free on every wave;
+  //   read the first-step fragments of stage kt+1; load stage kt+NSTAGE-1
+  //   into the free slot; MFMAs of the second step.
+  // The explicit LDS waits sit where the reads have had an MFMA block to
+  // arrive, so the compiler needs none of its own in front of the MFMAs.
+  const int nk = K / BK;
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < nk) issue(s, s);
+  // stage 0 landed (stages 1 .. NSTAGE-2 may be in flight)
+  if (nk >= NSTAGE - 1)
+    stage_barrier<NQ * (NSTAGE - 2), 0>();
+  else
+    stage_barrier<0, 0>();
+  read_frags(fw0, fx0, 0, coff0);
+  int kt = 0;
+  // steady state: at the barrier only stage kt+NSTAGE-2 may still be in
+  // flight; stage kt+NSTAGE-1 goes into the slot of stage kt-1
+  for (; kt + NSTAGE - 1 < nk; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): also settles scalar loads
+    read_frags(fw1, fx1, kt % NSTAGE, coff1);
+    mfmas(fw0, fx0);
+    reads_then_mfmas<NR, TM * TN>();
+    stage_barrier<NQ * (NSTAGE - 3), 0>();
+    read_frags(fw0, fx0, (kt + 1) % NSTAGE, coff0);
+    issue(kt + NSTAGE - 1, (kt + NSTAGE - 1) % NSTAGE);
+    mfmas(fw1, fx1);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // the LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x020, NQ, 0);       // the stage loads
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // the MFMAs
+  }
+  // drain: nothing left to load
+  for (; kt < nk; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    read_frags(fw1, fx1, kt % NSTAGE, coff1);
+    mfmas(fw0, fx0);
+    reads_then_mfmas<NR, TM * TN>();
+    stage_barrier<0, 0>();
+    // (on the last stage this reads a stale slot, unused)
+    read_frags(fw0, fx0, (kt + 1) % NSTAGE, coff0);
+    mfmas(fw1, fx1);
+    reads_then_mfmas<NR, TM * TN>();
+  }
+  stage_barrier<0, 0>();  // every wave is done with the ring: reuse it below
+
+  // ---- epilogue.  acc[in][im] holds C[m = im*32 + lane%32][n = in*32 + g*8
+  // + 4*(lane/32) + j] (g, j < 4) of this wave's 128 x 64 block.  SwiGLU:
+  // acc[0] is the gate and acc[1] the up projection of the same 32 hidden
+  // columns.
+  constexpr int NC = (EPI == EPI_SWIGLU) ? 32 : 64;   // output columns per wave
+  constexpr int SLOTS = NC / 4;                       // 16-byte slots per staged row
+  constexpr int LPR = NC / 8;                         // lanes per row on read-back
+  constexpr int RPP = 64 / LPR;                       // rows per read-back pass
+  float *stage_f = reinterpret_cast<float *>(smem) + wave * 32 * NC;
+  auto sslot = [&](int r, int c) {                    // physical slot of logical slot c
+    return r * SLOTS + (c ^ (SLOTS == 16 ? (r & 15) : ((r >> 1) & 7)));
+  };
+  const int out_cols = (EPI == EPI_SWIGLU) ? BNT / 2 : BNT;
+  const int col_base = nt * out_cols + wn * NC;
+  const int rr = lane / LPR, cc = (lane % LPR) * 2;   // read-back row in pass, first slot
 #pragma unroll
   for (int im = 0; im < TM; ++im) {
-    const int row = row0 + wm * TM * 32 + im * 32 + (lane & 31);
-    if (row >= row_end) continue;
-    if (EPI == EPI_SWIGLU) {
+    // stage this 32-row block
 #pragma unroll
-      for (int in = 0; in < TN / 2; ++in)
+    for (int in = 0; in < (EPI == EPI_SWIGLU ? 1 : TN); ++in)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int hcol = nt * (BNt / 2) + wn * TN * 16 + in * 32 + g * 8 + cq;
-          float gv[4], uv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            gv[j] = acc[in][im][g * 4 + j];
-            uv[j] = acc[in + TN / 2][im][g * 4 + j];
+      for (int g = 0; g < 4; ++g) {
+        float4 v;
+        if (EPI == EPI_SWIGLU) {
+          v.x = silu_fast(acc[0][im][4 * g + 0]) * acc[1][im][4 * g + 0];
+          v.y = silu_fast(acc[0][im][4 * g + 1]) * acc[1][im][4 * g + 1];
+          v.z = silu_fast(acc[0][im][4 * g + 2]) * acc[1][im][4 * g + 2];
+          v.w = silu_fast(acc[0][im][4 * g + 3]) * acc[1][im][4 * g + 3];
+        } else {
+          v = make_float4(acc[in][im][4 * g], acc[in][im][4 * g + 1], acc[in][im][4 * g + 2],
+                          acc[in][im][4 * g + 3]);
+          if (EPI == EPI_GELU) {
+            v.x = gelu_erf(v.x); v.y = gelu_erf(v.y); v.z = gelu_erf(v.z); v.w = gelu_erf(v.w);
           }
-          store_glu4<bf16_t>(P, row, hcol, gv, uv);
         }
-    } else {
+        const int c = in * 8 + 2 * g + (lane >> 5);   // logical 16-byte slot of the row
+        *reinterpret_cast<float4 *>(stage_f + sslot(lane & 31, c) * 4) = v;
+      }
+    // read back whole rows: lane -> row rr (+ RPP * pass), 8 columns from 4 * cc
 #pragma unroll
-      for (int in = 0; in < TN; ++in)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = nt * BNt + wn * TN * 32 + in * 32 + g * 8 + cq;
-          epilogue4<EPI, bf16_t>(P, row, col, acc[in][im][g * 4], acc[in][im][g * 4 + 1],
-                                 acc[in][im][g * 4 + 2], acc[in][im][g * 4 + 3]);
-        }
+    for (int pass = 0; pass < 32 / RPP; ++pass) {
+      const int r = rr + pass * RPP;
+      const float4 v0 = *reinterpret_cast<const float4 *>(stage_f + sslot(r, cc) * 4);
+      const float4 v1 = *reinterpret_cast<const float4 *>(stage_f + sslot(r, cc + 1) * 4);
+      const int row = row0 + wm * TM * 32 + im * 32 + r;
+      if (row >= row_end) continue;
+      const int col = col_base + cc * 4;
+      if (EPI == EPI_RESID) {
+        const size_t tok = (size_t)P.row_tok[row];
+        const float4 *sp = reinterpret_cast<const float4 *>(P.s + tok * P.ldc + col);
+        const float4 x0 = sp[0], x1 = sp[1];
+        float4 *hp = reinterpret_cast<float4 *>(reinterpret_cast<float *>(P.C) + (size_t)row * P.ldc + col);
+        hp[0] = make_float4(x0.x + v0.x, x0.y + v0.y, x0.z + v0.z, x0.w + v0.w);
+        hp[1] = make_float4(x1.x + v1.x, x1.y + v1.y, x1.z + v1.z, x1.w + v1.w);
+      } else if (EPI == EPI_BLEND) {
+        const size_t tok = (size_t)P.row_tok[row];
+        const float gt = P.row_gate[row];
+        float4 *sp = reinterpret_cast<float4 *>(P.s + tok * P.ldc + col);
+        const float4 *hp = reinterpret_cast<const float4 *>(P.h + (size_t)row * P.ldc + col);
+        const float4 x0 = sp[0], x1 = sp[1], h0 = hp[0], h1 = hp[1];
+        sp[0] = make_float4(x0.x + gt * (h0.x + v0.x - x0.x), x0.y + gt * (h0.y + v0.y - x0.y),
+                            x0.z + gt * (h0.z + v0.z - x0.z), x0.w + gt * (h0.w + v0.w - x0.w));
+        sp[1] = make_float4(x1.x + gt * (h1.x + v1.x - x1.x), x1.y + gt * (h1.y + v1.y - x1.y),
+                            x1.z + gt * (h1.z + v1.z - x1.z), x1.w + gt * (h1.w + v1.w - x1.w));
+      } else {
+        uint4 pk;
+        pk.x = pack_bf16x2(v0.x, v0.y);
+        pk.y = pack_bf16x2(v0.z, v0.w);
+        pk.z = pack_bf16x2(v1.x, v1.y);
+        pk.w = pack_bf16x2(v1.z, v1.w);
+        *reinterpret_cast<uint4 *>(reinterpret_cast<bf16_t *>(P.C) + (size_t)row * P.ldc + col) = pk;
+      }
     }
   }
 }
@@ -324,6 +499,7 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.ldc = a.N;
   P.glu_offset = a.glu_offset;
   P.mtile = ws.mtile;
+  P.mcount = ws.mcount;
   P.toff = ws.toff;
   P.row_tok = ws.row_tok;
   P.row_gate = ws.row_gate;
@@ -331,28 +507,14 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.s = a.s;
   P.h = a.h;
   if (p.cfg.dtype == LOL_BF16) {
-    // 256 x 256 tiles for the wide projections (QKV, gate/up); 256 x 128 for
-    // the d-wide ones (O, down), which otherwise leave CUs idle in the tail
-    const bool wide = (EPI == EPI_SWIGLU ? 2 * a.N : a.N) >= 2048;
-    if (wide && a.N % (EPI == EPI_SWIGLU ? 128 : 256) == 0) {
-      constexpr int TM = 4, TN = 4;
-      P.mtile = ws.mtile2;
-      P.n_tiles_n = (EPI == EPI_SWIGLU) ? a.N / (32 * TN) : a.N / (64 * TN);
-      const size_t smem = 2 * (size_t)(64 * TM + 64 * TN) * LDK * sizeof(bf16_t);
-      hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, TM, TN>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-      hipLaunchKernelGGL((k_gemm_bf16<EPI, TM, TN>), dim3(ws.max_mtiles2 * P.n_tiles_n), dim3(256),
-                         smem, st, P);
-    } else {
-      constexpr int TM = 4, TN = 2;
-      P.mtile = ws.mtile2;
-      P.n_tiles_n = (EPI == EPI_SWIGLU) ? a.N / (32 * TN) : a.N / (64 * TN);
-      const size_t smem = 2 * (size_t)(64 * TM + 64 * TN) * LDK * sizeof(bf16_t);
-      hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, TM, TN>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-      hipLaunchKernelGGL((k_gemm_bf16<EPI, TM, TN>), dim3(ws.max_mtiles2 * P.n_tiles_n), dim3(256),
-                         smem, st, P);
-    }
+    P.mtile = ws.mtile2;
+    P.mcount = ws.mcount + 1;
+    // weight rows per tile: BNT (SwiGLU: BNT/2 gate + BNT/2 up rows)
+    P.n_tiles_n = (EPI == EPI_SWIGLU) ? a.N / (BNT / 2) : a.N / BNT;
+    hipFuncSetAttribute((const void *)k_gemm_bf16<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        GEMM_LDS);
+    const int grid = ((ws.max_mtiles2 * P.n_tiles_n + 7) / 8) * 8;
+    hipLaunchKernelGGL((k_gemm_bf16<EPI>), dim3(grid), dim3(256), GEMM_LDS, st, P);
   } else {
     P.n_tiles_n = a.N / FBN;
     hipLaunchKernelGGL(k_gemm_f32<EPI>, dim3(ws.max_mtiles * P.n_tiles_n), dim3(256), 0, st, P);

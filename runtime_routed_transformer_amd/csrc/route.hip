@@ -152,7 +152,8 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t *__restrict__ win
                                                  int32_t *__restrict__ ecount,
                                                  int32_t *__restrict__ toff_out,
                                                  int32_t *__restrict__ mtile, int max_mtiles,
-                                                 int32_t *__restrict__ mtile2, int max_mtiles2, int n,
+                                                 int32_t *__restrict__ mtile2, int max_mtiles2,
+                                                 int32_t *__restrict__ mcount, int n,
                                                  int W, int delta, int K, int K_max, int n_slots,
                                                  int L) {
   __shared__ int s_exp[kMaxSlots];
@@ -191,6 +192,8 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t *__restrict__ win
     moff[L] = m;
     moff2[L] = m2;
     ecount[L] = w;
+    mcount[0] = m;
+    mcount[1] = m2;
   }
   __syncthreads();
   for (int e = tid; e <= L; e += blockDim.x) toff_out[e] = toff[e];
@@ -290,7 +293,7 @@ hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const
 
 hipError_t launch_bucket(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {
   hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, st, ws.win_exp, ws.win_row0, ws.ecount,
-                     ws.toff, ws.mtile, ws.max_mtiles, ws.mtile2, ws.max_mtiles2, p.cfg.n, p.cfg.W, g.delta, g.K, p.K_max,
+                     ws.toff, ws.mtile, ws.max_mtiles, ws.mtile2, ws.max_mtiles2, ws.mcount, p.cfg.n, p.cfg.W, g.delta, g.K, p.K_max,
                      p.n_slots, p.cfg.L);
   return hipGetLastError();
 }
