@@ -34,7 +34,24 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // u[row] = gamma * (g_e * x / sqrt(mean(x^2) + eps)) + beta, one wave per row.
 // FROM_S: x = s[row_tok[row]] (attention sublayer); else x = h[row] (MLP).
-template <typename act_t, bool FROM_S>
+// NCH > 0: d = 256 NCH; every lane keeps its NCH float4 chunks of the row in
+// registers (read once, 16-byte loads) and stores 4 outputs per chunk.
+// NCH = 0: any d (multiple of 64), element-wise.
+template <typename act_t>
+__device__ __forceinline__ void store4(act_t *p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float *p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t *p, float a, float b, float c, float d) {
+  uint2 pk;
+  pk.x = (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  pk.y = (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16);
+  *reinterpret_cast<uint2 *>(p) = pk;
+}
+
+template <typename act_t, bool FROM_S, int NCH>
 __global__ void __launch_bounds__(256) k_norm(const float *__restrict__ src,
                                               const int32_t *__restrict__ row_tok,
                                               const int32_t *__restrict__ row_exp,
@@ -47,20 +64,37 @@ __global__ void __launch_bounds__(256) k_norm(const float *__restrict__ src,
   const float *x = src + (FROM_S ? (size_t)row_tok[row] : (size_t)row) * d;
   const float *g = gain + (size_t)row_exp[row] * d;
   act_t *out = u + (size_t)row * d;
-  float ss = 0.f;
-  if ((d & 255) == 0) {
-    for (int c = lane * 4; c < d; c += 256) {
-      const float4 v = *reinterpret_cast<const float4 *>(x + c);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  if (NCH > 0) {
+    float4 xv[NCH > 0 ? NCH : 1];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      xv[i] = *reinterpret_cast<const float4 *>(x + i * 256 + lane * 4);
+      ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
+    }
+    const float inv = rsqrtf(wave_sum(ss) / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = i * 256 + lane * 4;
+      const float4 gv = *reinterpret_cast<const float4 *>(g + c);
+      float4 v = make_float4(xv[i].x * inv * gv.x, xv[i].y * inv * gv.y, xv[i].z * inv * gv.z,
+                             xv[i].w * inv * gv.w);
+      if (fg) {
+        const float4 a = *reinterpret_cast<const float4 *>(fg + c);
+        const float4 b = *reinterpret_cast<const float4 *>(fb + c);
+        v = make_float4(a.x * v.x + b.x, a.y * v.y + b.y, a.z * v.z + b.z, a.w * v.w + b.w);
+      }
+      store4<act_t>(out + c, v.x, v.y, v.z, v.w);
     }
   } else {
+    float ss = 0.f;
     for (int c = lane; c < d; c += 64) ss += x[c] * x[c];
-  }
-  const float inv = rsqrtf(wave_sum(ss) / (float)d + eps);
-  for (int c = lane; c < d; c += 64) {
-    float v = x[c] * inv * g[c];
-    if (fg) v = fg[c] * v + fb[c];
-    st<act_t>(out + c, v);
+    const float inv = rsqrtf(wave_sum(ss) / (float)d + eps);
+    for (int c = lane; c < d; c += 64) {
+      float v = x[c] * inv * g[c];
+      if (fg) v = fg[c] * v + fb[c];
+      st<act_t>(out + c, v);
+    }
   }
 }
 
@@ -393,21 +427,37 @@ __global__ void __launch_bounds__(256) k_attn_mfma(const bf16_t *__restrict__ qk
   }
 }
 
+template <typename act_t, int NCH>
+void norm_launch(const Plan &p, int which, const float *s, const lol_library &lib,
+                 const Workspace &ws, const float *fg, const float *fb, hipStream_t st) {
+  dim3 grid((p.T + 3) / 4);
+  if (which == 0)
+    hipLaunchKernelGGL((k_norm<act_t, true, NCH>), grid, dim3(256), 0, st, s, ws.row_tok,
+                       ws.row_exp, lib.g_attn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T,
+                       p.cfg.d, p.cfg.rms_eps);
+  else
+    hipLaunchKernelGGL((k_norm<act_t, false, NCH>), grid, dim3(256), 0, st, ws.h, ws.row_tok,
+                       ws.row_exp, lib.g_ffn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T,
+                       p.cfg.d, p.cfg.rms_eps);
+}
+
 template <typename act_t>
 hipError_t norm_typed(const Plan &p, int which, const float *s, const lol_library &lib,
                       const Workspace &ws, int depth, hipStream_t st) {
   const int d = p.cfg.d;
   const float *fg = lib.film_gamma ? lib.film_gamma + ((size_t)depth * 2 + which) * d : nullptr;
   const float *fb = lib.film_beta ? lib.film_beta + ((size_t)depth * 2 + which) * d : nullptr;
-  dim3 grid((p.T + 3) / 4);
-  if (which == 0)
-    hipLaunchKernelGGL((k_norm<act_t, true>), grid, dim3(256), 0, st, s, ws.row_tok, ws.row_exp,
-                       lib.g_attn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T, d,
-                       p.cfg.rms_eps);
-  else
-    hipLaunchKernelGGL((k_norm<act_t, false>), grid, dim3(256), 0, st, ws.h, ws.row_tok,
-                       ws.row_exp, lib.g_ffn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T, d,
-                       p.cfg.rms_eps);
+  switch ((d % 256 == 0) ? d / 256 : 0) {
+    case 1: norm_launch<act_t, 1>(p, which, s, lib, ws, fg, fb, st); break;
+    case 2: norm_launch<act_t, 2>(p, which, s, lib, ws, fg, fb, st); break;
+    case 3: norm_launch<act_t, 3>(p, which, s, lib, ws, fg, fb, st); break;
+    case 4: norm_launch<act_t, 4>(p, which, s, lib, ws, fg, fb, st); break;
+    case 5: norm_launch<act_t, 5>(p, which, s, lib, ws, fg, fb, st); break;
+    case 6: norm_launch<act_t, 6>(p, which, s, lib, ws, fg, fb, st); break;
+    case 7: norm_launch<act_t, 7>(p, which, s, lib, ws, fg, fb, st); break;
+    case 8: norm_launch<act_t, 8>(p, which, s, lib, ws, fg, fb, st); break;
+    default: norm_launch<act_t, 0>(p, which, s, lib, ws, fg, fb, st); break;
+  }
   return hipGetLastError();
 }
 

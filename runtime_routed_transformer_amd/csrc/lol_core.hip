@@ -121,7 +121,9 @@ size_t workspace_layout(const Plan &p, char *base, Workspace *ws) {
   };
   Workspace w;
   w.flags = (uint32_t *)carve(16);
-  w.mu = (float *)carve(ns * d * 4);
+  w.zpart = (float *)carve(ns * (d / 64) * (size_t)c.L * 4);
+  w.zpart0 = (float *)carve((size_t)c.batch * (d / 64) * c.L * 4);
+  w.zlog = (float *)carve(ns * (size_t)c.L * 4);
   w.win_exp = (int32_t *)carve(ns * 4);
   w.win_gate = (float *)carve(ns * 4);
   w.win_row0 = (int32_t *)carve(ns * 4);
@@ -208,10 +210,8 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     g.depth = l;
     g.delta = (int)(((long long)l * c.S) % c.W);
     g.K = (c.n - 1 + g.delta) / c.W + 1;
-    LOL_TRY(KK_POOL, launch_pool(p, g, s, ws.mu, st));
+    LOL_TRY(KK_POOL, launch_pool(p, g, s, ws, *rt, st));
     LOL_TRY(KK_ROUTE, launch_route(p, g, s, ws, *rt, forced_expert, forced_gate, path, st));
-    LOL_TRY(KK_BUCKET, launch_bucket(p, g, ws, st));
-    LOL_TRY(KK_ROWMETA, launch_rowmeta(p, g, ws, st));
     LOL_TRY(KK_NORM_ATTN, launch_norm(p, g, 0, s, *lib, ws, st));
     GemmArgs a{};
     a.A = ws.u;

@@ -43,7 +43,9 @@ struct DepthGeom {
 // Device buffers carved from the caller's workspace.
 struct Workspace {
   uint32_t *flags;     // [4]
-  float *mu;           // [B*K_max][d]       window means
+  float *zpart;        // [B*K_max][d/64][L] router logits of each window mean, per 64-column chunk
+  float *zpart0;       // [B][d/64][L]       the same for the first-window input (e_l + s_0)/2
+  float *zlog;         // [B*K_max][L]       router logits of every window
   int32_t *win_exp;    // [B*K_max]          expert of each window slot (-1 = none)
   float *win_gate;     // [B*K_max]
   int32_t *win_row0;   // [B*K_max]          first grouped row of each window slot
@@ -74,12 +76,14 @@ struct Plan {
 size_t workspace_layout(const Plan &p, char *base, Workspace *ws);
 
 // ---- launchers (all asynchronous on `st`) ----
-hipError_t launch_pool(const Plan &p, const DepthGeom &g, const float *s, float *mu, hipStream_t st);
+// window means, contracted with the router weights per 64-column chunk
+hipError_t launch_pool(const Plan &p, const DepthGeom &g, const float *s, const Workspace &ws,
+                       const lol_router &rt, hipStream_t st);
+// router (logits of the prefix inputs, softmax, choice, forcing), expert
+// bucketing and grouped-row metadata
 hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const Workspace &ws,
                         const lol_router &rt, const int32_t *forced_expert, const float *forced_gate,
                         const lol_path *path, hipStream_t st);
-hipError_t launch_bucket(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st);
-hipError_t launch_rowmeta(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st);
 // clears the flag word and builds the RoPE table
 hipError_t launch_setup(const Plan &p, const Workspace &ws, hipStream_t st);
 // which = 0: u = FiLM(Norm_attn(s[row_tok])) ; which = 1: u = FiLM(Norm_ffn(h))

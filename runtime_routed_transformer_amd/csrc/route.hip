@@ -26,20 +26,43 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// butterfly reductions inside aligned groups of G lanes (G a power of two)
+__device__ __forceinline__ float group_max(float v, int G) {
+  for (int o = G >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float group_sum(float v, int G) {
+  for (int o = G >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int group_min(int v, int G) {
+  for (int o = G >> 1; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
 
-// a2: mu[slot][c] = mean of s over the window's tokens.  Block = (window,
-// 64-column chunk); 16 row phases x 16 float4 columns, fixed-order reduction.
-__global__ void __launch_bounds__(256) k_pool(const float *__restrict__ s, float *__restrict__ mu,
-                                              int n, int d, int W, int delta, int K, int K_max) {
-  const int b = blockIdx.x / K, k = blockIdx.x % K;
+// a2, and the router's linear layer applied to it.  Block = (window,
+// 64-column chunk): mu = mean of s over the window's tokens in the chunk
+// (16 row phases x 16 float4 columns, fixed-order reduction), then
+// zpart[window][chunk][m] = sum_c W_r[m][c] mu[c] for every expert m.  The
+// router input of window k > 0 is the mean of the earlier windows' means, so
+// its logits are the mean of their zpart sums (the layer is linear); the
+// first window's input (e_l + s_0) / 2 is contracted here as well, by the
+// blocks of window 0.
+__global__ void __launch_bounds__(256) k_pool(const float *__restrict__ s,
+                                              const float *__restrict__ w_r,
+                                              const float *__restrict__ e_depth,
+                                              float *__restrict__ zpart, float *__restrict__ zpart0,
+                                              int n, int d, int L, int W, int delta, int K,
+                                              int K_max, int depth) {
+  const int b = blockIdx.x / K, k = blockIdx.x % K, chunk = blockIdx.y, nch = gridDim.y;
   const int start = win_start(k, W, delta), len = win_end(k, W, delta, n) - start + 1;
   const int c4 = threadIdx.x & 15, ph = threadIdx.x >> 4;
-  const int col = blockIdx.y * 64 + c4 * 4;
+  const int col = chunk * 64 + c4 * 4;
   const float *base = s + ((size_t)b * n + start) * d + col;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int r = ph; r < len; r += 16) {
@@ -47,6 +70,7 @@ __global__ void __launch_bounds__(256) k_pool(const float *__restrict__ s, float
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
   __shared__ float4 red[16][16];
+  __shared__ float mu[64], r0[64];
   red[ph][c4] = acc;
   __syncthreads();
   if (ph == 0) {
@@ -55,120 +79,150 @@ __global__ void __launch_bounds__(256) k_pool(const float *__restrict__ s, float
       t.x += red[i][c4].x; t.y += red[i][c4].y; t.z += red[i][c4].z; t.w += red[i][c4].w;
     }
     const float fl = (float)len;
-    t.x /= fl; t.y /= fl; t.z /= fl; t.w /= fl;
-    *reinterpret_cast<float4 *>(mu + ((size_t)b * K_max + k) * d + col) = t;
+    mu[c4 * 4 + 0] = t.x / fl; mu[c4 * 4 + 1] = t.y / fl;
+    mu[c4 * 4 + 2] = t.z / fl; mu[c4 * 4 + 3] = t.w / fl;
   }
-}
-
-// a3 + a4: one block per window slot (b, k).  r_0 = (e_l + s_0)/2, r_k =
-// mean of mu_0..mu_{k-1}; z = W_r r + b_r (fp32); a = softmax(z); choice =
-// first argmax of a + bias; gate = a_choice; forcing as documented in the
-// C ABI.  Slots k >= K get expert -1.
-__global__ void __launch_bounds__(256) k_route(
-    const float *__restrict__ s, const float *__restrict__ mu, const float *__restrict__ w_r,
-    const float *__restrict__ b_r, const float *__restrict__ e_depth, const float *__restrict__ bias,
-    const int32_t *__restrict__ forced_e, const float *__restrict__ forced_g,
-    int32_t *__restrict__ win_exp, float *__restrict__ win_gate, int32_t *__restrict__ path_e,
-    float *__restrict__ path_g, float *__restrict__ path_m, uint32_t *__restrict__ flags, int n,
-    int d, int L, int K, int K_max, int B, int depth) {
-  extern __shared__ float r[];  // [d]
-  __shared__ float z[kMaxExperts];
-  const int slot = blockIdx.x, b = slot / K_max, k = slot % K_max;
-  const size_t pidx = ((size_t)depth * B + b) * K_max + k;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (k >= K) {
-    if (tid == 0) {
-      win_exp[slot] = -1;
-      win_gate[slot] = 0.f;
-      if (path_e) path_e[pidx] = -1;
-      if (path_g) path_g[pidx] = 0.f;
-      if (path_m) path_m[pidx] = 0.f;
-    }
-    return;
-  }
-  for (int c = tid; c < d; c += blockDim.x) {
-    float v;
-    if (k == 0) {
-      v = 0.5f * (e_depth[(size_t)depth * d + c] + s[(size_t)b * n * d + c]);
-    } else {
-      float acc = 0.f;
-      for (int j = 0; j < k; ++j) acc += mu[((size_t)b * K_max + j) * d + c];
-      v = acc / (float)k;
-    }
-    r[c] = v;
+  if (k == 0 && threadIdx.x < 64) {
+    const int c = chunk * 64 + threadIdx.x;
+    r0[threadIdx.x] = 0.5f * (e_depth[(size_t)depth * d + c] + s[(size_t)b * n * d + c]);
   }
   __syncthreads();
+  // one wave per expert (4 waves), lane = column of the chunk
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int m = wave; m < L; m += 4) {
-    float acc = 0.f;
-    for (int c = lane; c < d; c += 64) acc += w_r[(size_t)m * d + c] * r[c];
-    acc = wave_sum(acc);
-    if (lane == 0) z[m] = acc + (b_r ? b_r[m] : 0.f);
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  const bool live = lane < L;
-  const float zl = live ? z[lane] : -INFINITY;
-  const float zmax = wave_max(zl);
-  const float ez = live ? expf(zl - zmax) : 0.f;
-  const float a = ez / wave_sum(ez);
-  const float sc = live ? a + (bias ? bias[lane] : 0.f) : -INFINITY;
-  const float top = wave_max(sc);
-  // lowest index attaining the maximum
-  int cand = (live && sc == top) ? lane : 64;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o, 64));
-  const int rho = cand;
-  const float second = wave_max((live && lane != rho) ? sc : -INFINITY);
-  const float margin = (L > 1) ? top - second : INFINITY;
-  int chosen = rho;
-  if (forced_e) {
-    const int fe = forced_e[pidx];
-    if (fe >= L) {
-      if (lane == 0) atomicOr(flags, (uint32_t)LOL_FLAG_BAD_FORCED_ID);
-    } else if (fe >= 0) {
-      chosen = fe;
+    const float w = w_r[(size_t)m * d + chunk * 64 + lane];
+    const float z = wave_sum(w * mu[lane]);
+    if (lane == 0) zpart[(((size_t)b * K_max + k) * nch + chunk) * L + m] = z;
+    if (k == 0) {
+      const float z0 = wave_sum(w * r0[lane]);
+      if (lane == 0) zpart0[((size_t)b * nch + chunk) * L + m] = z0;
     }
-  }
-  float alpha = __shfl(a, chosen, 64);
-  if (forced_g) {
-    const float fg = forced_g[pidx];
-    if (!isnan(fg)) alpha = fg;
-  }
-  if (lane == 0) {
-    win_exp[slot] = chosen;
-    win_gate[slot] = alpha;
-    if (path_e) path_e[pidx] = chosen;
-    if (path_g) path_g[pidx] = alpha;
-    if (path_m) path_m[pidx] = margin;
   }
 }
 
-// a5: expert bucketing in one block.  Windows are grouped by expert, in slot
-// order inside each expert (stable), so every expert's tokens form one
-// contiguous range of grouped rows; the M-tile table lists (expert, first
-// row) for every kTileM-row tile of every expert.
-__global__ void __launch_bounds__(1024) k_bucket(const int32_t *__restrict__ win_exp,
-                                                 int32_t *__restrict__ win_row0,
-                                                 int32_t *__restrict__ ecount,
-                                                 int32_t *__restrict__ toff_out,
-                                                 int32_t *__restrict__ mtile, int max_mtiles,
-                                                 int32_t *__restrict__ mtile2, int max_mtiles2,
-                                                 int32_t *__restrict__ mcount, int n,
-                                                 int W, int delta, int K, int K_max, int n_slots,
-                                                 int L) {
+// a3 - a5 in one workgroup of 1024 threads (16 waves), for all documents:
+//  1. router logits: Y_j = sum over chunks of zpart_j (= W_r mu_j), then
+//     z_k = (Y_0 + .. + Y_{k-1}) / k + b_r for k > 0 and z_0 = the window-0
+//     contraction + b_r (one thread per (document, expert), running sum
+//     over the windows in order);
+//  2. per window (one wave each): a = softmax(z) in fp32, choice = lowest
+//     index attaining max(a + bias), gate = a_choice, margin = top1 - top2
+//     of a + bias, forcing as documented in the C ABI; slots k >= K get
+//     expert -1;
+//  3. bucketing: windows grouped by expert, in slot order inside an expert
+//     (stable), so every expert's tokens form one contiguous range of grouped
+//     rows; per-expert counts and row offsets, the first grouped row of every
+//     window, and the M-tile tables (expert, first row) for kTileM- and
+//     kTileM2-row tiles;
+//  4. grouped-row metadata: token, window-local position, expert and gate of
+//     every grouped row.
+// Integer counts only (LDS atomics on integers), so the result does not
+// depend on thread timing.
+__global__ void __launch_bounds__(1024) k_route_all(
+    const float *__restrict__ zpart, float *__restrict__ zpart0, const float *__restrict__ b_r,
+    const float *__restrict__ bias, const int32_t *__restrict__ forced_e,
+    const float *__restrict__ forced_g, int32_t *__restrict__ win_exp, float *__restrict__ win_gate,
+    int32_t *__restrict__ win_row0, int32_t *__restrict__ path_e, float *__restrict__ path_g,
+    float *__restrict__ path_m, uint32_t *__restrict__ flags, int32_t *__restrict__ ecount,
+    int32_t *__restrict__ toff_out, int32_t *__restrict__ mtile, int max_mtiles,
+    int32_t *__restrict__ mtile2, int max_mtiles2, int32_t *__restrict__ mcount,
+    int32_t *__restrict__ row_tok, int32_t *__restrict__ row_pos, int32_t *__restrict__ row_exp,
+    float *__restrict__ row_gate, float *__restrict__ zlog, int n, int nch, int L, int W, int delta,
+    int K, int K_max, int B, int depth) {
   __shared__ int s_exp[kMaxSlots];
   __shared__ int s_len[kMaxSlots];
   __shared__ int cnt_w[kMaxExperts], cnt_t[kMaxExperts];
   __shared__ int toff[kMaxExperts + 1], moff[kMaxExperts + 1], moff2[kMaxExperts + 1];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < kMaxExperts; i += blockDim.x) { cnt_w[i] = 0; cnt_t[i] = 0; }
-  for (int slot = tid; slot < n_slots; slot += blockDim.x) {
-    const int k = slot % K_max;
-    const int e = win_exp[slot];
-    s_exp[slot] = e;
-    s_len[slot] = (k < K && e >= 0) ? win_end(k, W, delta, n) - win_start(k, W, delta) + 1 : 0;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n_slots = B * K_max;
+
+  // 1. logits of every window, zlog[b][k][m]: first Y_k = sum over chunks
+  // (slot k >= 1 holds Y_{k-1}; slot 0 the window-0 contraction), then one
+  // wave per (document, expert) turns Y into running means with a scan over k
+  for (int i = tid; i < B * K * L; i += blockDim.x) {
+    const int m = i % L, k = (i / L) % K, b = i / (L * K);
+    float y = 0.f;
+    if (k == 0) {
+      for (int c = 0; c < nch; ++c) y += zpart0[((size_t)b * nch + c) * L + m];
+    } else {
+      for (int c = 0; c < nch; ++c) y += zpart[(((size_t)b * K_max + k - 1) * nch + c) * L + m];
+    }
+    zlog[((size_t)b * K_max + k) * L + m] = y;
   }
   __syncthreads();
+  for (int bm = wave; bm < B * L; bm += 16) {
+    const int b = bm / L, m = bm % L;
+    const float br = b_r ? b_r[m] : 0.f;
+    float carry = 0.f;
+    for (int k0 = 0; k0 < K; k0 += 64) {
+      const int k = k0 + lane;
+      float *zp = zlog + ((size_t)b * K_max + k) * L + m;
+      const float y = k < K ? *zp : 0.f;
+      // inclusive scan of Y over k >= 1 (slot 0 is not part of the prefix)
+      float v = (k >= 1) ? y : 0.f;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+      }
+      v += carry;
+      if (k < K) *zp = (k == 0 ? y : v / (float)k) + br;
+      carry = __shfl(v, 63, 64);
+    }
+  }
+  for (int i = tid; i < kMaxExperts; i += blockDim.x) { cnt_w[i] = 0; cnt_t[i] = 0; }
+  __syncthreads();
+
+  // 2. score and select: groups of G lanes (G = the power of two >= L), one
+  // window per group, lane = expert inside it
+  const int G = L <= 1 ? 1 : 1 << (32 - __clz(L - 1));
+  const int gl = lane & (G - 1), per_wave = 64 / G;
+  for (int slot0 = wave * per_wave; slot0 < n_slots; slot0 += 16 * per_wave) {
+    const int slot = slot0 + lane / G;
+    const bool in_range = slot < n_slots;
+    const int b = slot / K_max, k = slot % K_max;
+    const bool win_ok = in_range && k < K;
+    const size_t pidx = ((size_t)depth * B + b) * K_max + k;
+    const bool live = win_ok && gl < L;
+    const float zl = live ? zlog[(size_t)slot * L + gl] : -INFINITY;
+    const float zmax = group_max(zl, G);
+    const float ez = live ? expf(zl - zmax) : 0.f;
+    const float a = ez / group_sum(ez, G);
+    const float sc = live ? a + (bias ? bias[gl] : 0.f) : -INFINITY;
+    const float top = group_max(sc, G);
+    // lowest index attaining the maximum
+    const int rho = group_min((live && sc == top) ? gl : 64, G);
+    const float second = group_max((live && gl != rho) ? sc : -INFINITY, G);
+    const float margin = (L > 1) ? top - second : INFINITY;
+    int chosen = rho;
+    if (forced_e && win_ok) {
+      const int fe = forced_e[pidx];
+      if (fe >= L) {
+        if (gl == 0) atomicOr(flags, (uint32_t)LOL_FLAG_BAD_FORCED_ID);
+      } else if (fe >= 0) {
+        chosen = fe;
+      }
+    }
+    // the chosen expert's probability, from lane (group base + chosen)
+    float alpha = __shfl(a, (lane & ~(G - 1)) + (chosen & (G - 1)), 64);
+    if (forced_g && win_ok) {
+      const float fg = forced_g[pidx];
+      if (!isnan(fg)) alpha = fg;
+    }
+    if (in_range && gl == 0) {
+      const int e = win_ok ? chosen : -1;
+      win_exp[slot] = e;
+      win_gate[slot] = win_ok ? alpha : 0.f;
+      s_exp[slot] = e;
+      s_len[slot] = win_ok ? win_end(k, W, delta, n) - win_start(k, W, delta) + 1 : 0;
+      if (path_e) path_e[pidx] = e;
+      if (path_g) path_g[pidx] = win_ok ? alpha : 0.f;
+      if (path_m) path_m[pidx] = win_ok ? margin : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // 3. bucketing
   for (int slot = tid; slot < n_slots; slot += blockDim.x) {
     const int e = s_exp[slot];
     if (e >= 0) {
@@ -198,16 +252,26 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t *__restrict__ win
   __syncthreads();
   for (int e = tid; e <= L; e += blockDim.x) toff_out[e] = toff[e];
   for (int e = tid; e < L; e += blockDim.x) ecount[e] = cnt_w[e];
-  for (int slot = tid; slot < n_slots; slot += blockDim.x) {
-    const int e = s_exp[slot];
-    if (e < 0) {
-      win_row0[slot] = -1;
-      continue;
+  // first grouped row of every window: one wave per expert walks the slots in
+  // order, 64 at a time, with an exclusive scan of the lengths
+  for (int e = wave; e < L; e += 16) {
+    int base = toff[e];
+    for (int s0 = 0; s0 < n_slots; s0 += 64) {
+      const int slot = s0 + lane;
+      const bool mine = slot < n_slots && s_exp[slot] == e;
+      int v = mine ? s_len[slot] : 0;
+      int incl = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      if (mine) win_row0[slot] = base + incl - v;
+      base += __shfl(incl, 63, 64);
     }
-    int before = 0;
-    for (int t = 0; t < slot; ++t) before += (s_exp[t] == e) ? s_len[t] : 0;
-    win_row0[slot] = toff[e] + before;
   }
+  for (int slot = tid; slot < n_slots; slot += blockDim.x)
+    if (s_exp[slot] < 0) win_row0[slot] = -1;
   for (int i = tid; i < max_mtiles; i += blockDim.x) {
     int e = -1, row0 = 0;
     if (i < moff[L]) {
@@ -228,31 +292,23 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t *__restrict__ win
     mtile2[2 * i] = e;
     mtile2[2 * i + 1] = row0;
   }
-}
+  __syncthreads();  // win_row0 complete
 
-// Grouped-row metadata: token, window-local position, expert and gate of
-// every grouped row.
-__global__ void __launch_bounds__(256) k_rowmeta(const int32_t *__restrict__ win_exp,
-                                                 const float *__restrict__ win_gate,
-                                                 const int32_t *__restrict__ win_row0,
-                                                 int32_t *__restrict__ row_tok,
-                                                 int32_t *__restrict__ row_pos,
-                                                 int32_t *__restrict__ row_exp,
-                                                 float *__restrict__ row_gate, int n, int W,
-                                                 int delta, int K_max) {
-  const int slot = blockIdx.x;
-  const int e = win_exp[slot];
-  if (e < 0) return;
-  const int b = slot / K_max, k = slot % K_max;
-  const int start = win_start(k, W, delta), len = win_end(k, W, delta, n) - start + 1;
-  const int base = win_row0[slot];
-  const float g = win_gate[slot];
-  for (int p = threadIdx.x; p < len; p += blockDim.x) {
-    const int row = base + p;
-    row_tok[row] = b * n + start + p;
-    row_pos[row] = p;
-    row_exp[row] = e;
-    row_gate[row] = g;
+  // 4. grouped-row metadata, one wave per window
+  for (int slot = wave; slot < n_slots; slot += 16) {
+    const int e = s_exp[slot];
+    if (e < 0) continue;
+    const int b = slot / K_max, k = slot % K_max;
+    const int start = win_start(k, W, delta), len = s_len[slot];
+    const int base = win_row0[slot];
+    const float g = win_gate[slot];
+    for (int p = lane; p < len; p += 64) {
+      const int row = base + p;
+      row_tok[row] = b * n + start + p;
+      row_pos[row] = p;
+      row_exp[row] = e;
+      row_gate[row] = g;
+    }
   }
 }
 
@@ -272,36 +328,25 @@ __global__ void k_setup(uint32_t *__restrict__ flags, float *__restrict__ cs, in
 
 }  // namespace
 
-hipError_t launch_pool(const Plan &p, const DepthGeom &g, const float *s, float *mu, hipStream_t st) {
+hipError_t launch_pool(const Plan &p, const DepthGeom &g, const float *s, const Workspace &ws,
+                       const lol_router &rt, hipStream_t st) {
   dim3 grid(p.cfg.batch * g.K, p.cfg.d / 64);
-  hipLaunchKernelGGL(k_pool, grid, dim3(256), 0, st, s, mu, p.cfg.n, p.cfg.d, p.cfg.W, g.delta,
-                     g.K, p.K_max);
+  hipLaunchKernelGGL(k_pool, grid, dim3(256), 0, st, s, rt.w_r, rt.e_depth, ws.zpart, ws.zpart0,
+                     p.cfg.n, p.cfg.d, p.cfg.L, p.cfg.W, g.delta, g.K, p.K_max, g.depth);
   return hipGetLastError();
 }
 
 hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const Workspace &ws,
                         const lol_router &rt, const int32_t *forced_expert,
                         const float *forced_gate, const lol_path *path, hipStream_t st) {
-  const size_t smem = (size_t)p.cfg.d * sizeof(float);
-  hipLaunchKernelGGL(k_route, dim3(p.n_slots), dim3(256), smem, st, s, ws.mu, rt.w_r, rt.b_r,
-                     rt.e_depth, rt.expert_bias, forced_expert, forced_gate, ws.win_exp,
-                     ws.win_gate, path ? path->expert : nullptr, path ? path->gate : nullptr,
-                     path ? path->margin : nullptr, ws.flags, p.cfg.n, p.cfg.d, p.cfg.L, g.K,
-                     p.K_max, p.cfg.batch, g.depth);
-  return hipGetLastError();
-}
-
-hipError_t launch_bucket(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {
-  hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, st, ws.win_exp, ws.win_row0, ws.ecount,
-                     ws.toff, ws.mtile, ws.max_mtiles, ws.mtile2, ws.max_mtiles2, ws.mcount, p.cfg.n, p.cfg.W, g.delta, g.K, p.K_max,
-                     p.n_slots, p.cfg.L);
-  return hipGetLastError();
-}
-
-hipError_t launch_rowmeta(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {
-  hipLaunchKernelGGL(k_rowmeta, dim3(p.n_slots), dim3(256), 0, st, ws.win_exp, ws.win_gate,
-                     ws.win_row0, ws.row_tok, ws.row_pos, ws.row_exp, ws.row_gate, p.cfg.n,
-                     p.cfg.W, g.delta, p.K_max);
+  (void)s;
+  hipLaunchKernelGGL(k_route_all, dim3(1), dim3(1024), 0, st, ws.zpart, ws.zpart0, rt.b_r,
+                     rt.expert_bias, forced_expert, forced_gate, ws.win_exp, ws.win_gate,
+                     ws.win_row0, path ? path->expert : nullptr, path ? path->gate : nullptr,
+                     path ? path->margin : nullptr, ws.flags, ws.ecount, ws.toff, ws.mtile,
+                     ws.max_mtiles, ws.mtile2, ws.max_mtiles2, ws.mcount, ws.row_tok, ws.row_pos,
+                     ws.row_exp, ws.row_gate, ws.zlog, p.cfg.n, p.cfg.d / 64, p.cfg.L, p.cfg.W,
+                     g.delta, g.K, p.K_max, p.cfg.batch, g.depth);
   return hipGetLastError();
 }
 
