@@ -127,13 +127,21 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 // slice run close together in time on one XCD's L2.
 // ---------------------------------------------------------------------------
 constexpr int TM = 4, TN = 2;           // 32 x 32 blocks per wave
-constexpr int BMT = 64 * TM, BNT = 64 * TN;
+constexpr int BMT = 64 * TM;            // 2 wave rows
 constexpr int BK = 32;
-constexpr int NSTAGE = 3;
 constexpr int GM = 4;
-constexpr int STAGE_BYTES = (BMT + BNT) * BK * 2;
-constexpr int GEMM_LDS = NSTAGE * STAGE_BYTES;  // 72 KiB
 static_assert(BMT == kTileM2, "M tiles of the grouped GEMM are kTileM2 rows");
+// Two shapes of workgroup: WN = 2 wave columns (256 x 128 tile, 4 waves,
+// 3-stage ring of 72 KiB, two workgroups per CU) or WN = 4 (256 x 256 tile,
+// 8 waves, 4-stage ring of 128 KiB, one workgroup per CU).
+template <int WN> struct Shape {
+  static constexpr int NW = 2 * WN;                      // waves
+  static constexpr int BNT = 32 * TN * WN;               // weight rows per tile
+  static constexpr int NSTAGE = WN == 2 ? 3 : 4;
+  static constexpr int STAGE_BYTES = (BMT + BNT) * BK * 2;
+  static constexpr int LDS = NSTAGE * STAGE_BYTES;
+  static constexpr int PER_CU = WN == 2 ? 2 : 1;
+};
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
@@ -184,10 +192,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int EPI>
-__global__ void __launch_bounds__(256, 2) k_gemm_bf16(GemmParams P) {
+template <int EPI, int WN>
+__global__ void __launch_bounds__(128 * WN, Shape<WN>::PER_CU) k_gemm_bf16(GemmParams P) {
+  using S = Shape<WN>;
+  constexpr int NW = S::NW, BNT = S::BNT, NSTAGE = S::NSTAGE, STAGE_BYTES = S::STAGE_BYTES;
   constexpr int A_BYTES = BMT * BK * 2;
-  constexpr int AQ = BMT / 64, BQ = BNT / 64;  // 1-KiB load instructions per wave per stage
+  constexpr int AQ = BMT / 16 / NW, BQ = BNT / 16 / NW;  // 1-KiB load instructions per wave per stage
   constexpr int NQ = AQ + BQ;
   constexpr int NR = TM + TN;                  // fragment reads per 16-k step
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -217,13 +227,13 @@ __global__ void __launch_bounds__(256, 2) k_gemm_bf16(GemmParams P) {
   const bf16_t *src[NQ];
 #pragma unroll
   for (int i = 0; i < AQ; ++i) {
-    const int r = (wave + 4 * i) * 16 + lrow;              // row inside the A tile
+    const int r = (wave + NW * i) * 16 + lrow;             // row inside the A tile
     const int arow = min(row0 + r, row_end - 1);
     src[i] = A + (size_t)arow * K + ((lchunk ^ swz(r)) << 3);
   }
 #pragma unroll
   for (int i = 0; i < BQ; ++i) {
-    const int r = (wave + 4 * i) * 16 + lrow;              // row inside the B tile
+    const int r = (wave + NW * i) * 16 + lrow;             // row inside the B tile
     int wrow;
     if (EPI == EPI_SWIGLU) {
       // each wave column's 64 B rows: 32 gate rows, then the 32 up rows of
@@ -240,14 +250,14 @@ __global__ void __launch_bounds__(256, 2) k_gemm_bf16(GemmParams P) {
     char *base = smem + slot * STAGE_BYTES;
     const int koff = stage * BK;
 #pragma unroll
-    for (int i = 0; i < AQ; ++i) lds_dma16(src[i] + koff, base + (wave + 4 * i) * 1024);
+    for (int i = 0; i < AQ; ++i) lds_dma16(src[i] + koff, base + (wave + NW * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < BQ; ++i) lds_dma16(src[AQ + i] + koff, base + A_BYTES + (wave + 4 * i) * 1024);
+    for (int i = 0; i < BQ; ++i) lds_dma16(src[AQ + i] + koff, base + A_BYTES + (wave + NW * i) * 1024);
   };
 
   // ---- fragment addresses: lane reads row (lane & 31) of each 32-row block
   // at logical chunk 2 kk + (lane >> 5)
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int frow = lane & 31;
   const int sw = swz(frow);
   const int coff0 = ((lane >> 5) ^ sw) << 4, coff1 = ((2 + (lane >> 5)) ^ sw) << 4;
@@ -288,8 +298,10 @@ __global__ void __launch_bounds__(256, 2) k_gemm_bf16(GemmParams P) {
   //   stage kt-1 is free on every wave;
   //   read the first-step fragments of stage kt+1; load stage kt+NSTAGE-1
   //   into the free slot; MFMAs of the second step.
-  // The explicit LDS waits sit where the reads have had an MFMA block to
-  // arrive, so the compiler needs none of its own in front of the MFMAs.
+  // (Requesting stages one iteration earlier, into the slot of stage kt,
+  // measured no faster.)  The explicit LDS waits sit where the reads have
+  // had an MFMA block to arrive, so the compiler needs none of its own in
+  // front of the MFMAs.
   const int nk = K / BK;
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
@@ -301,7 +313,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm_bf16(GemmParams P) {
     stage_barrier<0, 0>();
   read_frags(fw0, fx0, 0, coff0);
   int kt = 0;
-  // steady state: at the barrier only stage kt+NSTAGE-2 may still be in
+  // steady state: at the barrier stages kt+2 .. kt+NSTAGE-2 may still be in
   // flight; stage kt+NSTAGE-1 goes into the slot of stage kt-1
   for (; kt + NSTAGE - 1 < nk; ++kt) {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): also settles scalar loads
@@ -509,12 +521,25 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   if (p.cfg.dtype == LOL_BF16) {
     P.mtile = ws.mtile2;
     P.mcount = ws.mcount + 1;
-    // weight rows per tile: BNT (SwiGLU: BNT/2 gate + BNT/2 up rows)
-    P.n_tiles_n = (EPI == EPI_SWIGLU) ? a.N / (BNT / 2) : a.N / BNT;
-    hipFuncSetAttribute((const void *)k_gemm_bf16<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        GEMM_LDS);
-    const int grid = ((ws.max_mtiles2 * P.n_tiles_n + 7) / 8) * 8;
-    hipLaunchKernelGGL((k_gemm_bf16<EPI>), dim3(grid), dim3(256), GEMM_LDS, st, P);
+    // 256 x 256 tiles for the wide projections (QKV, gate/up) when they
+    // divide N; 256 x 128 for the d-wide ones (O, down), where wider tiles
+    // would leave CUs idle
+    const int n_w = EPI == EPI_SWIGLU ? 2 * a.N : a.N;   // weight rows
+    if (n_w >= 2048 && n_w % Shape<4>::BNT == 0) {
+      using S = Shape<4>;
+      P.n_tiles_n = n_w / S::BNT;
+      hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, 4>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+      const int grid = ((ws.max_mtiles2 * P.n_tiles_n + 7) / 8) * 8;
+      hipLaunchKernelGGL((k_gemm_bf16<EPI, 4>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
+    } else {
+      using S = Shape<2>;
+      P.n_tiles_n = n_w / S::BNT;
+      hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, 2>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+      const int grid = ((ws.max_mtiles2 * P.n_tiles_n + 7) / 8) * 8;
+      hipLaunchKernelGGL((k_gemm_bf16<EPI, 2>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
+    }
   } else {
     P.n_tiles_n = a.N / FBN;
     hipLaunchKernelGGL(k_gemm_f32<EPI>, dim3(ws.max_mtiles * P.n_tiles_n), dim3(256), 0, st, P);
