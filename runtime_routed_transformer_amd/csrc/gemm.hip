@@ -381,38 +381,72 @@ __global__ void __launch_bounds__(128 * WN, Shape<WN>::PER_CU) k_gemm_bf16(GemmP
         *reinterpret_cast<float4 *>(stage_f + sslot(lane & 31, c) * 4) = v;
       }
     // read back whole rows: lane -> row rr (+ RPP * pass), 8 columns from 4 * cc
+    constexpr int NP = 32 / RPP;
+    const int col = col_base + cc * 4;
+    int row[NP];
+    bool ok[NP];
+    float4 v0[NP], v1[NP];
 #pragma unroll
-    for (int pass = 0; pass < 32 / RPP; ++pass) {
+    for (int pass = 0; pass < NP; ++pass) {
       const int r = rr + pass * RPP;
-      const float4 v0 = *reinterpret_cast<const float4 *>(stage_f + sslot(r, cc) * 4);
-      const float4 v1 = *reinterpret_cast<const float4 *>(stage_f + sslot(r, cc + 1) * 4);
-      const int row = row0 + wm * TM * 32 + im * 32 + r;
-      if (row >= row_end) continue;
-      const int col = col_base + cc * 4;
-      if (EPI == EPI_RESID) {
-        const size_t tok = (size_t)P.row_tok[row];
-        const float4 *sp = reinterpret_cast<const float4 *>(P.s + tok * P.ldc + col);
-        const float4 x0 = sp[0], x1 = sp[1];
-        float4 *hp = reinterpret_cast<float4 *>(reinterpret_cast<float *>(P.C) + (size_t)row * P.ldc + col);
-        hp[0] = make_float4(x0.x + v0.x, x0.y + v0.y, x0.z + v0.z, x0.w + v0.w);
-        hp[1] = make_float4(x1.x + v1.x, x1.y + v1.y, x1.z + v1.z, x1.w + v1.w);
-      } else if (EPI == EPI_BLEND) {
-        const size_t tok = (size_t)P.row_tok[row];
-        const float gt = P.row_gate[row];
-        float4 *sp = reinterpret_cast<float4 *>(P.s + tok * P.ldc + col);
-        const float4 *hp = reinterpret_cast<const float4 *>(P.h + (size_t)row * P.ldc + col);
-        const float4 x0 = sp[0], x1 = sp[1], h0 = hp[0], h1 = hp[1];
-        sp[0] = make_float4(x0.x + gt * (h0.x + v0.x - x0.x), x0.y + gt * (h0.y + v0.y - x0.y),
-                            x0.z + gt * (h0.z + v0.z - x0.z), x0.w + gt * (h0.w + v0.w - x0.w));
-        sp[1] = make_float4(x1.x + gt * (h1.x + v1.x - x1.x), x1.y + gt * (h1.y + v1.y - x1.y),
-                            x1.z + gt * (h1.z + v1.z - x1.z), x1.w + gt * (h1.w + v1.w - x1.w));
-      } else {
+      v0[pass] = *reinterpret_cast<const float4 *>(stage_f + sslot(r, cc) * 4);
+      v1[pass] = *reinterpret_cast<const float4 *>(stage_f + sslot(r, cc + 1) * 4);
+      const int rw = row0 + wm * TM * 32 + im * 32 + r;
+      ok[pass] = rw < row_end;
+      row[pass] = ok[pass] ? rw : row_end - 1;   // rows past the expert: read a valid row, store nothing
+    }
+    if (EPI == EPI_RESID || EPI == EPI_BLEND) {
+      // every load of the block first (token ids, then the residual rows),
+      // then the arithmetic and the stores: the loads overlap each other
+      float *__restrict__ sres = P.s;
+      const float *__restrict__ hres = P.h;
+      size_t tok[NP];
+      float gt[NP];
+#pragma unroll
+      for (int pass = 0; pass < NP; ++pass) {
+        tok[pass] = (size_t)P.row_tok[row[pass]];
+        gt[pass] = EPI == EPI_BLEND ? P.row_gate[row[pass]] : 0.f;
+      }
+      float4 x0[NP], x1[NP], h0[NP], h1[NP];
+#pragma unroll
+      for (int pass = 0; pass < NP; ++pass) {
+        const float4 *sp = reinterpret_cast<const float4 *>(sres + tok[pass] * P.ldc + col);
+        x0[pass] = sp[0];
+        x1[pass] = sp[1];
+        if (EPI == EPI_BLEND) {
+          const float4 *hp = reinterpret_cast<const float4 *>(hres + (size_t)row[pass] * P.ldc + col);
+          h0[pass] = hp[0];
+          h1[pass] = hp[1];
+        }
+      }
+#pragma unroll
+      for (int pass = 0; pass < NP; ++pass) {
+        if (!ok[pass]) continue;
+        const float4 a0 = v0[pass], a1 = v1[pass], s0 = x0[pass], s1 = x1[pass];
+        if (EPI == EPI_RESID) {
+          float4 *hp = reinterpret_cast<float4 *>(reinterpret_cast<float *>(P.C) + (size_t)row[pass] * P.ldc + col);
+          hp[0] = make_float4(s0.x + a0.x, s0.y + a0.y, s0.z + a0.z, s0.w + a0.w);
+          hp[1] = make_float4(s1.x + a1.x, s1.y + a1.y, s1.z + a1.z, s1.w + a1.w);
+        } else {
+          const float g = gt[pass];
+          const float4 q0 = h0[pass], q1 = h1[pass];
+          float4 *sp = reinterpret_cast<float4 *>(sres + tok[pass] * P.ldc + col);
+          sp[0] = make_float4(s0.x + g * (q0.x + a0.x - s0.x), s0.y + g * (q0.y + a0.y - s0.y),
+                              s0.z + g * (q0.z + a0.z - s0.z), s0.w + g * (q0.w + a0.w - s0.w));
+          sp[1] = make_float4(s1.x + g * (q1.x + a1.x - s1.x), s1.y + g * (q1.y + a1.y - s1.y),
+                              s1.z + g * (q1.z + a1.z - s1.z), s1.w + g * (q1.w + a1.w - s1.w));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int pass = 0; pass < NP; ++pass) {
+        if (!ok[pass]) continue;
         uint4 pk;
-        pk.x = pack_bf16x2(v0.x, v0.y);
-        pk.y = pack_bf16x2(v0.z, v0.w);
-        pk.z = pack_bf16x2(v1.x, v1.y);
-        pk.w = pack_bf16x2(v1.z, v1.w);
-        *reinterpret_cast<uint4 *>(reinterpret_cast<bf16_t *>(P.C) + (size_t)row * P.ldc + col) = pk;
+        pk.x = pack_bf16x2(v0[pass].x, v0[pass].y);
+        pk.y = pack_bf16x2(v0[pass].z, v0[pass].w);
+        pk.z = pack_bf16x2(v1[pass].x, v1[pass].y);
+        pk.w = pack_bf16x2(v1[pass].z, v1[pass].w);
+        *reinterpret_cast<uint4 *>(reinterpret_cast<bf16_t *>(P.C) + (size_t)row[pass] * P.ldc + col) = pk;
       }
     }
   }
