@@ -562,15 +562,17 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
     if (n_w >= 2048 && n_w % Shape<4>::BNT == 0) {
       using S = Shape<4>;
       P.n_tiles_n = n_w / S::BNT;
-      hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, 4>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+      const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, 4>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+      if (e != hipSuccess) return e;
       const int grid = ((ws.max_mtiles2 * P.n_tiles_n + 7) / 8) * 8;
       hipLaunchKernelGGL((k_gemm_bf16<EPI, 4>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
     } else {
       using S = Shape<2>;
       P.n_tiles_n = n_w / S::BNT;
-      hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, 2>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+      const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, 2>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+      if (e != hipSuccess) return e;
       const int grid = ((ws.max_mtiles2 * P.n_tiles_n + 7) / 8) * 8;
       hipLaunchKernelGGL((k_gemm_bf16<EPI, 2>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
     }
