@@ -191,33 +191,55 @@ __global__ void __launch_bounds__(64) k_attn_simt(const act_t *__restrict__ qkv,
 }
 
 // bf16 window-causal attention on MFMA (v_mfma_f32_32x32x16_bf16).
-// Block = (window, head, chunk of 256 queries), 4 waves.  Keys and values
-// stream through LDS in chunks of 256 keys (K row-major with RoPE applied,
-// V transposed).  Each wave owns query blocks of 32 (wave w takes blocks w
-// and 7-w of the chunk, which balances the causal triangle) and computes
-// S^T = K Q^T, so every lane holds one query's scores for 16 of 32 keys:
-// the online softmax needs one exchange with the lane 32 apart.  Then
-// O^T += V^T P^T, with the key order inside each 16-key MFMA step permuted
-// to match where the scores already sit in the lane.
+// q and k arrive rotated (RoPE is applied in the QKV projection's epilogue).
+// Block = (window, head, chunk of 256 queries), 4 waves.  Keys and values of
+// a chunk of 256 keys are copied row-major into LDS by direct global-to-LDS
+// loads (no register staging), 16-byte chunks of each row XOR-swizzled so
+// that the fragment reads below are free of bank conflicts.  Each wave owns
+// query blocks of 32 (wave w takes blocks w and 7-w of the chunk, which
+// balances the causal triangle) and computes S^T = K Q^T, so every lane holds
+// one query's scores for 16 of 32 keys: the online softmax needs one exchange
+// with the lane 32 apart.  Then O^T += V^T P^T, where the V^T operand comes
+// from row-major V through the LDS transpose read (ds_read_b64_tr_b16: in
+// each group of 16 lanes, lane i receives element i % 4 of the 8-byte pieces
+// that lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4 address), and the key order
+// inside each 16-key MFMA step is the one in which the scores already sit.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+template <int DH> struct AttnLds {
+  static constexpr int RB = 2 * DH;        // bytes per K or V row
+  static constexpr int NCK = DH / 8;       // 16-byte chunks per row
+  static constexpr int RPI = 1024 / RB;    // rows per 1 KiB direct load
+  // K: physical chunk = logical ^ kswz(row).  16 lanes read one logical
+  // chunk of 16 consecutive rows; with this swizzle they cover all 64 banks.
+  static __device__ __forceinline__ int kswz(int r) { return (r / (256 / RB)) & (NCK - 1); }
+  // V: the transpose reads of one half-wave touch 4 consecutive rows and
+  // 64 bytes of each; for 128-byte rows, rows 2 and 3 of each group of 4
+  // move to the other half of the row.
+  static __device__ __forceinline__ int vswz(int r) { return DH == 64 ? ((r >> 1) & 1) << 2 : 0; }
+};
 
 template <int DH>
-__global__ void __launch_bounds__(256) k_attn_mfma(const bf16_t *__restrict__ qkv,
-                                                   bf16_t *__restrict__ o,
-                                                   const int32_t *__restrict__ win_exp,
-                                                   const int32_t *__restrict__ win_row0,
-                                                   const float *__restrict__ rope_cs, int n, int d,
-                                                   int W, int delta, int K_max, float qscale,
-                                                   int use_rope) {
-  constexpr int CH = 256;           // keys / queries per chunk
-  constexpr int LDKR = DH + 8;      // K row stride (elements)
-  constexpr int LDV = CH + 4;       // V^T row stride: 2-bank reads hit 32 distinct bank pairs
-  constexpr int HALF = DH / 2;
-  constexpr int KS = DH / 16;       // MFMA k-steps over the head dimension
-  constexpr int DB = DH / 32;       // 32-wide output blocks over the head dimension
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[CH * LDKR];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[DH * LDV];
+__global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__ qkv,
+                                                      bf16_t *__restrict__ o,
+                                                      const int32_t *__restrict__ win_exp,
+                                                      const int32_t *__restrict__ win_row0, int n,
+                                                      int d, int W, int delta, int K_max,
+                                                      float qscale) {
+  using LY = AttnLds<DH>;
+  constexpr int CH = 256;            // keys / queries per chunk
+  constexpr int RB = LY::RB, NCK = LY::NCK, RPI = LY::RPI;
+  constexpr int KS = DH / 16;        // MFMA k-steps over the head dimension
+  constexpr int DB = DH / 32;        // 32-wide output blocks over the head dimension
+  constexpr int NI = CH * RB / 1024 / 4;  // 1 KiB loads per wave per operand
+  __shared__ __attribute__((aligned(1024))) char lds[2 * CH * RB];
+  char *const Kl = lds;
+  char *const Vl = lds + CH * RB;
   const int slot = blockIdx.x, h = blockIdx.y, qc = blockIdx.z;
   if (win_exp[slot] < 0) return;
   const int k = slot % K_max;
@@ -230,44 +252,17 @@ __global__ void __launch_bounds__(256) k_attn_mfma(const bf16_t *__restrict__ qk
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hl = lane >> 5, col = lane & 31;
 
-  // ---- this wave's two query blocks: Q fragments (RoPE, scale) in registers
-  int qblk[2] = {wave, 7 - wave};
+  // ---- this wave's two query blocks: Q fragments straight from HBM
+  const int qblk[2] = {wave, 7 - wave};
   bf16x8_t qf[2][KS];
   float m_run[2], l_run[2];
   f32x16_t acc[2][DB];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int qpos = q_begin + qblk[b] * 32 + col;         // window-local query position
-    const int qrow = min(qpos, len - 1);
-    const bf16_t *qp = qkv + (size_t)(base + qrow) * ld3 + h * DH;
-    float x[KS][8];
+    const int qrow = min(q_begin + qblk[b] * 32 + col, len - 1);
+    const bf16_t *qp = qkv + (size_t)(base + qrow) * ld3 + h * DH + hl * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 raw = *reinterpret_cast<const uint4 *>(qp + ks * 16 + hl * 8);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[ks][2 * j] = __uint_as_float(w[j] << 16);
-        x[ks][2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-      }
-    }
-    if (use_rope) {
-      const float *cs = rope_cs + (size_t)qrow * HALF * 2;
-#pragma unroll
-      for (int ks = 0; ks < KS / 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int dd = ks * 16 + hl * 8 + j;                // < HALF; partner dd + HALF
-          const float c0 = cs[2 * dd], s0 = cs[2 * dd + 1];
-          const float x1 = x[ks][j], x2 = x[ks + KS / 2][j];
-          x[ks][j] = x1 * c0 - x2 * s0;
-          x[ks + KS / 2][j] = x1 * s0 + x2 * c0;
-        }
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qf[b][ks][j] = (__bf16)(x[ks][j] * qscale);
+    for (int ks = 0; ks < KS; ++ks) qf[b][ks] = *reinterpret_cast<const bf16x8_t *>(qp + ks * 16);
     m_run[b] = -INFINITY;
     l_run[b] = 0.f;
 #pragma unroll
@@ -276,69 +271,30 @@ __global__ void __launch_bounds__(256) k_attn_mfma(const bf16_t *__restrict__ qk
       for (int i = 0; i < 16; ++i) acc[b][db][i] = 0.f;
   }
 
+  // ---- per-lane pieces of the direct loads: row lr of each 1 KiB, physical chunk pc
+  const int lr = lane / NCK, pc = lane % NCK;
+  // transpose-read addressing: lane (group g = lane/16, p = lane%16) reads
+  // row 4 (g/2) + p/4 (+8 for the second read) and the 4 columns from
+  // (g%2) 16 + 4 (p%4) of each 32-column block
+  const int g16 = lane >> 4, p16 = lane & 15;
+  const int tr_row = 4 * (g16 >> 1) + (p16 >> 2);
+  const int tr_col = (g16 & 1) * 16 + 4 * (p16 & 3);
+
   for (int kc = 0; kc <= qc; ++kc) {
     const int k_begin = kc * CH;
-    __syncthreads();
-    // ---- stage K (RoPE) row-major and V transposed; zero rows past the window
-    {
-      const int kpos = k_begin + tid;
-      float x[DH];
-      if (kpos < len) {
-        const bf16_t *kp = qkv + (size_t)(base + kpos) * ld3 + d + h * DH;
+    if (kc > 0) __syncthreads();   // every wave is done with the previous chunk
 #pragma unroll
-        for (int c = 0; c < DH; c += 8) {
-          const uint4 raw = *reinterpret_cast<const uint4 *>(kp + c);
-          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x[c + 2 * j] = __uint_as_float(w[j] << 16);
-            x[c + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-          }
-        }
-        if (use_rope) {
-          const float *cs = rope_cs + (size_t)kpos * HALF * 2;
-#pragma unroll
-          for (int j = 0; j < HALF; ++j) {
-            const float c0 = cs[2 * j], s0 = cs[2 * j + 1];
-            const float x1 = x[j], x2 = x[j + HALF];
-            x[j] = x1 * c0 - x2 * s0;
-            x[j + HALF] = x1 * s0 + x2 * c0;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < DH; ++c) x[c] = 0.f;
-      }
-#pragma unroll
-      for (int c = 0; c < DH; c += 8) {
-        uint4 pk;
-        pk.x = (uint32_t)f2bf(x[c]) | ((uint32_t)f2bf(x[c + 1]) << 16);
-        pk.y = (uint32_t)f2bf(x[c + 2]) | ((uint32_t)f2bf(x[c + 3]) << 16);
-        pk.z = (uint32_t)f2bf(x[c + 4]) | ((uint32_t)f2bf(x[c + 5]) << 16);
-        pk.w = (uint32_t)f2bf(x[c + 6]) | ((uint32_t)f2bf(x[c + 7]) << 16);
-        *reinterpret_cast<uint4 *>(&Ks[tid * LDKR + c]) = pk;
-      }
-      // V^T: thread = (key pair, half of the head dims); packed 32-bit writes
-      const int pr = tid & 127, dh0 = (tid >> 7) * HALF;
-      const int k0 = k_begin + 2 * pr;
-      const bf16_t *v0 = qkv + (size_t)(base + min(k0, len - 1)) * ld3 + 2 * d + h * DH + dh0;
-      const bf16_t *v1 = qkv + (size_t)(base + min(k0 + 1, len - 1)) * ld3 + 2 * d + h * DH + dh0;
-      const bool ok0 = k0 < len, ok1 = k0 + 1 < len;
-#pragma unroll
-      for (int c = 0; c < HALF; c += 8) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(v0 + c);
-        const uint4 b = *reinterpret_cast<const uint4 *>(v1 + c);
-        const uint32_t wa[4] = {ok0 ? a.x : 0u, ok0 ? a.y : 0u, ok0 ? a.z : 0u, ok0 ? a.w : 0u};
-        const uint32_t wb[4] = {ok1 ? b.x : 0u, ok1 ? b.y : 0u, ok1 ? b.z : 0u, ok1 ? b.w : 0u};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = (wa[j] & 0xFFFFu) | (wb[j] << 16);          // dim c+2j
-          const uint32_t hi = (wa[j] >> 16) | (wb[j] & 0xFFFF0000u);      // dim c+2j+1
-          *reinterpret_cast<uint32_t *>(&Vt[(dh0 + c + 2 * j) * LDV + 2 * pr]) = lo;
-          *reinterpret_cast<uint32_t *>(&Vt[(dh0 + c + 2 * j + 1) * LDV + 2 * pr]) = hi;
-        }
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int piece = wave + 4 * i;
+      const int r = piece * RPI + lr;                       // row inside the chunk
+      const int key = min(k_begin + r, len - 1);            // rows past the window repeat the last key
+      const bf16_t *rowp = qkv + (size_t)(base + key) * ld3 + h * DH;
+      __builtin_amdgcn_global_load_lds((gbl_void_t *)(rowp + d + ((pc ^ LY::kswz(r)) << 3)),
+                                       (lds_void_t *)(Kl + piece * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void_t *)(rowp + 2 * d + ((pc ^ LY::vswz(r)) << 3)),
+                                       (lds_void_t *)(Vl + piece * 1024), 16, 0, 0);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads have landed
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -351,13 +307,15 @@ __global__ void __launch_bounds__(256) k_attn_mfma(const bf16_t *__restrict__ qk
         f32x16_t sc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+        const int kr = kb * 32 + col;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
+          const int lc = 2 * ks + hl;
           const bf16x8_t kf =
-              *reinterpret_cast<const bf16x8_t *>(&Ks[(kb * 32 + col) * LDKR + ks * 16 + hl * 8]);
+              *reinterpret_cast<const bf16x8_t *>(Kl + kr * RB + ((lc ^ LY::kswz(kr)) << 4));
           sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[b][ks], sc, 0, 0, 0);
         }
-        // sc[i] = score(key = k_begin + kb*32 + (i/4)*8 + 4*hl + i%4, query q), log2 units
+        // sc[i] = q.k for key = k_begin + kb*32 + (i/4)*8 + 4*hl + i%4, query q
         if (kc == qc && kb == qblk[b]) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -370,38 +328,43 @@ __global__ void __launch_bounds__(256) k_attn_mfma(const bf16_t *__restrict__ qk
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run[b], mx);
-        const float corr = exp2f(m_run[b] - m_new);
+        // softmax weights 2^((s - m) * log2(e) / sqrt(d_head)); the raw
+        // exp2 is exact to about 1 ulp and flushes tiny weights to zero
+        const float mc = m_new * qscale;
+        const float corr = __builtin_amdgcn_exp2f(m_run[b] * qscale - mc);
         float p[16], rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          p[i] = exp2f(sc[i] - m_new);
+          p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], qscale, -mc));
           rs += p[i];
         }
         rs += __shfl_xor(rs, 32, 64);
         l_run[b] = l_run[b] * corr + rs;
         m_run[b] = m_new;
+        if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {   // a running max moved
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+          for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[b][db][i] *= corr;
+            for (int i = 0; i < 16; ++i) acc[b][db][i] *= corr;
+        }
 #pragma unroll
         for (int step = 0; step < 2; ++step) {
           bf16x8_t pb;
 #pragma unroll
           for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * step + j];
-          const int key0 = kb * 32 + 16 * step + 4 * hl;
+          const int vr = kb * 32 + 16 * step + tr_row;     // rows vr (keys +0..3) and vr + 8
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const bf16_t *vr = &Vt[(db * 32 + col) * LDV + key0];
-            const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 8);
-            bf16x8_t va;
-            const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              va[2 * j] = __builtin_bit_cast(__bf16, (bf16_t)(w[j] & 0xFFFFu));
-              va[2 * j + 1] = __builtin_bit_cast(__bf16, (bf16_t)(w[j] >> 16));
-            }
+            const int c = db * 32 + tr_col;                 // first of the 4 columns
+            const int off = ((c >> 3) << 4) + ((c & 4) << 1);
+            const int sw0 = LY::vswz(vr) << 4, sw1 = LY::vswz(vr + 8) << 4;
+            // (element-wise copies out of the v4i16 form of this read are
+            // miscompiled by this compiler: only its low dword survives)
+            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4_t *)(Vl + vr * RB + (off ^ sw0)));
+            const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4_t *)(Vl + (vr + 8) * RB + (off ^ sw1)));
+            const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             acc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[b][db], 0, 0, 0);
           }
         }
@@ -479,8 +442,7 @@ hipError_t attn_mfma(const Plan &p, const DepthGeom &g, const Workspace &ws, hip
   const float qscale = 1.4426950408889634f / sqrtf((float)DH);
   hipLaunchKernelGGL((k_attn_mfma<DH>), grid, dim3(256), 0, st,
                      reinterpret_cast<const bf16_t *>(ws.qkv), reinterpret_cast<bf16_t *>(ws.o),
-                     ws.win_exp, ws.win_row0, ws.rope_cs, p.cfg.n, p.cfg.d, p.cfg.W, g.delta,
-                     p.K_max, qscale, p.cfg.rope_theta != 0.f ? 1 : 0);
+                     ws.win_exp, ws.win_row0, p.cfg.n, p.cfg.d, p.cfg.W, g.delta, p.K_max, qscale);
   return hipGetLastError();
 }
 

@@ -50,13 +50,17 @@ struct GemmParams {
   void *C;
   float *s;
   const float *h;
+  const int32_t *row_pos;  // QKV_ROPE: window-local position of each grouped row
+  const float *rope_cs;    // QKV_ROPE: [W][half][2] cos, sin of p * theta^(-2j/d_head)
+  int rope_cols;           // QKV_ROPE: columns [0, rope_cols) hold q and k
+  int half;                // QKV_ROPE: d_head / 2
 };
 
 // Writes 4 consecutive logical columns [col, col+4) of grouped row `row`.
 template <int EPI, typename act_t>
 __device__ __forceinline__ void epilogue4(const GemmParams &P, int row, int col, float v0, float v1,
                                           float v2, float v3) {
-  if (EPI == EPI_STORE || EPI == EPI_GELU) {
+  if (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_QKV_ROPE) {
     if (EPI == EPI_GELU) { v0 = gelu_erf(v0); v1 = gelu_erf(v1); v2 = gelu_erf(v2); v3 = gelu_erf(v3); }
     act_t *C = reinterpret_cast<act_t *>(P.C) + (size_t)row * P.ldc + col;
     if (sizeof(act_t) == 2) {
@@ -438,6 +442,33 @@ __global__ void __launch_bounds__(128 * WN, Shape<WN>::PER_CU) k_gemm_bf16(GemmP
         }
       }
     } else {
+      if (EPI == EPI_QKV_ROPE && col_base < P.rope_cols) {
+        // rotate-half RoPE: column c of a head pairs with c +- d_head/2, which
+        // this wave staged too (its 64 columns hold whole heads)
+        const int hs = P.half / 4;                     // pair distance in 16-byte slots
+        const int jc = (cc * 4) % (2 * P.half);        // column of the first of 8 inside the head
+        const bool lo = jc < P.half;
+        const int j0 = lo ? jc : jc - P.half;          // frequency index of the first column
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+          const int r = rr + pass * RPP;
+          const float4 w0 = *reinterpret_cast<const float4 *>(stage_f + sslot(r, cc ^ hs) * 4);
+          const float4 w1 = *reinterpret_cast<const float4 *>(stage_f + sslot(r, (cc ^ hs) + 1) * 4);
+          const float4 *cs = reinterpret_cast<const float4 *>(
+              P.rope_cs + ((size_t)P.row_pos[row[pass]] * P.half + j0) * 2);
+          const float4 c01 = cs[0], c23 = cs[1], c45 = cs[2], c67 = cs[3];  // (cos, sin) pairs
+          const float sg = lo ? -1.f : 1.f;   // x' = x cos - x_pair sin (low half), x cos + x_pair sin (high)
+          float4 &a = v0[pass], &b = v1[pass];
+          a.x = a.x * c01.x + sg * w0.x * c01.y;
+          a.y = a.y * c01.z + sg * w0.y * c01.w;
+          a.z = a.z * c23.x + sg * w0.z * c23.y;
+          a.w = a.w * c23.z + sg * w0.w * c23.w;
+          b.x = b.x * c45.x + sg * w1.x * c45.y;
+          b.y = b.y * c45.z + sg * w1.y * c45.w;
+          b.z = b.z * c67.x + sg * w1.z * c67.y;
+          b.w = b.w * c67.z + sg * w1.w * c67.w;
+        }
+      }
 #pragma unroll
       for (int pass = 0; pass < NP; ++pass) {
         if (!ok[pass]) continue;
@@ -552,6 +583,12 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.C = a.C;
   P.s = a.s;
   P.h = a.h;
+  P.row_pos = ws.row_pos;
+  P.rope_cs = ws.rope_cs;
+  P.rope_cols = a.rope_cols;
+  P.half = p.d_head / 2;
+  if (EPI == EPI_QKV_ROPE && (p.cfg.dtype != LOL_BF16 || (p.d_head != 32 && p.d_head != 64)))
+    return hipErrorInvalidValue;  // fp32 mode rotates inside its attention kernel
   if (p.cfg.dtype == LOL_BF16) {
     P.mtile = ws.mtile2;
     P.mcount = ws.mcount + 1;
@@ -592,6 +629,7 @@ hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hi
     case EPI_SWIGLU: return launch_typed<EPI_SWIGLU>(p, ws, a, st);
     case EPI_GELU: return launch_typed<EPI_GELU>(p, ws, a, st);
     case EPI_BLEND: return launch_typed<EPI_BLEND>(p, ws, a, st);
+    case EPI_QKV_ROPE: return launch_typed<EPI_QKV_ROPE>(p, ws, a, st);
   }
   return hipErrorInvalidValue;
 }

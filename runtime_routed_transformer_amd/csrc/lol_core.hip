@@ -219,7 +219,11 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.N = 3 * c.d;
     a.K = c.d;
     a.w_expert_stride = (long long)3 * d * d;
-    a.epi = EPI_STORE;
+    // bf16 mode rotates q and k in the GEMM epilogue, before their one
+    // rounding to bf16; fp32 mode rotates inside its attention kernel
+    const bool rope_in_gemm = c.dtype == LOL_BF16 && c.rope_theta != 0.f;
+    a.epi = rope_in_gemm ? EPI_QKV_ROPE : EPI_STORE;
+    a.rope_cols = rope_in_gemm ? 2 * c.d : 0;
     a.C = ws.qkv;
     LOL_TRY(KK_GEMM_QKV, launch_gemm(p, ws, a, st));
     LOL_TRY(KK_ATTN, launch_attention(p, g, ws, st));

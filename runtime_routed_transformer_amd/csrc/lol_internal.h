@@ -97,6 +97,8 @@ enum GemmEpilogue {
   EPI_SWIGLU = 2,   // hid (act) = silu(acc_gate) * acc_up
   EPI_GELU = 3,     // hid (act) = gelu(acc)
   EPI_BLEND = 4,    // s[row_tok] += gate * (h + acc - s[row_tok])
+  EPI_QKV_ROPE = 5, // C (act) = acc, with RoPE at the row's window position on
+                    // the q and k columns (bf16 mode only)
 };
 
 struct GemmArgs {
@@ -110,6 +112,7 @@ struct GemmArgs {
   void *C;              // output (act or fp32 depending on epilogue)
   float *s;             // residual stream (RESID, BLEND)
   const float *h;       // BLEND
+  int rope_cols;        // QKV_ROPE: columns [0, rope_cols) are rotated (2 d; 0 = no RoPE)
 };
 hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st);
 
