@@ -310,6 +310,31 @@ __global__ void __launch_bounds__(128 * WN, Shape<WN>::PER_CU) k_gemm_bf16(GemmP
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < nk) issue(s, s);
+  // RoPE of the QKV epilogue: window positions of this lane's rows and the
+  // (cos, sin) table entries of its first 32-row block, requested now so
+  // that they arrive under the main loop
+  const int out_cols = (EPI == EPI_SWIGLU) ? BNT / 2 : BNT;
+  const int col_base = nt * out_cols + wn * (EPI == EPI_SWIGLU ? 32 : 64);
+  const bool rope = EPI == EPI_QKV_ROPE && col_base < P.rope_cols;
+  int rpos[EPI == EPI_QKV_ROPE ? TM : 1];
+  float4 tq[EPI == EPI_QKV_ROPE ? 4 : 1][2];
+  // (cos, sin) of frequencies jb .. jb + 3 at position pos, jb = 8 g + 4 (lane / 32)
+  auto rope_table = [&](int pos, float4 (&t)[EPI == EPI_QKV_ROPE ? 4 : 1][2]) {
+    const float *cs = P.rope_cs + (size_t)pos * P.half * 2 + 8 * (lane >> 5);
+#pragma unroll
+    for (int g = 0; g < (EPI == EPI_QKV_ROPE ? 4 : 1); ++g) {
+      if (g < 2 || P.half == 32) {
+        t[g][0] = *reinterpret_cast<const float4 *>(cs + 16 * g);
+        t[g][1] = *reinterpret_cast<const float4 *>(cs + 16 * g + 4);
+      }
+    }
+  };
+  if (EPI == EPI_QKV_ROPE && rope) {
+#pragma unroll
+    for (int im = 0; im < TM; ++im)
+      rpos[im] = P.row_pos[min(row0 + wm * TM * 32 + im * 32 + (lane & 31), row_end - 1)];
+    rope_table(rpos[0], tq);
+  }
   // stage 0 landed (stages 1 .. NSTAGE-2 may be in flight)
   if (nk >= NSTAGE - 1)
     stage_barrier<NQ * (NSTAGE - 2), 0>();
@@ -358,11 +383,50 @@ __global__ void __launch_bounds__(128 * WN, Shape<WN>::PER_CU) k_gemm_bf16(GemmP
   auto sslot = [&](int r, int c) {                    // physical slot of logical slot c
     return r * SLOTS + (c ^ (SLOTS == 16 ? (r & 15) : ((r >> 1) & 7)));
   };
-  const int out_cols = (EPI == EPI_SWIGLU) ? BNT / 2 : BNT;
-  const int col_base = nt * out_cols + wn * NC;
   const int rr = lane / LPR, cc = (lane % LPR) * 2;   // read-back row in pass, first slot
+  // RoPE (QKV, q and k columns): before staging, every lane holds one row of
+  // each 32-row block and, for each of its columns in the low half of a
+  // head, also the partner column d_head/2 to the right: acc[0] / acc[1] for
+  // d_head = 64 (the wave's 64 columns are one head), blocks g and g + 2 of
+  // the same acc for d_head = 32 (two heads).  The rotation is done there, on
+  // the fp32 accumulators.  The table entries of block 0 were requested at
+  // the start of the tile, those of block im + 1 are requested while block im
+  // is rotated and stored.
 #pragma unroll
   for (int im = 0; im < TM; ++im) {
+    if (EPI == EPI_QKV_ROPE && rope) {
+      float4 tn[EPI == EPI_QKV_ROPE ? 4 : 1][2];
+      if (im + 1 < TM) rope_table(rpos[im + 1], tn);
+      // pair (x, y) at frequency j: x' = x cos - y sin, y' = x sin + y cos
+      auto rot = [](f32x16 &a, int i, f32x16 &b, int k, float c, float sn) {
+        const float x = a[i], y = b[k];
+        a[i] = x * c - y * sn;
+        b[k] = x * sn + y * c;
+      };
+      if (P.half == 32) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          rot(acc[0][im], 4 * g + 0, acc[1][im], 4 * g + 0, tq[g][0].x, tq[g][0].y);
+          rot(acc[0][im], 4 * g + 1, acc[1][im], 4 * g + 1, tq[g][0].z, tq[g][0].w);
+          rot(acc[0][im], 4 * g + 2, acc[1][im], 4 * g + 2, tq[g][1].x, tq[g][1].y);
+          rot(acc[0][im], 4 * g + 3, acc[1][im], 4 * g + 3, tq[g][1].z, tq[g][1].w);
+        }
+      } else {  // d_head = 32
+#pragma unroll
+        for (int in = 0; in < TN; ++in)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            rot(acc[in][im], 4 * g + 0, acc[in][im], 4 * g + 8, tq[g][0].x, tq[g][0].y);
+            rot(acc[in][im], 4 * g + 1, acc[in][im], 4 * g + 9, tq[g][0].z, tq[g][0].w);
+            rot(acc[in][im], 4 * g + 2, acc[in][im], 4 * g + 10, tq[g][1].x, tq[g][1].y);
+            rot(acc[in][im], 4 * g + 3, acc[in][im], 4 * g + 11, tq[g][1].z, tq[g][1].w);
+          }
+      }
+      if (im + 1 < TM) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) { tq[g][0] = tn[g][0]; tq[g][1] = tn[g][1]; }
+      }
+    }
     // stage this 32-row block
 #pragma unroll
     for (int in = 0; in < (EPI == EPI_SWIGLU ? 1 : TN); ++in)
@@ -442,33 +506,6 @@ __global__ void __launch_bounds__(128 * WN, Shape<WN>::PER_CU) k_gemm_bf16(GemmP
         }
       }
     } else {
-      if (EPI == EPI_QKV_ROPE && col_base < P.rope_cols) {
-        // rotate-half RoPE: column c of a head pairs with c +- d_head/2, which
-        // this wave staged too (its 64 columns hold whole heads)
-        const int hs = P.half / 4;                     // pair distance in 16-byte slots
-        const int jc = (cc * 4) % (2 * P.half);        // column of the first of 8 inside the head
-        const bool lo = jc < P.half;
-        const int j0 = lo ? jc : jc - P.half;          // frequency index of the first column
-#pragma unroll
-        for (int pass = 0; pass < NP; ++pass) {
-          const int r = rr + pass * RPP;
-          const float4 w0 = *reinterpret_cast<const float4 *>(stage_f + sslot(r, cc ^ hs) * 4);
-          const float4 w1 = *reinterpret_cast<const float4 *>(stage_f + sslot(r, (cc ^ hs) + 1) * 4);
-          const float4 *cs = reinterpret_cast<const float4 *>(
-              P.rope_cs + ((size_t)P.row_pos[row[pass]] * P.half + j0) * 2);
-          const float4 c01 = cs[0], c23 = cs[1], c45 = cs[2], c67 = cs[3];  // (cos, sin) pairs
-          const float sg = lo ? -1.f : 1.f;   // x' = x cos - x_pair sin (low half), x cos + x_pair sin (high)
-          float4 &a = v0[pass], &b = v1[pass];
-          a.x = a.x * c01.x + sg * w0.x * c01.y;
-          a.y = a.y * c01.z + sg * w0.y * c01.w;
-          a.z = a.z * c23.x + sg * w0.z * c23.y;
-          a.w = a.w * c23.z + sg * w0.w * c23.w;
-          b.x = b.x * c45.x + sg * w1.x * c45.y;
-          b.y = b.y * c45.z + sg * w1.y * c45.w;
-          b.z = b.z * c67.x + sg * w1.z * c67.y;
-          b.w = b.w * c67.z + sg * w1.w * c67.w;
-        }
-      }
 #pragma unroll
       for (int pass = 0; pass < NP; ++pass) {
         if (!ok[pass]) continue;
