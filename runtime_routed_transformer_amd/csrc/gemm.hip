@@ -136,23 +136,28 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 // ranges (workgroup i runs on XCD i mod 8), so that tiles sharing an A or B
 // slice run close together in time on one XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int TM = 4, TN = 2;           // 32 x 32 blocks per wave
-constexpr int BMT = 64 * TM;            // 2 wave rows
+constexpr int TM = 4, TN = 2;           // 32 x 32 blocks per wave: 128 x 64 outputs
 constexpr int BK = 32;
 constexpr int GM = 4;
-static_assert(BMT == kTileM2, "M tiles of the grouped GEMM are kTileM2 rows");
-// Two shapes of workgroup: WN = 2 wave columns (256 x 128 tile, 4 waves,
-// 3-stage ring of 72 KiB, two workgroups per CU) or WN = 4 (256 x 256 tile,
-// 8 waves, 4-stage ring of 128 KiB, one workgroup per CU).
-template <int WN> struct Shape {
-  static constexpr int NW = 2 * WN;                      // waves
+// Three shapes of workgroup, WM x WN waves:
+//   2 x 2: 256 x 128 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
+//   2 x 4: 256 x 256 tile, 8 waves, 4-stage ring of 128 KiB, one per CU
+//          (persistent);
+//   1 x 4: 128 x 256 tile, 4 waves, 3-stage ring of 72 KiB, two per CU.
+// 2 x 2 and 1 x 4 move the same bytes per MAC (every wave still owns 128 x
+// 64 outputs); 1 x 4 uses the 128-row tile tables, which fit expert row
+// counts that are multiples of 128 without a partial tile.
+template <int WM, int WN> struct Shape {
+  static constexpr int NW = WM * WN;                     // waves
+  static constexpr int BMT = 32 * TM * WM;               // rows of A per tile
   static constexpr int BNT = 32 * TN * WN;               // weight rows per tile
-  static constexpr int NSTAGE = WN == 2 ? 3 : 4;
+  static constexpr int NSTAGE = NW == 8 ? 4 : 3;
   static constexpr int STAGE_BYTES = (BMT + BNT) * BK * 2;
   static constexpr int LDS = NSTAGE * STAGE_BYTES;
-  static constexpr int PER_CU = WN == 2 ? 2 : 1;
+  static constexpr int PER_CU = NW == 8 ? 1 : 2;
   // one workgroup per CU walks a range of tiles (see "Persistent tiles")
-  static constexpr bool PERSIST = WN == 4;
+  static constexpr bool PERSIST = NW == 8;
+  static_assert(BMT == kTileM || BMT == kTileM2, "M tiles come from the 128- or 256-row tables");
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -204,10 +209,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int EPI, int WN>
-__global__ void __launch_bounds__(128 * WN, Shape<WN>::PER_CU) k_gemm_bf16(GemmParams P) {
-  using S = Shape<WN>;
-  constexpr int NW = S::NW, BNT = S::BNT, NSTAGE = S::NSTAGE, STAGE_BYTES = S::STAGE_BYTES;
+template <int EPI, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_bf16(GemmParams P) {
+  using S = Shape<WM, WN>;
+  constexpr int NW = S::NW, BMT = S::BMT, BNT = S::BNT, NSTAGE = S::NSTAGE;
+  constexpr int STAGE_BYTES = S::STAGE_BYTES;
   constexpr int A_BYTES = BMT * BK * 2;
   constexpr int AQ = BMT / 16 / NW, BQ = BNT / 16 / NW;  // 1-KiB load instructions per wave per stage
   constexpr int NQ = AQ + BQ;
@@ -672,6 +678,28 @@ hipError_t cu_count(int *n) {
   return hipSuccess;
 }
 
+template <int EPI, int WM, int WN>
+hipError_t launch_shape(GemmParams P, const Workspace &ws, int n_w, hipStream_t st) {
+  using S = Shape<WM, WN>;
+  const bool tall = S::BMT == kTileM2;
+  P.mtile = tall ? ws.mtile2 : ws.mtile;
+  P.mcount = tall ? ws.mcount + 1 : ws.mcount;
+  P.n_tiles_n = n_w / S::BNT;
+  const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, WM, WN>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+  if (e != hipSuccess) return e;
+  int grid = (((tall ? ws.max_mtiles2 : ws.max_mtiles) * P.n_tiles_n + 7) / 8) * 8;
+  if (S::PERSIST) {
+    // one workgroup per CU, a multiple of the 8 XCDs, never more than the tiles
+    int ncu = 0;
+    const hipError_t ec = cu_count(&ncu);
+    if (ec != hipSuccess) return ec;
+    grid = min(grid, max(8, ncu / 8 * 8));
+  }
+  hipLaunchKernelGGL((k_gemm_bf16<EPI, WM, WN>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
+  return hipGetLastError();
+}
+
 template <int EPI>
 hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st) {
   GemmParams P;
@@ -697,35 +725,13 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   if (EPI == EPI_QKV_ROPE && (p.cfg.dtype != LOL_BF16 || (p.d_head != 32 && p.d_head != 64)))
     return hipErrorInvalidValue;  // fp32 mode rotates inside its attention kernel
   if (p.cfg.dtype == LOL_BF16) {
-    P.mtile = ws.mtile2;
-    P.mcount = ws.mcount + 1;
     // 256 x 256 tiles for the wide projections (QKV, gate/up) when they
-    // divide N; 256 x 128 for the d-wide ones (O, down), where wider tiles
-    // would leave CUs idle
+    // divide N; 128 x 256 for the d-wide ones (O, down), where wider tiles
+    // would leave CUs idle; 256 x 128 otherwise
     const int n_w = EPI == EPI_SWIGLU ? 2 * a.N : a.N;   // weight rows
-    if (n_w >= 2048 && n_w % Shape<4>::BNT == 0) {
-      using S = Shape<4>;
-      P.n_tiles_n = n_w / S::BNT;
-      const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, 4>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
-      if (e != hipSuccess) return e;
-      // persistent: one workgroup per CU, a multiple of the 8 XCDs, never
-      // more than the tiles
-      const int tiles = ((ws.max_mtiles2 * P.n_tiles_n + 7) / 8) * 8;
-      int ncu = 0;
-      const hipError_t ec = cu_count(&ncu);
-      if (ec != hipSuccess) return ec;
-      const int grid = min(tiles, max(8, ncu / 8 * 8));
-      hipLaunchKernelGGL((k_gemm_bf16<EPI, 4>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
-    } else {
-      using S = Shape<2>;
-      P.n_tiles_n = n_w / S::BNT;
-      const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, 2>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
-      if (e != hipSuccess) return e;
-      const int grid = ((ws.max_mtiles2 * P.n_tiles_n + 7) / 8) * 8;
-      hipLaunchKernelGGL((k_gemm_bf16<EPI, 2>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
-    }
+    if (n_w >= 2048 && n_w % Shape<2, 4>::BNT == 0) return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
+    if (n_w % Shape<1, 4>::BNT == 0) return launch_shape<EPI, 1, 4>(P, ws, n_w, st);
+    return launch_shape<EPI, 2, 2>(P, ws, n_w, st);
   } else {
     P.n_tiles_n = a.N / FBN;
     hipLaunchKernelGGL(k_gemm_f32<EPI>, dim3(ws.max_mtiles * P.n_tiles_n), dim3(256), 0, st, P);
