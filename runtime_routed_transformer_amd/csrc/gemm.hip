@@ -729,7 +729,11 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
     // divide N; 128 x 256 for the d-wide ones (O, down), where wider tiles
     // would leave CUs idle; 256 x 128 otherwise
     const int n_w = EPI == EPI_SWIGLU ? 2 * a.N : a.N;   // weight rows
-    if (n_w >= 2048 && n_w % Shape<2, 4>::BNT == 0) return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
+    // (QKV: 128-row tiles unless every expert's rows are a multiple of 256,
+    // measured faster for it either way round; gate/up keeps 256 x 256)
+    const bool tall_fits = a.len_gcd % kTileM2 == 0 || EPI == EPI_SWIGLU || EPI == EPI_GELU;
+    if (n_w >= 2048 && n_w % Shape<2, 4>::BNT == 0 && tall_fits)
+      return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
     if (n_w % Shape<1, 4>::BNT == 0) return launch_shape<EPI, 1, 4>(P, ws, n_w, st);
     return launch_shape<EPI, 2, 2>(P, ws, n_w, st);
   } else {

@@ -46,6 +46,21 @@ lol_status validate(const lol_core_config *c) {
   return LOL_OK;
 }
 
+// gcd of the lengths of a depth's windows (first, full and last windows of
+// the partition with offset delta): every expert's grouped row count is a
+// multiple of it, which tells the GEMMs which M tile height leaves no
+// partial tiles.
+int window_length_gcd(int n, int W, int delta, int K) {
+  auto gcd = [](int a, int b) { while (b) { const int t = a % b; a = b; b = t; } return a; };
+  int g = 0;
+  for (int k = 0; k < K; ++k) {
+    const int start = k * W - delta > 0 ? k * W - delta : 0;
+    const int end = (k + 1) * W - delta - 1 < n - 1 ? (k + 1) * W - delta - 1 : n - 1;
+    g = gcd(g, end - start + 1);
+  }
+  return g;
+}
+
 Plan make_plan(const lol_core_config *c) {
   Plan p;
   p.cfg = *c;
@@ -210,6 +225,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     g.depth = l;
     g.delta = (int)(((long long)l * c.S) % c.W);
     g.K = (c.n - 1 + g.delta) / c.W + 1;
+    g.len_gcd = window_length_gcd(c.n, c.W, g.delta, g.K);
     LOL_TRY(KK_POOL, launch_pool(p, g, s, ws, *rt, st));
     LOL_TRY(KK_ROUTE, launch_route(p, g, s, ws, *rt, forced_expert, forced_gate, path, st));
     LOL_TRY(KK_NORM_ATTN, launch_norm(p, g, 0, s, *lib, ws, st));
@@ -221,6 +237,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.w_expert_stride = (long long)3 * d * d;
     // bf16 mode rotates q and k in the GEMM epilogue, before their one
     // rounding to bf16; fp32 mode rotates inside its attention kernel
+    a.len_gcd = g.len_gcd;
     const bool rope_in_gemm = c.dtype == LOL_BF16 && c.rope_theta != 0.f;
     a.epi = rope_in_gemm ? EPI_QKV_ROPE : EPI_STORE;
     a.rope_cols = rope_in_gemm ? 2 * c.d : 0;

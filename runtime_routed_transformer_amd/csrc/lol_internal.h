@@ -38,6 +38,7 @@ struct DepthGeom {
   int depth;      // 0-based depth index l-1
   int delta;      // ((l-1) S) mod W
   int K;          // windows per document at this depth
+  int len_gcd;    // greatest common divisor of the window lengths at this depth
 };
 
 // Device buffers carved from the caller's workspace.
@@ -113,6 +114,7 @@ struct GemmArgs {
   float *s;             // residual stream (RESID, BLEND)
   const float *h;       // BLEND
   int rope_cols;        // QKV_ROPE: columns [0, rope_cols) are rotated (2 d; 0 = no RoPE)
+  int len_gcd;          // gcd of the depth's window lengths: every expert's row count is a multiple
 };
 hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st);
 
