@@ -725,16 +725,21 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   if (EPI == EPI_QKV_ROPE && (p.cfg.dtype != LOL_BF16 || (p.d_head != 32 && p.d_head != 64)))
     return hipErrorInvalidValue;  // fp32 mode rotates inside its attention kernel
   if (p.cfg.dtype == LOL_BF16) {
-    // 256 x 256 tiles for the wide projections (QKV, gate/up) when they
-    // divide N; 128 x 256 for the d-wide ones (O, down), where wider tiles
-    // would leave CUs idle; 256 x 128 otherwise
+    // 256 x 256 tiles (persistent) when every expert's row count is a
+    // multiple of 256 and such tiles fill the CUs; otherwise 128 x 256 tiles
+    // from the 128-row table, which leave no partial tile when rows come in
+    // multiples of 128 (gate/up measured faster with 256 x 256 either way);
+    // 256 x 128 when N is not a multiple of 256
     const int n_w = EPI == EPI_SWIGLU ? 2 * a.N : a.N;   // weight rows
-    // (QKV: 128-row tiles unless every expert's rows are a multiple of 256,
-    // measured faster for it either way round; gate/up keeps 256 x 256)
-    const bool tall_fits = a.len_gcd % kTileM2 == 0 || EPI == EPI_SWIGLU || EPI == EPI_GELU;
-    if (n_w >= 2048 && n_w % Shape<2, 4>::BNT == 0 && tall_fits)
-      return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
-    if (n_w % Shape<1, 4>::BNT == 0) return launch_shape<EPI, 1, 4>(P, ws, n_w, st);
+    if (n_w % 256 == 0) {
+      int ncu = 0;
+      const hipError_t ec = cu_count(&ncu);
+      if (ec != hipSuccess) return ec;
+      const bool rows256 = a.len_gcd % kTileM2 == 0 || EPI == EPI_SWIGLU || EPI == EPI_GELU;
+      const long long tiles256 = (long long)(p.T / kTileM2) * (n_w / 256);
+      if (rows256 && tiles256 >= ncu) return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
+      return launch_shape<EPI, 1, 4>(P, ws, n_w, st);
+    }
     return launch_shape<EPI, 2, 2>(P, ws, n_w, st);
   } else {
     P.n_tiles_n = a.N / FBN;

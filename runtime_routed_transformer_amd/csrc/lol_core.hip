@@ -245,6 +245,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     LOL_TRY(KK_GEMM_QKV, launch_gemm(p, ws, a, st));
     LOL_TRY(KK_ATTN, launch_attention(p, g, ws, st));
     a = GemmArgs{};
+    a.len_gcd = g.len_gcd;
     a.A = ws.o;
     a.Wt = lib->wo;
     a.N = c.d;
@@ -256,6 +257,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     LOL_TRY(KK_GEMM_O, launch_gemm(p, ws, a, st));
     LOL_TRY(KK_NORM_FFN, launch_norm(p, g, 1, s, *lib, ws, st));
     a = GemmArgs{};
+    a.len_gcd = g.len_gcd;
     a.A = ws.u;
     a.Wt = lib->w_gu;
     a.N = c.d_ffn;
@@ -266,6 +268,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.C = ws.hid;
     LOL_TRY(KK_GEMM_GATE_UP, launch_gemm(p, ws, a, st));
     a = GemmArgs{};
+    a.len_gcd = g.len_gcd;
     a.A = ws.hid;
     a.Wt = lib->w_down;
     a.N = c.d;
