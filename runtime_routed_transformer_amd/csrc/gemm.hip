@@ -16,6 +16,8 @@
 // fp32 mode: an LDS-tiled FMA kernel with the same tiles and epilogues.
 #include <math.h>
 
+#include <type_traits>
+
 #include "lol_internal.h"
 
 namespace lol {
@@ -360,42 +362,61 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
       for (int b = 0; b < TM; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-    // stage 0 landed (stages 1 .. NSTAGE-2 may be in flight; for a tile after
-    // the first, also the previous epilogue's stores, which are younger than
-    // stages 0 and 1 and older than stage NSTAGE-2)
-    if (nk >= NSTAGE - 1)
-      stage_barrier<NQ * (NSTAGE - 2), 0>();
+    // A wave whose 128 rows all lie past the expert's last row (the second
+    // wave row of a partial tile with at most 128 rows) skips its fragment
+    // reads and MFMAs and only keeps the barriers and its share of the loads.
+    const bool active = wm * 32 * TM < row_end - row0;
+    auto main_loop = [&](auto act_tag) {
+      constexpr bool ACT = decltype(act_tag)::value;
+      // stage 0 landed (stages 1 .. NSTAGE-2 may be in flight; for a tile after
+      // the first, also the previous epilogue's stores, which are younger than
+      // stages 0 and 1 and older than stage NSTAGE-2)
+      if (nk >= NSTAGE - 1)
+        stage_barrier<NQ * (NSTAGE - 2), 0>();
+      else
+        stage_barrier<0, 0>();
+      if (ACT) read_frags(fw0, fx0, slot(0), coff0);
+      int kt = 0;
+      // steady state: at the barrier stages kt+2 .. kt+NSTAGE-2 may still be in
+      // flight; stage kt+NSTAGE-1 goes into the slot of stage kt-1
+      for (; kt + NSTAGE - 1 < nk; ++kt) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): also settles scalar loads
+        if (ACT) {
+          read_frags(fw1, fx1, slot(kt), coff1);
+          mfmas(fw0, fx0);
+          reads_then_mfmas<NR, TM * TN>();
+        }
+        stage_barrier<NQ * (NSTAGE - 3), 0>();
+        if (ACT) read_frags(fw0, fx0, slot(kt + 1), coff0);
+        issue(kt + NSTAGE - 1, slot(kt + NSTAGE - 1));
+        if (ACT) {
+          mfmas(fw1, fx1);
+          __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // the LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x020, NQ, 0);       // the stage loads
+          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // the MFMAs
+        }
+      }
+      // drain: nothing left to load
+      for (; kt < nk; ++kt) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        if (ACT) {
+          read_frags(fw1, fx1, slot(kt), coff1);
+          mfmas(fw0, fx0);
+          reads_then_mfmas<NR, TM * TN>();
+        }
+        stage_barrier<0, 0>();
+        if (ACT) {
+          // (on the last stage this reads a stale slot, unused)
+          read_frags(fw0, fx0, slot(kt + 1), coff0);
+          mfmas(fw1, fx1);
+          reads_then_mfmas<NR, TM * TN>();
+        }
+      }
+    };
+    if (active)
+      main_loop(std::true_type{});
     else
-      stage_barrier<0, 0>();
-    read_frags(fw0, fx0, slot(0), coff0);
-    int kt = 0;
-    // steady state: at the barrier stages kt+2 .. kt+NSTAGE-2 may still be in
-    // flight; stage kt+NSTAGE-1 goes into the slot of stage kt-1
-    for (; kt + NSTAGE - 1 < nk; ++kt) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): also settles scalar loads
-      read_frags(fw1, fx1, slot(kt), coff1);
-      mfmas(fw0, fx0);
-      reads_then_mfmas<NR, TM * TN>();
-      stage_barrier<NQ * (NSTAGE - 3), 0>();
-      read_frags(fw0, fx0, slot(kt + 1), coff0);
-      issue(kt + NSTAGE - 1, slot(kt + NSTAGE - 1));
-      mfmas(fw1, fx1);
-      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // the LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x020, NQ, 0);       // the stage loads
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // the MFMAs
-    }
-    // drain: nothing left to load
-    for (; kt < nk; ++kt) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      read_frags(fw1, fx1, slot(kt), coff1);
-      mfmas(fw0, fx0);
-      reads_then_mfmas<NR, TM * TN>();
-      stage_barrier<0, 0>();
-      // (on the last stage this reads a stale slot, unused)
-      read_frags(fw0, fx0, slot(kt + 1), coff0);
-      mfmas(fw1, fx1);
-      reads_then_mfmas<NR, TM * TN>();
-    }
+      main_loop(std::false_type{});
     stage_barrier<0, 0>();  // every wave is done with the ring: reuse it below
 
     // next tile (persistent): its stages 0 .. NSTAGE-3 go into the ring now,

@@ -132,7 +132,11 @@ __global__ void __launch_bounds__(1024) k_route_all(
   __shared__ int s_exp[kMaxSlots];
   __shared__ int s_len[kMaxSlots];
   __shared__ int cnt_w[kMaxExperts], cnt_t[kMaxExperts];
-  __shared__ int toff[kMaxExperts + 1], moff[kMaxExperts + 1], moff2[kMaxExperts + 1];
+  __shared__ int toff[kMaxExperts + 1];
+  // M-tile tables (128- and 256-row tiles): every expert's full tiles in
+  // expert order, then the partial last tiles, so that partial (cheaper)
+  // tiles are the last ones a GEMM hands out
+  __shared__ int fo[kMaxExperts + 1], po[kMaxExperts + 1], fo2[kMaxExperts + 1], po2[kMaxExperts + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n_slots = B * K_max;
 
@@ -232,22 +236,28 @@ __global__ void __launch_bounds__(1024) k_route_all(
   }
   __syncthreads();
   if (tid == 0) {
-    int t = 0, m = 0, m2 = 0, w = 0;
+    int t = 0, f = 0, q = 0, f2 = 0, q2 = 0, w = 0;
     for (int e = 0; e < L; ++e) {
       toff[e] = t;
-      moff[e] = m;
-      moff2[e] = m2;
+      fo[e] = f;
+      po[e] = q;
+      fo2[e] = f2;
+      po2[e] = q2;
       t += cnt_t[e];
-      m += (cnt_t[e] + kTileM - 1) / kTileM;
-      m2 += (cnt_t[e] + kTileM2 - 1) / kTileM2;
+      f += cnt_t[e] / kTileM;
+      q += cnt_t[e] % kTileM != 0;
+      f2 += cnt_t[e] / kTileM2;
+      q2 += cnt_t[e] % kTileM2 != 0;
       w += cnt_w[e];
     }
     toff[L] = t;
-    moff[L] = m;
-    moff2[L] = m2;
+    fo[L] = f;
+    po[L] = q;
+    fo2[L] = f2;
+    po2[L] = q2;
     ecount[L] = w;
-    mcount[0] = m;
-    mcount[1] = m2;
+    mcount[0] = f + q;
+    mcount[1] = f2 + q2;
   }
   __syncthreads();
   for (int e = tid; e <= L; e += blockDim.x) toff_out[e] = toff[e];
@@ -272,23 +282,32 @@ __global__ void __launch_bounds__(1024) k_route_all(
   }
   for (int slot = tid; slot < n_slots; slot += blockDim.x)
     if (s_exp[slot] < 0) win_row0[slot] = -1;
-  for (int i = tid; i < max_mtiles; i += blockDim.x) {
-    int e = -1, row0 = 0;
-    if (i < moff[L]) {
+  // tile i: full tile (i - fo[e]) of expert e, or the partial tile of the
+  // (i - F)-th expert that has one
+  auto tile_entry = [&](int i, const int *fo_, const int *po_, int H, int &e, int &row0) {
+    e = -1;
+    row0 = 0;
+    const int F = fo_[L];
+    if (i < F) {
       e = 0;
-      while (moff[e + 1] <= i) ++e;
-      row0 = toff[e] + (i - moff[e]) * kTileM;
+      while (fo_[e + 1] <= i) ++e;
+      row0 = toff[e] + (i - fo_[e]) * H;
+    } else if (i - F < po_[L]) {
+      const int j = i - F;
+      e = 0;
+      while (po_[e + 1] <= j) ++e;
+      row0 = toff[e] + (fo_[e + 1] - fo_[e]) * H;
     }
+  };
+  for (int i = tid; i < max_mtiles; i += blockDim.x) {
+    int e, row0;
+    tile_entry(i, fo, po, kTileM, e, row0);
     mtile[2 * i] = e;
     mtile[2 * i + 1] = row0;
   }
   for (int i = tid; i < max_mtiles2; i += blockDim.x) {
-    int e = -1, row0 = 0;
-    if (i < moff2[L]) {
-      e = 0;
-      while (moff2[e + 1] <= i) ++e;
-      row0 = toff[e] + (i - moff2[e]) * kTileM2;
-    }
+    int e, row0;
+    tile_entry(i, fo2, po2, kTileM2, e, row0);
     mtile2[2 * i] = e;
     mtile2[2 * i + 1] = row0;
   }
