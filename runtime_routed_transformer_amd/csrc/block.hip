@@ -279,6 +279,18 @@ __global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__
   const int g16 = lane >> 4, p16 = lane & 15;
   const int tr_row = 4 * (g16 >> 1) + (p16 >> 2);
   const int tr_col = (g16 & 1) * 16 + 4 * (p16 & 3);
+  // Both swizzles depend only on row bits below 32 (K: bits 1-3 or 2-3; V:
+  // bit 1), so every fragment address is a per-lane constant plus
+  // kb * 32 rows: no address arithmetic inside the key loop.
+  int k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = col * RB + (((2 * ks + hl) ^ LY::kswz(col)) << 4);
+  int v_off[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int c = db * 32 + tr_col;                     // first of the 4 columns
+    v_off[db] = tr_row * RB + ((((c >> 3) ^ LY::vswz(tr_row)) << 4) + ((c & 4) << 1));
+  }
 
   for (int kc = 0; kc <= qc; ++kc) {
     const int k_begin = kc * CH;
@@ -307,12 +319,10 @@ __global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__
         f32x16_t sc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = 0.f;
-        const int kr = kb * 32 + col;
+        const char *kbase = Kl + kb * 32 * RB;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int lc = 2 * ks + hl;
-          const bf16x8_t kf =
-              *reinterpret_cast<const bf16x8_t *>(Kl + kr * RB + ((lc ^ LY::kswz(kr)) << 4));
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(kbase + k_off[ks]);
           sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[b][ks], sc, 0, 0, 0);
         }
         // sc[i] = q.k for key = k_begin + kb*32 + (i/4)*8 + 4*hl + i%4, query q
@@ -327,11 +337,23 @@ __global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[b], mx);
-        // softmax weights 2^((s - m) * log2(e) / sqrt(d_head)); the raw
-        // exp2 is exact to about 1 ulp and flushes tiny weights to zero
-        const float mc = m_new * qscale;
-        const float corr = __builtin_amdgcn_exp2f(m_run[b] * qscale - mc);
+        // Softmax weights 2^((s - m) * log2(e) / sqrt(d_head)) against a
+        // reference maximum m that only moves (rescaling the running sum and
+        // output) when some lane's scores exceed it by more than 2^8; below
+        // that the weights stay <= 256, exact enough in fp32 and in the bf16
+        // operand.  The raw exp2 is exact to about 1 ulp and flushes tiny
+        // weights to zero.
+        if (__builtin_amdgcn_ballot_w64((mx - m_run[b]) * qscale > 8.f)) {
+          const float m_new = fmaxf(m_run[b], mx);
+          const float corr = __builtin_amdgcn_exp2f((m_run[b] - m_new) * qscale);
+          l_run[b] *= corr;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[b][db][i] *= corr;
+          m_run[b] = m_new;
+        }
+        const float mc = m_run[b] * qscale;
         float p[16], rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -339,31 +361,22 @@ __global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__
           rs += p[i];
         }
         rs += __shfl_xor(rs, 32, 64);
-        l_run[b] = l_run[b] * corr + rs;
-        m_run[b] = m_new;
-        if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {   // a running max moved
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[b][db][i] *= corr;
-        }
+        l_run[b] += rs;
 #pragma unroll
         for (int step = 0; step < 2; ++step) {
           bf16x8_t pb;
 #pragma unroll
           for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * step + j];
-          const int vr = kb * 32 + 16 * step + tr_row;     // rows vr (keys +0..3) and vr + 8
+          // rows kb*32 + 16 step + tr_row (keys +0..3) and 8 rows on
+          const char *vbase = Vl + (kb * 32 + 16 * step) * RB;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const int c = db * 32 + tr_col;                 // first of the 4 columns
-            const int off = ((c >> 3) << 4) + ((c & 4) << 1);
-            const int sw0 = LY::vswz(vr) << 4, sw1 = LY::vswz(vr + 8) << 4;
             // (element-wise copies out of the v4i16 form of this read are
             // miscompiled by this compiler: only its low dword survives)
-            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4_t *)(Vl + vr * RB + (off ^ sw0)));
-            const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4_t *)(Vl + (vr + 8) * RB + (off ^ sw1)));
+            const bf16x4_t lo =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(vbase + v_off[db]));
+            const bf16x4_t hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(vbase + v_off[db] + 8 * RB));
             const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             acc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[b][db], 0, 0, 0);
           }
