@@ -682,22 +682,6 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmParams P) {
   }
 }
 
-// Compute units of the current device (cached per device).
-hipError_t cu_count(int *n) {
-  static int cached[64] = {0};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (cached[dev] == 0) {
-    int v = 0;
-    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    cached[dev] = v;
-  }
-  *n = cached[dev];
-  return hipSuccess;
-}
 
 template <int EPI, int WM, int WN>
 hipError_t launch_shape(GemmParams P, const Workspace &ws, int n_w, hipStream_t st) {

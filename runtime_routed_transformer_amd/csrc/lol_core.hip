@@ -46,6 +46,7 @@ lol_status validate(const lol_core_config *c) {
   return LOL_OK;
 }
 
+
 // gcd of the lengths of a depth's windows (first, full and last windows of
 // the partition with offset delta): every expert's grouped row count is a
 // multiple of it, which tells the GEMMs which M tile height leaves no
@@ -121,6 +122,23 @@ struct Launch {
 };
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+hipError_t cu_count(int *n) {
+  static int cached[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cached[dev] == 0) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cached[dev] = v;
+  }
+  *n = cached[dev];
+  return hipSuccess;
+}
 
 size_t workspace_layout(const Plan &p, char *base, Workspace *ws) {
   const lol_core_config &c = p.cfg;

@@ -75,6 +75,8 @@ struct Plan {
 };
 
 size_t workspace_layout(const Plan &p, char *base, Workspace *ws);
+// compute units of the current device (cached per device)
+hipError_t cu_count(int *n);
 
 // ---- launchers (all asynchronous on `st`) ----
 // window means, contracted with the router weights per 64-column chunk
