@@ -65,25 +65,33 @@ __global__ void __launch_bounds__(256) k_norm(const float *__restrict__ src,
   const float *g = gain + (size_t)row_exp[row] * d;
   act_t *out = u + (size_t)row * d;
   if (NCH > 0) {
-    float4 xv[NCH > 0 ? NCH : 1];
-    float ss = 0.f;
+    // every load of the row (x, the expert gain, FiLM) is issued before the
+    // reduction, so the row waits for one round trip instead of one per chunk
+    constexpr int N1 = NCH > 0 ? NCH : 1;
+    float4 xv[N1], gv[N1], av[N1], bv[N1];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      xv[i] = *reinterpret_cast<const float4 *>(x + i * 256 + lane * 4);
-      ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
+      const int c = i * 256 + lane * 4;
+      xv[i] = *reinterpret_cast<const float4 *>(x + c);
+      gv[i] = *reinterpret_cast<const float4 *>(g + c);
+      if (fg) {
+        av[i] = *reinterpret_cast<const float4 *>(fg + c);
+        bv[i] = *reinterpret_cast<const float4 *>(fb + c);
+      }
     }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
     const float inv = rsqrtf(wave_sum(ss) / (float)d + eps);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = i * 256 + lane * 4;
-      const float4 gv = *reinterpret_cast<const float4 *>(g + c);
-      float4 v = make_float4(xv[i].x * inv * gv.x, xv[i].y * inv * gv.y, xv[i].z * inv * gv.z,
-                             xv[i].w * inv * gv.w);
-      if (fg) {
-        const float4 a = *reinterpret_cast<const float4 *>(fg + c);
-        const float4 b = *reinterpret_cast<const float4 *>(fb + c);
-        v = make_float4(a.x * v.x + b.x, a.y * v.y + b.y, a.z * v.z + b.z, a.w * v.w + b.w);
-      }
+      float4 v = make_float4(xv[i].x * inv * gv[i].x, xv[i].y * inv * gv[i].y,
+                             xv[i].z * inv * gv[i].z, xv[i].w * inv * gv[i].w);
+      if (fg)
+        v = make_float4(av[i].x * v.x + bv[i].x, av[i].y * v.y + bv[i].y, av[i].z * v.z + bv[i].z,
+                        av[i].w * v.w + bv[i].w);
       store4<act_t>(out + c, v.x, v.y, v.z, v.w);
     }
   } else {

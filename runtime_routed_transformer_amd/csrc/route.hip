@@ -65,9 +65,20 @@ __global__ void __launch_bounds__(256) k_pool(const float *__restrict__ s,
   const int col = chunk * 64 + c4 * 4;
   const float *base = s + ((size_t)b * n + start) * d + col;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int r = ph; r < len; r += 16) {
-    const float4 v = *reinterpret_cast<const float4 *>(base + (size_t)r * d);
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  // rows ph, ph + 16, ... in batches of 8 whose loads are all in flight
+  // before the first add
+  for (int r0 = ph; r0 < len; r0 += 8 * 16) {
+    float4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = r0 + 16 * i;
+      v[i] = r < len ? *reinterpret_cast<const float4 *>(base + (size_t)r * d)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc.x += v[i].x; acc.y += v[i].y; acc.z += v[i].z; acc.w += v[i].w;
+    }
   }
   __shared__ float4 red[16][16];
   __shared__ float mu[64], r0[64];
