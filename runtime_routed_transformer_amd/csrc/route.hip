@@ -156,11 +156,17 @@ __global__ void __launch_bounds__(1024) k_route_all(
   // wave per (document, expert) turns Y into running means with a scan over k
   for (int i = tid; i < B * K * L; i += blockDim.x) {
     const int m = i % L, k = (i / L) % K, b = i / (L * K);
+    // the chunk partials of one window, 16 loads in flight at a time, summed
+    // in chunk order
+    const float *zp = k == 0 ? zpart0 + (size_t)b * nch * L + m
+                             : zpart + ((size_t)b * K_max + k - 1) * nch * L + m;
     float y = 0.f;
-    if (k == 0) {
-      for (int c = 0; c < nch; ++c) y += zpart0[((size_t)b * nch + c) * L + m];
-    } else {
-      for (int c = 0; c < nch; ++c) y += zpart[(((size_t)b * K_max + k - 1) * nch + c) * L + m];
+    for (int c0 = 0; c0 < nch; c0 += 16) {
+      float t[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t[i] = c0 + i < nch ? zp[(size_t)(c0 + i) * L] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y += t[i];
     }
     zlog[((size_t)b * K_max + k) * L + m] = y;
   }
