@@ -15,6 +15,7 @@ namespace lol {
 namespace {
 
 constexpr int kMaxSlots = 8192;  // documents x window slots handled by one bucketing block
+constexpr int kZlogLds = 8192;   // window logits (slots x experts) kept in LDS up to this many
 
 __device__ __forceinline__ int win_start(int k, int W, int delta) { return max(0, k * W - delta); }
 __device__ __forceinline__ int win_end(int k, int W, int delta, int n) {
@@ -138,7 +139,7 @@ __global__ void __launch_bounds__(1024) k_route_all(
     int32_t *__restrict__ toff_out, int32_t *__restrict__ mtile, int max_mtiles,
     int32_t *__restrict__ mtile2, int max_mtiles2, int32_t *__restrict__ mcount,
     int32_t *__restrict__ row_tok, int32_t *__restrict__ row_pos, int32_t *__restrict__ row_exp,
-    float *__restrict__ row_gate, float *__restrict__ zlog, int n, int nch, int L, int W, int delta,
+    float *__restrict__ row_gate, float *__restrict__ zlog_g, int n, int nch, int L, int W, int delta,
     int K, int K_max, int B, int depth) {
   __shared__ int s_exp[kMaxSlots];
   __shared__ int s_len[kMaxSlots];
@@ -150,6 +151,9 @@ __global__ void __launch_bounds__(1024) k_route_all(
   __shared__ int fo[kMaxExperts + 1], po[kMaxExperts + 1], fo2[kMaxExperts + 1], po2[kMaxExperts + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n_slots = B * K_max;
+  // window logits live in LDS when they fit, else in the workspace
+  __shared__ float s_zlog[kZlogLds];
+  float *const zlog = (size_t)n_slots * L <= kZlogLds ? s_zlog : zlog_g;
 
   // 1. logits of every window, zlog[b][k][m]: first Y_k = sum over chunks
   // (slot k >= 1 holds Y_{k-1}; slot 0 the window-0 contraction), then one
