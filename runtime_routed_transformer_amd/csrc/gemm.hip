@@ -50,7 +50,8 @@ struct GemmParams {
   const int32_t *row_tok;
   const float *row_gate;
   void *C;
-  float *s;
+  const float *s_in;       // residual stream read (RESID, BLEND)
+  float *s;                // residual stream written (BLEND)
   const float *h;
   const int32_t *row_pos;  // QKV_ROPE: window-local position of each grouped row
   const float *rope_cs;    // QKV_ROPE: [W][half][2] cos, sin of p * theta^(-2j/d_head)
@@ -75,14 +76,14 @@ __device__ __forceinline__ void epilogue4(const GemmParams &P, int row, int col,
     }
   } else if (EPI == EPI_RESID) {
     const size_t tok = (size_t)P.row_tok[row];
-    const float4 x = *reinterpret_cast<const float4 *>(P.s + tok * P.ldc + col);
+    const float4 x = *reinterpret_cast<const float4 *>(P.s_in + tok * P.ldc + col);
     *reinterpret_cast<float4 *>(reinterpret_cast<float *>(P.C) + (size_t)row * P.ldc + col) =
         make_float4(x.x + v0, x.y + v1, x.z + v2, x.w + v3);
   } else if (EPI == EPI_BLEND) {
     const size_t tok = (size_t)P.row_tok[row];
     const float g = P.row_gate[row];
     float4 *sp = reinterpret_cast<float4 *>(P.s + tok * P.ldc + col);
-    const float4 x = *sp;
+    const float4 x = *reinterpret_cast<const float4 *>(P.s_in + tok * P.ldc + col);
     const float4 hv = *reinterpret_cast<const float4 *>(P.h + (size_t)row * P.ldc + col);
     *sp = make_float4(x.x + g * (hv.x + v0 - x.x), x.y + g * (hv.y + v1 - x.y),
                       x.z + g * (hv.z + v2 - x.z), x.w + g * (hv.w + v3 - x.w));
@@ -538,7 +539,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
       if (EPI == EPI_RESID || EPI == EPI_BLEND) {
         // every load of the block first (token ids, then the residual rows),
         // then the arithmetic and the stores: the loads overlap each other
-        float *__restrict__ sres = P.s;
+        const float *__restrict__ sres = P.s_in;
         const float *__restrict__ hres = P.h;
         size_t tok[NP];
         float gt[NP];
@@ -570,7 +571,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
           } else {
             const float g = gt[pass];
             const float4 q0 = h0[pass], q1 = h1[pass];
-            float4 *sp = reinterpret_cast<float4 *>(sres + tok[pass] * P.ldc + col);
+            float4 *sp = reinterpret_cast<float4 *>(P.s + tok[pass] * P.ldc + col);
             sp[0] = make_float4(s0.x + g * (q0.x + a0.x - s0.x), s0.y + g * (q0.y + a0.y - s0.y),
                                 s0.z + g * (q0.z + a0.z - s0.z), s0.w + g * (q0.w + a0.w - s0.w));
             sp[1] = make_float4(s1.x + g * (q1.x + a1.x - s1.x), s1.y + g * (q1.y + a1.y - s1.y),
@@ -721,6 +722,7 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.row_tok = ws.row_tok;
   P.row_gate = ws.row_gate;
   P.C = a.C;
+  P.s_in = a.s_in;
   P.s = a.s;
   P.h = a.h;
   P.row_pos = ws.row_pos;

@@ -233,12 +233,11 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     if (err != hipSuccess) return LOL_EHIP;           \
   } while (0)
 
-  if (s_out != s0)
-    LOL_TRY(KK_COPY, hipMemcpyAsync(s_out, s0, (size_t)p.T * d * sizeof(float),
-                                    hipMemcpyDeviceToDevice, st));
-  float *s = s_out;
+  // Depth 1 reads s0 and its blend writes s_out: every token lies in exactly
+  // one window per depth, so s_out is complete after it (no copy of s0).
   LOL_TRY(KK_COPY, launch_setup(p, ws, st));
   for (int l = 0; l < c.D; ++l) {
+    const float *s = l == 0 ? s0 : s_out;   // depth input
     DepthGeom g;
     g.depth = l;
     g.delta = (int)(((long long)l * c.S) % c.W);
@@ -271,7 +270,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.w_expert_stride = (long long)d * d;
     a.epi = EPI_RESID;
     a.C = ws.h;
-    a.s = s;
+    a.s_in = s;
     LOL_TRY(KK_GEMM_O, launch_gemm(p, ws, a, st));
     LOL_TRY(KK_NORM_FFN, launch_norm(p, g, 1, s, *lib, ws, st));
     a = GemmArgs{};
@@ -293,7 +292,8 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.K = c.d_ffn;
     a.w_expert_stride = (long long)d * f;
     a.epi = EPI_BLEND;
-    a.s = s;
+    a.s_in = s;
+    a.s = s_out;
     a.h = ws.h;
     LOL_TRY(KK_GEMM_DOWN, launch_gemm(p, ws, a, st));
   }

@@ -96,10 +96,10 @@ hipError_t launch_attention(const Plan &p, const DepthGeom &g, const Workspace &
 
 enum GemmEpilogue {
   EPI_STORE = 0,    // C (act) = acc
-  EPI_RESID = 1,    // h (fp32) = s[row_tok] + acc
+  EPI_RESID = 1,    // h (fp32) = s_in[row_tok] + acc
   EPI_SWIGLU = 2,   // hid (act) = silu(acc_gate) * acc_up
   EPI_GELU = 3,     // hid (act) = gelu(acc)
-  EPI_BLEND = 4,    // s[row_tok] += gate * (h + acc - s[row_tok])
+  EPI_BLEND = 4,    // s[row_tok] = s_in[row_tok] + gate * (h + acc - s_in[row_tok])
   EPI_QKV_ROPE = 5, // C (act) = acc, with RoPE at the row's window position on
                     // the q and k columns (bf16 mode only)
 };
@@ -113,7 +113,8 @@ struct GemmArgs {
   int glu_offset;       // SwiGLU: row offset of W_up inside an expert (= f)
   GemmEpilogue epi;
   void *C;              // output (act or fp32 depending on epilogue)
-  float *s;             // residual stream (RESID, BLEND)
+  const float *s_in;    // residual stream read (RESID, BLEND)
+  float *s;             // residual stream written (BLEND; may equal s_in)
   const float *h;       // BLEND
   int rope_cols;        // QKV_ROPE: columns [0, rope_cols) are rotated (2 d; 0 = no RoPE)
   int len_gcd;          // gcd of the depth's window lengths: every expert's row count is a multiple
