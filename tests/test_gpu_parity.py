@@ -96,6 +96,8 @@ def test_gate_zero_identity_and_determinism_and_inplace():
     b = core.forward().clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b), "two runs differ"
+    # out of place, the first depth reads s0 directly: it must stay untouched
+    np.testing.assert_array_equal(core.s0.cpu().numpy(), inp.s0)
     s = core.s0.clone()
     core.forward(s_in=s, s_out=s)
     torch.cuda.synchronize()
