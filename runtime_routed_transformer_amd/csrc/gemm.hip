@@ -87,6 +87,12 @@ __device__ __forceinline__ void epilogue4(const GemmParams &P, int row, int col,
     const float4 hv = *reinterpret_cast<const float4 *>(P.h + (size_t)row * P.ldc + col);
     *sp = make_float4(x.x + g * (hv.x + v0 - x.x), x.y + g * (hv.y + v1 - x.y),
                       x.z + g * (hv.z + v2 - x.z), x.w + g * (hv.w + v3 - x.w));
+  } else if (EPI == EPI_ACCUM) {
+    const size_t tok = (size_t)P.row_tok[row];
+    const float g = P.row_gate[row];
+    const float4 x = *reinterpret_cast<const float4 *>(P.s_in + tok * P.ldc + col);
+    *reinterpret_cast<float4 *>(P.s + tok * P.ldc + col) =
+        make_float4(x.x + g * v0, x.y + g * v1, x.z + g * v2, x.w + g * v3);
   }
 }
 
@@ -536,7 +542,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
         ok[pass] = rw < row_end;
         row[pass] = ok[pass] ? rw : row_end - 1;   // rows past the expert: read a valid row, store nothing
       }
-      if (EPI == EPI_RESID || EPI == EPI_BLEND) {
+      if (EPI == EPI_RESID || EPI == EPI_BLEND || EPI == EPI_ACCUM) {
         // every load of the block first (token ids, then the residual rows),
         // then the arithmetic and the stores: the loads overlap each other
         const float *__restrict__ sres = P.s_in;
@@ -546,7 +552,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
 #pragma unroll
         for (int pass = 0; pass < NP; ++pass) {
           tok[pass] = (size_t)P.row_tok[row[pass]];
-          gt[pass] = EPI == EPI_BLEND ? P.row_gate[row[pass]] : 0.f;
+          gt[pass] = EPI == EPI_BLEND || EPI == EPI_ACCUM ? P.row_gate[row[pass]] : 0.f;
         }
         float4 x0[NP], x1[NP], h0[NP], h1[NP];
 #pragma unroll
@@ -568,6 +574,11 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
             float4 *hp = reinterpret_cast<float4 *>(reinterpret_cast<float *>(P.C) + (size_t)row[pass] * P.ldc + col);
             hp[0] = make_float4(s0.x + a0.x, s0.y + a0.y, s0.z + a0.z, s0.w + a0.w);
             hp[1] = make_float4(s1.x + a1.x, s1.y + a1.y, s1.z + a1.z, s1.w + a1.w);
+          } else if (EPI == EPI_ACCUM) {
+            const float g = gt[pass];
+            float4 *sp = reinterpret_cast<float4 *>(P.s + tok[pass] * P.ldc + col);
+            sp[0] = make_float4(s0.x + g * a0.x, s0.y + g * a0.y, s0.z + g * a0.z, s0.w + g * a0.w);
+            sp[1] = make_float4(s1.x + g * a1.x, s1.y + g * a1.y, s1.z + g * a1.z, s1.w + g * a1.w);
           } else {
             const float g = gt[pass];
             const float4 q0 = h0[pass], q1 = h1[pass];
@@ -599,6 +610,277 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
     mt = mt2; nt = nt2; e = e2; row0 = r02; row_end = re2; gb = gb2;
     if (NSTAGE - 2 < nk) issue(NSTAGE - 2, slot(NSTAGE - 2));
   }  // tiles
+}
+
+// ---------------------------------------------------------------------------
+// Output projection fused with the feed-forward sublayer's RMSNorm + FiLM
+// (paper "Library of Layers (LoL)", App. A block: h = x + Attn(.), then the
+// MLP reads Norm_ffn(h); review Eq. 7 FiLM).  bf16, d = 256 TN.
+//
+// A workgroup owns 64 grouped rows and all d output columns, so the whole of
+// h for its rows exists in its registers and the norm needs no second pass
+// over HBM: h is never stored.  8 waves side by side, each 64 rows x 32 TN
+// columns = TN x 2 blocks of v_mfma_f32_32x32x16_bf16.  Every wave reads
+// the same 64 activation rows and its own slice of W_o.
+//
+// Main loop: one 16-k step per stage (2 KiB of activations + 32 d bytes of
+// weights), 4 stages in a ring, all four in flight: stage kt + 4 goes into
+// the slot of stage kt once every wave has read its fragments.  Rows of 16 k
+// = 32 bytes, two 16-byte chunks; logical chunk c of row r sits at c ^ ((r
+// >> 3) & 1), which spreads the 16 rows of a fragment read over all 64 banks.
+//
+// Epilogue, per 32-row half: every wave stages its accumulators in LDS as
+// fp32 rows (16-byte chunk c of row r at c ^ (r & 15)), then each wave takes
+// 4 whole rows: h = s_in[t] + y, one wave reduction of h^2, u = FiLM(g_e h /
+// rms) in bf16 and s[t] = s_in[t] + gate y, all as contiguous row accesses.
+// ---------------------------------------------------------------------------
+// W [L][d][d] (row n, contiguous k) -> Wp [L][d/16][d][16]: the 16-k
+// panel p of expert e holds W[e][n][16 p .. 16 p + 16) for every n, in n
+// order.  One thread per 16-byte piece, numbered in Wp order, so the
+// stores are contiguous.
+__global__ void __launch_bounds__(256) k_pack_panels(const bf16_t *__restrict__ W, bf16_t *__restrict__ Wp,
+                                                     int d, long long pieces) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  const int half = (int)(i & 1);
+  const long long nn = i >> 1;                 // (e, panel, n) in Wp order
+  const int n = (int)(nn % d);
+  const long long ep = nn / d;                 // e * (d / 16) + panel
+  const int panel = (int)(ep % (d / 16));
+  const long long e = ep / (d / 16);
+  const uint4 v = *reinterpret_cast<const uint4 *>(W + ((size_t)e * d + n) * d + panel * 16 + half * 8);
+  *reinterpret_cast<uint4 *>(Wp + (size_t)i * 8) = v;
+}
+
+struct ONormParams {
+  const bf16_t *A;         // o, [T][d]
+  const bf16_t *Wp;        // W_o in 16-k panels, [L][d/16][d][16]
+  const int32_t *mtile;    // 128-row tile table: (expert, first row)
+  const int32_t *mcount;
+  const int32_t *toff;
+  const int32_t *row_tok;
+  const float *row_gate;
+  const float *s_in;
+  float *s;
+  const float *gain;       // Norm_ffn gains, [L][d]
+  const float *fg, *fb;    // FiLM of this depth's MLP sublayer, [d] (null: off)
+  bf16_t *u;
+  float eps;
+};
+
+constexpr int kONormRows = 64;
+constexpr int kONormStages = 4;
+constexpr int kONormBK = 16;
+
+template <int TN> struct ONormShape {
+  static constexpr int D = 256 * TN;
+  static constexpr int A_STAGE = kONormRows * kONormBK * 2;   // 2 KiB
+  static constexpr int STAGE = A_STAGE + D * kONormBK * 2;
+  static constexpr int LDS = kONormStages * STAGE;
+  static_assert(32 * D * 4 <= LDS, "epilogue staging of 32 fp32 rows fits in the ring");
+};
+
+__device__ __forceinline__ void lds_dma4(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <int TN>
+__global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
+  using S = ONormShape<TN>;
+  constexpr int D = S::D, A_STAGE = S::A_STAGE, STAGE = S::STAGE, NS = kONormStages;
+  constexpr int NQ = 1 + TN;              // load instructions per wave per stage
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  // ---- tile: the 64-row half (t & 1) of 128-row table entry t >> 1; the
+  // 8 XCDs take contiguous ranges of tiles (workgroup i runs on XCD i mod 8),
+  // so that the tiles of one expert share W_o in one L2
+  const int n_t = 2 * P.mcount[0];
+  const int per = (n_t + 7) >> 3;
+  const int u_ = blockIdx.x >> 3;
+  const int t = (blockIdx.x & 7) * per + u_;
+  if (u_ >= per || t >= n_t) return;
+  const int e = P.mtile[2 * (t >> 1)];
+  if (e < 0) return;
+  const int row0 = P.mtile[2 * (t >> 1) + 1] + (t & 1) * kONormRows;
+  const int row_end = P.toff[e + 1];
+  if (row0 >= row_end) return;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  // ---- load sources.  Activations: wave w fetches rows 8 w .. 8 w + 7, 4
+  // bytes per lane (lane -> row 8 w + lane / 8, dword lane % 8 of the row's
+  // 32 bytes).  Weights: instruction q of wave w fetches rows (w + 8 q) 32 +
+  // lane / 2, 16 bytes per lane (physical chunk lane % 2).
+  const int last = row_end - 1 - row0;
+  const int ar = wave * 8 + (lane >> 3);
+  const int a_chunk = ((lane >> 2) & 1) ^ ((ar >> 3) & 1);
+  const bf16_t *a_src = P.A + (size_t)(row0 + min(ar, last)) * D + a_chunk * 8 + (lane & 3) * 2;
+  // weights in 16-k panels: stage k0 / 16 of expert e is the contiguous
+  // block Wp[e][k0 / 16][0 .. d)[0 .. 16), so every request is a whole line
+  const bf16_t *b_base = P.Wp + (size_t)e * D * D;
+  uint32_t boff[TN];
+#pragma unroll
+  for (int q = 0; q < TN; ++q) {
+    const int br = (wave + 8 * q) * 32 + (lane >> 1);
+    boff[q] = (uint32_t)br * kONormBK + (((lane & 1) ^ ((br >> 3) & 1)) << 3);
+  }
+  auto issue = [&](int stage, int slot) {
+    char *base = smem + slot * STAGE;
+    lds_dma4(a_src + stage * kONormBK, base + wave * 256);
+    const bf16_t *bp = b_base + (size_t)stage * (D * kONormBK);
+#pragma unroll
+    for (int q = 0; q < TN; ++q) lds_dma16(bp + boff[q], base + A_STAGE + (wave + 8 * q) * 1024);
+  };
+
+  // ---- fragments: lane reads row (lane & 31) of each 32-row block at logical
+  // chunk lane >> 5
+  const int frow = lane & 31;
+  const int coff = (((lane >> 5) ^ ((frow >> 3) & 1)) << 4) + frow * 32;
+  const int b_frag = A_STAGE + wave * 32 * TN * 32 + coff;
+  f32x16 acc[TN][2];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+  bf16x8 fw[2][TN], fx[2][2];
+  auto read_frags = [&](int buf, int slot) {
+    const char *base = smem + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) fw[buf][i] = *reinterpret_cast<const bf16x8 *>(base + b_frag + i * 32 * 32);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fx[buf][i] = *reinterpret_cast<const bf16x8 *>(base + coff + i * 32 * 32);
+  };
+
+  constexpr int nk = D / kONormBK;   // >= 16
+#pragma unroll
+  for (int st = 0; st < NS; ++st) issue(st, st);
+  stage_barrier<NQ * (NS - 1), 0>();   // stage 0 landed on every wave
+  read_frags(0, 0);
+  // step kt: the fragments of stage kt were read during step kt - 1.  After
+  // the barrier stage kt + 1 has landed everywhere and no wave reads slot kt
+  // any more, so stage kt + 4 goes there.  Past the last stage the loads
+  // repeat it into slots nobody reads again (and the last step reads a stale
+  // slot), which keeps every step free of branches and its wait counts fixed.
+  // (The barrier's own lgkmcnt(0) covers this wave's reads of stage kt; an
+  // extra explicit wait in front of it made the compiler add another one
+  // between the MFMAs.)
+  auto step = [&](int kt, auto cur_tag) {
+    constexpr int cur = decltype(cur_tag)::value;
+    stage_barrier<NQ * 2, 0>();
+    issue(min(kt + NS, nk - 1), kt % NS);
+    read_frags(cur ^ 1, (kt + 1) % NS);
+#pragma unroll
+    for (int in = 0; in < TN; ++in)
+#pragma unroll
+      for (int im = 0; im < 2; ++im)
+        acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][in], fx[cur][im], acc[in][im], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, NQ, 0);       // the stage loads
+    __builtin_amdgcn_sched_group_barrier(0x100, TN + 2, 0);   // the fragment reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * TN, 0);   // the MFMAs
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
+  }
+  stage_barrier<0, 0>();   // every wave is done with the ring: the epilogue reuses it
+
+  // ---- epilogue.  acc[in][im] holds y[m = im*32 + lane%32][n = wave*32*TN +
+  // in*32 + g*8 + 4*(lane/32) + j] (g, j < 4).
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));
+  float *stg = reinterpret_cast<float *>(smem);
+  constexpr int CH = D / 4;   // 16-byte chunks per staged row
+  const float *gain = P.gain + (size_t)e * D;
+  float4 gv[TN], av[TN], bv[TN];
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+    const int c = (i * 64 + lane_e) * 4;
+    gv[i] = *reinterpret_cast<const float4 *>(gain + c);
+    if (P.fg) {
+      av[i] = *reinterpret_cast<const float4 *>(P.fg + c);
+      bv[i] = *reinterpret_cast<const float4 *>(P.fb + c);
+    } else {
+      av[i] = make_float4(1.f, 1.f, 1.f, 1.f);
+      bv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+#pragma unroll
+  for (int im = 0; im < 2; ++im) {
+    if (im) stage_barrier<63, 0>();   // every wave is done reading the first half
+    {
+      const int r = lane_e & 31;
+#pragma unroll
+      for (int in = 0; in < TN; ++in)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = wave * 8 * TN + in * 8 + 2 * g + (lane_e >> 5);
+          *reinterpret_cast<float4 *>(stg + (r * CH + (c ^ (r & 15))) * 4) =
+              make_float4(acc[in][im][4 * g], acc[in][im][4 * g + 1], acc[in][im][4 * g + 2],
+                          acc[in][im][4 * g + 3]);
+        }
+    }
+    stage_barrier<63, 0>();
+    // rows 4 wave .. 4 wave + 3 of this half, two at a time: every load of the
+    // pair first
+#pragma unroll
+    for (int j0 = 0; j0 < 4; j0 += 2) {
+      int grow[2];
+      size_t tok[2];
+      float gate[2];
+      float4 x[2][TN], y[2][TN];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wave * 4 + j0 + j;
+        grow[j] = row0 + im * 32 + r;
+        const int rr = min(grow[j], row_end - 1);   // past the expert: read a valid row, store nothing
+        tok[j] = (size_t)P.row_tok[rr];
+        gate[j] = P.row_gate[rr];
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const int c = i * 64 + lane_e;
+          x[j][i] = *reinterpret_cast<const float4 *>(P.s_in + tok[j] * D + c * 4);
+          y[j][i] = *reinterpret_cast<const float4 *>(stg + (r * CH + (c ^ (r & 15))) * 4);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (grow[j] >= row_end) continue;
+        float4 h[TN];
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          h[i] = make_float4(x[j][i].x + y[j][i].x, x[j][i].y + y[j][i].y, x[j][i].z + y[j][i].z,
+                             x[j][i].w + y[j][i].w);
+          ss += h[i].x * h[i].x + h[i].y * h[i].y + h[i].z * h[i].z + h[i].w * h[i].w;
+        }
+        const float rinv = rsqrtf(wave_sum64(ss) / (float)D + P.eps);
+        const float gt = gate[j];
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const int c = (i * 64 + lane_e) * 4;
+          *reinterpret_cast<float4 *>(P.s + tok[j] * D + c) =
+              make_float4(x[j][i].x + gt * y[j][i].x, x[j][i].y + gt * y[j][i].y,
+                          x[j][i].z + gt * y[j][i].z, x[j][i].w + gt * y[j][i].w);
+          const float v0 = av[i].x * (h[i].x * rinv * gv[i].x) + bv[i].x;
+          const float v1 = av[i].y * (h[i].y * rinv * gv[i].y) + bv[i].y;
+          const float v2 = av[i].z * (h[i].z * rinv * gv[i].z) + bv[i].z;
+          const float v3 = av[i].w * (h[i].w * rinv * gv[i].w) + bv[i].w;
+          uint2 pk;
+          pk.x = pack_bf16x2(v0, v1);
+          pk.y = pack_bf16x2(v2, v3);
+          *reinterpret_cast<uint2 *>(P.u + (size_t)grow[j] * D + c) = pk;
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -755,7 +1037,69 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   return hipGetLastError();
 }
 
+template <int TN>
+hipError_t launch_o_norm_tn(const ONormParams &P, const Workspace &ws, hipStream_t st) {
+  constexpr int LDS = ONormShape<TN>::LDS;
+  const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_o_norm<TN>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  if (e != hipSuccess) return e;
+  const int grid = ((2 * ws.max_mtiles + 7) / 8) * 8;   // 64-row halves of the 128-row table
+  hipLaunchKernelGGL((k_gemm_o_norm<TN>), dim3(grid), dim3(512), LDS, st, P);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool o_norm_eligible(const lol_core_config &c) {
+  return c.dtype == LOL_BF16 && c.d % 256 == 0 && c.d <= 1024;
+}
+
+bool o_norm_fused(const Plan &p) {
+  const int d = p.cfg.d;
+  if (!o_norm_eligible(p.cfg)) return false;
+  int dev = 0, lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return false;
+  return lds >= kONormStages * (kONormRows * kONormBK * 2 + d * kONormBK * 2);
+}
+
+hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws, const float *s_in,
+                         float *s, const lol_library &lib, hipStream_t st) {
+  if (!o_norm_fused(p)) return hipErrorInvalidValue;
+  const int d = p.cfg.d;
+  ONormParams P;
+  P.A = reinterpret_cast<const bf16_t *>(ws.o);
+  P.Wp = ws.wo_p;
+  P.mtile = ws.mtile;
+  P.mcount = ws.mcount;
+  P.toff = ws.toff;
+  P.row_tok = ws.row_tok;
+  P.row_gate = ws.row_gate;
+  P.s_in = s_in;
+  P.s = s;
+  P.gain = lib.g_ffn;
+  // FiLM of the MLP sublayer (index 1) of this depth
+  P.fg = lib.film_gamma ? lib.film_gamma + ((size_t)g.depth * 2 + 1) * d : nullptr;
+  P.fb = lib.film_beta ? lib.film_beta + ((size_t)g.depth * 2 + 1) * d : nullptr;
+  P.u = reinterpret_cast<bf16_t *>(ws.u);
+  P.eps = p.cfg.rms_eps;
+  switch (d / 256) {
+    case 1: return launch_o_norm_tn<1>(P, ws, st);
+    case 2: return launch_o_norm_tn<2>(P, ws, st);
+    case 3: return launch_o_norm_tn<3>(P, ws, st);
+    case 4: return launch_o_norm_tn<4>(P, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_pack_wo(const Plan &p, const Workspace &ws, const lol_library &lib, hipStream_t st) {
+  if (!ws.wo_p) return hipErrorInvalidValue;
+  const int d = p.cfg.d;
+  const long long pieces = (long long)p.cfg.L * d * d / 8;   // 16-byte pieces
+  hipLaunchKernelGGL(k_pack_panels, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const bf16_t *>(lib.wo), ws.wo_p, d, pieces);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st) {
   switch (a.epi) {
@@ -765,6 +1109,7 @@ hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hi
     case EPI_GELU: return launch_typed<EPI_GELU>(p, ws, a, st);
     case EPI_BLEND: return launch_typed<EPI_BLEND>(p, ws, a, st);
     case EPI_QKV_ROPE: return launch_typed<EPI_QKV_ROPE>(p, ws, a, st);
+    case EPI_ACCUM: return launch_typed<EPI_ACCUM>(p, ws, a, st);
   }
   return hipErrorInvalidValue;
 }

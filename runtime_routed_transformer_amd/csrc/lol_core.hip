@@ -175,6 +175,7 @@ size_t workspace_layout(const Plan &p, char *base, Workspace *ws) {
   w.o = carve(T * d * p.act_bytes);
   w.h = (float *)carve(T * d * 4);
   w.hid = carve(T * f * p.act_bytes);
+  w.wo_p = o_norm_eligible(c) ? (bf16_t *)carve((size_t)c.L * d * d * 2) : nullptr;
   w.max_mtiles = max_mtiles;
   w.max_mtiles2 = max_mtiles2;
   if (ws) *ws = w;
@@ -235,7 +236,12 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
 
   // Depth 1 reads s0 and its blend writes s_out: every token lies in exactly
   // one window per depth, so s_out is complete after it (no copy of s0).
+  // With the fused output projection (bf16, d a multiple of 256 up to 1024)
+  // the blend is split: the O kernel writes s_out = s + gate * Attn and the
+  // down projection adds gate * MLP.
+  const bool fused_o = o_norm_fused(p);
   LOL_TRY(KK_COPY, launch_setup(p, ws, st));
+  if (fused_o) LOL_TRY(KK_COPY, launch_pack_wo(p, ws, *lib, st));
   for (int l = 0; l < c.D; ++l) {
     const float *s = l == 0 ? s0 : s_out;   // depth input
     DepthGeom g;
@@ -261,18 +267,22 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.C = ws.qkv;
     LOL_TRY(KK_GEMM_QKV, launch_gemm(p, ws, a, st));
     LOL_TRY(KK_ATTN, launch_attention(p, g, ws, st));
-    a = GemmArgs{};
-    a.len_gcd = g.len_gcd;
-    a.A = ws.o;
-    a.Wt = lib->wo;
-    a.N = c.d;
-    a.K = c.d;
-    a.w_expert_stride = (long long)d * d;
-    a.epi = EPI_RESID;
-    a.C = ws.h;
-    a.s_in = s;
-    LOL_TRY(KK_GEMM_O, launch_gemm(p, ws, a, st));
-    LOL_TRY(KK_NORM_FFN, launch_norm(p, g, 1, s, *lib, ws, st));
+    if (fused_o) {
+      LOL_TRY(KK_GEMM_O, launch_o_norm(p, g, ws, s, s_out, *lib, st));
+    } else {
+      a = GemmArgs{};
+      a.len_gcd = g.len_gcd;
+      a.A = ws.o;
+      a.Wt = lib->wo;
+      a.N = c.d;
+      a.K = c.d;
+      a.w_expert_stride = (long long)d * d;
+      a.epi = EPI_RESID;
+      a.C = ws.h;
+      a.s_in = s;
+      LOL_TRY(KK_GEMM_O, launch_gemm(p, ws, a, st));
+      LOL_TRY(KK_NORM_FFN, launch_norm(p, g, 1, s, *lib, ws, st));
+    }
     a = GemmArgs{};
     a.len_gcd = g.len_gcd;
     a.A = ws.u;
@@ -291,10 +301,15 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.N = c.d;
     a.K = c.d_ffn;
     a.w_expert_stride = (long long)d * f;
-    a.epi = EPI_BLEND;
-    a.s_in = s;
+    if (fused_o) {
+      a.epi = EPI_ACCUM;
+      a.s_in = s_out;
+    } else {
+      a.epi = EPI_BLEND;
+      a.s_in = s;
+      a.h = ws.h;
+    }
     a.s = s_out;
-    a.h = ws.h;
     LOL_TRY(KK_GEMM_DOWN, launch_gemm(p, ws, a, st));
   }
 #undef LOL_TRY

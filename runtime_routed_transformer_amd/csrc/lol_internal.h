@@ -65,6 +65,7 @@ struct Workspace {
   void *o;             // [T][d]   act       attention output
   float *h;            // [T][d]   fp32      after the attention sublayer
   void *hid;           // [T][f]   act       MLP hidden
+  bf16_t *wo_p;        // [L][d/16][d][16] bf16  W_o in 16-k panels (fused output projection only)
   int max_mtiles, max_mtiles2;
 };
 
@@ -102,6 +103,7 @@ enum GemmEpilogue {
   EPI_BLEND = 4,    // s[row_tok] = s_in[row_tok] + gate * (h + acc - s_in[row_tok])
   EPI_QKV_ROPE = 5, // C (act) = acc, with RoPE at the row's window position on
                     // the q and k columns (bf16 mode only)
+  EPI_ACCUM = 6,    // s[row_tok] = s_in[row_tok] + gate * acc (s_in may equal s)
 };
 
 struct GemmArgs {
@@ -120,5 +122,19 @@ struct GemmArgs {
   int len_gcd;          // gcd of the depth's window lengths: every expert's row count is a multiple
 };
 hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st);
+
+// Output projection fused with the feed-forward sublayer's input norm (bf16,
+// d a multiple of 256 up to 1024).  Per grouped row r of token t, expert e
+// and gate g, with y = o[r] W_o[e]^T and h = s_in[t] + y:
+//   u[r] = FiLM_ffn(RMSNorm_e(h))  (bf16)   and   s[t] = s_in[t] + g y,
+// so that the down projection finishes the gated blend with EPI_ACCUM.
+// h is never stored.  s may equal s_in.
+bool o_norm_eligible(const lol_core_config &c);   // bf16, d a multiple of 256 up to 1024
+bool o_norm_fused(const Plan &p);                  // eligible and the device's LDS holds the ring
+// W_o [L][d][d] -> 16-k panels [L][d/16][d][16]: one 16-k stage of all d
+// rows of an expert becomes one contiguous block
+hipError_t launch_pack_wo(const Plan &p, const Workspace &ws, const lol_library &lib, hipStream_t st);
+hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws, const float *s_in,
+                         float *s, const lol_library &lib, hipStream_t st);
 
 }  // namespace lol
