@@ -240,8 +240,8 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
   // the blend is split: the O kernel writes s_out = s + gate * Attn and the
   // down projection adds gate * MLP.
   const bool fused_o = o_norm_fused(p);
-  LOL_TRY(KK_COPY, launch_setup(p, ws, st));
-  if (fused_o) LOL_TRY(KK_COPY, launch_pack_wo(p, ws, *lib, st));
+  LOL_TRY(KK_SETUP, launch_setup(p, ws, st));
+  if (fused_o) LOL_TRY(KK_SETUP, launch_pack_wo(p, ws, *lib, st));
   for (int l = 0; l < c.D; ++l) {
     const float *s = l == 0 ? s0 : s_out;   // depth input
     DepthGeom g;
@@ -356,7 +356,7 @@ lol_status lol_core_timing_collect(double *ms, int32_t *launches) {
 
 const char *lol_core_kernel_name(int32_t kind) {
   static const char *names[LOL_KERNEL_KINDS] = {
-      "copy_s0",  "pool",     "route",  "bucket", "rowmeta",      "norm_attn",
+      "setup",    "pool",     "route",  "bucket", "rowmeta",      "norm_attn",
       "gemm_qkv", "win_attn", "gemm_o", "norm_ffn", "gemm_gate_up", "gemm_down"};
   if (kind < 0 || kind >= LOL_KERNEL_KINDS) return nullptr;
   return names[kind];

@@ -13,7 +13,7 @@ typedef uint16_t bf16_t;  // raw bfloat16 bits
 
 // Kernel kinds for the timing instrumentation (order = lol_core_kernel_name).
 enum KernelKind {
-  KK_COPY = 0,
+  KK_SETUP = 0,
   KK_POOL,
   KK_ROUTE,
   KK_BUCKET,
