@@ -57,6 +57,7 @@ struct GemmParams {
   const float *rope_cs;    // QKV_ROPE: [W][half][2] cos, sin of p * theta^(-2j/d_head)
   int rope_cols;           // QKV_ROPE: columns [0, rope_cols) hold q and k
   int half;                // QKV_ROPE: d_head / 2
+  int a_panel_rows;        // 0: A is [rows][K]; else A is in 32-k panels [K/32][a_panel_rows][32]
 };
 
 // Writes 4 consecutive logical columns [col, col+4) of grouped row `row`.
@@ -265,14 +266,18 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
   // lane and load instruction
   const bf16_t *a_base, *b_base;
   uint32_t soff[NQ];
+  // A row stride and per-stage step: row-major, or 32-k panels (a stage of
+  // the tile is then one contiguous block of whole lines)
+  const int a_rs = P.a_panel_rows ? BK : K;
+  const size_t a_ks = P.a_panel_rows ? (size_t)P.a_panel_rows * BK : BK;
   auto set_src = [&](int e_, int row0_, int row_end_, int nt_) {
-    a_base = A + (size_t)row0_ * K;
+    a_base = A + (size_t)row0_ * a_rs;
     b_base = reinterpret_cast<const bf16_t *>(P.Wt) + (size_t)e_ * P.w_stride;
     const int last = row_end_ - 1 - row0_;                   // last valid row of the A tile
 #pragma unroll
     for (int i = 0; i < AQ; ++i) {
       const int r = (wave + NW * i) * 16 + lrow;             // row inside the A tile
-      soff[i] = (uint32_t)min(r, last) * K + ((lchunk ^ swz(r)) << 3);
+      soff[i] = (uint32_t)min(r, last) * a_rs + ((lchunk ^ swz(r)) << 3);
     }
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
@@ -294,8 +299,9 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
   auto issue = [&](int stage, int slot) {
     char *base = smem + slot * STAGE_BYTES;
     const int koff = stage * BK;
+    const bf16_t *ap = a_base + stage * a_ks;
 #pragma unroll
-    for (int i = 0; i < AQ; ++i) lds_dma16(a_base + soff[i] + koff, base + (wave + NW * i) * 1024);
+    for (int i = 0; i < AQ; ++i) lds_dma16(ap + soff[i], base + (wave + NW * i) * 1024);
 #pragma unroll
     for (int i = 0; i < BQ; ++i)
       lds_dma16(b_base + soff[AQ + i] + koff, base + A_BYTES + (wave + NW * i) * 1024);
@@ -665,6 +671,7 @@ struct ONormParams {
   const float *gain;       // Norm_ffn gains, [L][d]
   const float *fg, *fb;    // FiLM of this depth's MLP sublayer, [d] (null: off)
   bf16_t *u;
+  int u_panel_rows;        // 0: u is [T][d]; else u is in 32-k panels [d/32][u_panel_rows][32]
   float eps;
 };
 
@@ -876,7 +883,10 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
           uint2 pk;
           pk.x = pack_bf16x2(v0, v1);
           pk.y = pack_bf16x2(v2, v3);
-          *reinterpret_cast<uint2 *>(P.u + (size_t)grow[j] * D + c) = pk;
+          bf16_t *up = P.u_panel_rows
+                           ? P.u + ((size_t)(c >> 5) * P.u_panel_rows + grow[j]) * 32 + (c & 31)
+                           : P.u + (size_t)grow[j] * D + c;
+          *reinterpret_cast<uint2 *>(up) = pk;
         }
       }
     }
@@ -1011,6 +1021,8 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.rope_cs = ws.rope_cs;
   P.rope_cols = a.rope_cols;
   P.half = p.d_head / 2;
+  P.a_panel_rows = a.a_panel_rows;
+  if (a.a_panel_rows && p.cfg.dtype != LOL_BF16) return hipErrorInvalidValue;
   if (EPI == EPI_QKV_ROPE && (p.cfg.dtype != LOL_BF16 || (p.d_head != 32 && p.d_head != 64)))
     return hipErrorInvalidValue;  // fp32 mode rotates inside its attention kernel
   if (p.cfg.dtype == LOL_BF16) {
@@ -1064,7 +1076,7 @@ bool o_norm_fused(const Plan &p) {
 }
 
 hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws, const float *s_in,
-                         float *s, const lol_library &lib, hipStream_t st) {
+                         float *s, const lol_library &lib, int u_panel_rows, hipStream_t st) {
   if (!o_norm_fused(p)) return hipErrorInvalidValue;
   const int d = p.cfg.d;
   ONormParams P;
@@ -1082,6 +1094,7 @@ hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws,
   P.fg = lib.film_gamma ? lib.film_gamma + ((size_t)g.depth * 2 + 1) * d : nullptr;
   P.fb = lib.film_beta ? lib.film_beta + ((size_t)g.depth * 2 + 1) * d : nullptr;
   P.u = reinterpret_cast<bf16_t *>(ws.u);
+  P.u_panel_rows = u_panel_rows;
   P.eps = p.cfg.rms_eps;
   switch (d / 256) {
     case 1: return launch_o_norm_tn<1>(P, ws, st);

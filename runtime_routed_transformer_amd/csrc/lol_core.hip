@@ -268,7 +268,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     LOL_TRY(KK_GEMM_QKV, launch_gemm(p, ws, a, st));
     LOL_TRY(KK_ATTN, launch_attention(p, g, ws, st));
     if (fused_o) {
-      LOL_TRY(KK_GEMM_O, launch_o_norm(p, g, ws, s, s_out, *lib, st));
+      LOL_TRY(KK_GEMM_O, launch_o_norm(p, g, ws, s, s_out, *lib, p.T, st));
     } else {
       a = GemmArgs{};
       a.len_gcd = g.len_gcd;
@@ -293,6 +293,8 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.glu_offset = c.d_ffn;
     a.epi = glu ? EPI_SWIGLU : EPI_GELU;
     a.C = ws.hid;
+    // the fused O kernel leaves u in 32-k panels: whole-line loads per stage
+    a.a_panel_rows = fused_o ? p.T : 0;
     LOL_TRY(KK_GEMM_GATE_UP, launch_gemm(p, ws, a, st));
     a = GemmArgs{};
     a.len_gcd = g.len_gcd;

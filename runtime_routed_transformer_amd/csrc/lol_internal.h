@@ -120,6 +120,7 @@ struct GemmArgs {
   const float *h;       // BLEND
   int rope_cols;        // QKV_ROPE: columns [0, rope_cols) are rotated (2 d; 0 = no RoPE)
   int len_gcd;          // gcd of the depth's window lengths: every expert's row count is a multiple
+  int a_panel_rows;     // 0: A is [T][K]; else 32-k panels [K/32][a_panel_rows][32] (bf16 only)
 };
 hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st);
 
@@ -134,7 +135,9 @@ bool o_norm_fused(const Plan &p);                  // eligible and the device's 
 // W_o [L][d][d] -> 16-k panels [L][d/16][d][16]: one 16-k stage of all d
 // rows of an expert becomes one contiguous block
 hipError_t launch_pack_wo(const Plan &p, const Workspace &ws, const lol_library &lib, hipStream_t st);
+// u_panel_rows > 0 writes u in 32-k panels [d/32][u_panel_rows][32] (the
+// A layout the next GEMM reads with GemmArgs::a_panel_rows)
 hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws, const float *s_in,
-                         float *s, const lol_library &lib, hipStream_t st);
+                         float *s, const lol_library &lib, int u_panel_rows, hipStream_t st);
 
 }  // namespace lol
