@@ -58,7 +58,7 @@ __global__ void __launch_bounds__(256) k_norm(const float *__restrict__ src,
                                               const float *__restrict__ gain,
                                               const float *__restrict__ fg,
                                               const float *__restrict__ fb, act_t *__restrict__ u,
-                                              int T, int d, float eps) {
+                                              int T, int d, float eps, int panel_rows) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= T) return;
   const float *x = src + (FROM_S ? (size_t)row_tok[row] : (size_t)row) * d;
@@ -92,7 +92,9 @@ __global__ void __launch_bounds__(256) k_norm(const float *__restrict__ src,
       if (fg)
         v = make_float4(av[i].x * v.x + bv[i].x, av[i].y * v.y + bv[i].y, av[i].z * v.z + bv[i].z,
                         av[i].w * v.w + bv[i].w);
-      store4<act_t>(out + c, v.x, v.y, v.z, v.w);
+      // panel_rows > 0 (NCH > 0 only): u in 32-column panels [d/32][panel_rows][32]
+      act_t *dst = panel_rows ? u + ((size_t)(c >> 5) * panel_rows + row) * 32 + (c & 31) : out + c;
+      store4<act_t>(dst, v.x, v.y, v.z, v.w);
     }
   } else {
     float ss = 0.f;
@@ -101,7 +103,7 @@ __global__ void __launch_bounds__(256) k_norm(const float *__restrict__ src,
     for (int c = lane; c < d; c += 64) {
       float v = x[c] * inv * g[c];
       if (fg) v = fg[c] * v + fb[c];
-      st<act_t>(out + c, v);
+      st<act_t>(panel_rows ? u + ((size_t)(c >> 5) * panel_rows + row) * 32 + (c & 31) : out + c, v);
     }
   }
 }
@@ -413,34 +415,34 @@ __global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__
 
 template <typename act_t, int NCH>
 void norm_launch(const Plan &p, int which, const float *s, const lol_library &lib,
-                 const Workspace &ws, const float *fg, const float *fb, hipStream_t st) {
+                 const Workspace &ws, const float *fg, const float *fb, int panel_rows, hipStream_t st) {
   dim3 grid((p.T + 3) / 4);
   if (which == 0)
     hipLaunchKernelGGL((k_norm<act_t, true, NCH>), grid, dim3(256), 0, st, s, ws.row_tok,
                        ws.row_exp, lib.g_attn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T,
-                       p.cfg.d, p.cfg.rms_eps);
+                       p.cfg.d, p.cfg.rms_eps, panel_rows);
   else
     hipLaunchKernelGGL((k_norm<act_t, false, NCH>), grid, dim3(256), 0, st, ws.h, ws.row_tok,
                        ws.row_exp, lib.g_ffn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T,
-                       p.cfg.d, p.cfg.rms_eps);
+                       p.cfg.d, p.cfg.rms_eps, panel_rows);
 }
 
 template <typename act_t>
 hipError_t norm_typed(const Plan &p, int which, const float *s, const lol_library &lib,
-                      const Workspace &ws, int depth, hipStream_t st) {
+                      const Workspace &ws, int depth, int panel_rows, hipStream_t st) {
   const int d = p.cfg.d;
   const float *fg = lib.film_gamma ? lib.film_gamma + ((size_t)depth * 2 + which) * d : nullptr;
   const float *fb = lib.film_beta ? lib.film_beta + ((size_t)depth * 2 + which) * d : nullptr;
   switch ((d % 256 == 0) ? d / 256 : 0) {
-    case 1: norm_launch<act_t, 1>(p, which, s, lib, ws, fg, fb, st); break;
-    case 2: norm_launch<act_t, 2>(p, which, s, lib, ws, fg, fb, st); break;
-    case 3: norm_launch<act_t, 3>(p, which, s, lib, ws, fg, fb, st); break;
-    case 4: norm_launch<act_t, 4>(p, which, s, lib, ws, fg, fb, st); break;
-    case 5: norm_launch<act_t, 5>(p, which, s, lib, ws, fg, fb, st); break;
-    case 6: norm_launch<act_t, 6>(p, which, s, lib, ws, fg, fb, st); break;
-    case 7: norm_launch<act_t, 7>(p, which, s, lib, ws, fg, fb, st); break;
-    case 8: norm_launch<act_t, 8>(p, which, s, lib, ws, fg, fb, st); break;
-    default: norm_launch<act_t, 0>(p, which, s, lib, ws, fg, fb, st); break;
+    case 1: norm_launch<act_t, 1>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
+    case 2: norm_launch<act_t, 2>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
+    case 3: norm_launch<act_t, 3>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
+    case 4: norm_launch<act_t, 4>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
+    case 5: norm_launch<act_t, 5>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
+    case 6: norm_launch<act_t, 6>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
+    case 7: norm_launch<act_t, 7>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
+    case 8: norm_launch<act_t, 8>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
+    default: norm_launch<act_t, 0>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
   }
   return hipGetLastError();
 }
@@ -470,9 +472,10 @@ hipError_t attn_mfma(const Plan &p, const DepthGeom &g, const Workspace &ws, hip
 }  // namespace
 
 hipError_t launch_norm(const Plan &p, const DepthGeom &g, int which, const float *s,
-                       const lol_library &lib, const Workspace &ws, hipStream_t st) {
-  if (p.cfg.dtype == LOL_BF16) return norm_typed<bf16_t>(p, which, s, lib, ws, g.depth, st);
-  return norm_typed<float>(p, which, s, lib, ws, g.depth, st);
+                       const lol_library &lib, const Workspace &ws, int panel_rows, hipStream_t st) {
+  if (panel_rows && (p.cfg.dtype != LOL_BF16 || p.cfg.d % 32 != 0)) return hipErrorInvalidValue;
+  if (p.cfg.dtype == LOL_BF16) return norm_typed<bf16_t>(p, which, s, lib, ws, g.depth, panel_rows, st);
+  return norm_typed<float>(p, which, s, lib, ws, g.depth, 0, st);
 }
 
 hipError_t launch_attention(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {

@@ -58,6 +58,7 @@ struct GemmParams {
   int rope_cols;           // QKV_ROPE: columns [0, rope_cols) hold q and k
   int half;                // QKV_ROPE: d_head / 2
   int a_panel_rows;        // 0: A is [rows][K]; else A is in 32-k panels [K/32][a_panel_rows][32]
+  int c_panel_rows;        // bf16 store epilogues: 0 = C is [rows][ldc]; else 32-column panels
 };
 
 // Writes 4 consecutive logical columns [col, col+4) of grouped row `row`.
@@ -604,7 +605,10 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
           pk.y = pack_bf16x2(v0[pass].z, v0[pass].w);
           pk.z = pack_bf16x2(v1[pass].x, v1[pass].y);
           pk.w = pack_bf16x2(v1[pass].z, v1[pass].w);
-          *reinterpret_cast<uint4 *>(reinterpret_cast<bf16_t *>(P.C) + (size_t)row[pass] * P.ldc + col) = pk;
+          bf16_t *cp = P.c_panel_rows
+                           ? reinterpret_cast<bf16_t *>(P.C) + ((size_t)(col >> 5) * P.c_panel_rows + row[pass]) * 32 + (col & 31)
+                           : reinterpret_cast<bf16_t *>(P.C) + (size_t)row[pass] * P.ldc + col;
+          *reinterpret_cast<uint4 *>(cp) = pk;
         }
       }
     }
@@ -1022,7 +1026,9 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.rope_cols = a.rope_cols;
   P.half = p.d_head / 2;
   P.a_panel_rows = a.a_panel_rows;
-  if (a.a_panel_rows && p.cfg.dtype != LOL_BF16) return hipErrorInvalidValue;
+  P.c_panel_rows = a.c_panel_rows;
+  if ((a.a_panel_rows || a.c_panel_rows) && p.cfg.dtype != LOL_BF16) return hipErrorInvalidValue;
+  if (a.c_panel_rows && (EPI == EPI_RESID || EPI == EPI_BLEND || EPI == EPI_ACCUM)) return hipErrorInvalidValue;
   if (EPI == EPI_QKV_ROPE && (p.cfg.dtype != LOL_BF16 || (p.d_head != 32 && p.d_head != 64)))
     return hipErrorInvalidValue;  // fp32 mode rotates inside its attention kernel
   if (p.cfg.dtype == LOL_BF16) {

@@ -240,6 +240,11 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
   // the blend is split: the O kernel writes s_out = s + gate * Attn and the
   // down projection adds gate * MLP.
   const bool fused_o = o_norm_fused(p);
+  // bf16 GEMM inputs written by this library's own kernels go in 32-k
+  // panels: a stage of an A tile is then one block of whole lines
+  const bool bf16 = c.dtype == LOL_BF16;
+  const bool qkv_panels = bf16;    // u from the attention norm
+  const bool down_panels = bf16;   // hid from the gate/up epilogue
   LOL_TRY(KK_SETUP, launch_setup(p, ws, st));
   if (fused_o) LOL_TRY(KK_SETUP, launch_pack_wo(p, ws, *lib, st));
   for (int l = 0; l < c.D; ++l) {
@@ -251,7 +256,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     g.len_gcd = window_length_gcd(c.n, c.W, g.delta, g.K);
     LOL_TRY(KK_POOL, launch_pool(p, g, s, ws, *rt, st));
     LOL_TRY(KK_ROUTE, launch_route(p, g, s, ws, *rt, forced_expert, forced_gate, path, st));
-    LOL_TRY(KK_NORM_ATTN, launch_norm(p, g, 0, s, *lib, ws, st));
+    LOL_TRY(KK_NORM_ATTN, launch_norm(p, g, 0, s, *lib, ws, qkv_panels ? p.T : 0, st));
     GemmArgs a{};
     a.A = ws.u;
     a.Wt = lib->wqkv;
@@ -265,6 +270,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.epi = rope_in_gemm ? EPI_QKV_ROPE : EPI_STORE;
     a.rope_cols = rope_in_gemm ? 2 * c.d : 0;
     a.C = ws.qkv;
+    a.a_panel_rows = qkv_panels ? p.T : 0;
     LOL_TRY(KK_GEMM_QKV, launch_gemm(p, ws, a, st));
     LOL_TRY(KK_ATTN, launch_attention(p, g, ws, st));
     if (fused_o) {
@@ -281,7 +287,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
       a.C = ws.h;
       a.s_in = s;
       LOL_TRY(KK_GEMM_O, launch_gemm(p, ws, a, st));
-      LOL_TRY(KK_NORM_FFN, launch_norm(p, g, 1, s, *lib, ws, st));
+      LOL_TRY(KK_NORM_FFN, launch_norm(p, g, 1, s, *lib, ws, 0, st));
     }
     a = GemmArgs{};
     a.len_gcd = g.len_gcd;
@@ -295,6 +301,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.C = ws.hid;
     // the fused O kernel leaves u in 32-k panels: whole-line loads per stage
     a.a_panel_rows = fused_o ? p.T : 0;
+    a.c_panel_rows = down_panels ? p.T : 0;
     LOL_TRY(KK_GEMM_GATE_UP, launch_gemm(p, ws, a, st));
     a = GemmArgs{};
     a.len_gcd = g.len_gcd;
@@ -303,6 +310,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     a.N = c.d;
     a.K = c.d_ffn;
     a.w_expert_stride = (long long)d * f;
+    a.a_panel_rows = down_panels ? p.T : 0;
     if (fused_o) {
       a.epi = EPI_ACCUM;
       a.s_in = s_out;

@@ -90,9 +90,10 @@ hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const
                         const lol_path *path, hipStream_t st);
 // clears the flag word and builds the RoPE table
 hipError_t launch_setup(const Plan &p, const Workspace &ws, hipStream_t st);
-// which = 0: u = FiLM(Norm_attn(s[row_tok])) ; which = 1: u = FiLM(Norm_ffn(h))
+// which = 0: u = FiLM(Norm_attn(s[row_tok])) ; which = 1: u = FiLM(Norm_ffn(h)).
+// panel_rows > 0 (bf16) writes u in 32-column panels [d/32][panel_rows][32].
 hipError_t launch_norm(const Plan &p, const DepthGeom &g, int which, const float *s,
-                       const lol_library &lib, const Workspace &ws, hipStream_t st);
+                       const lol_library &lib, const Workspace &ws, int panel_rows, hipStream_t st);
 hipError_t launch_attention(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st);
 
 enum GemmEpilogue {
@@ -121,6 +122,7 @@ struct GemmArgs {
   int rope_cols;        // QKV_ROPE: columns [0, rope_cols) are rotated (2 d; 0 = no RoPE)
   int len_gcd;          // gcd of the depth's window lengths: every expert's row count is a multiple
   int a_panel_rows;     // 0: A is [T][K]; else 32-k panels [K/32][a_panel_rows][32] (bf16 only)
+  int c_panel_rows;     // SwiGLU / GELU / STORE (bf16): 0 = C is [T][N]; else 32-column panels
 };
 hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st);
 
