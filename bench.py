@@ -97,7 +97,7 @@ def stored_traffic(kernel, workload):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mid_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -145,16 +145,21 @@ def main(argv=None):
     gemm_ms = sum(kt[k][0] for k in flops) / args.timing_steps
     gemm_tflops = sum(flops.values()) * cfg.D / (gemm_ms / 1e3) / 1e12
 
-    # timed region: K whole forwards; events only around the dominant kernel
+    # timed region: K whole forwards.  HIP events on the launch stream time
+    # the dominant kernel; each timed launch costs the stream a few
+    # microseconds, so every forward times it at one depth, the depth
+    # advancing from step to step (all depths are sampled when K >= D)
     B.lol_core_timing_enable(1 << B.kernel_kind(dominant))
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        B.lol_core_timing_depth(i % cfg.D)
         core.forward(stream=stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     B.lol_core_timing_enable(0)
+    B.lol_core_timing_depth(-1)
     ms = ev0.elapsed_time(ev1) / args.steps
     tokens_per_s = cfg.tokens / (ms / 1e3)
     dom_total, dom_n = B.lol_core_timing_collect()[dominant]

@@ -162,6 +162,14 @@ lol_status lol_core_read_flags(void *workspace, uint32_t *flags, void *stream);
 #define LOL_KERNEL_KINDS 12
 #define LOL_TIMING_ALL 0xFFFu
 lol_status lol_core_timing_enable(uint32_t mask);
+/* Restricts the timing above to the launches of depth index `depth`
+ * (0 <= depth < D of the forwards that follow); -1 (the default) times
+ * every depth.  Each timed launch costs the stream a few microseconds (the
+ * events are attached to the kernel's dispatch, created without a
+ * system-scope fence), so a caller that needs one kernel's average
+ * duration inside a timed region can sample one depth per forward.
+ * LOL_EINVAL for depth < -1. */
+lol_status lol_core_timing_depth(int32_t depth);
 lol_status lol_core_timing_collect(double *ms, int32_t *launches);
 /* Name of kernel kind k (0 <= k < LOL_KERNEL_KINDS), or NULL. */
 const char *lol_core_kernel_name(int32_t kind);

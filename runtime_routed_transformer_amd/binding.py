@@ -56,6 +56,7 @@ _SIGNATURES.update({
                                    POINTER(lol_path), c_void_p, c_size_t, c_void_p]),
     "lol_core_read_flags": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
     "lol_core_timing_enable": (c_int32, [c_uint32]),
+    "lol_core_timing_depth": (c_int32, [c_int32]),
     "lol_core_timing_collect": (c_int32, [POINTER(c_double), POINTER(c_int32)]),
     "lol_core_kernel_name": (c_char_p, [c_int32]),
     "lol_status_str": (c_char_p, [c_int32]),
@@ -124,6 +125,11 @@ def lol_core_read_flags(workspace, stream) -> int:
 def lol_core_timing_enable(mask: int) -> None:
     """Bit k of ``mask`` times kernel kind k; 0 disables, LOL_TIMING_ALL times all."""
     _check(load().lol_core_timing_enable(int(mask)), "lol_core_timing_enable")
+
+
+def lol_core_timing_depth(depth: int) -> None:
+    """Time only the launches of depth index ``depth`` (-1: every depth)."""
+    _check(load().lol_core_timing_depth(int(depth)), "lol_core_timing_depth")
 
 
 def kernel_kind(name: str) -> int:

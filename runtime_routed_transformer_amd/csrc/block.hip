@@ -418,11 +418,11 @@ void norm_launch(const Plan &p, int which, const float *s, const lol_library &li
                  const Workspace &ws, const float *fg, const float *fb, int panel_rows, hipStream_t st) {
   dim3 grid((p.T + 3) / 4);
   if (which == 0)
-    hipLaunchKernelGGL((k_norm<act_t, true, NCH>), grid, dim3(256), 0, st, s, ws.row_tok,
+    lol_launch((k_norm<act_t, true, NCH>), grid, dim3(256), 0, st, s, ws.row_tok,
                        ws.row_exp, lib.g_attn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T,
                        p.cfg.d, p.cfg.rms_eps, panel_rows);
   else
-    hipLaunchKernelGGL((k_norm<act_t, false, NCH>), grid, dim3(256), 0, st, ws.h, ws.row_tok,
+    lol_launch((k_norm<act_t, false, NCH>), grid, dim3(256), 0, st, ws.h, ws.row_tok,
                        ws.row_exp, lib.g_ffn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T,
                        p.cfg.d, p.cfg.rms_eps, panel_rows);
 }
@@ -451,7 +451,7 @@ template <typename act_t, int DH>
 hipError_t attn_typed(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {
   dim3 grid(p.n_slots, p.cfg.n_heads, (p.cfg.W + 63) / 64);
   const float scale = 1.0f / sqrtf((float)DH);
-  hipLaunchKernelGGL((k_attn_simt<act_t, DH>), grid, dim3(64), 0, st,
+  lol_launch((k_attn_simt<act_t, DH>), grid, dim3(64), 0, st,
                      reinterpret_cast<const act_t *>(ws.qkv), reinterpret_cast<act_t *>(ws.o),
                      ws.win_exp, ws.win_row0, ws.rope_cs, p.cfg.n, p.cfg.d, p.cfg.W, g.delta,
                      p.K_max, scale, p.cfg.rope_theta != 0.f ? 1 : 0);
@@ -463,7 +463,7 @@ hipError_t attn_mfma(const Plan &p, const DepthGeom &g, const Workspace &ws, hip
   dim3 grid(p.n_slots, p.cfg.n_heads, (p.cfg.W + 255) / 256);
   // scores come out in log2 units: softmax uses exp2
   const float qscale = 1.4426950408889634f / sqrtf((float)DH);
-  hipLaunchKernelGGL((k_attn_mfma<DH>), grid, dim3(256), 0, st,
+  lol_launch((k_attn_mfma<DH>), grid, dim3(256), 0, st,
                      reinterpret_cast<const bf16_t *>(ws.qkv), reinterpret_cast<bf16_t *>(ws.o),
                      ws.win_exp, ws.win_row0, p.cfg.n, p.cfg.d, p.cfg.W, g.delta, p.K_max, qscale);
   return hipGetLastError();

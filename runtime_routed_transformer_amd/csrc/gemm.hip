@@ -998,7 +998,7 @@ hipError_t launch_shape(GemmParams P, const Workspace &ws, int n_w, hipStream_t 
     if (ec != hipSuccess) return ec;
     grid = min(grid, max(8, ncu / 8 * 8));
   }
-  hipLaunchKernelGGL((k_gemm_bf16<EPI, WM, WN>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
+  lol_launch((k_gemm_bf16<EPI, WM, WN>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
   return hipGetLastError();
 }
 
@@ -1050,7 +1050,7 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
     return launch_shape<EPI, 2, 2>(P, ws, n_w, st);
   } else {
     P.n_tiles_n = a.N / FBN;
-    hipLaunchKernelGGL(k_gemm_f32<EPI>, dim3(ws.max_mtiles * P.n_tiles_n), dim3(256), 0, st, P);
+    lol_launch(k_gemm_f32<EPI>, dim3(ws.max_mtiles * P.n_tiles_n), dim3(256), 0, st, P);
   }
   return hipGetLastError();
 }
@@ -1062,7 +1062,7 @@ hipError_t launch_o_norm_tn(const ONormParams &P, const Workspace &ws, hipStream
                                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
   const int grid = ((2 * ws.max_mtiles + 7) / 8) * 8;   // 64-row halves of the 128-row table
-  hipLaunchKernelGGL((k_gemm_o_norm<TN>), dim3(grid), dim3(512), LDS, st, P);
+  lol_launch((k_gemm_o_norm<TN>), dim3(grid), dim3(512), LDS, st, P);
   return hipGetLastError();
 }
 
@@ -1115,7 +1115,7 @@ hipError_t launch_pack_wo(const Plan &p, const Workspace &ws, const lol_library 
   if (!ws.wo_p) return hipErrorInvalidValue;
   const int d = p.cfg.d;
   const long long pieces = (long long)p.cfg.L * d * d / 8;   // 16-byte pieces
-  hipLaunchKernelGGL(k_pack_panels, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
+  lol_launch(k_pack_panels, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
                      reinterpret_cast<const bf16_t *>(lib.wo), ws.wo_p, d, pieces);
   return hipGetLastError();
 }

@@ -74,12 +74,16 @@ Plan make_plan(const lol_core_config *c) {
 }
 
 // ---- timing instrumentation ----
+}  // namespace
+thread_local LaunchEvents g_launch_ev;
+namespace {
 struct TimingRec {
   int kind;
   hipEvent_t a, b;
 };
 std::mutex g_tmu;
 uint32_t g_timing = 0;  // bit k: time kernel kind k
+int32_t g_timing_depth = -1;  // only this depth index (-1: all)
 std::vector<TimingRec> g_recs;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -89,32 +93,46 @@ hipEvent_t take_event() {
     g_event_pool.pop_back();
     return e;
   }
+  // timing only: no system-scope fence when the event completes, so no L2
+  // writeback and invalidate between the timed kernel and the next one
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
+// Times one launcher call: its kernels are launched with the event pair
+// attached to their dispatch packets (hipExtLaunchKernel), so the start and
+// end timestamps are those of the kernels themselves and no marker packet
+// sits between kernels (a separate hipEventRecord left the GPU idle about
+// 6 us per marker).
 struct Launch {
   hipStream_t st;
   bool timing;
   int kind;
-  hipEvent_t a = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
   Launch(hipStream_t s, bool t, int k) : st(s), timing(t), kind(k) {
     if (timing) {
       std::lock_guard<std::mutex> lk(g_tmu);
       a = take_event();
-      if (a) hipEventRecord(a, st);
+      b = a ? take_event() : nullptr;
+      if (a && !b) {
+        g_event_pool.push_back(a);
+        a = nullptr;
+      }
+      g_launch_ev.start = a;
+      g_launch_ev.stop = b;
     }
   }
   hipError_t done(hipError_t err) {
-    if (timing && a) {
+    if (a) {
+      const bool launched = g_launch_ev.start == nullptr;   // a kernel took the start event
+      g_launch_ev = LaunchEvents{};
       std::lock_guard<std::mutex> lk(g_tmu);
-      hipEvent_t b = take_event();
-      if (b) {
-        hipEventRecord(b, st);
+      if (launched && err == hipSuccess) {
         g_recs.push_back({kind, a, b});
       } else {
         g_event_pool.push_back(a);
+        g_event_pool.push_back(b);
       }
     }
     return err;
@@ -219,17 +237,20 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
   workspace_layout(p, static_cast<char *>(workspace), &ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint32_t timing;
+  int32_t timing_depth;
   {
     std::lock_guard<std::mutex> lk(g_tmu);
     timing = g_timing;
+    timing_depth = g_timing_depth;
   }
+  int cur_depth = -1;   // depth index of the launches below (-1: before the first depth)
   const lol_core_config &c = p.cfg;
   const size_t d = c.d, f = c.d_ffn;
   const bool glu = c.mlp == LOL_MLP_SWIGLU;
   hipError_t err;
 #define LOL_TRY(kind, call)                           \
   do {                                                \
-    Launch _l(st, (timing >> (kind)) & 1u, kind);     \
+    Launch _l(st, ((timing >> (kind)) & 1u) && (timing_depth < 0 || timing_depth == cur_depth), kind); \
     err = _l.done(call);                              \
     if (err != hipSuccess) return LOL_EHIP;           \
   } while (0)
@@ -248,6 +269,7 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
   LOL_TRY(KK_SETUP, launch_setup(p, ws, st));
   if (fused_o) LOL_TRY(KK_SETUP, launch_pack_wo(p, ws, *lib, st));
   for (int l = 0; l < c.D; ++l) {
+    cur_depth = l;
     const float *s = l == 0 ? s0 : s_out;   // depth input
     DepthGeom g;
     g.depth = l;
@@ -342,6 +364,13 @@ lol_status lol_core_timing_enable(uint32_t mask) {
   if (mask & ~(uint32_t)LOL_TIMING_ALL) return LOL_EINVAL;
   std::lock_guard<std::mutex> lk(g_tmu);
   g_timing = mask;
+  return LOL_OK;
+}
+
+lol_status lol_core_timing_depth(int32_t depth) {
+  if (depth < -1) return LOL_EINVAL;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing_depth = depth;
   return LOL_OK;
 }
 

@@ -2,6 +2,7 @@
 // Not part of the C ABI (that is include/lol_core.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -74,6 +75,25 @@ struct Plan {
   int K_max, d_head, T, n_slots;
   size_t act_bytes;    // 2 (bf16) or 4 (fp32)
 };
+
+// Timing events of the launcher call in progress (set by the forward's
+// timing wrapper for the kinds being timed, empty otherwise).  The first
+// kernel a launcher starts takes the start event and every kernel the stop
+// event, so the pair spans all of the call's kernels.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_ev;
+
+// Every kernel of the library is launched through this, with the timing
+// events (if any) attached to its dispatch packet.
+template <typename F, typename... Args>
+inline void lol_launch(F kernel, const dim3 &grid, const dim3 &block, uint32_t shmem, hipStream_t st,
+                       Args... args) {
+  hipEvent_t a = g_launch_ev.start;
+  g_launch_ev.start = nullptr;
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, a, g_launch_ev.stop, 0u, args...);
+}
 
 size_t workspace_layout(const Plan &p, char *base, Workspace *ws);
 // compute units of the current device (cached per device)

@@ -371,7 +371,7 @@ __global__ void k_setup(uint32_t *__restrict__ flags, float *__restrict__ cs, in
 hipError_t launch_pool(const Plan &p, const DepthGeom &g, const float *s, const Workspace &ws,
                        const lol_router &rt, hipStream_t st) {
   dim3 grid(p.cfg.batch * g.K, p.cfg.d / 64);
-  hipLaunchKernelGGL(k_pool, grid, dim3(256), 0, st, s, rt.w_r, rt.e_depth, ws.zpart, ws.zpart0,
+  lol_launch(k_pool, grid, dim3(256), 0, st, s, rt.w_r, rt.e_depth, ws.zpart, ws.zpart0,
                      p.cfg.n, p.cfg.d, p.cfg.L, p.cfg.W, g.delta, g.K, p.K_max, g.depth);
   return hipGetLastError();
 }
@@ -380,7 +380,7 @@ hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const
                         const lol_router &rt, const int32_t *forced_expert,
                         const float *forced_gate, const lol_path *path, hipStream_t st) {
   (void)s;
-  hipLaunchKernelGGL(k_route_all, dim3(1), dim3(1024), 0, st, ws.zpart, ws.zpart0, rt.b_r,
+  lol_launch(k_route_all, dim3(1), dim3(1024), 0, st, ws.zpart, ws.zpart0, rt.b_r,
                      rt.expert_bias, forced_expert, forced_gate, ws.win_exp, ws.win_gate,
                      ws.win_row0, path ? path->expert : nullptr, path ? path->gate : nullptr,
                      path ? path->margin : nullptr, ws.flags, ws.ecount, ws.toff, ws.mtile,
@@ -393,7 +393,7 @@ hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const
 hipError_t launch_setup(const Plan &p, const Workspace &ws, hipStream_t st) {
   const int half = p.d_head / 2;
   const int total = p.cfg.W * half;
-  hipLaunchKernelGGL(k_setup, dim3((total + 255) / 256), dim3(256), 0, st, ws.flags, ws.rope_cs,
+  lol_launch(k_setup, dim3((total + 255) / 256), dim3(256), 0, st, ws.flags, ws.rope_cs,
                      p.cfg.W, half, (double)p.cfg.rope_theta, p.cfg.rope_theta != 0.f ? 1 : 0);
   return hipGetLastError();
 }
