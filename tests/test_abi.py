@@ -99,3 +99,12 @@ def test_status_and_kernel_names(lib):
     names = [B.lol_core_kernel_name(k) for k in range(B.LOL_KERNEL_KINDS)]
     assert all(names) and len(set(names)) == len(names)
     assert B.lol_core_kernel_name(B.LOL_KERNEL_KINDS) is None
+
+
+def test_timing_controls_validate(lib):
+    # host-only calls: the kind mask and the depth filter
+    assert lib.lol_core_timing_enable(1 << B.LOL_KERNEL_KINDS) == B.LOL_EINVAL
+    assert lib.lol_core_timing_depth(-2) == B.LOL_EINVAL
+    for depth in (0, 5, -1):
+        assert lib.lol_core_timing_depth(depth) == B.LOL_OK
+    assert lib.lol_core_timing_enable(0) == B.LOL_OK
