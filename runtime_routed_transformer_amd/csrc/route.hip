@@ -334,20 +334,38 @@ __global__ void __launch_bounds__(1024) k_route_all(
   }
   __syncthreads();  // win_row0 complete
 
-  // 4. grouped-row metadata, one wave per window
-  for (int slot = wave; slot < n_slots; slot += 16) {
-    const int e = s_exp[slot];
-    if (e < 0) continue;
-    const int b = slot / K_max, k = slot % K_max;
-    const int start = win_start(k, W, delta), len = s_len[slot];
-    const int base = win_row0[slot];
-    const float g = win_gate[slot];
-    for (int p = lane; p < len; p += 64) {
-      const int row = base + p;
-      row_tok[row] = b * n + start + p;
-      row_pos[row] = p;
-      row_exp[row] = e;
-      row_gate[row] = g;
+  // 4. grouped-row metadata, one wave per window.  A wave takes windows
+  // wave, wave + 16, ...: lane j first fetches the first row and gate of its
+  // j-th window (one round trip for up to 64 windows), then the wave walks
+  // them with shuffles.
+  for (int r0 = wave; r0 < n_slots; r0 += 16 * 64) {
+    const int my_slot = r0 + 16 * lane;
+    int my_e = -1, my_len = 0, my_row0 = 0;
+    float my_gate = 0.f;
+    if (my_slot < n_slots) {
+      my_e = s_exp[my_slot];
+      my_len = s_len[my_slot];
+      if (my_e >= 0) {
+        my_row0 = win_row0[my_slot];
+        my_gate = win_gate[my_slot];
+      }
+    }
+    for (int j = 0; j < 64; ++j) {
+      const int slot = r0 + 16 * j;
+      if (slot >= n_slots) break;
+      const int e = __shfl(my_e, j, 64);
+      if (e < 0) continue;
+      const int len = __shfl(my_len, j, 64), base = __shfl(my_row0, j, 64);
+      const float g = __shfl(my_gate, j, 64);
+      const int b = slot / K_max, k = slot % K_max;
+      const int start = win_start(k, W, delta);
+      for (int p = lane; p < len; p += 64) {
+        const int row = base + p;
+        row_tok[row] = b * n + start + p;
+        row_pos[row] = p;
+        row_exp[row] = e;
+        row_gate[row] = g;
+      }
     }
   }
 }
