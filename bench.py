@@ -174,6 +174,7 @@ def main(argv=None):
         "config": {"workload": cfg.name, "batch": cfg.batch, "n": cfg.n, "d": cfg.d,
                    "heads": cfg.n_heads, "d_ffn": cfg.d_ffn, "mlp": cfg.mlp, "L": cfg.L,
                    "D": cfg.D, "W": cfg.W, "S": cfg.S, "film": cfg.film,
+                   "router": cfg.router, "film_mode": cfg.film_mode,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -83,21 +83,33 @@ typedef struct {
  *   w_down [L][d][f]
  * element type = cfg.dtype (bf16 stored as raw 16-bit patterns).
  *   g_attn, g_ffn          [L][d] fp32 RMSNorm gains of each expert
- *   film_gamma, film_beta  [D][2][d] fp32 depth FiLM (index 0 = attention
- *                          norm, 1 = MLP norm), shared by all experts; both
- *                          NULL = no FiLM (gamma 1, beta 0). */
+ *   film_gamma, film_beta  fp32 FiLM after each norm (index s = 0 for the
+ *                          attention norm, 1 for the MLP norm); both NULL =
+ *                          no FiLM (gamma 1, beta 0).  Layout by
+ *                          film_per_expert:
+ *                            0: [D][2][d], per depth, shared by all experts
+ *                               (the paper's gamma_{l,s}, beta_{l,s});
+ *                            1: [D][L][2][d], per depth and expert (the
+ *                               released configs' depth_expert_film): a
+ *                               window uses the FiLM of its chosen expert. */
 typedef struct {
   const void *wqkv, *wo, *w_gu, *w_down;
   const float *g_attn, *g_ffn;
   const float *film_gamma, *film_beta;
+  int32_t film_per_expert;
 } lol_library;
 
-/* The router (DEVICE, fp32), tied across depths:
- *   w_r [L][d], b_r [L] (NULL = 0): logits z = W_r r + b_r
+/* The router (DEVICE, fp32):
+ *   w_r, b_r (b_r NULL = 0): logits z = W_r r + b_r, with
+ *     per_depth = 0: w_r [L][d], b_r [L], tied across depths (the default
+ *                    of the released code);
+ *     per_depth = 1: w_r [D][L][d], b_r [D][L], one router per routed depth
+ *                    (the paper's untied-router ablation, Fig. 9)
  *   e_depth [D][d]: the learned vector of each depth used by window 0
  *   expert_bias [L] (NULL = 0): balancing bias, used for the choice only */
 typedef struct {
   const float *w_r, *b_r, *e_depth, *expert_bias;
+  int32_t per_depth;
 } lol_router;
 
 /* Per-window routing path (DEVICE), [D][batch][K_max], indexed by depth,

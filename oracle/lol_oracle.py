@@ -26,7 +26,14 @@ same precision.  Activations are never rounded to bf16.
 Readings of points the pages leave open:
   * RMSNorm eps = 1e-6; Norm_s(x) = g_s * x / sqrt(mean(x^2) + eps) with a
     per-expert gain g_s, followed by the depth FiLM gamma_{l,s}, beta_{l,s}
-    that is shared by all experts (review Eq. 7; paper App. A).
+    that is shared by all experts (review Eq. 7; paper App. A).  Variant
+    "depth_expert" (the released configs' depth_expert_film flag, blog
+    "Where the configs and the text disagree"): one FiLM pair per depth and
+    expert, taken from the window's chosen expert.
+  * Router tied across depths (blog "How the order is chosen": tied by
+    default).  Variant "per_depth" (paper App. B, Fig. 9, untied router):
+    W_r and b_r of routed depth l route that depth; e^(l) is per depth in
+    both.
   * RoPE: theta = 10000, rotate-half pairing (j, j + d_h/2), angle
     pos * theta^(-2j/d_h), positions = token index in the document.
   * Bias-free attention with scale 1/sqrt(d_h) and a causal mask confined
@@ -274,8 +281,10 @@ def forward(inp, forced_expert: Optional[np.ndarray] = None,
     n = cfg.n if n_tokens is None else int(n_tokens)
     D, L, K_max = cfg.D, cfg.L, cfg.k_max
     params = [expert_params(inp, m) for m in range(L)]
-    w_r = np.asarray(inp.w_r, np.float32)
-    b_r = np.asarray(inp.b_r, np.float32)
+    per_depth = getattr(cfg, "router", "tied") == "per_depth"
+    per_expert_film = getattr(cfg, "film_mode", "depth") == "depth_expert"
+    w_r_all = np.asarray(inp.w_r, np.float32)
+    b_r_all = np.asarray(inp.b_r, np.float32)
     bias = np.asarray(inp.expert_bias, np.float32)
     s = np.asarray(inp.s0[rows, :n], np.float64).copy()
     expert = np.full((D, len(rows), K_max), -1, np.int32)
@@ -283,12 +292,20 @@ def forward(inp, forced_expert: Optional[np.ndarray] = None,
     margin = np.zeros((D, len(rows), K_max), np.float32)
     for depth in range(1, D + 1):
         windows = partition(n, cfg.W, cfg.S, depth)
-        if inp.film_gamma is not None:
+        # the router of this depth (untied) or the shared one
+        w_r = w_r_all[depth - 1] if per_depth else w_r_all
+        b_r = b_r_all[depth - 1] if per_depth else b_r_all
+
+        def film_of(rho):
+            # (gamma_attn, beta_attn, gamma_ffn, beta_ffn) of this depth, and
+            # of expert rho in the per-(depth, expert) variant
+            if inp.film_gamma is None:
+                return None
             fg = np.asarray(inp.film_gamma[depth - 1], np.float64)
             fb = np.asarray(inp.film_beta[depth - 1], np.float64)
-            film = (fg[0], fb[0], fg[1], fb[1])
-        else:
-            film = None
+            if per_expert_film:
+                fg, fb = fg[rho], fb[rho]
+            return (fg[0], fb[0], fg[1], fb[1])
         s_next = s.copy()
         for bi, b in enumerate(rows):
             r = router_inputs(s[bi], windows, np.asarray(inp.e_depth[depth - 1], np.float64))
@@ -301,7 +318,7 @@ def forward(inp, forced_expert: Optional[np.ndarray] = None,
                 if forced_gate is not None and not np.isnan(forced_gate[depth - 1, b, k]):
                     alpha = float(forced_gate[depth - 1, b, k])
                 x = s[bi, a0:a1 + 1]
-                y = expert_block(x, params[rho], cfg.n_heads, np.arange(a0, a1 + 1), film,
+                y = expert_block(x, params[rho], cfg.n_heads, np.arange(a0, a1 + 1), film_of(rho),
                                  cfg.rms_eps, cfg.rope_theta)
                 s_next[bi, a0:a1 + 1] = x + np.float64(np.float32(alpha)) * (y - x)
                 expert[depth - 1, bi, k] = rho

@@ -36,11 +36,13 @@ class lol_core_config(ctypes.Structure):
 
 class lol_library(ctypes.Structure):
     _fields_ = [(name, c_void_p) for name in
-                ("wqkv", "wo", "w_gu", "w_down", "g_attn", "g_ffn", "film_gamma", "film_beta")]
+                ("wqkv", "wo", "w_gu", "w_down", "g_attn", "g_ffn", "film_gamma", "film_beta")] + \
+               [("film_per_expert", c_int32)]
 
 
 class lol_router(ctypes.Structure):
-    _fields_ = [(name, c_void_p) for name in ("w_r", "b_r", "e_depth", "expert_bias")]
+    _fields_ = [(name, c_void_p) for name in ("w_r", "b_r", "e_depth", "expert_bias")] + \
+               [("per_depth", c_int32)]
 
 
 class lol_path(ctypes.Structure):

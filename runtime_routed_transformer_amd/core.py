@@ -54,9 +54,11 @@ class DeviceCore:
         self.lib = B.lol_library(
             wqkv=_ptr(self.w["wqkv"]), wo=_ptr(self.w["wo"]), w_gu=_ptr(self.w["w_gu"]),
             w_down=_ptr(self.w["w_down"]), g_attn=_ptr(self.g_attn), g_ffn=_ptr(self.g_ffn),
-            film_gamma=_ptr(self.film_gamma), film_beta=_ptr(self.film_beta))
+            film_gamma=_ptr(self.film_gamma), film_beta=_ptr(self.film_beta),
+            film_per_expert=1 if self.cfg.film_mode == "depth_expert" else 0)
         self.rt = B.lol_router(w_r=_ptr(self.w_r), b_r=_ptr(self.b_r), e_depth=_ptr(self.e_depth),
-                               expert_bias=_ptr(self.expert_bias))
+                               expert_bias=_ptr(self.expert_bias),
+                               per_depth=1 if self.cfg.router == "per_depth" else 0)
         self.k_max = B.lol_core_k_max(self.ccfg)
         self.ws_bytes = B.lol_core_workspace_size(self.ccfg)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)

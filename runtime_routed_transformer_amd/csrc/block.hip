@@ -58,11 +58,17 @@ __global__ void __launch_bounds__(256) k_norm(const float *__restrict__ src,
                                               const float *__restrict__ gain,
                                               const float *__restrict__ fg,
                                               const float *__restrict__ fb, act_t *__restrict__ u,
-                                              int T, int d, float eps, int panel_rows) {
+                                              int T, int d, float eps, int panel_rows, int film_stride) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= T) return;
   const float *x = src + (FROM_S ? (size_t)row_tok[row] : (size_t)row) * d;
-  const float *g = gain + (size_t)row_exp[row] * d;
+  const int e = row_exp[row];
+  const float *g = gain + (size_t)e * d;
+  // FiLM of this depth and sublayer; per expert when film_stride > 0
+  if (fg) {
+    fg += (size_t)e * film_stride;
+    fb += (size_t)e * film_stride;
+  }
   act_t *out = u + (size_t)row * d;
   if (NCH > 0) {
     // every load of the row (x, the expert gain, FiLM) is issued before the
@@ -417,22 +423,26 @@ template <typename act_t, int NCH>
 void norm_launch(const Plan &p, int which, const float *s, const lol_library &lib,
                  const Workspace &ws, const float *fg, const float *fb, int panel_rows, hipStream_t st) {
   dim3 grid((p.T + 3) / 4);
+  const int film_stride = lib.film_per_expert ? 2 * p.cfg.d : 0;
   if (which == 0)
     lol_launch((k_norm<act_t, true, NCH>), grid, dim3(256), 0, st, s, ws.row_tok,
                        ws.row_exp, lib.g_attn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T,
-                       p.cfg.d, p.cfg.rms_eps, panel_rows);
+                       p.cfg.d, p.cfg.rms_eps, panel_rows, film_stride);
   else
     lol_launch((k_norm<act_t, false, NCH>), grid, dim3(256), 0, st, ws.h, ws.row_tok,
                        ws.row_exp, lib.g_ffn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T,
-                       p.cfg.d, p.cfg.rms_eps, panel_rows);
+                       p.cfg.d, p.cfg.rms_eps, panel_rows, film_stride);
 }
 
 template <typename act_t>
 hipError_t norm_typed(const Plan &p, int which, const float *s, const lol_library &lib,
                       const Workspace &ws, int depth, int panel_rows, hipStream_t st) {
   const int d = p.cfg.d;
-  const float *fg = lib.film_gamma ? lib.film_gamma + ((size_t)depth * 2 + which) * d : nullptr;
-  const float *fb = lib.film_beta ? lib.film_beta + ((size_t)depth * 2 + which) * d : nullptr;
+  // FiLM rows of (depth, sublayer): [D][2][d], or [D][L][2][d] per expert
+  // (then the kernel adds expert * 2d)
+  const size_t film_off = ((size_t)depth * (lib.film_per_expert ? p.cfg.L : 1) * 2 + which) * d;
+  const float *fg = lib.film_gamma ? lib.film_gamma + film_off : nullptr;
+  const float *fb = lib.film_beta ? lib.film_beta + film_off : nullptr;
   switch ((d % 256 == 0) ? d / 256 : 0) {
     case 1: norm_launch<act_t, 1>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
     case 2: norm_launch<act_t, 2>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;

@@ -674,6 +674,7 @@ struct ONormParams {
   float *s;
   const float *gain;       // Norm_ffn gains, [L][d]
   const float *fg, *fb;    // FiLM of this depth's MLP sublayer, [d] (null: off)
+  int film_stride;         // > 0: per-expert FiLM, expert e's rows at fg + e * film_stride
   bf16_t *u;
   int u_panel_rows;        // 0: u is [T][d]; else u is in 32-k panels [d/32][u_panel_rows][32]
   float eps;
@@ -816,8 +817,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
     const int c = (i * 64 + lane_e) * 4;
     gv[i] = *reinterpret_cast<const float4 *>(gain + c);
     if (P.fg) {
-      av[i] = *reinterpret_cast<const float4 *>(P.fg + c);
-      bv[i] = *reinterpret_cast<const float4 *>(P.fb + c);
+      av[i] = *reinterpret_cast<const float4 *>(P.fg + (size_t)e * P.film_stride + c);
+      bv[i] = *reinterpret_cast<const float4 *>(P.fb + (size_t)e * P.film_stride + c);
     } else {
       av[i] = make_float4(1.f, 1.f, 1.f, 1.f);
       bv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1096,9 +1097,12 @@ hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws,
   P.s_in = s_in;
   P.s = s;
   P.gain = lib.g_ffn;
-  // FiLM of the MLP sublayer (index 1) of this depth
-  P.fg = lib.film_gamma ? lib.film_gamma + ((size_t)g.depth * 2 + 1) * d : nullptr;
-  P.fb = lib.film_beta ? lib.film_beta + ((size_t)g.depth * 2 + 1) * d : nullptr;
+  // FiLM of the MLP sublayer (index 1) of this depth: [D][2][d], or
+  // [D][L][2][d] per expert (the kernel adds expert * 2d)
+  const size_t film_off = ((size_t)g.depth * (lib.film_per_expert ? p.cfg.L : 1) * 2 + 1) * d;
+  P.fg = lib.film_gamma ? lib.film_gamma + film_off : nullptr;
+  P.fb = lib.film_beta ? lib.film_beta + film_off : nullptr;
+  P.film_stride = lib.film_per_expert ? 2 * d : 0;
   P.u = reinterpret_cast<bf16_t *>(ws.u);
   P.u_panel_rows = u_panel_rows;
   P.eps = p.cfg.rms_eps;

@@ -229,6 +229,8 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     return LOL_EINVAL;
   if ((lib->film_gamma == nullptr) != (lib->film_beta == nullptr)) return LOL_EINVAL;
   if (!rt->w_r || !rt->e_depth) return LOL_EINVAL;
+  if ((rt->per_depth != 0 && rt->per_depth != 1) || (lib->film_per_expert != 0 && lib->film_per_expert != 1))
+    return LOL_EINVAL;
   const Plan p = make_plan(cfg);
   const size_t need = workspace_layout(p, nullptr, nullptr);
   if (!workspace || workspace_bytes < need) return LOL_EWORKSPACE;

@@ -389,7 +389,9 @@ __global__ void k_setup(uint32_t *__restrict__ flags, float *__restrict__ cs, in
 hipError_t launch_pool(const Plan &p, const DepthGeom &g, const float *s, const Workspace &ws,
                        const lol_router &rt, hipStream_t st) {
   dim3 grid(p.cfg.batch * g.K, p.cfg.d / 64);
-  lol_launch(k_pool, grid, dim3(256), 0, st, s, rt.w_r, rt.e_depth, ws.zpart, ws.zpart0,
+  // untied router: this depth's W_r
+  const float *w_r = rt.w_r + (rt.per_depth ? (size_t)g.depth * p.cfg.L * p.cfg.d : 0);
+  lol_launch(k_pool, grid, dim3(256), 0, st, s, w_r, rt.e_depth, ws.zpart, ws.zpart0,
                      p.cfg.n, p.cfg.d, p.cfg.L, p.cfg.W, g.delta, g.K, p.K_max, g.depth);
   return hipGetLastError();
 }
@@ -398,7 +400,9 @@ hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const
                         const lol_router &rt, const int32_t *forced_expert,
                         const float *forced_gate, const lol_path *path, hipStream_t st) {
   (void)s;
-  lol_launch(k_route_all, dim3(1), dim3(1024), 0, st, ws.zpart, ws.zpart0, rt.b_r,
+  // untied router: this depth's b_r
+  const float *b_r = rt.b_r && rt.per_depth ? rt.b_r + (size_t)g.depth * p.cfg.L : rt.b_r;
+  lol_launch(k_route_all, dim3(1), dim3(1024), 0, st, ws.zpart, ws.zpart0, b_r,
                      rt.expert_bias, forced_expert, forced_gate, ws.win_exp, ws.win_gate,
                      ws.win_row0, path ? path->expert : nullptr, path ? path->gate : nullptr,
                      path ? path->margin : nullptr, ws.flags, ws.ecount, ws.toff, ws.mtile,

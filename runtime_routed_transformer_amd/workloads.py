@@ -22,8 +22,11 @@ contiguous along the reduction dimension):
   w_down  [L][d][f]    (GELU: W_2)
   g_attn, g_ffn [L][d] RMSNorm gains, fp32
   film_gamma, film_beta [D][2][d] depth FiLM (index 0 = attention norm,
-                       1 = MLP norm), fp32, or None for "no FiLM"
-  w_r [L][d], b_r [L], e_depth [D][d], expert_bias [L]  router, fp32
+                       1 = MLP norm), fp32, or None for "no FiLM";
+                       [D][L][2][d] with film_mode "depth_expert"
+  w_r [L][d], b_r [L], e_depth [D][d], expert_bias [L]  router, fp32;
+                       w_r [D][L][d], b_r [D][L] with router "per_depth"
+                       (untied)
 
 bf16 workloads round every block matrix to bf16 once (round to nearest even);
 ``*_f32`` holds those rounded values exactly as fp32 for the oracle and
@@ -60,6 +63,8 @@ class CoreConfig:
     rms_eps: float = 1e-6
     bias_mode: str = "zero"      # "zero" | "skewed" (large-library load skew)
     path_mode: str = "free"      # "free" | "forced_seq" (one id sequence for all windows)
+    router: str = "tied"         # "tied" | "per_depth" (one router per routed depth)
+    film_mode: str = "depth"     # "depth" (shared by experts) | "depth_expert"
 
     @property
     def d_head(self) -> int:
@@ -100,6 +105,14 @@ CONFIGS = [
                path_mode="forced_seq"),
 ]
 CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+# Variants of the mid workload (not among the five above): one router per
+# routed depth and FiLM per depth and expert (paper App. B Fig. 9; the
+# released configs' depth_expert_film), for bench.py --workload.
+VARIANT_CONFIGS = [
+    CONFIG_BY_NAME["mid_bf16"].with_(name="mid_bf16_untied_expertfilm", router="per_depth",
+                                     film_mode="depth_expert"),
+]
+CONFIG_BY_NAME.update({c.name: c for c in VARIANT_CONFIGS})
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -126,10 +139,10 @@ class CoreInputs:
     w_down: np.ndarray
     g_attn: np.ndarray             # [L][d]
     g_ffn: np.ndarray
-    film_gamma: Optional[np.ndarray]   # [D][2][d] or None
+    film_gamma: Optional[np.ndarray]   # [D][2][d], [D][L][2][d] (depth_expert) or None
     film_beta: Optional[np.ndarray]
-    w_r: np.ndarray                # [L][d]
-    b_r: np.ndarray                # [L]
+    w_r: np.ndarray                # [L][d], or [D][L][d] (per_depth)
+    b_r: np.ndarray                # [L], or [D][L] (per_depth)
     e_depth: np.ndarray            # [D][d]
     expert_bias: np.ndarray        # [L]
     forced_expert: Optional[np.ndarray]  # [D][B][K_max] int32, -1 = free, or None
@@ -177,13 +190,15 @@ def generate(cfg: CoreConfig) -> CoreInputs:
         g_attn[m] = 1.0 + _normal(rng, (d,), WEIGHT_STD)
         g_ffn[m] = 1.0 + _normal(rng, (d,), WEIGHT_STD)
     if cfg.film:
-        film_gamma = (1.0 + _normal(rng, (D, 2, d), WEIGHT_STD)).astype(np.float32)
-        film_beta = _normal(rng, (D, 2, d), WEIGHT_STD)
+        fshape = (D, L, 2, d) if cfg.film_mode == "depth_expert" else (D, 2, d)
+        film_gamma = (1.0 + _normal(rng, fshape, WEIGHT_STD)).astype(np.float32)
+        film_beta = _normal(rng, fshape, WEIGHT_STD)
     else:
         film_gamma = film_beta = None
-    w_r = _normal(rng, (L, d), WEIGHT_STD)
+    per_depth = cfg.router == "per_depth"
+    w_r = _normal(rng, (D, L, d) if per_depth else (L, d), WEIGHT_STD)
     e_depth = _normal(rng, (D, d), WEIGHT_STD)
-    b_r = np.zeros(L, np.float32)
+    b_r = np.zeros((D, L) if per_depth else L, np.float32)
     expert_bias = np.zeros(L, np.float32)
     forced = None
     if cfg.path_mode == "forced_seq":

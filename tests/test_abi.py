@@ -108,3 +108,15 @@ def test_timing_controls_validate(lib):
     for depth in (0, 5, -1):
         assert lib.lol_core_timing_depth(depth) == B.LOL_OK
     assert lib.lol_core_timing_enable(0) == B.LOL_OK
+
+
+def test_forward_rejects_unknown_variant_flags(lib):
+    # router tying and FiLM layout flags are 0 or 1; anything else is rejected
+    # before any launch
+    c = make_config(CONFIG_BY_NAME["tiny_fp32"])
+    ws = B.lol_core_workspace_size(c)
+    for lib_flag, rt_flag in ((2, 0), (0, 2), (-1, 0)):
+        libw = B.lol_library(wqkv=16, wo=16, w_gu=16, w_down=16, g_attn=16, g_ffn=16,
+                             film_per_expert=lib_flag)
+        rt = B.lol_router(w_r=16, e_depth=16, per_depth=rt_flag)
+        assert B.lol_core_forward(c, 16, libw, rt, None, None, 16, None, 256, ws, None) == B.LOL_EINVAL

@@ -76,6 +76,29 @@ EDGE = [
 ]
 
 
+# the untied router (one W_r, b_r per routed depth) and per-(depth, expert)
+# FiLM, on the fused bf16 path (d = 512 and 1024), the unfused bf16 path
+# (d = 128) and fp32
+VARIANTS = [
+    CONFIG_BY_NAME["small_bf16"].scaled(2, 384).with_(
+        name="variant_small_untied_expertfilm", router="per_depth", film_mode="depth_expert"),
+    CONFIG_BY_NAME["mid_bf16"].scaled(1, 640).with_(
+        name="variant_mid_untied_expertfilm", router="per_depth", film_mode="depth_expert"),
+    CoreConfig("variant_bf16_d128_untied", batch=2, n=150, d=128, n_heads=2, d_ffn=256, L=3, D=3,
+               W=40, S=13, mlp="swiglu", dtype="bf16", seed=31, router="per_depth",
+               film_mode="depth_expert"),
+    CoreConfig("variant_fp32_untied_expertfilm", batch=2, n=37, d=64, n_heads=2, d_ffn=128, L=3,
+               D=4, W=5, S=3, mlp="swiglu", dtype="fp32", seed=32, router="per_depth",
+               film_mode="depth_expert"),
+]
+
+
+@pytest.mark.parametrize("cfg", VARIANTS, ids=lambda c: c.name)
+def test_parity_variants(cfg):
+    print(f"[parity-variant] {cfg.name}", flush=True)
+    _report(parity.run(parity.prepare(cfg)))
+
+
 @pytest.mark.parametrize("cfg", EDGE, ids=lambda c: c.name)
 def test_parity_edge_cases(cfg):
     print(f"[parity-edge] {cfg.name}", flush=True)

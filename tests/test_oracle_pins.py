@@ -340,3 +340,76 @@ def test_path_layout_and_padding():
         assert (res.expert[depth - 1, :, K:] == -1).all()
         assert (res.gate[depth - 1, :, K:] == 0).all()
         assert (res.gate[depth - 1, :, :K] > 0).all()
+
+
+# ---------------------------------------------------------------- variants
+def test_untied_router_routes_each_depth_with_its_own_router():
+    """Untied router (paper App. B, Fig. 9): depth l is routed by W_r[l], b_r[l].
+
+    A bias of +40 on expert (l + 1) mod L in depth l's b_r leaves that expert
+    as the only choice at depth l; the path then shows each depth's own
+    router.  With every depth given the tied router's values the result is
+    the tied run, bit for bit.
+    """
+    cfg = tiny(router="per_depth", D=4, L=3)
+    inp = generate(cfg)
+    for depth in range(cfg.D):
+        inp.b_r[depth] = 0.0
+        inp.b_r[depth, (depth + 1) % cfg.L] = 40.0
+    res = oracle.forward(inp)
+    for depth in range(cfg.D):
+        K = len(oracle.partition(cfg.n, cfg.W, cfg.S, depth + 1))
+        assert (res.expert[depth, :, :K] == (depth + 1) % cfg.L).all(), depth
+        assert (res.gate[depth, :, :K] > 0.999).all()
+    tied = generate(tiny(D=4, L=3))
+    untied = generate(tiny(router="per_depth", D=4, L=3))
+    untied.w_r = np.broadcast_to(tied.w_r, untied.w_r.shape).copy()
+    untied.b_r = np.broadcast_to(tied.b_r, untied.b_r.shape).copy()
+    for name in ("s0", "wqkv", "wo", "w_gu", "w_down", "g_attn", "g_ffn", "film_gamma",
+                 "film_beta", "e_depth"):
+        setattr(untied, name, getattr(tied, name))
+    a, b = oracle.forward(tied), oracle.forward(untied)
+    np.testing.assert_array_equal(a.s, b.s)
+    np.testing.assert_array_equal(a.expert, b.expert)
+
+
+def test_per_expert_film_uses_the_chosen_experts_film():
+    """Per-(depth, expert) FiLM (the released configs' depth_expert_film flag).
+
+    With every window forced to expert m (gate 1, one window, S = 0) only
+    expert m's FiLM rows may matter: the others hold large values that would
+    show.  The result must equal D applications of the ordinary causal block
+    (PyTorch library routines) with expert m's FiLM of each depth.
+    """
+    cfg = tiny(L=3, D=3, n=24, W=24, S=0, film_mode="depth_expert")
+    inp = generate(cfg)
+    m = 1
+    for e in range(cfg.L):
+        if e != m:
+            inp.film_gamma[:, e] = 7.0
+            inp.film_beta[:, e] = -3.0
+    forced = np.full((cfg.D, cfg.batch, cfg.k_max), m, np.int32)
+    gate = np.ones((cfg.D, cfg.batch, cfg.k_max), np.float32)
+    res = oracle.forward(inp, forced_expert=forced, forced_gate=gate)
+    for b in range(cfg.batch):
+        x = inp.s0[b].astype(np.float64)
+        for depth in range(cfg.D):
+            x = torch_block.block(
+                x, inp.wqkv[m], inp.wo[m], inp.w_gu[m], inp.w_down[m], inp.g_attn[m],
+                inp.g_ffn[m], cfg.n_heads, "swiglu",
+                film=(inp.film_gamma[depth, m], inp.film_beta[depth, m]))
+        np.testing.assert_allclose(res.s64[b], x, rtol=0, atol=1e-11)
+
+
+def test_per_expert_film_with_equal_rows_is_the_shared_film():
+    shared = generate(tiny())
+    per = generate(tiny(film_mode="depth_expert"))
+    L = shared.cfg.L
+    per.film_gamma = np.repeat(shared.film_gamma[:, None], L, axis=1)
+    per.film_beta = np.repeat(shared.film_beta[:, None], L, axis=1)
+    for name in ("s0", "wqkv", "wo", "w_gu", "w_down", "g_attn", "g_ffn", "w_r", "b_r",
+                 "e_depth"):
+        setattr(per, name, getattr(shared, name))
+    a, b = oracle.forward(shared), oracle.forward(per)
+    np.testing.assert_array_equal(a.s, b.s)
+    np.testing.assert_array_equal(a.expert, b.expert)
