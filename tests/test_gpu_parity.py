@@ -148,3 +148,36 @@ def test_forced_own_path_and_bad_forced_id_flag():
     assert core.flags() & binding.LOL_FLAG_BAD_FORCED_ID
     assert torch.equal(out, free)    # the bad id was treated as free
     assert core.flags() == 0         # reading clears the flag
+
+
+def test_forward_replays_from_a_hip_graph():
+    """The whole forward captured once into a HIP graph (no memsets, no host
+    synchronisation, no allocation inside it) and replayed: every replay,
+    with eager work and synchronisations between them, equals the eager run."""
+    import torch
+    from runtime_routed_transformer_amd.core import DeviceCore
+    cfg = CONFIG_BY_NAME["mid_bf16"].scaled(2, 512)
+    inp = parity.prepare(cfg)
+    core = DeviceCore(inp)
+    eager = core.forward().clone()
+    path_eager = [t.clone() for t in (core.path_expert, core.path_gate, core.path_margin)]
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        core.forward(s_out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, capture_error_mode="relaxed"):
+        core.forward(s_out=out)
+    for i in range(4):
+        out.zero_()
+        core.path_expert.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager forward"
+        assert torch.equal(core.path_expert, path_eager[0]), f"replay {i}: path differs"
+        assert torch.equal(core.path_gate, path_eager[1])
