@@ -186,6 +186,42 @@ lol_status lol_core_timing_collect(double *ms, int32_t *launches);
 /* Name of kernel kind k (0 <= k < LOL_KERNEL_KINDS), or NULL. */
 const char *lol_core_kernel_name(int32_t kind);
 
+/* ---- Around the core: token embedding and vocabulary readout ----------
+ * The paper's Algorithm 1 (Appendix A) runs a causal prelude on the token
+ * sequence, the routed core, then the causal coda and the vocabulary
+ * readout; its Sec. 3.1 describes prelude and coda as fixed-order stacks of
+ * decoder layers with full causal attention.  Such a stack of P layers is
+ * lol_core_forward with W >= n, S = 0, L = D = P, every window forced to
+ * expert l at depth l with gate 1, and no FiLM: one window per document,
+ * s + 1 (E(s) - s) = E(s).  The two entry points below are the parts that
+ * are not blocks. */
+
+/* Embedding lookup: s[t][:] = table[tokens[t]][:], converted to fp32.
+ *   tokens  DEVICE [T] int32 token ids; an id outside [0, V) yields a zero row
+ *   table   DEVICE [V][d], element type dtype (bf16 as raw 16-bit patterns)
+ *   s       DEVICE [T][d] fp32 output
+ * T >= 1, V >= 1, d % 4 == 0.  Asynchronous on stream. */
+lol_status lol_embed(const int32_t *tokens, int32_t T, const void *table, int32_t V, int32_t d,
+                     int32_t dtype, float *s, void *stream);
+
+/* Bytes of device workspace lol_lm_head needs (0 for invalid sizes). */
+size_t lol_lm_head_workspace_size(int32_t T, int32_t d, int32_t V, int32_t dtype);
+
+/* Vocabulary readout: logits[t][v] = sum_k u[t][k] * w_vocab[v][k] with
+ * u[t] = g_final * s[t] / sqrt(mean(s[t]^2) + eps), a final RMSNorm with a
+ * gain; the softmax over v is left to the consumer (the loss or a sampler
+ * takes it from the logits).  bf16 mode rounds u to bf16 and accumulates
+ * in fp32, like every GEMM of the core.
+ *   s        DEVICE [T][d] fp32 (the coda's output)
+ *   g_final  DEVICE [d] fp32
+ *   w_vocab  DEVICE [V][d], element type dtype
+ *   logits   DEVICE [T][V] fp32 output
+ * Supported: bf16: d % 128 == 0, V % 128 == 0; fp32: d % 64 == 0,
+ * V % 64 == 0.  LOL_EWORKSPACE if the workspace is too small. */
+lol_status lol_lm_head(const float *s, int32_t T, int32_t d, const float *g_final, float eps,
+                       const void *w_vocab, int32_t V, int32_t dtype, float *logits,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *lol_status_str(lol_status status);
 

@@ -53,6 +53,7 @@ numeric forward output.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from dataclasses import dataclass
 from typing import List, Optional, Tuple
@@ -326,3 +327,62 @@ def forward(inp, forced_expert: Optional[np.ndarray] = None,
                 margin[depth - 1, bi, k] = rt.margin
         s = s_next
     return OracleResult(s.astype(np.float32), s, expert, gate, margin)
+
+
+# --------------------------------------------------------------------------
+# Around the core: embedding, fixed-order stacks, vocabulary readout
+#   [paper] Appendix A, Algorithm 1: the prelude is applied to the token
+#   sequence, the routed core follows, then the causal coda and the
+#   vocabulary readout.  Sec. 3.1: prelude and coda are fixed-order stacks
+#   of decoder layers with full causal attention.
+# Readings: the token sequence enters through an embedding table (one row
+# per token id); the readout is a final RMSNorm with a gain followed by a
+# linear map onto the vocabulary, giving logits (the pages' softmax over
+# them is left to the consumer); the vocabulary size is a free parameter.
+# --------------------------------------------------------------------------
+def embed(tokens: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Rows of the embedding table, float64 [B][n][d]."""
+    return np.asarray(table, np.float64)[np.asarray(tokens)]
+
+
+def causal_stack(x: np.ndarray, params: List[BlockParams], n_heads: int, eps: float,
+                 theta: float) -> np.ndarray:
+    """Apply the blocks in order to one document x [n][d], attention causal
+    over the whole document (the window is the document)."""
+    positions = np.arange(x.shape[0])
+    for p in params:
+        x = expert_block(x, p, n_heads, positions, None, eps, theta)
+    return x
+
+
+def lm_head(s: np.ndarray, g_final: np.ndarray, w_vocab: np.ndarray, eps: float) -> np.ndarray:
+    """logits = RMSNorm_g(s) W_vocab^T, float64."""
+    return rms_norm(np.asarray(s, np.float64), np.asarray(g_final, np.float64), eps) @ \
+        np.asarray(w_vocab, np.float64).T
+
+
+@dataclass
+class FullResult:
+    logits: np.ndarray         # [B][n][V] float64
+    prelude_out: np.ndarray    # [B][n][d] float64 (s^(0) of the core)
+    core: OracleResult         # the routed core on it
+    coda_out: np.ndarray       # [B][n][d] float64
+
+
+def full_forward(full, core_forced_expert: Optional[np.ndarray] = None) -> FullResult:
+    """Algorithm 1 end to end: embedding, prelude stack, routed core, coda
+    stack, readout.  ``full`` is a ``FullInputs``."""
+    core_cfg = full.core.cfg
+    pre = [expert_params(full.prelude, m) for m in range(full.prelude.cfg.L)]
+    coda = [expert_params(full.coda, m) for m in range(full.coda.cfg.L)]
+    x = embed(full.tokens, full.embedding)
+    h0 = np.stack([causal_stack(x[b], pre, core_cfg.n_heads, core_cfg.rms_eps, core_cfg.rope_theta)
+                   for b in range(core_cfg.batch)])
+    # the core's input s^(0) is fp32, as on the device
+    core_in = dataclasses.replace(full.core, s0=h0.astype(np.float32))
+    res = forward(core_in, forced_expert=core_forced_expert)
+    hD = np.stack([causal_stack(res.s64[b], coda, core_cfg.n_heads, core_cfg.rms_eps,
+                                core_cfg.rope_theta) for b in range(core_cfg.batch)])
+    logits = np.stack([lm_head(hD[b], full.g_final, full.w_vocab, core_cfg.rms_eps)
+                       for b in range(core_cfg.batch)])
+    return FullResult(logits, h0, res, hD)

@@ -59,6 +59,11 @@ _SIGNATURES.update({
     "lol_core_read_flags": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
     "lol_core_timing_enable": (c_int32, [c_uint32]),
     "lol_core_timing_depth": (c_int32, [c_int32]),
+    "lol_embed": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                            c_void_p]),
+    "lol_lm_head_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+    "lol_lm_head": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_float, c_void_p, c_int32,
+                              c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "lol_core_timing_collect": (c_int32, [POINTER(c_double), POINTER(c_int32)]),
     "lol_core_kernel_name": (c_char_p, [c_int32]),
     "lol_status_str": (c_char_p, [c_int32]),

@@ -596,6 +596,14 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
                                 s1.z + g * (q1.z + a1.z - s1.z), s1.w + g * (q1.w + a1.w - s1.w));
           }
         }
+      } else if (EPI == EPI_STORE_F32) {
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+          if (!ok[pass]) continue;
+          float4 *cp = reinterpret_cast<float4 *>(reinterpret_cast<float *>(P.C) + (size_t)row[pass] * P.ldc + col);
+          cp[0] = v0[pass];
+          cp[1] = v1[pass];
+        }
       } else {
 #pragma unroll
         for (int pass = 0; pass < NP; ++pass) {
@@ -1133,6 +1141,9 @@ hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hi
     case EPI_BLEND: return launch_typed<EPI_BLEND>(p, ws, a, st);
     case EPI_QKV_ROPE: return launch_typed<EPI_QKV_ROPE>(p, ws, a, st);
     case EPI_ACCUM: return launch_typed<EPI_ACCUM>(p, ws, a, st);
+    case EPI_STORE_F32:
+      if (p.cfg.dtype != LOL_BF16) return hipErrorInvalidValue;
+      return launch_typed<EPI_STORE_F32>(p, ws, a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -125,6 +125,7 @@ enum GemmEpilogue {
   EPI_QKV_ROPE = 5, // C (act) = acc, with RoPE at the row's window position on
                     // the q and k columns (bf16 mode only)
   EPI_ACCUM = 6,    // s[row_tok] = s_in[row_tok] + gate * acc (s_in may equal s)
+  EPI_STORE_F32 = 7, // C (fp32) = acc (bf16 mode: the vocabulary logits)
 };
 
 struct GemmArgs {

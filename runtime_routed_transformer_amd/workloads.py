@@ -208,3 +208,75 @@ def generate(cfg: CoreConfig) -> CoreInputs:
         wqkv, wo, w_gu, w_down = (bf16_round(w) for w in (wqkv, wo, w_gu, w_down))
     return CoreInputs(cfg, s0, wqkv, wo, w_gu, w_down, g_attn, g_ffn,
                       film_gamma, film_beta, w_r, b_r, e_depth, expert_bias, forced)
+
+
+# --------------------------------------------------------------------------
+# Full model around the routed core (paper Appendix A, Algorithm 1: causal
+# prelude on the token sequence, routed core, causal coda, vocabulary
+# readout; Sec. 3.1: prelude and coda are fixed-order stacks of decoder
+# layers with full causal attention).
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class FullConfig:
+    name: str
+    core: CoreConfig
+    vocab: int
+    prelude: int      # layers before the routed core
+    coda: int         # layers after it
+    seed: int
+
+
+@dataclass
+class FullInputs:
+    cfg: FullConfig
+    tokens: np.ndarray          # [B][n] int32 in [0, vocab)
+    embedding: np.ndarray       # [V][d] fp32 values (bf16-exact in bf16 mode)
+    prelude: CoreInputs         # a stack: L = D = prelude, one window per document, forced path
+    core: CoreInputs
+    coda: CoreInputs
+    g_final: np.ndarray         # [d] fp32 final RMSNorm gain
+    w_vocab: np.ndarray         # [V][d] fp32 values (bf16-exact in bf16 mode)
+
+
+def stack_config(core: CoreConfig, layers: int, seed: int, name: str) -> CoreConfig:
+    """A fixed-order stack of ``layers`` blocks as a routed-core config: one
+    window per document (W = n, S = 0), library = the stack's layers, no FiLM."""
+    return core.with_(name=name, L=layers, D=layers, W=core.n, S=0, film=False, seed=seed,
+                      bias_mode="zero", path_mode="free", router="tied", film_mode="depth")
+
+
+def stack_path(cfg: CoreConfig) -> np.ndarray:
+    """Forced ids of a stack: layer l at depth l, every window."""
+    return np.broadcast_to(np.arange(cfg.D, dtype=np.int32)[:, None, None],
+                           (cfg.D, cfg.batch, cfg.k_max)).copy()
+
+
+def generate_full(cfg: FullConfig) -> FullInputs:
+    """Core inputs as ``generate(cfg.core)``; the stacks from seeds + 1 and
+    + 2; then tokens, embedding, final gain and readout from seed + 3.
+    Embedding and readout rows are N(0, 0.02^2) like every weight, the final
+    gain 1 + N(0, 0.02^2), tokens uniform over the vocabulary."""
+    core = generate(cfg.core)
+    pre = generate(stack_config(cfg.core, cfg.prelude, cfg.seed + 1, cfg.name + "/prelude"))
+    coda = generate(stack_config(cfg.core, cfg.coda, cfg.seed + 2, cfg.name + "/coda"))
+    pre.forced_expert = stack_path(pre.cfg)
+    coda.forced_expert = stack_path(coda.cfg)
+    rng = np.random.default_rng(cfg.seed + 3)
+    B, n, d, V = cfg.core.batch, cfg.core.n, cfg.core.d, cfg.vocab
+    tokens = rng.integers(0, V, size=(B, n)).astype(np.int32)
+    emb = _normal(rng, (V, d), WEIGHT_STD)
+    g_final = (1.0 + _normal(rng, (d,), WEIGHT_STD)).astype(np.float32)
+    w_vocab = _normal(rng, (V, d), WEIGHT_STD)
+    if cfg.core.dtype == "bf16":
+        emb, w_vocab = bf16_round(emb), bf16_round(w_vocab)
+    return FullInputs(cfg, tokens, emb, pre, core, coda, g_final, w_vocab)
+
+
+# The pages fix no vocabulary size; 32,768 (a multiple of the readout's
+# 128-wide tiles) stands in for it.  The 1B setup of the pages uses 4 prelude
+# and 4 coda layers around 8 routed depths (paper Sec. 4.2).
+FULL_CONFIGS = [
+    FullConfig("full_mid_bf16", CONFIG_BY_NAME["mid_bf16"], vocab=32768, prelude=4, coda=4,
+               seed=40),
+]
+FULL_BY_NAME = {c.name: c for c in FULL_CONFIGS}

@@ -97,3 +97,52 @@ def run(inp, rows=None, n_tokens=None, device="cuda:0", core=None) -> ParityRepo
     n_forced = int(np.count_nonzero(cmp_all & (ref.margin <= MARGIN)))
     return ParityReport(cfg.name, rel, upd, mism, int(np.count_nonzero(free_cmp)), n_forced,
                         gate_err, TOL[cfg.dtype], UPDATE_TOL[cfg.dtype])
+
+
+@dataclass
+class FullReport:
+    name: str
+    logit_err: float
+    hidden_err: float
+    id_mismatch: int
+    ids_compared: int
+    forced_windows: int
+    tol: float
+
+    @property
+    def ok(self) -> bool:
+        return self.logit_err <= self.tol and self.hidden_err <= self.tol and self.id_mismatch == 0
+
+    def __str__(self):
+        return (f"{self.name}: logit_err={self.logit_err:.3e} coda_out_err={self.hidden_err:.3e} "
+                f"(tol {self.tol:g}) core ids {self.ids_compared - self.id_mismatch}/"
+                f"{self.ids_compared} equal, forced {self.forced_windows}")
+
+
+def run_full(full, device="cuda:0") -> FullReport:
+    """Algorithm 1 end to end (embedding, prelude, routed core, coda,
+    readout) on the GPU against the oracle; near-tie core windows are forced
+    to the oracle's choice as in ``run``."""
+    import torch
+    from runtime_routed_transformer_amd.model import DeviceModel
+
+    core_cfg = full.core.cfg
+    ref = oracle.full_forward(full, core_forced_expert=full.core.forced_expert)
+    rows = list(range(core_cfg.batch))
+    forced, compared = forced_for_gpu(full.core, ref.core, rows, core_cfg.n)
+    model = DeviceModel(full, device)
+    model.set_core_forcing(forced)
+    logits = model.forward()
+    torch.cuda.synchronize(model.device)
+    lg = logits.cpu().numpy().astype(np.float64)
+    hid = model.s.cpu().numpy().astype(np.float64)
+    logit_err = float(np.abs(lg - ref.logits).max() / np.abs(ref.logits).max())
+    hidden_err = float(np.abs(hid - ref.coda_out).max() / np.abs(ref.coda_out).max())
+    pe, _, _ = model.core.path_numpy()
+    free_cmp = compared & (ref.core.margin > MARGIN)
+    if full.core.forced_expert is not None:
+        free_cmp &= full.core.forced_expert < 0
+    mism = int(np.count_nonzero(free_cmp & (pe != ref.core.expert)))
+    n_forced = int(np.count_nonzero(compared & (ref.core.margin <= MARGIN)))
+    return FullReport(full.cfg.name, logit_err, hidden_err, mism, int(np.count_nonzero(free_cmp)),
+                      n_forced, TOL[core_cfg.dtype])

@@ -120,3 +120,28 @@ def test_forward_rejects_unknown_variant_flags(lib):
                              film_per_expert=lib_flag)
         rt = B.lol_router(w_r=16, e_depth=16, per_depth=rt_flag)
         assert B.lol_core_forward(c, 16, libw, rt, None, None, 16, None, 256, ws, None) == B.LOL_EINVAL
+
+
+def test_embedding_and_readout_reject_bad_arguments(lib):
+    # host-checked before any launch
+    assert lib.lol_lm_head_workspace_size(64, 128, 256, B.LOL_BF16) > 0
+    assert lib.lol_lm_head_workspace_size(64, 96, 256, B.LOL_BF16) == 0    # d % 128
+    assert lib.lol_lm_head_workspace_size(64, 128, 200, B.LOL_BF16) == 0   # V % 128
+    assert lib.lol_lm_head_workspace_size(64, 64, 64, B.LOL_FP32) > 0
+    assert lib.lol_lm_head_workspace_size(0, 64, 64, B.LOL_FP32) == 0
+    ws = lib.lol_lm_head_workspace_size(64, 128, 256, B.LOL_BF16)
+    args = dict(s=16, T=64, d=128, g=16, eps=1e-6, w=16, V=256, dt=B.LOL_BF16, out=16)
+    def head(**kw):
+        a = {**args, **kw}
+        return lib.lol_lm_head(a["s"], a["T"], a["d"], a["g"], a["eps"], a["w"], a["V"], a["dt"],
+                               a["out"], kw.get("ws", 256), kw.get("wsb", ws), None)
+    assert head(s=None) == B.LOL_EINVAL
+    assert head(eps=0.0) == B.LOL_EINVAL
+    assert head(V=200) == B.LOL_EINVAL
+    assert head(dt=7) == B.LOL_EINVAL
+    assert head(wsb=ws - 1) == B.LOL_EWORKSPACE
+    assert head(ws=None) == B.LOL_EWORKSPACE
+    assert lib.lol_embed(None, 4, 16, 10, 64, B.LOL_FP32, 16, None) == B.LOL_EINVAL
+    assert lib.lol_embed(16, 4, 16, 10, 62, B.LOL_FP32, 16, None) == B.LOL_EINVAL
+    assert lib.lol_embed(16, 0, 16, 10, 64, B.LOL_FP32, 16, None) == B.LOL_EINVAL
+    assert lib.lol_embed(16, 4, 16, 10, 64, 5, 16, None) == B.LOL_EINVAL

@@ -413,3 +413,52 @@ def test_per_expert_film_with_equal_rows_is_the_shared_film():
     a, b = oracle.forward(shared), oracle.forward(per)
     np.testing.assert_array_equal(a.s, b.s)
     np.testing.assert_array_equal(a.expert, b.expert)
+
+
+# ---------------------------------------------------------------- around the core
+def test_embedding_and_readout_against_library_routines():
+    """Embedding rows (torch.nn.functional.embedding) and the readout: a final
+    RMSNorm with gain (torch.nn.functional.rms_norm) then a linear map onto
+    the vocabulary (paper App. A, Algorithm 1: the coda ends in the
+    vocabulary readout)."""
+    import torch
+    rng = np.random.default_rng(5)
+    V, d, T = 97, 48, 31
+    table = rng.standard_normal((V, d))
+    tokens = rng.integers(0, V, size=(3, T))
+    want = torch.nn.functional.embedding(torch.from_numpy(tokens), torch.from_numpy(table)).numpy()
+    np.testing.assert_array_equal(oracle.embed(tokens, table), want)
+    s = rng.standard_normal((T, d)) * 3.0
+    g = 1.0 + 0.1 * rng.standard_normal(d)
+    w = rng.standard_normal((V, d)) * 0.1
+    ts = torch.from_numpy(s)
+    ref = torch.nn.functional.linear(
+        torch.nn.functional.rms_norm(ts, (d,), weight=torch.from_numpy(g), eps=1e-6), torch.from_numpy(w))
+    np.testing.assert_allclose(oracle.lm_head(s, g, w, 1e-6), ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_causal_stack_is_the_ordinary_decoder_stack():
+    """Prelude and coda (paper Sec. 3.1): fixed-order stacks of decoder layers
+    with full causal attention.  Two different layers applied in order equal
+    two ordinary causal blocks from PyTorch library routines."""
+    from runtime_routed_transformer_amd.workloads import FullConfig, generate_full
+    full = generate_full(FullConfig("pin_full", tiny(n=24, W=8, S=4), vocab=64, prelude=2, coda=1,
+                                    seed=3))
+    pre = full.prelude
+    params = [oracle.expert_params(pre, m) for m in range(pre.cfg.L)]
+    x0 = oracle.embed(full.tokens, full.embedding)
+    for b in range(pre.cfg.batch):
+        got = oracle.causal_stack(x0[b], params, pre.cfg.n_heads, pre.cfg.rms_eps, pre.cfg.rope_theta)
+        x = x0[b]
+        for m in range(pre.cfg.L):
+            x = torch_block.block(x, pre.wqkv[m], pre.wo[m], pre.w_gu[m], pre.w_down[m],
+                                  pre.g_attn[m], pre.g_ffn[m], pre.cfg.n_heads, "swiglu")
+        np.testing.assert_allclose(got, x, rtol=0, atol=1e-11)
+    # the routed-core machinery with the stack's forced path computes the same
+    res = oracle.forward(pre.__class__(**{**pre.__dict__, "s0": x0.astype(np.float32)}),
+                         forced_expert=pre.forced_expert,
+                         forced_gate=np.ones(pre.forced_expert.shape, np.float32))
+    for b in range(pre.cfg.batch):
+        want = oracle.causal_stack(x0[b].astype(np.float32).astype(np.float64), params,
+                                   pre.cfg.n_heads, pre.cfg.rms_eps, pre.cfg.rope_theta)
+        np.testing.assert_allclose(res.s64[b], want, rtol=0, atol=1e-11)
