@@ -94,6 +94,137 @@ def stored_traffic(kernel, workload):
     return float(rec["bytes_per_launch"])
 
 
+FULL_METRIC = ("full-model fwd tokens/sec on 1 MI355X (embedding, causal prelude, routed core, "
+               "causal coda, vocabulary readout)")
+
+
+def bench_full(args):
+    """The whole forward of Algorithm 1 (``--workload full_*``): the same
+    protocol as the routed core, with the readout GEMM among the candidates
+    for the dominant kernel."""
+    import torch
+    import oracle
+    from runtime_routed_transformer_amd import binding as B
+    from runtime_routed_transformer_amd.model import DeviceModel
+    from runtime_routed_transformer_amd.workloads import FULL_BY_NAME, FullConfig, generate_full
+
+    fcfg = FULL_BY_NAME[args.workload]
+    cc = fcfg.core
+    model = DeviceModel(generate_full(fcfg), "cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        model.forward(stream)
+    torch.cuda.synchronize()
+
+    # breakdown (untimed): events after every step, and the library's
+    # per-kernel events inside the three lol_core_forward calls
+    B.lol_core_timing_collect()
+    B.lol_core_timing_enable(B.LOL_TIMING_ALL)
+    step_ms = {k: 0.0 for k in DeviceModel.STEPS}
+    for _ in range(args.timing_steps):
+        marks = []
+
+        def after(step):
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            marks.append((step, ev))
+
+        start = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        model.forward(stream, after=after)
+        torch.cuda.synchronize()
+        prev = start
+        for step, ev in marks:
+            step_ms[step] += prev.elapsed_time(ev) / args.timing_steps
+            prev = ev
+    B.lol_core_timing_enable(0)
+    kt = B.lol_core_timing_collect()
+    per_kernel = {k: {"ms_avg": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items() if v[1]}
+    flops = gemm_flops(cc)
+    flops["lm_head"] = 2.0 * cc.tokens * cc.d * fcfg.vocab
+    per_fwd = {k: kt[k][0] / args.timing_steps for k in flops if k in kt}
+    per_fwd["lm_head"] = step_ms["lm_head"]
+    dominant = max(per_fwd, key=per_fwd.get)
+    layers = fcfg.prelude + cc.D + fcfg.coda
+
+    # timed region: K whole forwards; the dominant kernel timed with HIP
+    # events on the launch stream (library events at one depth per forward,
+    # or torch events around the readout)
+    head_evs = []
+    if dominant != "lm_head":
+        B.lol_core_timing_enable(1 << B.kernel_kind(dominant))
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        B.lol_core_timing_depth(i % max(cc.D, fcfg.prelude, fcfg.coda))
+        if dominant == "lm_head":
+            pair = []
+
+            def after(step, pair=pair):
+                if step in ("coda", "lm_head"):
+                    ev = torch.cuda.Event(enable_timing=True)
+                    ev.record(stream)
+                    pair.append(ev)
+
+            model.forward(stream, after=after)
+            head_evs.append(pair)
+        else:
+            model.forward(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    B.lol_core_timing_enable(0)
+    B.lol_core_timing_depth(-1)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    if dominant == "lm_head":
+        dom_n = len(head_evs)
+        dom_ms = sum(a.elapsed_time(b) for a, b in head_evs) / dom_n
+    else:
+        dom_total, dom_n = B.lol_core_timing_collect()[dominant]
+        dom_ms = dom_total / dom_n
+    achieved = flops[dominant] / (dom_ms / 1e3) / 1e12
+    gemm_flops_fwd = sum(flops[k] * layers for k in gemm_flops(cc)) + flops["lm_head"]
+    gemm_ms_fwd = sum(per_fwd[k] for k in per_fwd)
+    result = {
+        "metric": FULL_METRIC, "value": cc.tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cc.dtype,
+        "data": "synthetic (seeded uniform token ids, N(0,0.02) weights)",
+        "config": {"workload": fcfg.name, "batch": cc.batch, "n": cc.n, "d": cc.d,
+                   "heads": cc.n_heads, "d_ffn": cc.d_ffn, "mlp": cc.mlp, "vocab": fcfg.vocab,
+                   "prelude": fcfg.prelude, "coda": fcfg.coda, "L": cc.L, "D": cc.D, "W": cc.W,
+                   "S": cc.S, "film": cc.film, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel_ms_avg": dom_ms, "kernel_launches_timed": dom_n,
+                     "flops_per_launch": flops[dominant]},
+        "mfma_util_pct": 100.0 * gemm_flops_fwd / (gemm_ms_fwd / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "steps_ms": step_ms,
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's composition on one 2,048-token document of the same model
+        n_s = min(cc.n, 2048)
+        sample = FullConfig(f"{fcfg.name}@1x{n_s}", cc.scaled(1, n_s), fcfg.vocab, fcfg.prelude,
+                            fcfg.coda, fcfg.seed)
+        full = generate_full(sample)
+        t0 = time.perf_counter()
+        oracle.full_forward(full, core_forced_expert=full.core.forced_expert)
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        result["cpu_baseline"] = {"value": n_s / dt, "unit": "tokens/s", "cores": int(threads),
+                                  "kind": "oracle",
+                                  "sample": f"one {n_s}-token document of {fcfg.name}, numpy "
+                                            f"float64, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +239,10 @@ def main(argv=None):
               "(the routed core shards over documents with no forward communication; "
               "the multi-GPU path is not built)", file=sys.stderr)
         return 2
+
+    from runtime_routed_transformer_amd.workloads import FULL_BY_NAME
+    if args.workload in FULL_BY_NAME:
+        return bench_full(args)
 
     import torch
     from runtime_routed_transformer_amd import binding as B

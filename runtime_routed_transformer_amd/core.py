@@ -75,9 +75,9 @@ class DeviceCore:
     def set_forcing(self, forced_expert=None, forced_gate=None) -> None:
         shape = (self.cfg.D, self.cfg.batch, self.k_max)
         self.forced_expert = None if forced_expert is None else torch.from_numpy(
-            np.ascontiguousarray(np.broadcast_to(forced_expert, shape), np.int32)).to(self.device)
+            np.array(np.broadcast_to(forced_expert, shape), np.int32)).to(self.device)
         self.forced_gate = None if forced_gate is None else torch.from_numpy(
-            np.ascontiguousarray(np.broadcast_to(forced_gate, shape), np.float32)).to(self.device)
+            np.array(np.broadcast_to(forced_gate, shape), np.float32)).to(self.device)
 
     def forward(self, s_in: Optional[torch.Tensor] = None, s_out: Optional[torch.Tensor] = None,
                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:

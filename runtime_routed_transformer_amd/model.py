@@ -58,20 +58,30 @@ class DeviceModel:
     def set_core_forcing(self, forced_expert=None) -> None:
         self.core.set_forcing(forced_expert=forced_expert)
 
-    def forward(self, stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-        """Queue the whole forward on ``stream``; returns the logits [B][n][V]."""
+    STEPS = ("embed", "prelude", "core", "coda", "lm_head")
+
+    def forward(self, stream: Optional[torch.cuda.Stream] = None, after=None) -> torch.Tensor:
+        """Queue the whole forward on ``stream``; returns the logits [B][n][V].
+        ``after(step)``, if given, is called once each step is queued (the
+        benchmark records events there)."""
         lib = B.load()
         st = (stream or torch.cuda.current_stream(self.device)).cuda_stream
         status = lib.lol_embed(self.tokens.data_ptr(), self.T, self.embedding.data_ptr(), self.V,
                                self.d, self.dtype, self.s.data_ptr(), st)
         if status != B.LOL_OK:
             raise B.LolError(status, "lol_embed")
-        for part in (self.prelude, self.core, self.coda):
+        if after:
+            after("embed")
+        for name, part in (("prelude", self.prelude), ("core", self.core), ("coda", self.coda)):
             part.forward(s_in=self.s, s_out=self.s, stream=stream)
+            if after:
+                after(name)
         status = lib.lol_lm_head(self.s.data_ptr(), self.T, self.d, self.g_final.data_ptr(),
                                  self.full.core.cfg.rms_eps, self.w_vocab.data_ptr(), self.V,
                                  self.dtype, self.logits.data_ptr(), self.head_ws.data_ptr(),
                                  self.head_ws_bytes, st)
         if status != B.LOL_OK:
             raise B.LolError(status, "lol_lm_head")
+        if after:
+            after("lm_head")
         return self.logits
