@@ -208,9 +208,9 @@ __global__ void __launch_bounds__(64) k_attn_simt(const act_t *__restrict__ qkv,
 
 // bf16 window-causal attention on MFMA (v_mfma_f32_32x32x16_bf16).
 // q and k arrive rotated (RoPE is applied in the QKV projection's epilogue).
-// Block = (window, head, chunk of 256 queries), 4 waves.  Keys and values of
-// a chunk of 256 keys are copied row-major into LDS by direct global-to-LDS
-// loads (no register staging), 16-byte chunks of each row XOR-swizzled so
+// Block = (window, head, chunk of 256 queries), 4 waves, three blocks per
+// CU.  Keys and values of a chunk of 128 keys at a time are copied row-major
+// into LDS by direct global-to-LDS loads (no register staging), 16-byte chunks of each row XOR-swizzled so
 // that the fragment reads below are free of bank conflicts.  Each wave owns
 // query blocks of 32 (wave w takes blocks w and 7-w of the chunk, which
 // balances the causal triangle) and computes S^T = K Q^T, so every lane holds
@@ -241,7 +241,7 @@ template <int DH> struct AttnLds {
 };
 
 template <int DH>
-__global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__ qkv,
+__global__ void __launch_bounds__(256, 3) k_attn_mfma(const bf16_t *__restrict__ qkv,
                                                       bf16_t *__restrict__ o,
                                                       const int32_t *__restrict__ win_exp,
                                                       const int32_t *__restrict__ win_row0, int n,
@@ -252,10 +252,14 @@ __global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__
   constexpr int RB = LY::RB, NCK = LY::NCK, RPI = LY::RPI;
   constexpr int KS = DH / 16;        // MFMA k-steps over the head dimension
   constexpr int DB = DH / 32;        // 32-wide output blocks over the head dimension
-  constexpr int NI = CH * RB / 1024 / 4;  // 1 KiB loads per wave per operand
-  __shared__ __attribute__((aligned(1024))) char lds[2 * CH * RB];
+  // keys per LDS chunk: 32 KiB of K and V, so three blocks share a CU (four
+  // would leave under 128 registers per lane and spill; 256-key chunks
+  // allowed only two and measured 38.6 vs 34.9 us at mid_bf16)
+  constexpr int KC = CH / 2;
+  constexpr int NI = KC * RB / 1024 / 4;  // 1 KiB loads per wave per operand
+  __shared__ __attribute__((aligned(1024))) char lds[2 * KC * RB];
   char *const Kl = lds;
-  char *const Vl = lds + CH * RB;
+  char *const Vl = lds + KC * RB;
   const int slot = blockIdx.x, h = blockIdx.y, qc = blockIdx.z;
   if (win_exp[slot] < 0) return;
   const int k = slot % K_max;
@@ -308,8 +312,10 @@ __global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__
     v_off[db] = tr_row * RB + ((((c >> 3) ^ LY::vswz(tr_row)) << 4) + ((c & 4) << 1));
   }
 
-  for (int kc = 0; kc <= qc; ++kc) {
-    const int k_begin = kc * CH;
+  // key chunks of KC keys up to the block's last query
+  const int nkc = (min(q_begin + CH, len) + KC - 1) / KC;
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int k_begin = kc * KC;
     if (kc > 0) __syncthreads();   // every wave is done with the previous chunk
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -329,8 +335,11 @@ __global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__
       const int q_lo = q_begin + qblk[b] * 32;            // first query of the block
       if (q_lo >= len) continue;
       const int q = q_lo + col;
-      // key blocks of this chunk that the query block can see
-      const int kb_end = (kc < qc) ? CH / 32 : qblk[b] + 1;
+      // key blocks of this chunk that the query block can see (32-key block
+      // indices over the window: the chunk starts at kb0, the query block is qg)
+      const int kb0 = kc * (KC / 32), qg = qc * (CH / 32) + qblk[b];
+      if (qg < kb0) continue;
+      const int kb_end = min(KC / 32, qg - kb0 + 1);
       for (int kb = 0; kb < kb_end; ++kb) {
         f32x16_t sc;
 #pragma unroll
@@ -342,7 +351,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_mfma(const bf16_t *__restrict__
           sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[b][ks], sc, 0, 0, 0);
         }
         // sc[i] = q.k for key = k_begin + kb*32 + (i/4)*8 + 4*hl + i%4, query q
-        if (kc == qc && kb == qblk[b]) {
+        if (kb0 + kb == qg) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k_begin + kb * 32 + (i >> 2) * 8 + 4 * hl + (i & 3);
