@@ -27,17 +27,20 @@ PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 
 
-def gemm_flops(cfg):
-    """Algorithmic FLOPs per launch (one depth) of each grouped GEMM kind."""
-    T, d, f = cfg.tokens, cfg.d, cfg.d_ffn
+def gemm_flops(cfg, tokens=None):
+    """Algorithmic FLOPs per launch (one depth) of each grouped GEMM kind
+    (every token is one grouped row: ``tokens`` of them, default batch n)."""
+    T, d, f = (cfg.tokens if tokens is None else tokens), cfg.d, cfg.d_ffn
     up = 2 * f if cfg.mlp == "swiglu" else f
     return {"gemm_qkv": 2.0 * T * 3 * d * d, "gemm_o": 2.0 * T * d * d,
             "gemm_gate_up": 2.0 * T * up * d, "gemm_down": 2.0 * T * d * f}
 
 
-def cpu_baseline(inp, budget_s=12.0):
+def cpu_baseline(inp, budget_s=12.0, lengths=None):
     """The oracle, unchanged, on whole documents of the workload, one after
-    another until about ``budget_s`` seconds of CPU work are done."""
+    another until about ``budget_s`` seconds of CPU work are done
+    (``lengths``: packed documents, document b = the first lengths[b]
+    tokens of row b)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -45,15 +48,17 @@ def cpu_baseline(inp, budget_s=12.0):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     cfg = inp.cfg
-    done, t0 = 0, time.perf_counter()
+    lens = [cfg.n] * cfg.batch if lengths is None else [int(x) for x in lengths]
+    done, tokens, t0 = 0, 0, time.perf_counter()
     while done < cfg.batch:
-        oracle.forward(inp, forced_expert=inp.forced_expert, rows=[done])
+        oracle.forward(inp, forced_expert=inp.forced_expert, rows=[done], n_tokens=lens[done])
+        tokens += lens[done]
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": done * cfg.n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {cfg.batch} documents of {cfg.name} ({done * cfg.n} tokens x "
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} documents of {cfg.name} ({tokens} tokens x "
                       f"{cfg.D} depths), numpy float64, {dt:.1f} s"}
 
 
@@ -247,22 +252,45 @@ def main(argv=None):
     import torch
     from runtime_routed_transformer_amd import binding as B
     from runtime_routed_transformer_amd.core import DeviceCore
-    from runtime_routed_transformer_amd.workloads import CONFIG_BY_NAME, generate
+    from runtime_routed_transformer_amd.workloads import (CONFIG_BY_NAME, PACKED_BY_NAME,
+                                                          generate, generate_packed)
 
-    cfg = CONFIG_BY_NAME[args.workload]
-    inp = generate(cfg)
+    packed = None
+    if args.workload in PACKED_BY_NAME:
+        # packed documents: one token stream, a document table
+        packed = generate_packed(PACKED_BY_NAME[args.workload])
+        inp = packed.core
+    else:
+        inp = generate(CONFIG_BY_NAME[args.workload])
+    cfg = inp.cfg
     if cfg.bias_mode == "skewed":
         from oracle.calibrate import apply_skew  # input preparation only
         apply_skew(inp)
     core = DeviceCore(inp, "cuda:0")
     core.set_forcing(inp.forced_expert)
     stream = torch.cuda.current_stream()
+    if packed is None:
+        tokens = cfg.tokens
+
+        def forward():
+            core.forward(stream=stream)
+    else:
+        tokens = int(packed.length.sum())
+        p_in = torch.from_numpy(packed.stream()).to(core.device)
+        p_out = torch.empty_like(p_in)
+        p_start = torch.from_numpy(packed.start).to(core.device)
+        p_len = torch.from_numpy(packed.length).to(core.device)
+        core.s0 = core.s_out = None   # the [batch][n] layout is not used
+
+        def forward():
+            core.forward_docs(p_in, p_out, p_start, p_len, stream=stream)
     # one plain device-to-device copy of s^(0) (untimed): the reference
     # kernel that the HBM-traffic counters of the profiles are scaled by
-    torch.empty_like(core.s0).copy_(core.s0)
+    s_ref = core.s0 if packed is None else p_in
+    torch.empty_like(s_ref).copy_(s_ref)
 
     for _ in range(args.warmup):
-        core.forward(stream=stream)
+        forward()
     torch.cuda.synchronize()
 
     # per-kernel breakdown: HIP events the library records on the launch
@@ -270,11 +298,11 @@ def main(argv=None):
     B.lol_core_timing_collect()  # drop anything stale
     B.lol_core_timing_enable(B.LOL_TIMING_ALL)
     for _ in range(args.timing_steps):
-        core.forward(stream=stream)
+        forward()
     torch.cuda.synchronize()
     B.lol_core_timing_enable(0)
     kt = B.lol_core_timing_collect()
-    flops = gemm_flops(cfg)
+    flops = gemm_flops(cfg, tokens)
     per_kernel = {k: {"ms_avg": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items() if v[1]}
     dominant = max(flops, key=lambda k: kt[k][0])
     gemm_ms = sum(kt[k][0] for k in flops) / args.timing_steps
@@ -290,13 +318,15 @@ def main(argv=None):
     ev0.record(stream)
     for i in range(args.steps):
         B.lol_core_timing_depth(i % cfg.D)
-        core.forward(stream=stream)
+        forward()
     ev1.record(stream)
     torch.cuda.synchronize()
     B.lol_core_timing_enable(0)
     B.lol_core_timing_depth(-1)
     ms = ev0.elapsed_time(ev1) / args.steps
-    tokens_per_s = cfg.tokens / (ms / 1e3)
+    if packed is not None:
+        assert core.flags() == 0, "document table rejected by the device"
+    tokens_per_s = tokens / (ms / 1e3)
     dom_total, dom_n = B.lol_core_timing_collect()[dominant]
     dom_ms = dom_total / dom_n
     achieved = flops[dominant] / (dom_ms / 1e3) / 1e12
@@ -311,6 +341,10 @@ def main(argv=None):
                    "D": cfg.D, "W": cfg.W, "S": cfg.S, "film": cfg.film,
                    "router": cfg.router, "film_mode": cfg.film_mode,
                    "parallelism": "single GPU"},
+        "packed": None if packed is None else {
+            "documents": cfg.batch, "tokens": tokens, "n_tokens": packed.n_tokens,
+            "lengths": "log-uniform %d..%d, seed %d" % (packed.cfg.min_len, cfg.n, packed.cfg.seed),
+            "min_len": int(packed.length.min()), "max_len": int(packed.length.max())},
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
@@ -321,7 +355,7 @@ def main(argv=None):
         "kernels": per_kernel,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp)
+        result["cpu_baseline"] = cpu_baseline(inp, lengths=None if packed is None else packed.length)
     print(json.dumps(result), flush=True)
     return 0
 

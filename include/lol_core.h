@@ -157,8 +157,46 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0,
                             float *s_out, const lol_path *path,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* Packed documents: the same forward over a batch of documents of
+ * different lengths laid out back to back in one token stream.  Each
+ * document is partitioned into windows, routed and attended exactly as if
+ * it were a row of its own: the router's running mean of window means
+ * restarts at every document's first window, window 0 uses the document's
+ * own first token, and no attention crosses a document (paper App. A uses
+ * document-blocked attention; the explainer "Library of Layers: a
+ * transformer that picks its own layer order", The forward pass, term by
+ * term, has the router's prefix sum restart at each document boundary; the
+ * review "Library of Layers: Routing Whole Transformer Blocks at Runtime",
+ * Deriving prefix-only routing, asks for routing isolated per document in
+ * packed execution).
+ *   cfg           as for lol_core_forward, with batch = number of
+ *                 documents and n = the longest a document may be (window
+ *                 slots and workspace are sized by n)
+ *   n_tokens      rows of s0 and s_out, 1 <= n_tokens < 2^30
+ *   doc_start     DEVICE [batch] int32, first row of each document
+ *   doc_len       DEVICE [batch] int32, its length
+ *   s0, s_out     DEVICE [n_tokens][d] fp32; rows outside every document
+ *                 are not written (s_out may equal s0)
+ *   forced_expert, forced_gate, path
+ *                 [D][batch][K_max] as for lol_core_forward, indexed by
+ *                 document; slots past a document's last window hold
+ *                 expert -1, gate 0, margin 0 in `path`
+ * The documents must be disjoint, in increasing order of doc_start, each of
+ * 1..n tokens inside [0, n_tokens).  A table that breaks this raises
+ * LOL_FLAG_BAD_DOC; the kernels then clamp every entry into range (so no
+ * access leaves the buffers) but the result is unspecified.  Both tables
+ * NULL is lol_core_forward on the [batch][n] layout (n_tokens = batch n);
+ * one NULL is LOL_EINVAL. */
+lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
+                                 const int32_t *doc_start, const int32_t *doc_len,
+                                 const float *s0, const lol_library *lib, const lol_router *rt,
+                                 const int32_t *forced_expert, const float *forced_gate,
+                                 float *s_out, const lol_path *path,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* Device-side error flags of the last forward that used `workspace`. */
 #define LOL_FLAG_BAD_FORCED_ID 1u
+#define LOL_FLAG_BAD_DOC 2u
 /* Copies the flag word to *flags (HOST) and clears it; synchronises
  * `stream`. */
 lol_status lol_core_read_flags(void *workspace, uint32_t *flags, void *stream);

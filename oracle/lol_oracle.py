@@ -44,6 +44,9 @@ Readings of points the pages leave open:
     (a + b) in probability units (+inf when L = 1).
   * Forcing: forced id >= 0 replaces the router's choice; the gate is the
     forced gate if given and not NaN, else the router's unbiased a_rho.
+  * Packed documents: each document is partitioned, routed and attended as
+    a row of its own (window offsets from its first token, window 0 from
+    its own first token, prefix means over its own windows only).
 
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 (worked values printed on the pages, closed forms, library routines on
@@ -327,6 +330,41 @@ def forward(inp, forced_expert: Optional[np.ndarray] = None,
                 margin[depth - 1, bi, k] = rt.margin
         s = s_next
     return OracleResult(s.astype(np.float32), s, expert, gate, margin)
+
+
+# --------------------------------------------------------------------------
+# Packed documents
+#   [paper] Appendix A: attention is blocked by document (no token attends
+#   to another document).  [blog] "The forward pass, term by term": the
+#   router's cumulative sum over window means restarts at each document
+#   boundary.  [review] "Deriving prefix-only routing": packed execution
+#   needs the routing summaries reset and isolated per document.
+# Reading: a document of a packed stream is partitioned from its own first
+# token (window offsets count from it), routed with its own window-0 rule
+# and its own prefix means, and attended inside itself, so its result is the
+# core's result on that document run alone as a row of its own length.
+# --------------------------------------------------------------------------
+def forward_docs(inp, lengths, forced_expert: Optional[np.ndarray] = None,
+                 forced_gate: Optional[np.ndarray] = None) -> List[OracleResult]:
+    """Document b = the first ``lengths[b]`` tokens of row b of ``inp.s0``;
+    returns one result per document (batch axis of length 1), each computed
+    with only that document's tokens present."""
+    out = []
+    for b, ln in enumerate(lengths):
+        fe = None if forced_expert is None else forced_expert[:, b:b + 1]
+        fg = None if forced_gate is None else forced_gate[:, b:b + 1]
+        one = dataclasses.replace(inp, s0=np.asarray(inp.s0[b:b + 1, :int(ln)]))
+        one_cfg = dataclasses.replace(inp.cfg, batch=1, n=int(ln))
+        one = dataclasses.replace(one, cfg=one_cfg)
+        r = forward(one, forced_expert=None if fe is None else _fit_slots(fe, one_cfg.k_max),
+                    forced_gate=None if fg is None else _fit_slots(fg, one_cfg.k_max))
+        out.append(r)
+    return out
+
+
+def _fit_slots(a: np.ndarray, k: int) -> np.ndarray:
+    """The first k window slots of a [D][1][K_max] forcing array."""
+    return np.ascontiguousarray(a[:, :, :k])
 
 
 # --------------------------------------------------------------------------

@@ -15,6 +15,7 @@ LOL_OK, LOL_EINVAL, LOL_EUNSUPPORTED, LOL_EWORKSPACE, LOL_EHIP = range(5)
 LOL_FP32, LOL_BF16 = 0, 1
 LOL_MLP_SWIGLU, LOL_MLP_GELU = 0, 1
 LOL_FLAG_BAD_FORCED_ID = 1
+LOL_FLAG_BAD_DOC = 2
 LOL_KERNEL_KINDS = 12
 LOL_TIMING_ALL = (1 << LOL_KERNEL_KINDS) - 1
 
@@ -56,6 +57,10 @@ _SIGNATURES.update({
     "lol_core_forward": (c_int32, [POINTER(lol_core_config), c_void_p, POINTER(lol_library),
                                    POINTER(lol_router), c_void_p, c_void_p, c_void_p,
                                    POINTER(lol_path), c_void_p, c_size_t, c_void_p]),
+    "lol_core_forward_docs": (c_int32, [POINTER(lol_core_config), ctypes.c_int64, c_void_p,
+                                        c_void_p, c_void_p, POINTER(lol_library),
+                                        POINTER(lol_router), c_void_p, c_void_p, c_void_p,
+                                        POINTER(lol_path), c_void_p, c_size_t, c_void_p]),
     "lol_core_read_flags": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
     "lol_core_timing_enable": (c_int32, [c_uint32]),
     "lol_core_timing_depth": (c_int32, [c_int32]),
@@ -121,6 +126,16 @@ def lol_core_forward(cfg, s0, lib, rt, forced_expert, forced_gate, s_out, path, 
                                    forced_expert, forced_gate, s_out,
                                    ctypes.byref(path) if path is not None else None,
                                    workspace, workspace_bytes, stream)
+
+
+def lol_core_forward_docs(cfg, n_tokens, doc_start, doc_len, s0, lib, rt, forced_expert,
+                          forced_gate, s_out, path, workspace, workspace_bytes, stream) -> int:
+    """Packed documents: doc_start / doc_len are device int32 [batch] arrays (ints)."""
+    return load().lol_core_forward_docs(ctypes.byref(cfg), int(n_tokens), doc_start, doc_len, s0,
+                                        ctypes.byref(lib), ctypes.byref(rt), forced_expert,
+                                        forced_gate, s_out,
+                                        ctypes.byref(path) if path is not None else None,
+                                        workspace, workspace_bytes, stream)
 
 
 def lol_core_read_flags(workspace, stream) -> int:

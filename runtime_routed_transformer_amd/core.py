@@ -93,6 +93,29 @@ class DeviceCore:
             raise B.LolError(status, "lol_core_forward")
         return s_out
 
+    def forward_docs(self, s_in: torch.Tensor, s_out: torch.Tensor, doc_start: torch.Tensor,
+                     doc_len: torch.Tensor, stream: Optional[torch.cuda.Stream] = None
+                     ) -> torch.Tensor:
+        """Queue one forward over packed documents: ``s_in`` / ``s_out`` are
+        [n_tokens][d] fp32 streams, ``doc_start`` / ``doc_len`` int32 [batch]
+        device tensors (document b = rows doc_start[b] .. + doc_len[b] - 1)."""
+        if (s_in.dim() != 2 or s_in.shape != s_out.shape or s_in.shape[1] != self.cfg.d
+                or s_in.dtype != torch.float32 or s_out.dtype != torch.float32
+                or not (s_in.is_contiguous() and s_out.is_contiguous())):
+            raise ValueError("s_in / s_out must be contiguous fp32 [n_tokens][d]")
+        for t in (doc_start, doc_len):
+            if t.dtype != torch.int32 or t.numel() != self.cfg.batch or not t.is_contiguous():
+                raise ValueError("doc_start / doc_len must be contiguous int32 [batch]")
+        st = (stream or torch.cuda.current_stream(self.device)).cuda_stream
+        status = B.lol_core_forward_docs(self.ccfg, s_in.shape[0], doc_start.data_ptr(),
+                                         doc_len.data_ptr(), s_in.data_ptr(), self.lib, self.rt,
+                                         _ptr(self.forced_expert), _ptr(self.forced_gate),
+                                         s_out.data_ptr(), self.path, self.workspace.data_ptr(),
+                                         self.ws_bytes, st)
+        if status != B.LOL_OK:
+            raise B.LolError(status, "lol_core_forward_docs")
+        return s_out
+
     def flags(self, stream: Optional[torch.cuda.Stream] = None) -> int:
         st = (stream or torch.cuda.current_stream(self.device)).cuda_stream
         return B.lol_core_read_flags(self.workspace.data_ptr(), st)

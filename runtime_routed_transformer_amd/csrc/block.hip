@@ -58,9 +58,12 @@ __global__ void __launch_bounds__(256) k_norm(const float *__restrict__ src,
                                               const float *__restrict__ gain,
                                               const float *__restrict__ fg,
                                               const float *__restrict__ fb, act_t *__restrict__ u,
-                                              int T, int d, float eps, int panel_rows, int film_stride) {
+                                              const int32_t *__restrict__ n_rows, int d, float eps,
+                                              int panel_rows, int film_stride) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= T) return;
+  // grouped rows in use this depth (the grid covers the most there can be;
+  // packed documents fill fewer, and the rows past them hold no metadata)
+  if (row >= *n_rows) return;
   const float *x = src + (FROM_S ? (size_t)row_tok[row] : (size_t)row) * d;
   const int e = row_exp[row];
   const float *g = gain + (size_t)e * d;
@@ -123,17 +126,15 @@ __global__ void __launch_bounds__(64) k_attn_simt(const act_t *__restrict__ qkv,
                                                   act_t *__restrict__ o,
                                                   const int32_t *__restrict__ win_exp,
                                                   const int32_t *__restrict__ win_row0,
-                                                  const float *__restrict__ rope_cs, int n, int d,
-                                                  int W, int delta, int K_max, float scale,
-                                                  int use_rope) {
+                                                  const int32_t *__restrict__ win_len,
+                                                  const float *__restrict__ rope_cs, int d,
+                                                  float scale, int use_rope) {
   constexpr int HALF = DH / 2;
   __shared__ float ks[64][DH + 1];
   __shared__ float vs[64][DH + 1];
   const int slot = blockIdx.x, h = blockIdx.y, q0 = blockIdx.z * 64;
   if (win_exp[slot] < 0) return;
-  const int k = slot % K_max;
-  const int start = max(0, k * W - delta);
-  const int len = min(n - 1, (k + 1) * W - delta - 1) - start + 1;
+  const int len = win_len[slot];  // tokens of the window (its document's end clips the last one)
   if (q0 >= len) return;
   const int base = win_row0[slot];
   const int lane = threadIdx.x;
@@ -244,8 +245,8 @@ template <int DH>
 __global__ void __launch_bounds__(256, 3) k_attn_mfma(const bf16_t *__restrict__ qkv,
                                                       bf16_t *__restrict__ o,
                                                       const int32_t *__restrict__ win_exp,
-                                                      const int32_t *__restrict__ win_row0, int n,
-                                                      int d, int W, int delta, int K_max,
+                                                      const int32_t *__restrict__ win_row0,
+                                                      const int32_t *__restrict__ win_len, int d,
                                                       float qscale) {
   using LY = AttnLds<DH>;
   constexpr int CH = 256;            // keys / queries per chunk
@@ -262,9 +263,7 @@ __global__ void __launch_bounds__(256, 3) k_attn_mfma(const bf16_t *__restrict__
   char *const Vl = lds + KC * RB;
   const int slot = blockIdx.x, h = blockIdx.y, qc = blockIdx.z;
   if (win_exp[slot] < 0) return;
-  const int k = slot % K_max;
-  const int start = max(0, k * W - delta);
-  const int len = min(n - 1, (k + 1) * W - delta - 1) - start + 1;
+  const int len = win_len[slot];  // tokens of the window (its document's end clips the last one)
   const int q_begin = qc * CH;
   if (q_begin >= len) return;
   const int base = win_row0[slot];
@@ -433,13 +432,14 @@ void norm_launch(const Plan &p, int which, const float *s, const lol_library &li
                  const Workspace &ws, const float *fg, const float *fb, int panel_rows, hipStream_t st) {
   dim3 grid((p.T + 3) / 4);
   const int film_stride = lib.film_per_expert ? 2 * p.cfg.d : 0;
+  const int32_t *n_rows = ws.toff + p.cfg.L;   // total grouped rows, written by the router
   if (which == 0)
     lol_launch((k_norm<act_t, true, NCH>), grid, dim3(256), 0, st, s, ws.row_tok,
-                       ws.row_exp, lib.g_attn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T,
+                       ws.row_exp, lib.g_attn, fg, fb, reinterpret_cast<act_t *>(ws.u), n_rows,
                        p.cfg.d, p.cfg.rms_eps, panel_rows, film_stride);
   else
     lol_launch((k_norm<act_t, false, NCH>), grid, dim3(256), 0, st, ws.h, ws.row_tok,
-                       ws.row_exp, lib.g_ffn, fg, fb, reinterpret_cast<act_t *>(ws.u), p.T,
+                       ws.row_exp, lib.g_ffn, fg, fb, reinterpret_cast<act_t *>(ws.u), n_rows,
                        p.cfg.d, p.cfg.rms_eps, panel_rows, film_stride);
 }
 
@@ -472,8 +472,8 @@ hipError_t attn_typed(const Plan &p, const DepthGeom &g, const Workspace &ws, hi
   const float scale = 1.0f / sqrtf((float)DH);
   lol_launch((k_attn_simt<act_t, DH>), grid, dim3(64), 0, st,
                      reinterpret_cast<const act_t *>(ws.qkv), reinterpret_cast<act_t *>(ws.o),
-                     ws.win_exp, ws.win_row0, ws.rope_cs, p.cfg.n, p.cfg.d, p.cfg.W, g.delta,
-                     p.K_max, scale, p.cfg.rope_theta != 0.f ? 1 : 0);
+                     ws.win_exp, ws.win_row0, ws.win_len, ws.rope_cs, p.cfg.d, scale,
+                     p.cfg.rope_theta != 0.f ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -484,7 +484,7 @@ hipError_t attn_mfma(const Plan &p, const DepthGeom &g, const Workspace &ws, hip
   const float qscale = 1.4426950408889634f / sqrtf((float)DH);
   lol_launch((k_attn_mfma<DH>), grid, dim3(256), 0, st,
                      reinterpret_cast<const bf16_t *>(ws.qkv), reinterpret_cast<bf16_t *>(ws.o),
-                     ws.win_exp, ws.win_row0, p.cfg.n, p.cfg.d, p.cfg.W, g.delta, p.K_max, qscale);
+                     ws.win_exp, ws.win_row0, ws.win_len, p.cfg.d, qscale);
   return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ Plan make_plan(const lol_core_config *c) {
   p.d_head = c->d / c->n_heads;
   p.T = c->batch * c->n;
   p.n_slots = c->batch * p.K_max;
+  p.n_tokens = p.T;
   p.act_bytes = c->dtype == LOL_BF16 ? 2 : 4;
   return p;
 }
@@ -178,6 +179,7 @@ size_t workspace_layout(const Plan &p, char *base, Workspace *ws) {
   w.win_exp = (int32_t *)carve(ns * 4);
   w.win_gate = (float *)carve(ns * 4);
   w.win_row0 = (int32_t *)carve(ns * 4);
+  w.win_len = (int32_t *)carve(ns * 4);
   w.ecount = (int32_t *)carve((size_t)(c.L + 1) * 4);
   w.toff = (int32_t *)carve((size_t)(c.L + 1) * 4);
   w.mtile = (int32_t *)carve((size_t)max_mtiles * 8);
@@ -224,14 +226,33 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
                             void *workspace, size_t workspace_bytes, void *stream) {
   const lol_status vs = validate(cfg);
   if (vs != LOL_OK) return vs;
+  return lol_core_forward_docs(cfg, (int64_t)cfg->batch * cfg->n, nullptr, nullptr, s0, lib, rt,
+                               forced_expert, forced_gate, s_out, path, workspace, workspace_bytes,
+                               stream);
+}
+
+lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
+                                 const int32_t *doc_start, const int32_t *doc_len,
+                                 const float *s0, const lol_library *lib, const lol_router *rt,
+                                 const int32_t *forced_expert, const float *forced_gate,
+                                 float *s_out, const lol_path *path, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+  const lol_status vs = validate(cfg);
+  if (vs != LOL_OK) return vs;
   if (!s0 || !s_out || !lib || !rt) return LOL_EINVAL;
+  if ((doc_start == nullptr) != (doc_len == nullptr)) return LOL_EINVAL;
+  if (n_tokens < 1 || n_tokens >= (1LL << 30)) return LOL_EINVAL;
+  if (!doc_len && n_tokens != (int64_t)cfg->batch * cfg->n) return LOL_EINVAL;
   if (!lib->wqkv || !lib->wo || !lib->w_gu || !lib->w_down || !lib->g_attn || !lib->g_ffn)
     return LOL_EINVAL;
   if ((lib->film_gamma == nullptr) != (lib->film_beta == nullptr)) return LOL_EINVAL;
   if (!rt->w_r || !rt->e_depth) return LOL_EINVAL;
   if ((rt->per_depth != 0 && rt->per_depth != 1) || (lib->film_per_expert != 0 && lib->film_per_expert != 1))
     return LOL_EINVAL;
-  const Plan p = make_plan(cfg);
+  Plan p = make_plan(cfg);
+  p.doc_start = doc_start;
+  p.doc_len = doc_len;
+  p.n_tokens = (int)n_tokens;
   const size_t need = workspace_layout(p, nullptr, nullptr);
   if (!workspace || workspace_bytes < need) return LOL_EWORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return LOL_EINVAL;
@@ -257,8 +278,9 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     if (err != hipSuccess) return LOL_EHIP;           \
   } while (0)
 
-  // Depth 1 reads s0 and its blend writes s_out: every token lies in exactly
-  // one window per depth, so s_out is complete after it (no copy of s0).
+  // Depth 1 reads s0 and its blend writes s_out: every token (of every
+  // document) lies in exactly one window per depth, so s_out is complete
+  // after it (no copy of s0).
   // With the fused output projection (bf16, d a multiple of 256 up to 1024)
   // the blend is split: the O kernel writes s_out = s + gate * Attn and the
   // down projection adds gate * MLP.
@@ -277,7 +299,8 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0, const l
     g.depth = l;
     g.delta = (int)(((long long)l * c.S) % c.W);
     g.K = (c.n - 1 + g.delta) / c.W + 1;
-    g.len_gcd = window_length_gcd(c.n, c.W, g.delta, g.K);
+    // ragged documents end windows anywhere: no common divisor to exploit
+    g.len_gcd = doc_len ? 1 : window_length_gcd(c.n, c.W, g.delta, g.K);
     LOL_TRY(KK_POOL, launch_pool(p, g, s, ws, *rt, st));
     LOL_TRY(KK_ROUTE, launch_route(p, g, s, ws, *rt, forced_expert, forced_gate, path, st));
     LOL_TRY(KK_NORM_ATTN, launch_norm(p, g, 0, s, *lib, ws, qkv_panels ? p.T : 0, st));

@@ -51,6 +51,7 @@ struct Workspace {
   int32_t *win_exp;    // [B*K_max]          expert of each window slot (-1 = none)
   float *win_gate;     // [B*K_max]
   int32_t *win_row0;   // [B*K_max]          first grouped row of each window slot
+  int32_t *win_len;    // [B*K_max]          tokens of each window slot (0 = none)
   int32_t *ecount;     // [L+1]              windows per expert (+ total)
   int32_t *toff;       // [L+1]              grouped-row offset of each expert
   int32_t *mtile;      // [max_mtiles][2]    (expert, first row) per kTileM-row tile, -1 = idle
@@ -74,6 +75,11 @@ struct Plan {
   lol_core_config cfg;
   int K_max, d_head, T, n_slots;
   size_t act_bytes;    // 2 (bf16) or 4 (fp32)
+  // packed documents (DEVICE [batch] each, NULL for the [batch][n] layout):
+  // document b is tokens doc_start[b] .. + doc_len[b] - 1 of a stream of
+  // n_tokens rows (n_tokens = batch n without a table)
+  const int32_t *doc_start = nullptr, *doc_len = nullptr;
+  int n_tokens = 0;
 };
 
 // Timing events of the launcher call in progress (set by the forward's

@@ -22,6 +22,23 @@ __device__ __forceinline__ int win_end(int k, int W, int delta, int n) {
   return min(n - 1, (k + 1) * W - delta - 1);
 }
 
+// Document b: its first token in the residual stream and its length.
+// Without a document table it is row b of the [B][n] layout.  With one, the
+// entry is clamped so that the document lies inside the n_tokens rows of the
+// stream with 1 <= length <= n; k_route_all flags entries that needed it.
+struct DocSpan {
+  int start, len;
+};
+__device__ __forceinline__ DocSpan doc_span(const int32_t *__restrict__ doc_start,
+                                            const int32_t *__restrict__ doc_len, int b, int n,
+                                            int n_tokens) {
+  if (!doc_len) return {b * n, n};
+  const int len = min(min(max(doc_len[b], 1), n), n_tokens);
+  return {min(max(doc_start[b], 0), n_tokens - len), len};
+}
+// windows of a document of nb tokens at offset delta
+__device__ __forceinline__ int doc_windows(int nb, int W, int delta) { return (nb - 1 + delta) / W + 1; }
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -59,12 +76,16 @@ __global__ void __launch_bounds__(256) k_pool(const float *__restrict__ s,
                                               const float *__restrict__ e_depth,
                                               float *__restrict__ zpart, float *__restrict__ zpart0,
                                               int n, int d, int L, int W, int delta, int K,
-                                              int K_max, int depth) {
+                                              int K_max, int depth,
+                                              const int32_t *__restrict__ doc_start,
+                                              const int32_t *__restrict__ doc_len, int n_tokens) {
   const int b = blockIdx.x / K, k = blockIdx.x % K, chunk = blockIdx.y, nch = gridDim.y;
-  const int start = win_start(k, W, delta), len = win_end(k, W, delta, n) - start + 1;
+  const DocSpan doc = doc_span(doc_start, doc_len, b, n, n_tokens);
+  if (k >= doc_windows(doc.len, W, delta)) return;  // past the end of a shorter document
+  const int start = win_start(k, W, delta), len = win_end(k, W, delta, doc.len) - start + 1;
   const int c4 = threadIdx.x & 15, ph = threadIdx.x >> 4;
   const int col = chunk * 64 + c4 * 4;
-  const float *base = s + ((size_t)b * n + start) * d + col;
+  const float *base = s + ((size_t)doc.start + start) * d + col;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   // rows ph, ph + 16, ... in batches of 8 whose loads are all in flight
   // before the first add
@@ -96,7 +117,7 @@ __global__ void __launch_bounds__(256) k_pool(const float *__restrict__ s,
   }
   if (k == 0 && threadIdx.x < 64) {
     const int c = chunk * 64 + threadIdx.x;
-    r0[threadIdx.x] = 0.5f * (e_depth[(size_t)depth * d + c] + s[(size_t)b * n * d + c]);
+    r0[threadIdx.x] = 0.5f * (e_depth[(size_t)depth * d + c] + s[(size_t)doc.start * d + c]);
   }
   __syncthreads();
   // one wave per expert (4 waves), lane = column of the chunk
@@ -140,7 +161,8 @@ __global__ void __launch_bounds__(1024) k_route_all(
     int32_t *__restrict__ mtile2, int max_mtiles2, int32_t *__restrict__ mcount,
     int32_t *__restrict__ row_tok, int32_t *__restrict__ row_pos, int32_t *__restrict__ row_exp,
     float *__restrict__ row_gate, float *__restrict__ zlog_g, int n, int nch, int L, int W, int delta,
-    int K, int K_max, int B, int depth) {
+    int K, int K_max, int B, int depth, int32_t *__restrict__ win_len,
+    const int32_t *__restrict__ doc_start, const int32_t *__restrict__ doc_len, int n_tokens) {
   __shared__ int s_exp[kMaxSlots];
   __shared__ int s_len[kMaxSlots];
   __shared__ int cnt_w[kMaxExperts], cnt_t[kMaxExperts];
@@ -196,6 +218,16 @@ __global__ void __launch_bounds__(1024) k_route_all(
     }
   }
   for (int i = tid; i < kMaxExperts; i += blockDim.x) { cnt_w[i] = 0; cnt_t[i] = 0; }
+  // a document table must hold, in increasing order, disjoint documents of
+  // 1..n tokens inside the stream's n_tokens rows
+  if (doc_len && depth == 0) {
+    for (int b = tid; b < B; b += blockDim.x) {
+      const int st = doc_start[b], ln = doc_len[b];
+      bool bad = ln < 1 || ln > n || st < 0 || st > n_tokens - ln;
+      if (!bad && b + 1 < B) bad = st + ln > doc_start[b + 1];
+      if (bad) atomicOr(flags, (uint32_t)LOL_FLAG_BAD_DOC);
+    }
+  }
   __syncthreads();
 
   // 2. score and select: groups of G lanes (G = the power of two >= L), one
@@ -206,7 +238,8 @@ __global__ void __launch_bounds__(1024) k_route_all(
     const int slot = slot0 + lane / G;
     const bool in_range = slot < n_slots;
     const int b = slot / K_max, k = slot % K_max;
-    const bool win_ok = in_range && k < K;
+    const int nb = in_range ? doc_span(doc_start, doc_len, b, n, n_tokens).len : n;
+    const bool win_ok = in_range && k < K && k < doc_windows(nb, W, delta);
     const size_t pidx = ((size_t)depth * B + b) * K_max + k;
     const bool live = win_ok && gl < L;
     const float zl = live ? zlog[(size_t)slot * L + gl] : -INFINITY;
@@ -239,7 +272,8 @@ __global__ void __launch_bounds__(1024) k_route_all(
       win_exp[slot] = e;
       win_gate[slot] = win_ok ? alpha : 0.f;
       s_exp[slot] = e;
-      s_len[slot] = win_ok ? win_end(k, W, delta, n) - win_start(k, W, delta) + 1 : 0;
+      s_len[slot] = win_ok ? win_end(k, W, delta, nb) - win_start(k, W, delta) + 1 : 0;
+      win_len[slot] = s_len[slot];
       if (path_e) path_e[pidx] = e;
       if (path_g) path_g[pidx] = win_ok ? alpha : 0.f;
       if (path_m) path_m[pidx] = win_ok ? margin : 0.f;
@@ -358,10 +392,10 @@ __global__ void __launch_bounds__(1024) k_route_all(
       const int len = __shfl(my_len, j, 64), base = __shfl(my_row0, j, 64);
       const float g = __shfl(my_gate, j, 64);
       const int b = slot / K_max, k = slot % K_max;
-      const int start = win_start(k, W, delta);
+      const int tok0 = doc_span(doc_start, doc_len, b, n, n_tokens).start + win_start(k, W, delta);
       for (int p = lane; p < len; p += 64) {
         const int row = base + p;
-        row_tok[row] = b * n + start + p;
+        row_tok[row] = tok0 + p;
         row_pos[row] = p;
         row_exp[row] = e;
         row_gate[row] = g;
@@ -392,7 +426,8 @@ hipError_t launch_pool(const Plan &p, const DepthGeom &g, const float *s, const 
   // untied router: this depth's W_r
   const float *w_r = rt.w_r + (rt.per_depth ? (size_t)g.depth * p.cfg.L * p.cfg.d : 0);
   lol_launch(k_pool, grid, dim3(256), 0, st, s, w_r, rt.e_depth, ws.zpart, ws.zpart0,
-                     p.cfg.n, p.cfg.d, p.cfg.L, p.cfg.W, g.delta, g.K, p.K_max, g.depth);
+                     p.cfg.n, p.cfg.d, p.cfg.L, p.cfg.W, g.delta, g.K, p.K_max, g.depth,
+                     p.doc_start, p.doc_len, p.n_tokens);
   return hipGetLastError();
 }
 
@@ -408,7 +443,8 @@ hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const
                      path ? path->margin : nullptr, ws.flags, ws.ecount, ws.toff, ws.mtile,
                      ws.max_mtiles, ws.mtile2, ws.max_mtiles2, ws.mcount, ws.row_tok, ws.row_pos,
                      ws.row_exp, ws.row_gate, ws.zlog, p.cfg.n, p.cfg.d / 64, p.cfg.L, p.cfg.W,
-                     g.delta, g.K, p.K_max, p.cfg.batch, g.depth);
+                     g.delta, g.K, p.K_max, p.cfg.batch, g.depth, ws.win_len, p.doc_start,
+                     p.doc_len, p.n_tokens);
   return hipGetLastError();
 }
 

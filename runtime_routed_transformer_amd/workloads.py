@@ -280,3 +280,77 @@ FULL_CONFIGS = [
                seed=40),
 ]
 FULL_BY_NAME = {c.name: c for c in FULL_CONFIGS}
+
+
+# --------------------------------------------------------------------------
+# Packed documents: documents of different lengths laid out back to back in
+# one token stream, each partitioned, routed and attended as its own row
+# (paper App. A: document-blocked attention; the explainer's router prefix
+# sum restarts at every document boundary).
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class PackedConfig:
+    name: str
+    core: CoreConfig   # widths, library, windows; n = the longest a document may be
+    total: int         # document tokens in the stream
+    min_len: int       # shortest document drawn
+    gap: int           # unused rows before every document (0 = back to back)
+    seed: int
+
+
+@dataclass
+class PackedInputs:
+    cfg: PackedConfig
+    core: CoreInputs        # batch = number of documents; document b is core.s0[b, :length[b]]
+    start: np.ndarray       # int32 [B] first row of each document in the stream
+    length: np.ndarray      # int32 [B]
+    n_tokens: int           # rows of the stream
+
+    def stream(self) -> np.ndarray:
+        """The packed residual stream [n_tokens][d]; rows outside every
+        document hold a constant 1000 (never read by the core)."""
+        d = self.core.cfg.d
+        out = np.full((self.n_tokens, d), 1000.0, np.float32)
+        for b, (a, ln) in enumerate(zip(self.start, self.length)):
+            out[a:a + ln] = self.core.s0[b, :ln]
+        return out
+
+
+def doc_lengths(total: int, n_max: int, min_len: int, rng) -> list:
+    """Lengths log-uniform in [min_len, n_max] (rounded), drawn until they
+    cover ``total`` tokens; the last one is cut to fit."""
+    out, left = [], total
+    while left > 0:
+        x = int(round(float(np.exp(rng.uniform(np.log(min_len), np.log(n_max))))))
+        x = min(max(x, min_len), n_max, left)
+        out.append(x)
+        left -= x
+    return out
+
+
+def generate_packed(cfg: PackedConfig, lengths: Optional[list] = None) -> PackedInputs:
+    """Document lengths from ``default_rng(cfg.seed)`` (or as given), then
+    every core input as ``generate(cfg.core)`` with batch = the number of
+    documents; document b is placed ``cfg.gap`` rows after the end of b - 1."""
+    rng = np.random.default_rng(cfg.seed)
+    lens = list(lengths) if lengths is not None else doc_lengths(cfg.total, cfg.core.n,
+                                                                  cfg.min_len, rng)
+    if not lens or min(lens) < 1 or max(lens) > cfg.core.n:
+        raise ValueError("document lengths must lie in [1, n]")
+    core = generate(cfg.core.with_(name=cfg.name, batch=len(lens)))
+    starts, pos = [], 0
+    for ln in lens:
+        pos += cfg.gap
+        starts.append(pos)
+        pos += ln
+    return PackedInputs(cfg, core, np.asarray(starts, np.int32), np.asarray(lens, np.int32),
+                        pos + cfg.gap)
+
+
+# The mid core on 16,384 packed tokens (as many as its 4 x 4,096 layout) in
+# documents of 64 .. 4,096 tokens.
+PACKED_CONFIGS = [
+    PackedConfig("mid_bf16_packed", CONFIG_BY_NAME["mid_bf16"], total=16384, min_len=64, gap=0,
+                 seed=50),
+]
+PACKED_BY_NAME = {c.name: c for c in PACKED_CONFIGS}

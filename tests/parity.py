@@ -146,3 +146,98 @@ def run_full(full, device="cuda:0") -> FullReport:
     n_forced = int(np.count_nonzero(compared & (ref.core.margin <= MARGIN)))
     return FullReport(full.cfg.name, logit_err, hidden_err, mism, int(np.count_nonzero(free_cmp)),
                       n_forced, TOL[core_cfg.dtype])
+
+
+@dataclass
+class DocsReport:
+    name: str
+    docs: int
+    rel_err: float
+    id_mismatch: int
+    ids_compared: int
+    forced_windows: int
+    gate_err: float
+    gaps_untouched: bool
+    pad_slots_ok: bool
+    tol: float
+
+    @property
+    def ok(self) -> bool:
+        return (self.rel_err <= self.tol and self.id_mismatch == 0 and self.gaps_untouched
+                and self.pad_slots_ok)
+
+    def __str__(self):
+        return (f"{self.name}: {self.docs} docs rel_err={self.rel_err:.3e} (tol {self.tol:g}) ids "
+                f"{self.ids_compared - self.id_mismatch}/{self.ids_compared} equal, forced "
+                f"{self.forced_windows}, gate_err={self.gate_err:.2e}, gaps untouched="
+                f"{self.gaps_untouched}, padding slots ok={self.pad_slots_ok}")
+
+
+def run_docs(packed, docs=None, prefix=None, device="cuda:0") -> DocsReport:
+    """Packed documents on the GPU (``lol_core_forward_docs``) against the
+    oracle run on each document alone.  ``docs``: the documents compared
+    (default all); ``prefix``: compare only each document's first ``prefix``
+    tokens (by the core's causality they equal a run of that prefix alone).
+    Near-tie windows are forced to the oracle's choice as in ``run``."""
+    import torch
+    from runtime_routed_transformer_amd.core import DeviceCore
+
+    inp = packed.core
+    cfg = inp.cfg
+    docs = list(range(cfg.batch)) if docs is None else list(docs)
+    forced = (inp.forced_expert.copy() if inp.forced_expert is not None
+              else np.full((cfg.D, cfg.batch, cfg.k_max), -1, np.int32))
+    refs, ns = {}, {}
+    for b in docs:
+        n_b = int(packed.length[b]) if prefix is None else min(int(packed.length[b]), prefix)
+        ns[b] = n_b
+        refs[b] = oracle.forward(inp, forced_expert=inp.forced_expert, rows=[b], n_tokens=n_b)
+        for depth in range(1, cfg.D + 1):
+            for k in range(len(oracle.partition(n_b, cfg.W, cfg.S, depth))):
+                if refs[b].margin[depth - 1, 0, k] <= MARGIN:
+                    forced[depth - 1, b, k] = refs[b].expert[depth - 1, 0, k]
+    core = DeviceCore(inp, device)
+    core.set_forcing(forced_expert=forced)
+    stream = packed.stream()
+    s_in = torch.from_numpy(stream).to(core.device)
+    s_out = torch.full_like(s_in, -7.0)
+    d_start = torch.from_numpy(packed.start).to(core.device)
+    d_len = torch.from_numpy(packed.length).to(core.device)
+    core.forward_docs(s_in, s_out, d_start, d_len)
+    torch.cuda.synchronize(core.device)
+    flags = core.flags()
+    out = s_out.cpu().numpy()
+    pe, pg, pm = core.path_numpy()
+    del core
+    inside = np.zeros(packed.n_tokens, bool)
+    for a, ln in zip(packed.start, packed.length):
+        inside[a:a + ln] = True
+    gaps_ok = bool((out[~inside] == -7.0).all()) and flags == 0
+    err = ref_max = 0.0
+    mism = cmp = n_forced = 0
+    gate_err = 0.0
+    pad_ok = True
+    for b in docs:
+        a, n_b, ref = int(packed.start[b]), ns[b], refs[b]
+        err = max(err, float(np.abs(out[a:a + n_b] - ref.s64[0]).max()))
+        ref_max = max(ref_max, float(np.abs(ref.s64[0]).max()))
+        for depth in range(1, cfg.D + 1):
+            K_full = len(oracle.partition(int(packed.length[b]), cfg.W, cfg.S, depth))
+            K_b = len(oracle.partition(n_b, cfg.W, cfg.S, depth))
+            # slots past the document's last window: expert -1, gate 0
+            pad_ok &= bool((pe[depth - 1, b, K_full:] == -1).all()
+                           and (pg[depth - 1, b, K_full:] == 0).all())
+            # a window's route reads only earlier (complete) windows, so a
+            # prefix run routes its windows as the whole document does
+            for k in range(K_b):
+                free = (ref.margin[depth - 1, 0, k] > MARGIN
+                        and (inp.forced_expert is None or inp.forced_expert[depth - 1, b, k] < 0))
+                if free:
+                    cmp += 1
+                    mism += int(pe[depth - 1, b, k] != ref.expert[depth - 1, 0, k])
+                else:
+                    n_forced += int(ref.margin[depth - 1, 0, k] <= MARGIN)
+                gate_err = max(gate_err,
+                               abs(float(pg[depth - 1, b, k]) - float(ref.gate[depth - 1, 0, k])))
+    return DocsReport(packed.cfg.name, len(docs), err / ref_max, mism, cmp, n_forced, gate_err,
+                      gaps_ok, pad_ok, TOL[cfg.dtype])

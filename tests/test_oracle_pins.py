@@ -462,3 +462,49 @@ def test_causal_stack_is_the_ordinary_decoder_stack():
         want = oracle.causal_stack(x0[b].astype(np.float32).astype(np.float64), params,
                                    pre.cfg.n_heads, pre.cfg.rms_eps, pre.cfg.rope_theta)
         np.testing.assert_allclose(res.s64[b], want, rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------- packed documents
+def test_packed_documents_route_from_their_own_prefix():
+    """Packed documents (blog 'The forward pass, term by term': the router's
+    prefix sum restarts at each document boundary; review 'Deriving
+    prefix-only routing').  Depth-1 routes of every document, by brute force
+    from the document's own tokens: window 0 from (e^(1) + its first token) / 2,
+    window k from the mean of its own earlier windows' means."""
+    cfg = tiny(batch=3, n=40, L=4, D=2, W=8, S=3)
+    inp = generate(cfg)
+    lengths = [40, 13, 1]
+    res = oracle.forward_docs(inp, lengths)
+    w_r, b_r = inp.w_r.astype(np.float32), inp.b_r.astype(np.float32)
+    for b, ln in enumerate(lengths):
+        x = inp.s0[b, :ln].astype(np.float64)
+        starts = list(range(0, ln, cfg.W))   # depth 1: offset 0
+        means = [x[a:a + cfg.W].mean(axis=0) for a in starts]
+        for k in range(len(starts)):
+            r = (0.5 * (inp.e_depth[0] + x[0]) if k == 0 else np.mean(means[:k], axis=0))
+            z = w_r @ r.astype(np.float32) + b_r
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            assert res[b].expert[0, 0, k] == int(np.argmax(p))
+            np.testing.assert_allclose(res[b].gate[0, 0, k], p.max(), rtol=1e-5)
+        assert (res[b].expert[0, 0, len(starts):] == -1).all()
+
+
+def test_packed_documents_attend_only_inside_themselves():
+    """Paper App. A (document-blocked attention): with one window per
+    document (W >= n, S = 0) and every window forced to block m with gate 1,
+    each packed document is D ordinary causal blocks applied to it alone."""
+    cfg = tiny(batch=3, L=2, D=2, n=24, W=24, S=0)
+    inp = generate(cfg)
+    lengths = [24, 7, 16]
+    m = 1
+    forced = np.full((cfg.D, cfg.batch, cfg.k_max), m, np.int32)
+    gate = np.ones((cfg.D, cfg.batch, cfg.k_max), np.float32)
+    res = oracle.forward_docs(inp, lengths, forced_expert=forced, forced_gate=gate)
+    for b, ln in enumerate(lengths):
+        x = inp.s0[b, :ln].astype(np.float64)
+        for depth in range(cfg.D):
+            x = torch_block.block(x, inp.wqkv[m], inp.wo[m], inp.w_gu[m], inp.w_down[m],
+                                  inp.g_attn[m], inp.g_ffn[m], cfg.n_heads, "swiglu",
+                                  film=(inp.film_gamma[depth], inp.film_beta[depth]))
+        np.testing.assert_allclose(res[b].s64[0], x, rtol=0, atol=1e-11)
