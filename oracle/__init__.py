@@ -8,5 +8,6 @@ from .lol_oracle import (  # noqa: F401
     OracleResult, Route, BlockParams, window_offset, window_ids, partition,
     window_means, router_inputs, route, rms_norm, rope, window_causal_attention,
     silu, gelu_erf, expert_block, expert_params, forward, forward_docs,
+    DecodeState, decode_state, block_step, decode,
     embed, causal_stack, lm_head, FullResult, full_forward,
 )

@@ -368,6 +368,134 @@ def _fit_slots(a: np.ndarray, k: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Incremental decode
+#   [review] "Deriving prefix-only routing": a window's route and gate are
+#   fixed when the window opens, since the router reads only earlier,
+#   completed windows (and, for window 0, the document's first token);
+#   serving keeps per-depth window boundaries and summaries.  [blog] "What it
+#   costs": attention never leaves the window, so a depth only needs the open
+#   window's keys and values, computed by the block that window runs.
+# One token of a document enters at a time.  At every routed depth the
+# state is: the sum of the completed windows' means, the running sum and
+# length of the open window, its route, and its keys and values.  When a
+# token opens a window, the window before it (if any) is closed and its mean
+# joins the prefix sum, the new window is routed from the prefix (or by the
+# window-0 rule) and its cache starts empty.  The token then runs the
+# window's block against the cached keys and values plus its own.
+# --------------------------------------------------------------------------
+@dataclass
+class DecodeState:
+    prefix: np.ndarray       # [D][d] sum of completed window means
+    cur_sum: np.ndarray      # [D][d] sum of the open window's depth inputs
+    cur_len: np.ndarray      # [D]
+    expert: np.ndarray       # [D] route of the open window
+    gate: np.ndarray         # [D]
+    keys: list               # [D] list of [H][d_h] arrays (rotated)
+    values: list             # [D] list of [H][d_h] arrays
+
+
+def decode_state(D: int, d: int) -> DecodeState:
+    return DecodeState(np.zeros((D, d)), np.zeros((D, d)), np.zeros(D, np.int64),
+                       np.full(D, -1, np.int64), np.zeros(D), [[] for _ in range(D)],
+                       [[] for _ in range(D)])
+
+
+def block_step(x: np.ndarray, p: BlockParams, n_heads: int, pos: int, film, eps: float,
+               rope_theta: float, keys: list, values: list) -> np.ndarray:
+    """E_m on one token x [d] at document position ``pos``: its key and value
+    join ``keys`` / ``values`` (the open window's), and its query attends to
+    all of them."""
+    d = x.shape[0]
+    dh = d // n_heads
+    u = rms_norm(x[None], p.g_attn, eps)
+    if film is not None:
+        u = film[0] * u + film[1]
+    at = np.array([pos])
+    q = rope((u @ p.wq.T).reshape(1, n_heads, dh), at, rope_theta)[0]
+    k = rope((u @ p.wk.T).reshape(1, n_heads, dh), at, rope_theta)[0]
+    v = (u @ p.wv.T).reshape(n_heads, dh)
+    keys.append(k)
+    values.append(v)
+    K = np.stack(keys)          # [j][H][d_h]
+    V = np.stack(values)
+    o = np.empty((n_heads, dh))
+    for h in range(n_heads):
+        sc = K[:, h, :] @ q[h] / math.sqrt(dh)
+        w = np.exp(sc - sc.max())
+        o[h] = (w / w.sum()) @ V[:, h, :]
+    hh = x + o.reshape(d) @ p.wo.T
+    u2 = rms_norm(hh[None], p.g_ffn, eps)[0]
+    if film is not None:
+        u2 = film[2] * u2 + film[3]
+    if p.w_gate is not None:
+        mid = silu(u2 @ p.w_gate.T) * (u2 @ p.w_up.T)
+    else:
+        mid = gelu_erf(u2 @ p.w_up.T)
+    return hh + mid @ p.w_down.T
+
+
+def decode(inp, n_tokens: int, forced_expert: Optional[np.ndarray] = None,
+           forced_gate: Optional[np.ndarray] = None,
+           rows: Optional[List[int]] = None) -> OracleResult:
+    """Feed tokens 0 .. n_tokens-1 of each document (row of ``inp.s0``) one
+    at a time; returns s^(D) of every token and the path, laid out as
+    ``forward``'s result."""
+    cfg = inp.cfg
+    rows = list(range(cfg.batch)) if rows is None else list(rows)
+    D, L, W, K_max = cfg.D, cfg.L, cfg.W, cfg.k_max
+    params = [expert_params(inp, m) for m in range(L)]
+    per_depth = getattr(cfg, "router", "tied") == "per_depth"
+    per_expert_film = getattr(cfg, "film_mode", "depth") == "depth_expert"
+    bias = np.asarray(inp.expert_bias, np.float32)
+    out = np.zeros((len(rows), n_tokens, cfg.d))
+    expert = np.full((D, len(rows), K_max), -1, np.int32)
+    gate = np.zeros((D, len(rows), K_max), np.float32)
+    margin = np.zeros((D, len(rows), K_max), np.float32)
+    for bi, b in enumerate(rows):
+        st = decode_state(D, cfg.d)
+        for i in range(n_tokens):
+            x = np.asarray(inp.s0[b, i], np.float64)
+            for l in range(D):
+                delta = window_offset(l + 1, W, cfg.S)
+                k = (i + delta) // W
+                if i == max(0, k * W - delta):
+                    # the token opens window k: close k - 1, route k
+                    if k > 0:
+                        st.prefix[l] += st.cur_sum[l] / st.cur_len[l]
+                    r = (0.5 * (np.asarray(inp.e_depth[l], np.float64) + x) if k == 0
+                         else st.prefix[l] / k)
+                    w_r = np.asarray(inp.w_r[l] if per_depth else inp.w_r, np.float32)
+                    b_r = np.asarray(inp.b_r[l] if per_depth else inp.b_r, np.float32)
+                    rt = route(r, w_r, b_r, bias)
+                    rho, alpha = rt.expert, rt.gate
+                    if forced_expert is not None and forced_expert[l, b, k] >= 0:
+                        rho = int(forced_expert[l, b, k])
+                        alpha = float(rt.probs[rho])
+                    if forced_gate is not None and not np.isnan(forced_gate[l, b, k]):
+                        alpha = float(forced_gate[l, b, k])
+                    st.expert[l], st.gate[l] = rho, alpha
+                    st.cur_sum[l] = 0.0
+                    st.cur_len[l] = 0
+                    st.keys[l], st.values[l] = [], []
+                    expert[l, bi, k], gate[l, bi, k], margin[l, bi, k] = rho, alpha, rt.margin
+                st.cur_sum[l] += x
+                st.cur_len[l] += 1
+                rho = int(st.expert[l])
+                film = None
+                if inp.film_gamma is not None:
+                    fg = np.asarray(inp.film_gamma[l], np.float64)
+                    fb = np.asarray(inp.film_beta[l], np.float64)
+                    if per_expert_film:
+                        fg, fb = fg[rho], fb[rho]
+                    film = (fg[0], fb[0], fg[1], fb[1])
+                y = block_step(x, params[rho], cfg.n_heads, i, film, cfg.rms_eps,
+                               cfg.rope_theta, st.keys[l], st.values[l])
+                x = x + np.float64(np.float32(st.gate[l])) * (y - x)
+            out[bi, i] = x
+    return OracleResult(out.astype(np.float32), out, expert, gate, margin)
+
+
+# --------------------------------------------------------------------------
 # Around the core: embedding, fixed-order stacks, vocabulary readout
 #   [paper] Appendix A, Algorithm 1: the prelude is applied to the token
 #   sequence, the routed core follows, then the causal coda and the

@@ -508,3 +508,39 @@ def test_packed_documents_attend_only_inside_themselves():
                                   inp.g_attn[m], inp.g_ffn[m], cfg.n_heads, "swiglu",
                                   film=(inp.film_gamma[depth], inp.film_beta[depth]))
         np.testing.assert_allclose(res[b].s64[0], x, rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------- incremental decode
+@pytest.mark.parametrize("kw", [dict(), dict(mlp="gelu", film=False, S=0),
+                                dict(router="per_depth", film_mode="depth_expert", S=7)])
+def test_decode_token_by_token_equals_the_whole_forward(kw):
+    """Review 'Deriving prefix-only routing': a window's route is fixed when
+    it opens and earlier windows are complete then, so feeding a document one
+    token at a time (routes at window openings from running sums, attention
+    over the open window's cached keys and values) reproduces the forward of
+    the whole document at every position, path included."""
+    cfg = tiny(**{**dict(batch=2, n=29, W=6, S=4, D=3), **kw})
+    inp = generate(cfg)
+    full = oracle.forward(inp)
+    dec = oracle.decode(inp, cfg.n)
+    np.testing.assert_allclose(dec.s64, full.s64, rtol=0, atol=1e-11)
+    np.testing.assert_array_equal(dec.expert, full.expert)
+    np.testing.assert_allclose(dec.gate, full.gate, rtol=1e-6, atol=0)
+
+
+def test_decode_forcing_and_window_openings():
+    """Forced ids and gates act at the window's opening as in the forward; a
+    window's cache is the window's own tokens only (with S = 0, W = 4, every
+    fourth token starts over)."""
+    cfg = tiny(batch=1, n=13, W=4, S=0, D=2, L=3)
+    inp = generate(cfg)
+    rng = np.random.default_rng(5)
+    fe = rng.integers(-1, cfg.L, size=(cfg.D, cfg.batch, cfg.k_max)).astype(np.int32)
+    fg = np.where(rng.random((cfg.D, cfg.batch, cfg.k_max)) < 0.5, np.nan, 0.3).astype(np.float32)
+    full = oracle.forward(inp, forced_expert=fe, forced_gate=fg)
+    dec = oracle.decode(inp, cfg.n, forced_expert=fe, forced_gate=fg)
+    np.testing.assert_allclose(dec.s64, full.s64, rtol=0, atol=1e-11)
+    np.testing.assert_array_equal(dec.expert, full.expert)
+    # a prefix of the decode is the decode of the prefix
+    part = oracle.decode(inp, 6, forced_expert=fe, forced_gate=fg)
+    np.testing.assert_array_equal(part.s64, dec.s64[:, :6])
