@@ -194,9 +194,11 @@ lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
                                  float *s_out, const lol_path *path,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
-/* Device-side error flags of the last forward that used `workspace`. */
+/* Device-side error flags of the last forward that used `workspace` (and,
+ * LOL_FLAG_BAD_POS, of decode calls on a decode state). */
 #define LOL_FLAG_BAD_FORCED_ID 1u
 #define LOL_FLAG_BAD_DOC 2u
+#define LOL_FLAG_BAD_POS 4u
 /* Copies the flag word to *flags (HOST) and clears it; synchronises
  * `stream`. */
 lol_status lol_core_read_flags(void *workspace, uint32_t *flags, void *stream);
@@ -223,6 +225,62 @@ lol_status lol_core_timing_depth(int32_t depth);
 lol_status lol_core_timing_collect(double *ms, int32_t *launches);
 /* Name of kernel kind k (0 <= k < LOL_KERNEL_KINDS), or NULL. */
 const char *lol_core_kernel_name(int32_t kind);
+
+/* ---- Incremental decode -------------------------------------------------
+ * The routed core one token at a time, for `batch` documents in lockstep
+ * (every call brings token `pos` of each document).  The review "Library of
+ * Layers: Routing Whole Transformer Blocks at Runtime", Deriving prefix-only
+ * routing, notes that a window's router reads only earlier, completed
+ * windows (window 0: the document's first token and the depth vector), so a
+ * window's route and gate are fixed when its first token arrives and a
+ * server keeps each depth's window boundaries and summaries; the explainer
+ * "Library of Layers: a transformer that picks its own layer order", What
+ * it costs, notes that attention never leaves a window.  A decode state
+ * holds, per depth and document, the sum of the completed windows' means,
+ * the open window's running sum, length, expert and gate, and the open
+ * window's keys and values ([W] slots per head).  Feeding tokens 0 .. n-1
+ * gives, token by token, the s^(D) rows and path of lol_core_forward on the
+ * whole documents, up to rounding (the GEMM operands are rounded at the
+ * same points; the sums run in another order).
+ * Supported: every config lol_core_validate accepts with batch <= 64,
+ * d <= 4096 and W <= 8192 (else LOL_EUNSUPPORTED). */
+
+/* Bytes of the device decode state for cfg (0 if invalid or unsupported).
+ * HOST, pure. */
+size_t lol_decode_state_size(const lol_core_config *cfg);
+
+/* Starts new documents on `state` (DEVICE, state_bytes >= the size above,
+ * 256-byte aligned): the next call must bring pos = 0; clears the flags.
+ * Asynchronous on stream. */
+lol_status lol_decode_reset(const lol_core_config *cfg, void *state, size_t state_bytes,
+                            void *stream);
+
+/* One token per document through every routed depth.
+ *   pos           the token's position in its document, 0 <= pos < n; calls
+ *                 must bring 0, 1, 2, ... after a reset (a call out of turn
+ *                 raises LOL_FLAG_BAD_POS and its result is unspecified)
+ *   x             DEVICE [batch][d] fp32, s^(0) of the tokens
+ *   lib, rt       as for lol_core_forward
+ *   forced_expert, forced_gate
+ *                 DEVICE [D][batch][K_max] or NULL, as for lol_core_forward;
+ *                 read for the windows that open at this position
+ *   y             DEVICE [batch][d] fp32, receives s^(D) of the tokens; may
+ *                 equal x
+ *   path          HOST struct of DEVICE [D][batch][K_max] pointers, or NULL:
+ *                 the entries of the windows that open at this position are
+ *                 written (expert, gate, margin); others are left untouched
+ *   state         the decode state (DEVICE); its per-call scratch is inside
+ * Returns LOL_OK once queued; LOL_EINVAL for NULL inputs or pos outside
+ * [0, n); LOL_EWORKSPACE for a state that is missing, too small or not
+ * 256-byte aligned.  Calls on one state must run in order on one stream. */
+lol_status lol_decode_step(const lol_core_config *cfg, int32_t pos, const float *x,
+                           const lol_library *lib, const lol_router *rt,
+                           const int32_t *forced_expert, const float *forced_gate, float *y,
+                           const lol_path *path, void *state, size_t state_bytes, void *stream);
+
+/* Copies the decode state's flag word (LOL_FLAG_BAD_FORCED_ID,
+ * LOL_FLAG_BAD_POS) to *flags (HOST) and clears it; synchronises stream. */
+lol_status lol_decode_read_flags(void *state, uint32_t *flags, void *stream);
 
 /* ---- Around the core: token embedding and vocabulary readout ----------
  * The paper's Algorithm 1 (Appendix A) runs a causal prelude on the token

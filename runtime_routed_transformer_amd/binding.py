@@ -16,6 +16,7 @@ LOL_FP32, LOL_BF16 = 0, 1
 LOL_MLP_SWIGLU, LOL_MLP_GELU = 0, 1
 LOL_FLAG_BAD_FORCED_ID = 1
 LOL_FLAG_BAD_DOC = 2
+LOL_FLAG_BAD_POS = 4
 LOL_KERNEL_KINDS = 12
 LOL_TIMING_ALL = (1 << LOL_KERNEL_KINDS) - 1
 
@@ -69,6 +70,12 @@ _SIGNATURES.update({
     "lol_lm_head_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
     "lol_lm_head": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_float, c_void_p, c_int32,
                               c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "lol_decode_state_size": (c_size_t, [POINTER(lol_core_config)]),
+    "lol_decode_reset": (c_int32, [POINTER(lol_core_config), c_void_p, c_size_t, c_void_p]),
+    "lol_decode_step": (c_int32, [POINTER(lol_core_config), c_int32, c_void_p,
+                                  POINTER(lol_library), POINTER(lol_router), c_void_p, c_void_p,
+                                  c_void_p, POINTER(lol_path), c_void_p, c_size_t, c_void_p]),
+    "lol_decode_read_flags": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
     "lol_core_timing_collect": (c_int32, [POINTER(c_double), POINTER(c_int32)]),
     "lol_core_kernel_name": (c_char_p, [c_int32]),
     "lol_status_str": (c_char_p, [c_int32]),
@@ -141,6 +148,29 @@ def lol_core_forward_docs(cfg, n_tokens, doc_start, doc_len, s0, lib, rt, forced
 def lol_core_read_flags(workspace, stream) -> int:
     out = c_uint32(0)
     _check(load().lol_core_read_flags(workspace, ctypes.byref(out), stream), "lol_core_read_flags")
+    return int(out.value)
+
+
+def lol_decode_state_size(cfg: lol_core_config) -> int:
+    return load().lol_decode_state_size(ctypes.byref(cfg))
+
+
+def lol_decode_reset(cfg, state, state_bytes, stream) -> int:
+    return load().lol_decode_reset(ctypes.byref(cfg), state, state_bytes, stream)
+
+
+def lol_decode_step(cfg, pos, x, lib, rt, forced_expert, forced_gate, y, path, state,
+                    state_bytes, stream) -> int:
+    """One token per document: x / y are device [batch][d] fp32 addresses."""
+    return load().lol_decode_step(ctypes.byref(cfg), int(pos), x, ctypes.byref(lib),
+                                  ctypes.byref(rt), forced_expert, forced_gate, y,
+                                  ctypes.byref(path) if path is not None else None, state,
+                                  state_bytes, stream)
+
+
+def lol_decode_read_flags(state, stream) -> int:
+    out = c_uint32(0)
+    _check(load().lol_decode_read_flags(state, ctypes.byref(out), stream), "lol_decode_read_flags")
     return int(out.value)
 
 

@@ -123,3 +123,49 @@ class DeviceCore:
     def path_numpy(self):
         return (self.path_expert.cpu().numpy(), self.path_gate.cpu().numpy(),
                 self.path_margin.cpu().numpy())
+
+
+class DeviceDecoder:
+    """Incremental decode on the GPU: ``step(pos, x)`` feeds token ``pos`` of
+    every document (x: [batch][d] fp32 device tensor) through the routed
+    depths with ``lol_decode_step`` and returns s^(D) of those tokens.  The
+    library and router are those of a ``DeviceCore`` (shared device memory)."""
+
+    def __init__(self, core: DeviceCore):
+        self.core = core
+        self.cfg = core.cfg
+        self.state_bytes = B.lol_decode_state_size(core.ccfg)
+        if self.state_bytes == 0:
+            raise B.LolError(B.LOL_EUNSUPPORTED, f"decode of config {self.cfg.name}")
+        self.state = torch.empty(self.state_bytes, dtype=torch.uint8, device=core.device)
+        self.y = torch.empty((self.cfg.batch, self.cfg.d), dtype=torch.float32,
+                             device=core.device)
+        self.reset()
+
+    def _stream(self, stream):
+        return (stream or torch.cuda.current_stream(self.core.device)).cuda_stream
+
+    def reset(self, stream: Optional[torch.cuda.Stream] = None) -> None:
+        status = B.lol_decode_reset(self.core.ccfg, self.state.data_ptr(), self.state_bytes,
+                                    self._stream(stream))
+        if status != B.LOL_OK:
+            raise B.LolError(status, "lol_decode_reset")
+
+    def step(self, pos: int, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        y = self.y if y is None else y
+        for t in (x, y):
+            if (t.shape != (self.cfg.batch, self.cfg.d) or t.dtype != torch.float32
+                    or not t.is_contiguous()):
+                raise ValueError("x / y must be contiguous fp32 [batch][d]")
+        c = self.core
+        status = B.lol_decode_step(c.ccfg, pos, x.data_ptr(), c.lib, c.rt,
+                                   _ptr(c.forced_expert), _ptr(c.forced_gate), y.data_ptr(),
+                                   c.path, self.state.data_ptr(), self.state_bytes,
+                                   self._stream(stream))
+        if status != B.LOL_OK:
+            raise B.LolError(status, "lol_decode_step")
+        return y
+
+    def flags(self, stream: Optional[torch.cuda.Stream] = None) -> int:
+        return B.lol_decode_read_flags(self.state.data_ptr(), self._stream(stream))

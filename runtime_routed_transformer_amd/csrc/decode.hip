@@ -1,0 +1,698 @@
+// Incremental decode of the routed core: one new token per document per
+// call, carried through every routed depth.
+//
+// Review "Library of Layers: Routing Whole Transformer Blocks at Runtime",
+// "Deriving prefix-only routing": a window's router input depends only on
+// earlier, completed windows (window 0: the document's first token and the
+// depth vector), so its route and gate are fixed when its first token
+// arrives, and serving keeps per-depth window boundaries and summaries.
+// Blog "Library of Layers: a transformer that picks its own layer order",
+// "What it costs": attention stays inside a window, so a depth only needs
+// the open window's keys and values.
+//
+// Per depth and document the state holds: the sum of the completed
+// windows' means, the running sum and length of the open window, its expert
+// and gate, and its keys and values.  One call runs, per depth:
+//   k_dec_route   close/open windows, route a window that opens, the
+//                 attention RMSNorm + FiLM of the token  (one block per document)
+//   k_dec_gemv    QKV projection                         (grouped by expert)
+//   k_dec_attn    RoPE, cache append, attention over the open window
+//   k_dec_gemv    output projection + residual
+//   k_dec_norm    MLP RMSNorm + FiLM
+//   k_dec_gemv    gate/up + SwiGLU (or GELU)
+//   k_dec_gemv    down projection + gated blend
+// A token's rows are few (one per document), so the projections are
+// matrix-vector products bound by reading the weights once: every block
+// streams a few weight rows of one expert with 16-byte loads, and all rows
+// (documents) routed to that expert share the read.
+#include <math.h>
+
+#include "lol_internal.h"
+
+namespace lol {
+namespace {
+
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over the 256 threads of a block (red: 4 floats of LDS).
+__device__ __forceinline__ float block_sum(float v, float *red) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// out = FiLM(g * x / sqrt(mean(x^2) + eps)) over one row of d, by a block of
+// 256 threads (paper App. A RMSNorm with the depth FiLM of the review's Eq. 7).
+template <typename act_t>
+__device__ void norm_row(const float *__restrict__ x, int d, const float *__restrict__ g,
+                         const float *__restrict__ fg, const float *__restrict__ fb, float eps,
+                         act_t *__restrict__ out, float *red) {
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) ss += x[c] * x[c];
+  const float inv = rsqrtf(block_sum(ss, red) / (float)d + eps);
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float v = x[c] * inv * g[c];
+    if (fg) v = fg[c] * v + fb[c];
+    out[c] = from_f<act_t>(v);
+  }
+}
+
+__global__ void k_dec_reset(int32_t *__restrict__ hdr, int32_t *__restrict__ cur_len,
+                            int32_t *__restrict__ expert, float *__restrict__ gate, int n_state,
+                            float *__restrict__ cs, int W, int half, double theta, int use_rope) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < 2) hdr[idx] = 0;
+  if (idx < n_state) {
+    cur_len[idx] = 0;
+    expert[idx] = 0;
+    gate[idx] = 0.f;
+  }
+  if (use_rope && idx < W * half) {
+    // cos / sin of p * theta^(-2j/d_head) at window-local position p
+    const int p = idx / half, j = idx % half;
+    const double ang = (double)p * pow(theta, -2.0 * (double)j / (double)(2 * half));
+    cs[2 * idx] = (float)cos(ang);
+    cs[2 * idx + 1] = (float)sin(ang);
+  }
+}
+
+// One block per document.  At position pos of depth index `depth` the token
+// lies in window k, which starts at `start`:
+//  - if the token opens window k (pos == start), window k-1 is closed (its
+//    mean joins the prefix sum), the router input is built (the depth vector
+//    and the token for k = 0, else the mean of the k completed windows'
+//    means), the fp32 router scores it (softmax, lowest index attaining
+//    max(a + bias), gate = a of the applied expert, margin top1 - top2,
+//    forcing), and the open window's running sum restarts at the token;
+//  - else the token joins the open window's running sum;
+//  - then u = FiLM_attn(RMSNorm_e(token)) for the window's expert e.
+// The state's position counter is checked and advanced at depth 0.
+template <typename act_t>
+__global__ void __launch_bounds__(256) k_dec_route(
+    const float *__restrict__ x, int d, int L, int B, int depth, int pos, int k, int opens,
+    int K_max, int32_t *__restrict__ hdr, float *__restrict__ prefix, float *__restrict__ cur_sum,
+    int32_t *__restrict__ cur_len, int32_t *__restrict__ expert, float *__restrict__ gate,
+    const float *__restrict__ w_r, const float *__restrict__ b_r, const float *__restrict__ e_vec,
+    const float *__restrict__ bias, const int32_t *__restrict__ forced_e,
+    const float *__restrict__ forced_g, int32_t *__restrict__ path_e, float *__restrict__ path_g,
+    float *__restrict__ path_m, const float *__restrict__ g_attn, const float *__restrict__ fg,
+    const float *__restrict__ fb, int film_stride, float eps, act_t *__restrict__ u) {
+  extern __shared__ float s_r[];   // [d] router input
+  __shared__ float s_z[kMaxExperts];
+  __shared__ float red[4];
+  __shared__ int s_e;
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float *xr = x + (size_t)b * d;
+  const size_t sidx = (size_t)depth * B + b;
+  float *pre = prefix + sidx * d;
+  float *cs = cur_sum + sidx * d;
+  if (depth == 0 && b == 0 && tid == 0) {
+    if (hdr[0] != pos) atomicOr(reinterpret_cast<unsigned int *>(hdr + 1), (unsigned)LOL_FLAG_BAD_POS);
+    hdr[0] = pos + 1;
+  }
+  if (opens) {
+    const float inv_prev = 1.f / (float)max(cur_len[sidx], 1);
+    for (int c = tid; c < d; c += 256) {
+      const float xc = xr[c];
+      const float p = k > 0 ? pre[c] + cs[c] * inv_prev : 0.f;
+      pre[c] = p;
+      s_r[c] = k > 0 ? p / (float)k : 0.5f * (e_vec[c] + xc);
+      cs[c] = xc;
+    }
+    __syncthreads();
+    for (int m = wave; m < L; m += 4) {
+      const float *wm = w_r + (size_t)m * d;
+      float acc = 0.f;
+      for (int c = lane; c < d; c += 64) acc += wm[c] * s_r[c];
+      acc = wave_sum(acc);
+      if (lane == 0) s_z[m] = acc + (b_r ? b_r[m] : 0.f);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const bool live = lane < L;
+      const float zl = live ? s_z[lane] : -INFINITY;
+      const float zmax = wave_max(zl);
+      const float ez = live ? expf(zl - zmax) : 0.f;
+      const float a = ez / wave_sum(ez);
+      const float sc = live ? a + (bias ? bias[lane] : 0.f) : -INFINITY;
+      const float top = wave_max(sc);
+      const int rho = wave_min_i((live && sc == top) ? lane : 64);
+      const float second = wave_max((live && lane != rho) ? sc : -INFINITY);
+      const float margin = L > 1 ? top - second : INFINITY;
+      const size_t pidx = sidx * K_max + k;
+      int chosen = rho;
+      if (forced_e) {
+        const int fe = forced_e[pidx];
+        if (fe >= L) {
+          if (lane == 0) atomicOr(reinterpret_cast<unsigned int *>(hdr + 1), (unsigned)LOL_FLAG_BAD_FORCED_ID);
+        } else if (fe >= 0) {
+          chosen = fe;
+        }
+      }
+      float alpha = __shfl(a, chosen, 64);
+      if (forced_g) {
+        const float fgv = forced_g[pidx];
+        if (!isnan(fgv)) alpha = fgv;
+      }
+      if (lane == 0) {
+        expert[sidx] = chosen;
+        gate[sidx] = alpha;
+        cur_len[sidx] = 1;
+        if (path_e) path_e[pidx] = chosen;
+        if (path_g) path_g[pidx] = alpha;
+        if (path_m) path_m[pidx] = margin;
+        s_e = chosen;
+      }
+    }
+  } else {
+    for (int c = tid; c < d; c += 256) cs[c] += xr[c];
+    if (tid == 0) {
+      cur_len[sidx] += 1;
+      s_e = min(max(expert[sidx], 0), L - 1);
+    }
+  }
+  __syncthreads();
+  const int e = s_e;
+  norm_row<act_t>(xr, d, g_attn + (size_t)e * d, fg ? fg + (size_t)e * film_stride : nullptr,
+                  fb ? fb + (size_t)e * film_stride : nullptr, eps, u + (size_t)b * d, red);
+}
+
+// u = FiLM_ffn(RMSNorm_e(h)) of every document's token, one block each.
+template <typename act_t>
+__global__ void __launch_bounds__(256) k_dec_norm(const float *__restrict__ h, int d, int L,
+                                                  const int32_t *__restrict__ expert,
+                                                  const float *__restrict__ g_ffn,
+                                                  const float *__restrict__ fg,
+                                                  const float *__restrict__ fb, int film_stride,
+                                                  float eps, act_t *__restrict__ u) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const int e = min(max(expert[b], 0), L - 1);
+  norm_row<act_t>(h + (size_t)b * d, d, g_ffn + (size_t)e * d,
+                  fg ? fg + (size_t)e * film_stride : nullptr,
+                  fb ? fb + (size_t)e * film_stride : nullptr, eps, u + (size_t)b * d, red);
+}
+
+// Sum of the NV x MR values of each lane over the 64 lanes of a wave: every
+// exchange step halves the values a lane carries (the partner keeps the
+// other half), then plain butterflies finish.  Afterwards a lane holds the
+// total of value index lane >> (6 - log2 N), N = NV MR a power of two <= 64.
+template <int N>
+__device__ __forceinline__ float wave_reduce_many(float (&v)[N], int lane) {
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    const int o = 32 >> s;
+    if ((N >> s) > 1) {
+      const int n2 = (N >> s) / 2;
+      const bool hi = (lane & o) != 0;
+#pragma unroll
+      for (int i = 0; i < n2; ++i) {
+        const float send = hi ? v[i] : v[i + n2];
+        const float keep = hi ? v[i + n2] : v[i];
+        v[i] = keep + __shfl_xor(send, o, 64);
+      }
+    } else {
+      v[0] += __shfl_xor(v[0], o, 64);
+    }
+  }
+  return v[0];
+}
+
+template <int N> struct Log2 { static constexpr int v = 1 + Log2<N / 2>::v; };
+template <> struct Log2<1> { static constexpr int v = 0; };
+
+// 16 bytes of weights or activations
+template <typename wt> struct Vec16;
+template <> struct Vec16<bf16_t> {
+  uint4 v;
+  __device__ __forceinline__ float dot(const Vec16 &a, float acc) const {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.x),
+                                          __builtin_bit_cast(bf16x2_t, a.v.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.y),
+                                          __builtin_bit_cast(bf16x2_t, a.v.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.z),
+                                          __builtin_bit_cast(bf16x2_t, a.v.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.w),
+                                          __builtin_bit_cast(bf16x2_t, a.v.w), acc, false);
+    return acc;
+  }
+};
+template <> struct Vec16<float> {
+  float4 v;
+  __device__ __forceinline__ float dot(const Vec16 &a, float acc) const {
+    acc = fmaf(v.x, a.v.x, acc);
+    acc = fmaf(v.y, a.v.y, acc);
+    acc = fmaf(v.z, a.v.z, acc);
+    return fmaf(v.w, a.v.w, acc);
+  }
+};
+template <typename wt> __device__ __forceinline__ Vec16<wt> ld16(const wt *p) {
+  Vec16<wt> r;
+  r.v = *reinterpret_cast<const decltype(r.v) *>(p);
+  return r;
+}
+template <typename wt> __device__ __forceinline__ Vec16<wt> zero16() {
+  Vec16<wt> r;
+  r.v = {};
+  return r;
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+__device__ __forceinline__ float gelu_erf(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+struct DecGemv {
+  const void *A;            // [B][K] act: the documents' inputs
+  const void *W;            // [L][rows][K] weights (act type)
+  long long w_estride;      // elements between experts
+  int K;
+  int n_cols;               // output columns (SwiGLU: f; the up rows start at glu_off)
+  int glu_off;
+  int B, L;
+  const int32_t *expert;    // [B] this depth's expert of each document
+  const float *gate;        // [B]
+  const float *x;           // [B][n_cols] depth input (RESID, BLEND)
+  const float *h;           // [B][n_cols] (BLEND)
+  float *out;               // [B][n_cols] fp32 (STORE, RESID, BLEND; may equal x)
+  void *out_act;            // [B][n_cols] act (SWIGLU, GELU)
+};
+
+enum DecEpi { DEC_STORE = 0, DEC_RESID = 1, DEC_SWIGLU = 2, DEC_GELU = 3, DEC_BLEND = 4 };
+
+// Grouped matrix-vector products of one depth.  blockIdx.y = g picks the
+// g-th distinct expert among the documents (in order of first appearance);
+// blocks of a g past the distinct count exit.  Each of the 4 waves owns CPW
+// output columns (2 CPW weight rows with SwiGLU: gate row c and up row
+// glu_off + c) and reads them whole, 64 lanes x 16 bytes per load; the
+// documents of the group (up to MR at a time) are staged in LDS in chunks of
+// KC inputs and share every weight load.
+template <typename wt, int CPW, int EPI>
+__global__ void __launch_bounds__(256) k_dec_gemv(DecGemv a) {
+  constexpr int VEC = 16 / (int)sizeof(wt);
+  constexpr int STEP = 64 * VEC;           // inputs one wave load covers
+  constexpr int NT = 4;                    // loads per lane per chunk
+  constexpr int KC = NT * STEP;            // inputs staged per chunk
+  constexpr int MR = 8;                    // documents per pass
+  constexpr bool GLU = EPI == DEC_SWIGLU;
+  constexpr int NV = GLU ? 2 * CPW : CPW;  // weight rows per wave
+  constexpr int NR = NV * MR;              // sums per lane
+  __shared__ Vec16<wt> s_a[MR * (KC / VEC)];
+  __shared__ float s_res[4][NV][MR];
+  __shared__ int s_rows[64];
+  __shared__ int s_info[2];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  if (wave == 0) {
+    int el = lane < a.B ? min(max(a.expert[lane], 0), a.L - 1) : -1;
+    bool dup = false;
+    for (int j = 0; j < a.B; ++j) {
+      const int ej = __shfl(el, j, 64);
+      if (j < lane && ej == el) dup = true;
+    }
+    const unsigned long long first = __ballot(lane < a.B && !dup);
+    const int g = blockIdx.y;
+    if (__popcll(first) <= g) {
+      if (lane == 0) s_info[0] = 0;
+    } else {
+      unsigned long long mm = first;
+      for (int i = 0; i < g; ++i) mm &= mm - 1;
+      const int leader = __ffsll((long long)mm) - 1;
+      const int e = __shfl(el, leader, 64);
+      const bool mine = lane < a.B && el == e;
+      const unsigned long long rm = __ballot(mine);
+      if (mine) s_rows[__popcll(rm & ((1ull << lane) - 1ull))] = lane;
+      if (lane == 0) {
+        s_info[0] = __popcll(rm);
+        s_info[1] = e;
+      }
+    }
+  }
+  __syncthreads();
+  const int m = s_info[0];
+  if (m == 0) return;
+  const int e = s_info[1];
+  const int K = a.K;
+  const wt *We = static_cast<const wt *>(a.W) + (size_t)e * a.w_estride;
+  const wt *A = static_cast<const wt *>(a.A);
+  const int col_blk = blockIdx.x * 4 * CPW;
+  const wt *wrow[NV];
+  bool wok[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int j = GLU ? v / 2 : v;
+    const int c = col_blk + wave * CPW + j;
+    wok[v] = c < a.n_cols;
+    const int r = (GLU && (v & 1)) ? a.glu_off + c : c;
+    wrow[v] = We + (size_t)(wok[v] ? r : 0) * K;
+  }
+
+  for (int r0 = 0; r0 < m; r0 += MR) {
+    const int mr = min(MR, m - r0);
+    float acc[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) acc[i] = 0.f;
+    for (int kc0 = 0; kc0 < K; kc0 += KC) {
+      const int kcl = min(KC, K - kc0);
+      __syncthreads();   // the previous chunk (and pass) is consumed
+      for (int i = tid; i < mr * (KC / VEC); i += 256) {
+        const int r = i / (KC / VEC), q = i % (KC / VEC);
+        if (q * VEC < kcl) s_a[i] = ld16<wt>(A + (size_t)s_rows[r0 + r] * K + kc0 + q * VEC);
+      }
+      __syncthreads();
+      // every weight load of the chunk is issued before the products
+      Vec16<wt> w[NT][NV];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int kl = t * STEP + lane * VEC;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          w[t][v] = (wok[v] && kl < kcl) ? ld16<wt>(wrow[v] + kc0 + kl) : zero16<wt>();
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int kl = t * STEP + lane * VEC;
+        if (kl >= kcl) continue;
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+          if (r >= mr) break;
+          const Vec16<wt> av = s_a[r * (KC / VEC) + kl / VEC];
+#pragma unroll
+          for (int v = 0; v < NV; ++v) acc[v * MR + r] = w[t][v].dot(av, acc[v * MR + r]);
+        }
+      }
+    }
+    const float tot = wave_reduce_many<NR>(acc, lane);
+    constexpr int SH = 6 - Log2<NR>::v;
+    if ((lane & ((1 << SH) - 1)) == 0) {
+      const int idx = lane >> SH;
+      s_res[wave][idx / MR][idx % MR] = tot;
+    }
+    __syncthreads();
+    for (int i = tid; i < 4 * CPW * MR; i += 256) {
+      const int r = i % MR, cj = i / MR;
+      const int wv = cj / CPW, j = cj % CPW;
+      const int c = col_blk + cj;
+      if (r >= mr || c >= a.n_cols) continue;
+      const int row = s_rows[r0 + r];
+      const size_t o = (size_t)row * a.n_cols + c;
+      const float v0 = s_res[wv][GLU ? 2 * j : j][r];
+      if (EPI == DEC_STORE) {
+        a.out[o] = v0;
+      } else if (EPI == DEC_RESID) {
+        a.out[o] = a.x[o] + v0;
+      } else if (EPI == DEC_SWIGLU) {
+        const float up = s_res[wv][2 * j + 1][r];
+        static_cast<wt *>(a.out_act)[o] = from_f<wt>(silu(v0) * up);
+      } else if (EPI == DEC_GELU) {
+        static_cast<wt *>(a.out_act)[o] = from_f<wt>(gelu_erf(v0));
+      } else {
+        const float xv = a.x[o];
+        const float y = a.h[o] + v0;
+        a.out[o] = xv + a.gate[row] * (y - xv);
+      }
+    }
+  }
+}
+
+// Attention of every document's token (block x = document, y = head, one
+// wave) over the open window of one depth: q and k of the token are rotated
+// at its window-local position p (RoPE, rotate-half pairs), rounded to the
+// operand type, k and v are appended to the cache at slot p, and the token
+// attends to slots 0..p (paper Sec. 3.2.1: causal inside the window; review
+// Eq. 1: scores scaled by 1/sqrt(d_head)).
+template <typename act_t, int DH>
+__global__ void __launch_bounds__(64) k_dec_attn(const float *__restrict__ qkv,
+                                                 act_t *__restrict__ kc, act_t *__restrict__ vc,
+                                                 act_t *__restrict__ o,
+                                                 const float *__restrict__ rope_cs, int d, int H,
+                                                 int W, int p, float scale, int use_rope) {
+  extern __shared__ float s_p[];   // [p + 1] scores, then weights
+  __shared__ float s_q[DH], s_k[DH], s_v[DH];
+  constexpr int HALF = DH / 2;
+  const int b = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const float *qr = qkv + (size_t)b * 3 * d + h * DH;
+  const size_t cbase = ((size_t)b * H + h) * W * DH;
+  act_t *kcache = kc + cbase, *vcache = vc + cbase;
+  if (lane < DH) {
+    float q = qr[lane], k = qr[d + lane];
+    const float v = qr[2 * d + lane];
+    if (use_rope) {
+      const int j = lane % HALF;
+      const float c = rope_cs[((size_t)p * HALF + j) * 2], s = rope_cs[((size_t)p * HALF + j) * 2 + 1];
+      const int partner = lane < HALF ? lane + HALF : lane - HALF;
+      const float qp = qr[partner], kp = qr[d + partner];
+      q = lane < HALF ? q * c - qp * s : q * c + qp * s;
+      k = lane < HALF ? k * c - kp * s : k * c + kp * s;
+    }
+    const act_t qa = from_f<act_t>(q), ka = from_f<act_t>(k), va = from_f<act_t>(v);
+    s_q[lane] = to_f<act_t>(qa);
+    s_k[lane] = to_f<act_t>(ka);
+    s_v[lane] = to_f<act_t>(va);
+    kcache[(size_t)p * DH + lane] = ka;
+    vcache[(size_t)p * DH + lane] = va;
+  }
+  __syncthreads();
+  float mloc = -INFINITY;
+  for (int j = lane; j <= p; j += 64) {
+    float sc = 0.f;
+    if (j == p) {
+#pragma unroll
+      for (int t = 0; t < DH; ++t) sc += s_q[t] * s_k[t];
+    } else {
+      const act_t *kr = kcache + (size_t)j * DH;
+#pragma unroll
+      for (int t = 0; t < DH; ++t) sc += s_q[t] * to_f<act_t>(kr[t]);
+    }
+    sc *= scale;
+    s_p[j] = sc;
+    mloc = fmaxf(mloc, sc);
+  }
+  const float mx = wave_max(mloc);
+  float lsum = 0.f;
+  for (int j = lane; j <= p; j += 64) {
+    const float w = expf(s_p[j] - mx);
+    s_p[j] = w;
+    lsum += w;
+  }
+  const float inv = 1.f / wave_sum(lsum);
+  __syncthreads();
+  if (lane < DH) {
+    float acc = s_p[p] * s_v[lane];
+    int j = 0;
+    for (; j + 4 <= p; j += 4) {
+      const float v0 = to_f<act_t>(vcache[(size_t)j * DH + lane]);
+      const float v1 = to_f<act_t>(vcache[(size_t)(j + 1) * DH + lane]);
+      const float v2 = to_f<act_t>(vcache[(size_t)(j + 2) * DH + lane]);
+      const float v3 = to_f<act_t>(vcache[(size_t)(j + 3) * DH + lane]);
+      acc += s_p[j] * v0 + s_p[j + 1] * v1 + s_p[j + 2] * v2 + s_p[j + 3] * v3;
+    }
+    for (; j < p; ++j) acc += s_p[j] * to_f<act_t>(vcache[(size_t)j * DH + lane]);
+    o[(size_t)b * d + h * DH + lane] = from_f<act_t>(acc * inv);
+  }
+}
+
+template <typename wt, int CPW, int EPI>
+hipError_t gemv_launch(const DecGemv &a, hipStream_t st) {
+  const int cols = 4 * CPW;
+  dim3 grid((a.n_cols + cols - 1) / cols, min(a.B, a.L));
+  lol_launch(k_dec_gemv<wt, CPW, EPI>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename wt>
+hipError_t gemv_typed(const DecGemv &a, int which, bool glu, hipStream_t st) {
+  switch (which) {
+    case DEC_QKV: return gemv_launch<wt, 2, DEC_STORE>(a, st);
+    case DEC_O: return gemv_launch<wt, 1, DEC_RESID>(a, st);
+    case DEC_GU:
+      return glu ? gemv_launch<wt, 1, DEC_SWIGLU>(a, st) : gemv_launch<wt, 2, DEC_GELU>(a, st);
+    default: return gemv_launch<wt, 1, DEC_BLEND>(a, st);
+  }
+}
+
+template <typename act_t>
+hipError_t attn_launch(const lol_core_config &c, const DecodeBufs &s, int depth, int p,
+                       hipStream_t st) {
+  const int dh = c.d / c.n_heads;
+  const size_t per_depth = (size_t)c.batch * c.n_heads * c.W * dh;
+  act_t *kc = static_cast<act_t *>(s.kc) + (size_t)depth * per_depth;
+  act_t *vc = static_cast<act_t *>(s.vc) + (size_t)depth * per_depth;
+  const float scale = 1.0f / sqrtf((float)dh);
+  const int use_rope = c.rope_theta != 0.f ? 1 : 0;
+  dim3 grid(c.batch, c.n_heads);
+  const uint32_t shm = (uint32_t)(p + 1) * sizeof(float);
+  if (dh == 64)
+    lol_launch(k_dec_attn<act_t, 64>, grid, dim3(64), shm, st, s.qkv, kc, vc,
+               static_cast<act_t *>(s.o), s.rope_cs, c.d, c.n_heads, c.W, p, scale, use_rope);
+  else
+    lol_launch(k_dec_attn<act_t, 32>, grid, dim3(64), shm, st, s.qkv, kc, vc,
+               static_cast<act_t *>(s.o), s.rope_cs, c.d, c.n_heads, c.W, p, scale, use_rope);
+  return hipGetLastError();
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+bool decode_supported(const lol_core_config &c) {
+  return c.batch <= 64 && c.d <= 4096 && c.W <= 8192;
+}
+
+size_t decode_layout(const lol_core_config &c, char *base, DecodeBufs *out) {
+  const size_t B = c.batch, d = c.d, f = c.d_ffn, D = c.D;
+  const size_t act = c.dtype == LOL_BF16 ? 2 : 4;
+  const size_t dh = d / c.n_heads;
+  size_t off = 0;
+  auto carve = [&](size_t bytes) -> char * {
+    char *ptr = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return ptr;
+  };
+  DecodeBufs s;
+  s.hdr = (int32_t *)carve(2 * 4);
+  s.prefix = (float *)carve(D * B * d * 4);
+  s.cur_sum = (float *)carve(D * B * d * 4);
+  s.cur_len = (int32_t *)carve(D * B * 4);
+  s.expert = (int32_t *)carve(D * B * 4);
+  s.gate = (float *)carve(D * B * 4);
+  s.kc = carve(D * B * c.n_heads * (size_t)c.W * dh * act);
+  s.vc = carve(D * B * c.n_heads * (size_t)c.W * dh * act);
+  s.rope_cs = (float *)carve((size_t)c.W * (dh / 2) * 2 * 4);
+  s.u = carve(B * d * act);
+  s.qkv = (float *)carve(B * 3 * d * 4);
+  s.o = carve(B * d * act);
+  s.h = (float *)carve(B * d * 4);
+  s.hid = carve(B * f * act);
+  if (out) *out = s;
+  return off;
+}
+
+hipError_t launch_dec_reset(const lol_core_config &c, const DecodeBufs &s, hipStream_t st) {
+  const int half = c.d / c.n_heads / 2;
+  const int n_state = c.D * c.batch;
+  const int total = max(max(n_state, c.W * half), 2);
+  lol_launch(k_dec_reset, dim3((total + 255) / 256), dim3(256), 0, st, s.hdr, s.cur_len, s.expert,
+             s.gate, n_state, s.rope_cs, c.W, half, (double)c.rope_theta,
+             c.rope_theta != 0.f ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_route(const lol_core_config &c, const DecodeBufs &s, int depth, int pos,
+                            int k, int opens, const float *x, const lol_library &lib,
+                            const lol_router &rt, const int32_t *forced_e, const float *forced_g,
+                            const lol_path *path, hipStream_t st) {
+  const int d = c.d, L = c.L;
+  const int K_max = (c.n + c.W - 1) / c.W + 1;
+  const float *w_r = rt.w_r + (rt.per_depth ? (size_t)depth * L * d : 0);
+  const float *b_r = rt.b_r ? rt.b_r + (rt.per_depth ? (size_t)depth * L : 0) : nullptr;
+  const size_t film_off = ((size_t)depth * (lib.film_per_expert ? L : 1) * 2 + 0) * d;
+  const float *fg = lib.film_gamma ? lib.film_gamma + film_off : nullptr;
+  const float *fb = lib.film_beta ? lib.film_beta + film_off : nullptr;
+  const int film_stride = lib.film_per_expert ? 2 * d : 0;
+  const uint32_t shm = (uint32_t)d * sizeof(float);
+  int32_t *pe = path ? path->expert : nullptr;
+  float *pg = path ? path->gate : nullptr, *pm = path ? path->margin : nullptr;
+  if (c.dtype == LOL_BF16)
+    lol_launch(k_dec_route<bf16_t>, dim3(c.batch), dim3(256), shm, st, x, d, L, c.batch, depth,
+               pos, k, opens, K_max, s.hdr, s.prefix, s.cur_sum, s.cur_len, s.expert, s.gate, w_r,
+               b_r, rt.e_depth + (size_t)depth * d, rt.expert_bias, forced_e, forced_g, pe, pg, pm,
+               lib.g_attn, fg, fb, film_stride, c.rms_eps, static_cast<bf16_t *>(s.u));
+  else
+    lol_launch(k_dec_route<float>, dim3(c.batch), dim3(256), shm, st, x, d, L, c.batch, depth,
+               pos, k, opens, K_max, s.hdr, s.prefix, s.cur_sum, s.cur_len, s.expert, s.gate, w_r,
+               b_r, rt.e_depth + (size_t)depth * d, rt.expert_bias, forced_e, forced_g, pe, pg, pm,
+               lib.g_attn, fg, fb, film_stride, c.rms_eps, static_cast<float *>(s.u));
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_norm(const lol_core_config &c, const DecodeBufs &s, int depth,
+                           const lol_library &lib, hipStream_t st) {
+  const int d = c.d, L = c.L;
+  const size_t film_off = ((size_t)depth * (lib.film_per_expert ? L : 1) * 2 + 1) * d;
+  const float *fg = lib.film_gamma ? lib.film_gamma + film_off : nullptr;
+  const float *fb = lib.film_beta ? lib.film_beta + film_off : nullptr;
+  const int film_stride = lib.film_per_expert ? 2 * d : 0;
+  const int32_t *ex = s.expert + (size_t)depth * c.batch;
+  if (c.dtype == LOL_BF16)
+    lol_launch(k_dec_norm<bf16_t>, dim3(c.batch), dim3(256), 0, st, s.h, d, L, ex, lib.g_ffn, fg,
+               fb, film_stride, c.rms_eps, static_cast<bf16_t *>(s.u));
+  else
+    lol_launch(k_dec_norm<float>, dim3(c.batch), dim3(256), 0, st, s.h, d, L, ex, lib.g_ffn, fg,
+               fb, film_stride, c.rms_eps, static_cast<float *>(s.u));
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_attn(const lol_core_config &c, const DecodeBufs &s, int depth, int p,
+                           hipStream_t st) {
+  if (p < 0 || p >= c.W) return hipErrorInvalidValue;
+  if (c.dtype == LOL_BF16) return attn_launch<bf16_t>(c, s, depth, p, st);
+  return attn_launch<float>(c, s, depth, p, st);
+}
+
+hipError_t launch_dec_gemv(const lol_core_config &c, const DecodeBufs &s, int depth, int which,
+                           const float *x, float *y, const lol_library &lib, hipStream_t st) {
+  const size_t d = c.d, f = c.d_ffn;
+  const bool glu = c.mlp == LOL_MLP_SWIGLU;
+  DecGemv a{};
+  a.B = c.batch;
+  a.L = c.L;
+  a.expert = s.expert + (size_t)depth * c.batch;
+  a.gate = s.gate + (size_t)depth * c.batch;
+  switch (which) {
+    case DEC_QKV:
+      a.A = s.u; a.W = lib.wqkv; a.w_estride = (long long)(3 * d * d); a.K = (int)d;
+      a.n_cols = (int)(3 * d); a.out = s.qkv;
+      break;
+    case DEC_O:
+      a.A = s.o; a.W = lib.wo; a.w_estride = (long long)(d * d); a.K = (int)d;
+      a.n_cols = (int)d; a.x = x; a.out = s.h;
+      break;
+    case DEC_GU:
+      a.A = s.u; a.W = lib.w_gu; a.w_estride = (long long)((glu ? 2 : 1) * f * d); a.K = (int)d;
+      a.n_cols = (int)f; a.glu_off = (int)f; a.out_act = s.hid;
+      break;
+    case DEC_DOWN:
+      a.A = s.hid; a.W = lib.w_down; a.w_estride = (long long)(d * f); a.K = (int)f;
+      a.n_cols = (int)d; a.x = x; a.h = s.h; a.out = y;
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  if (c.dtype == LOL_BF16) return gemv_typed<bf16_t>(a, which, glu, st);
+  return gemv_typed<float>(a, which, glu, st);
+}
+
+}  // namespace lol

@@ -373,6 +373,94 @@ lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
   return LOL_OK;
 }
 
+size_t lol_decode_state_size(const lol_core_config *cfg) {
+  if (validate(cfg) != LOL_OK || !decode_supported(*cfg)) return 0;
+  return decode_layout(*cfg, nullptr, nullptr);
+}
+
+lol_status lol_decode_reset(const lol_core_config *cfg, void *state, size_t state_bytes,
+                            void *stream) {
+  const lol_status vs = validate(cfg);
+  if (vs != LOL_OK) return vs;
+  if (!decode_supported(*cfg)) return LOL_EUNSUPPORTED;
+  if (!state || state_bytes < decode_layout(*cfg, nullptr, nullptr) ||
+      (reinterpret_cast<uintptr_t>(state) & 255))
+    return LOL_EWORKSPACE;
+  DecodeBufs s;
+  decode_layout(*cfg, static_cast<char *>(state), &s);
+  if (launch_dec_reset(*cfg, s, static_cast<hipStream_t>(stream)) != hipSuccess) return LOL_EHIP;
+  return LOL_OK;
+}
+
+lol_status lol_decode_step(const lol_core_config *cfg, int32_t pos, const float *x,
+                           const lol_library *lib, const lol_router *rt,
+                           const int32_t *forced_expert, const float *forced_gate, float *y,
+                           const lol_path *path, void *state, size_t state_bytes, void *stream) {
+  const lol_status vs = validate(cfg);
+  if (vs != LOL_OK) return vs;
+  if (!decode_supported(*cfg)) return LOL_EUNSUPPORTED;
+  if (!x || !y || !lib || !rt) return LOL_EINVAL;
+  if (!lib->wqkv || !lib->wo || !lib->w_gu || !lib->w_down || !lib->g_attn || !lib->g_ffn)
+    return LOL_EINVAL;
+  if ((lib->film_gamma == nullptr) != (lib->film_beta == nullptr)) return LOL_EINVAL;
+  if (!rt->w_r || !rt->e_depth) return LOL_EINVAL;
+  if ((rt->per_depth != 0 && rt->per_depth != 1) || (lib->film_per_expert != 0 && lib->film_per_expert != 1))
+    return LOL_EINVAL;
+  if (pos < 0 || pos >= cfg->n) return LOL_EINVAL;
+  if (!state || state_bytes < decode_layout(*cfg, nullptr, nullptr) ||
+      (reinterpret_cast<uintptr_t>(state) & 255))
+    return LOL_EWORKSPACE;
+  DecodeBufs s;
+  decode_layout(*cfg, static_cast<char *>(state), &s);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t timing;
+  int32_t timing_depth;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    timing = g_timing;
+    timing_depth = g_timing_depth;
+  }
+  const lol_core_config &c = *cfg;
+  int cur_depth = -1;
+  hipError_t err;
+#define LOL_TRY(kind, call)                           \
+  do {                                                \
+    Launch _l(st, ((timing >> (kind)) & 1u) && (timing_depth < 0 || timing_depth == cur_depth), kind); \
+    err = _l.done(call);                              \
+    if (err != hipSuccess) return LOL_EHIP;           \
+  } while (0)
+  for (int l = 0; l < c.D; ++l) {
+    cur_depth = l;
+    // the token's window at this depth (partition with offset ((l-1) S) mod W)
+    const int delta = (int)(((long long)l * c.S) % c.W);
+    const int k = (pos + delta) / c.W;
+    const int start = k * c.W - delta > 0 ? k * c.W - delta : 0;
+    const float *xin = l == 0 ? x : y;   // depth input; y holds s^(l) afterwards
+    LOL_TRY(KK_ROUTE, launch_dec_route(c, s, l, pos, k, pos == start ? 1 : 0, xin, *lib, *rt,
+                                       forced_expert, forced_gate, path, st));
+    LOL_TRY(KK_GEMM_QKV, launch_dec_gemv(c, s, l, DEC_QKV, xin, y, *lib, st));
+    LOL_TRY(KK_ATTN, launch_dec_attn(c, s, l, pos - start, st));
+    LOL_TRY(KK_GEMM_O, launch_dec_gemv(c, s, l, DEC_O, xin, y, *lib, st));
+    LOL_TRY(KK_NORM_FFN, launch_dec_norm(c, s, l, *lib, st));
+    LOL_TRY(KK_GEMM_GATE_UP, launch_dec_gemv(c, s, l, DEC_GU, xin, y, *lib, st));
+    LOL_TRY(KK_GEMM_DOWN, launch_dec_gemv(c, s, l, DEC_DOWN, xin, y, *lib, st));
+  }
+#undef LOL_TRY
+  return LOL_OK;
+}
+
+lol_status lol_decode_read_flags(void *state, uint32_t *flags, void *stream) {
+  if (!state || !flags) return LOL_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t *dflags = static_cast<uint32_t *>(state) + 1;  // header word 1
+  if (hipMemcpyAsync(flags, dflags, sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return LOL_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return LOL_EHIP;
+  if (hipMemsetAsync(dflags, 0, sizeof(uint32_t), st) != hipSuccess) return LOL_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return LOL_EHIP;
+  return LOL_OK;
+}
+
 lol_status lol_core_read_flags(void *workspace, uint32_t *flags, void *stream) {
   if (!workspace || !flags) return LOL_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -169,4 +169,45 @@ hipError_t launch_pack_wo(const Plan &p, const Workspace &ws, const lol_library 
 hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws, const float *s_in,
                          float *s, const lol_library &lib, int u_panel_rows, hipStream_t st);
 
+// ---- incremental decode (one token per document per call) ----
+// Device buffers carved from the caller's decode state.
+struct DecodeBufs {
+  int32_t *hdr;        // [0] the position the next call must bring, [1] flags
+  float *prefix;       // [D][B][d]  sum of the completed windows' means
+  float *cur_sum;      // [D][B][d]  sum of the open window's depth inputs
+  int32_t *cur_len;    // [D][B]     tokens in the open window
+  int32_t *expert;     // [D][B]     route of the open window
+  float *gate;         // [D][B]
+  void *kc, *vc;       // [D][B][H][W][d_head] act: keys (rotated) and values of the open window
+  float *rope_cs;      // [W][d_head/2][2]
+  void *u;             // [B][d]   act   normed input of QKV, then of gate/up
+  float *qkv;          // [B][3d]  fp32  projections before RoPE
+  void *o;             // [B][d]   act   attention output
+  float *h;            // [B][d]   fp32  after the attention sublayer
+  void *hid;           // [B][f]   act   MLP hidden
+};
+enum DecodeProj { DEC_QKV = 0, DEC_O = 1, DEC_GU = 2, DEC_DOWN = 3 };
+// sizes the decode kernels handle (on top of a valid config): batch <= 64,
+// d <= 4096, W <= 8192
+bool decode_supported(const lol_core_config &c);
+size_t decode_layout(const lol_core_config &c, char *base, DecodeBufs *s);
+// position counter and flags to 0, window routes to expert 0, RoPE table
+hipError_t launch_dec_reset(const lol_core_config &c, const DecodeBufs &s, hipStream_t st);
+// window bookkeeping and routing of depth index `depth` for the token at
+// `pos` (in window k; opens = it is the window's first token), then the
+// attention norm into s.u
+hipError_t launch_dec_route(const lol_core_config &c, const DecodeBufs &s, int depth, int pos,
+                            int k, int opens, const float *x, const lol_library &lib,
+                            const lol_router &rt, const int32_t *forced_e, const float *forced_g,
+                            const lol_path *path, hipStream_t st);
+// MLP norm of s.h into s.u
+hipError_t launch_dec_norm(const lol_core_config &c, const DecodeBufs &s, int depth,
+                           const lol_library &lib, hipStream_t st);
+// attention at window-local position p (0 <= p < W)
+hipError_t launch_dec_attn(const lol_core_config &c, const DecodeBufs &s, int depth, int p,
+                           hipStream_t st);
+// one projection (DecodeProj) grouped by expert; x = depth input, y = depth output
+hipError_t launch_dec_gemv(const lol_core_config &c, const DecodeBufs &s, int depth, int which,
+                           const float *x, float *y, const lol_library &lib, hipStream_t st);
+
 }  // namespace lol

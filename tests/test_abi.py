@@ -145,3 +145,39 @@ def test_embedding_and_readout_reject_bad_arguments(lib):
     assert lib.lol_embed(16, 4, 16, 10, 62, B.LOL_FP32, 16, None) == B.LOL_EINVAL
     assert lib.lol_embed(16, 0, 16, 10, 64, B.LOL_FP32, 16, None) == B.LOL_EINVAL
     assert lib.lol_embed(16, 4, 16, 10, 64, 5, 16, None) == B.LOL_EINVAL
+
+
+def test_decode_sizes_and_host_checks(lib):
+    # decode state sizes, supported range and host-side rejections (no launch)
+    for cfg in CONFIGS:
+        c = make_config(cfg)
+        size = B.lol_decode_state_size(c)
+        # keys and values of one open window per depth, document and head dominate
+        act = 2 if cfg.dtype == "bf16" else 4
+        assert size >= 2 * cfg.D * cfg.batch * cfg.W * cfg.d * act, cfg.name
+    c = make_config(CONFIG_BY_NAME["small_bf16"]); c.batch = 65
+    assert B.lol_decode_state_size(c) == 0
+    c = make_config(CONFIG_BY_NAME["small_bf16"]); c.W = 0
+    assert B.lol_decode_state_size(c) == 0
+    c = make_config(CONFIG_BY_NAME["tiny_fp32"])
+    size = B.lol_decode_state_size(c)
+    libw = B.lol_library(wqkv=16, wo=16, w_gu=16, w_down=16, g_attn=16, g_ffn=16)
+    rt = B.lol_router(w_r=16, e_depth=16)
+
+    def step(pos=0, x=16, y=16, state=256, nbytes=size, libx=libw, rtx=rt):
+        return B.lol_decode_step(c, pos, x, libx, rtx, None, None, y, None, state, nbytes, None)
+    assert step(x=None) == B.LOL_EINVAL
+    assert step(y=None) == B.LOL_EINVAL
+    assert step(pos=-1) == B.LOL_EINVAL
+    assert step(pos=c.n) == B.LOL_EINVAL
+    assert step(nbytes=size - 1) == B.LOL_EWORKSPACE
+    assert step(state=None) == B.LOL_EWORKSPACE
+    assert step(state=256 + 16) == B.LOL_EWORKSPACE       # not 256-byte aligned
+    assert step(libx=B.lol_library(wqkv=16, wo=16, w_gu=16, w_down=None, g_attn=16,
+                                   g_ffn=16)) == B.LOL_EINVAL
+    assert step(rtx=B.lol_router(w_r=16, e_depth=16, per_depth=3)) == B.LOL_EINVAL
+    assert B.lol_decode_reset(c, None, size, None) == B.LOL_EWORKSPACE
+    assert B.lol_decode_reset(c, 256, size - 1, None) == B.LOL_EWORKSPACE
+    big = make_config(CONFIG_BY_NAME["tiny_fp32"]); big.d = 8192; big.n_heads = 128
+    assert B.lol_decode_reset(big, 256, 1 << 40, None) == B.LOL_EUNSUPPORTED
+    assert lib.lol_decode_read_flags(None, None, None) == B.LOL_EINVAL

@@ -1,0 +1,157 @@
+"""GPU parity of incremental decode (lol_decode_step): documents fed one
+token at a time through the routed depths, against the oracle.
+
+The oracle side is ``oracle.decode`` for the small cases and
+``oracle.forward`` on the same document prefix for the larger ones (the
+CPU pins show the two agree to 1e-11: a window's route is fixed when it
+opens, review "Deriving prefix-only routing").  As in the forward's parity,
+windows whose top-1 margin is at most 1e-3 are forced to the oracle's
+choice; ids must match on every other window, and s^(D) of every token must
+agree to the mode's tolerance.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from runtime_routed_transformer_amd.workloads import CONFIG_BY_NAME, CoreConfig
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _decode_gpu(inp, forced_expert, forced_gate, n_tokens, in_place=False):
+    import torch
+    from runtime_routed_transformer_amd.core import DeviceCore, DeviceDecoder
+
+    core = DeviceCore(inp)
+    core.set_forcing(forced_expert=forced_expert, forced_gate=forced_gate)
+    core.path_expert.fill_(-7)
+    dec = DeviceDecoder(core)
+    out = torch.empty((inp.cfg.batch, n_tokens, inp.cfg.d), dtype=torch.float32, device=core.device)
+    for pos in range(n_tokens):
+        x = core.s0[:, pos].contiguous()
+        y = dec.step(pos, x, y=x if in_place else None)
+        out[:, pos] = y
+    torch.cuda.synchronize(core.device)
+    flags = dec.flags()
+    return out.cpu().numpy(), core.path_numpy(), flags
+
+
+def _check(inp, n_tokens, use_decode_oracle, forced_gate=None, in_place=False):
+    cfg = inp.cfg
+    rows = list(range(cfg.batch))
+    if use_decode_oracle:
+        ref = oracle.decode(inp, n_tokens, forced_expert=inp.forced_expert, forced_gate=forced_gate)
+    else:
+        ref = oracle.forward(inp, forced_expert=inp.forced_expert, forced_gate=forced_gate,
+                             n_tokens=n_tokens)
+    forced, compared = parity.forced_for_gpu(inp, ref, rows, n_tokens)
+    s_gpu, (pe, pg, pm), flags = _decode_gpu(inp, forced, forced_gate, n_tokens, in_place)
+    s_ref = ref.s64
+    s0 = inp.s0[:, :n_tokens].astype(np.float64)
+    rel = float(np.abs(s_gpu - s_ref).max() / np.abs(s_ref).max())
+    upd = float(np.abs((s_gpu - s0) - (s_ref - s0)).max() / np.abs(s_ref - s0).max())
+    free_cmp = compared & (ref.margin > parity.MARGIN)
+    if inp.forced_expert is not None:
+        free_cmp &= inp.forced_expert < 0
+    mism = int(np.count_nonzero(free_cmp & (pe != ref.expert)))
+    gate_err = float(np.abs(pg - ref.gate)[compared].max())
+    # every window slot that opened was written; the others kept the fill
+    opened = compared
+    assert np.all(pe[opened] >= 0) and np.all(pe[~opened] == -7)
+    print(f"{cfg.name}: rel_err={rel:.3e} update_err={upd:.3e} ids "
+          f"{int(free_cmp.sum()) - mism}/{int(free_cmp.sum())} gate_err={gate_err:.2e} "
+          f"flags={flags}", flush=True)
+    tol = parity.TOL[cfg.dtype]
+    assert flags == 0
+    assert mism == 0
+    assert rel <= tol and upd <= parity.UPDATE_TOL[cfg.dtype]
+    # gates come from fp32 routers on depth inputs that, in bf16 mode, carry
+    # the bf16 GEMM operands' rounding of every earlier depth
+    assert gate_err <= (1e-5 if cfg.dtype == "fp32" else 2e-3)
+    return s_gpu
+
+
+SMALL = CONFIG_BY_NAME["small_bf16"]
+CASES = [
+    # (config, tokens, oracle.decode?)
+    (CONFIG_BY_NAME["tiny_fp32"], 64, True),
+    (SMALL.scaled(2, 200), 200, False),
+    (CONFIG_BY_NAME["mid_bf16"].scaled(2, 300), 300, False),
+    # 32 experts with skewed bias: up to 4 distinct experts per depth
+    (CONFIG_BY_NAME["sparse_bf16"].scaled(4, 270), 270, False),
+    # every document on one expert per depth: 20 rows share each weight read
+    # (passes of 8, 8 and 4 documents)
+    (CONFIG_BY_NAME["forced_bf16"].scaled(20, 72), 72, False),
+    # untied router, FiLM per depth and expert
+    (SMALL.with_(name="small_untied_expertfilm", router="per_depth",
+                 film_mode="depth_expert").scaled(2, 160), 160, False),
+    # bf16 GELU, d_head 32, S = 0 (fixed windows), ragged last window
+    (CoreConfig("dec_gelu_bf16", batch=3, n=75, d=128, n_heads=4, d_ffn=256, L=3, D=3, W=32,
+                S=0, mlp="gelu", dtype="bf16", seed=61), 75, True),
+    # one expert (margin +inf, gate 1), no FiLM, no RoPE, S > W
+    (CoreConfig("dec_l1_fp32", batch=2, n=40, d=64, n_heads=1, d_ffn=128, L=1, D=2, W=12, S=17,
+                mlp="swiglu", dtype="fp32", seed=62, film=False, rope_theta=0.0), 40, True),
+]
+
+
+@pytest.mark.parametrize("cfg,n_tokens,use_dec", CASES, ids=[c[0].name for c in CASES])
+def test_decode_parity(cfg, n_tokens, use_dec):
+    print(f"case {cfg.name} tokens {n_tokens}", flush=True)
+    inp = parity.prepare(cfg)
+    _check(inp, n_tokens, use_dec)
+
+
+def test_decode_forced_gates_and_in_place():
+    """Forced ids and gates, y written over x, on an fp32 and a bf16 case."""
+    for cfg in (CONFIG_BY_NAME["tiny_fp32"].with_(name="tiny_forced"),
+                CoreConfig("dec_forced_bf16", batch=2, n=90, d=256, n_heads=4, d_ffn=512, L=4,
+                           D=3, W=24, S=10, mlp="swiglu", dtype="bf16", seed=63)):
+        print(f"case {cfg.name}", flush=True)
+        inp = parity.prepare(cfg)
+        rng = np.random.default_rng(7)
+        shape = (cfg.D, cfg.batch, cfg.k_max)
+        fe = rng.integers(-1, cfg.L, size=shape).astype(np.int32)
+        fg = np.where(rng.random(shape) < 0.5, np.nan, rng.uniform(0, 1, shape)).astype(np.float32)
+        inp.forced_expert = fe
+        _check(inp, cfg.n, True, forced_gate=fg, in_place=True)
+
+
+def test_decode_is_deterministic_and_flags_bad_positions():
+    import torch
+    from runtime_routed_transformer_amd import binding as B
+    from runtime_routed_transformer_amd.core import DeviceCore, DeviceDecoder
+
+    cfg = CoreConfig("dec_flags", batch=2, n=48, d=128, n_heads=2, d_ffn=256, L=3, D=2, W=16,
+                     S=5, mlp="swiglu", dtype="bf16", seed=64)
+    inp = parity.prepare(cfg)
+    core = DeviceCore(inp)
+    dec = DeviceDecoder(core)
+    runs = []
+    for _ in range(2):
+        dec.reset()
+        outs = [dec.step(p, core.s0[:, p].contiguous()).clone() for p in range(cfg.n)]
+        runs.append(torch.stack(outs, 1).cpu().numpy())
+    np.testing.assert_array_equal(runs[0], runs[1])
+    assert dec.flags() == 0
+    # a skipped position is flagged (the kernels stay in bounds)
+    dec.reset()
+    dec.step(0, core.s0[:, 0].contiguous())
+    dec.step(2, core.s0[:, 2].contiguous())
+    assert dec.flags() == B.LOL_FLAG_BAD_POS
+    # a forced id outside the library is flagged and the window routed freely
+    dec.reset()
+    core.set_forcing(forced_expert=np.full((cfg.D, cfg.batch, cfg.k_max), cfg.L, np.int32))
+    free = runs[0][:, 0]
+    got = dec.step(0, core.s0[:, 0].contiguous()).cpu().numpy()
+    assert dec.flags() == B.LOL_FLAG_BAD_FORCED_ID
+    np.testing.assert_array_equal(got, free)
