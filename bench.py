@@ -230,10 +230,151 @@ def bench_full(args):
     return 0
 
 
+DECODE_METRIC = ("routed-core incremental decode tokens/sec on 1 MI355X (one token per document "
+                 "per step through every routed depth)")
+
+
+def decode_weight_bytes(cfg):
+    """Bytes of one expert's matrices read by each projection kind."""
+    act = 2 if cfg.dtype == "bf16" else 4
+    d, f = cfg.d, cfg.d_ffn
+    up = 2 * f if cfg.mlp == "swiglu" else f
+    return {"gemm_qkv": 3 * d * d * act, "gemm_o": d * d * act, "gemm_gate_up": up * d * act,
+            "gemm_down": f * d * act}
+
+
+def decode_launch_bytes(cfg, kind, n_experts):
+    """Algorithmic HBM bytes of one decode projection launch: the weights of
+    the ``n_experts`` distinct experts the documents use at that depth, plus
+    each document's input and output rows."""
+    act = 2 if cfg.dtype == "bf16" else 4
+    d, f, B = cfg.d, cfg.d_ffn, cfg.batch
+    io = {"gemm_qkv": B * (d * act + 3 * d * 4), "gemm_o": B * (d * act + 2 * d * 4),
+          "gemm_gate_up": B * (d * act + f * act), "gemm_down": B * (f * act + 3 * d * 4)}
+    return n_experts * decode_weight_bytes(cfg)[kind] + io[kind]
+
+
+def bench_decode(args):
+    """Incremental decode (``--workload <core>_decode``): documents of the
+    core workload are decoded token by token from position 0; one step = one
+    token of every document through all D depths.  W untimed steps warm up,
+    the state is reset, then K steps (positions 0..K-1) are timed.  The
+    dominant projection is timed with HIP events at one depth per step."""
+    import numpy as np
+    import torch
+    import oracle
+    from runtime_routed_transformer_amd import binding as B
+    from runtime_routed_transformer_amd.core import DeviceCore, DeviceDecoder
+    from runtime_routed_transformer_amd.workloads import CONFIG_BY_NAME, generate
+
+    base = args.workload[: -len("_decode")]
+    inp = generate(CONFIG_BY_NAME[base])
+    cfg = inp.cfg
+    if cfg.bias_mode == "skewed":
+        from oracle.calibrate import apply_skew  # input preparation only
+        apply_skew(inp)
+    steps = args.steps if args.steps is not None else min(cfg.n, 2 * cfg.W)
+    if steps > cfg.n or args.warmup > cfg.n:
+        raise SystemExit(f"--steps and --warmup must be at most n = {cfg.n} positions")
+    core = DeviceCore(inp, "cuda:0")
+    core.set_forcing(inp.forced_expert)
+    dec = DeviceDecoder(core)
+    stream = torch.cuda.current_stream()
+    xs = core.s0.transpose(0, 1).contiguous()    # [n][batch][d]: token p of every document
+    core.s0 = core.s_out = None
+
+    def run(n_steps):
+        dec.reset(stream)
+        for p in range(n_steps):
+            dec.step(p, xs[p], stream=stream)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    # per-kernel breakdown over a whole untimed pass of the timed positions
+    B.lol_core_timing_collect()
+    B.lol_core_timing_enable(B.LOL_TIMING_ALL)
+    run(steps)
+    torch.cuda.synchronize()
+    B.lol_core_timing_enable(0)
+    kt = B.lol_core_timing_collect()
+    per_kernel = {k: {"ms_avg": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items() if v[1]}
+    kinds = ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down")
+    dominant = max(kinds, key=lambda k: kt[k][0])
+
+    # timed region
+    B.lol_core_timing_enable(1 << B.kernel_kind(dominant))
+    dec.reset(stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for p in range(steps):
+        B.lol_core_timing_depth(p % cfg.D)
+        dec.step(p, xs[p], stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    B.lol_core_timing_enable(0)
+    B.lol_core_timing_depth(-1)
+    assert dec.flags() == 0, "decode state flagged an error"
+    ms = ev0.elapsed_time(ev1) / steps
+    dom_total, dom_n = B.lol_core_timing_collect()[dominant]
+    # distinct experts of every (position, depth) from the path the timed run wrote
+    pe = core.path_expert.cpu().numpy()
+    n_exp = np.zeros((steps, cfg.D), np.int64)
+    for p in range(steps):
+        for l in range(cfg.D):
+            k = (p + (l * cfg.S) % cfg.W) // cfg.W
+            n_exp[p, l] = len(set(pe[l, :, k].tolist()))
+    timed_bytes = sum(decode_launch_bytes(cfg, dominant, n_exp[p, p % cfg.D]) for p in range(steps))
+    achieved = timed_bytes / (dom_total / 1e3) / 1e9
+    step_bytes = sum(decode_launch_bytes(cfg, k, n_exp[p, l]) for k in kinds
+                     for p in range(steps) for l in range(cfg.D)) / steps
+    proj_ms = sum(kt[k][0] for k in kinds) / steps
+    result = {
+        "metric": DECODE_METRIC, "value": cfg.batch / (ms / 1e3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) states, N(0,0.02) weights)",
+        "config": {"workload": args.workload, "batch": cfg.batch, "positions": f"0..{steps - 1}",
+                   "d": cfg.d, "heads": cfg.n_heads, "d_ffn": cfg.d_ffn, "mlp": cfg.mlp,
+                   "L": cfg.L, "D": cfg.D, "W": cfg.W, "S": cfg.S, "film": cfg.film,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": None, "kernel_ms_avg": dom_total / dom_n,
+                     "kernel_launches_timed": dom_n,
+                     "bytes_per_launch_avg": timed_bytes / dom_n},
+        "projections_gbs": step_bytes / (proj_ms / 1e3) / 1e9,
+        "distinct_experts_per_depth_avg": float(n_exp.mean()),
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        # the oracle's decode on document 0, a growing prefix until ~10 s of work
+        n_s, dt = 8, 0.0
+        while True:
+            t0 = time.perf_counter()
+            oracle.decode(inp, n_s, forced_expert=inp.forced_expert, rows=[0])
+            dt = time.perf_counter() - t0
+            if dt >= 5.0 or n_s >= steps:
+                break
+            n_s = min(steps, n_s * 2)
+        result["cpu_baseline"] = {"value": n_s / dt, "unit": "tokens/s", "cores": int(threads),
+                                  "kind": "oracle",
+                                  "sample": f"oracle.decode of positions 0..{n_s - 1} of document "
+                                            f"0 of {base}, numpy float64, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=24)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 24; decode workloads: 2 W positions)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mid_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -246,6 +387,10 @@ def main(argv=None):
         return 2
 
     from runtime_routed_transformer_amd.workloads import FULL_BY_NAME
+    if args.workload.endswith("_decode"):
+        return bench_decode(args)
+    if args.steps is None:
+        args.steps = 24
     if args.workload in FULL_BY_NAME:
         return bench_full(args)
 
