@@ -13,16 +13,15 @@
 // Per depth and document the state holds: the sum of the completed
 // windows' means, the running sum and length of the open window, its expert
 // and gate, and its keys and values.  One call runs, per depth:
-//   k_dec_route   close/open windows, route a window that opens, the
-//                 attention RMSNorm + FiLM of the token  (one block per document)
-//   k_dec_gemv    QKV projection                         (grouped by expert)
+//   k_dec_route   close/open windows, route a window that opens
+//                 (one block per document)
+//   k_dec_gemv    attention RMSNorm + FiLM, QKV projection (grouped by expert)
 //   k_dec_attn    RoPE, cache append, attention over the open window
 //   k_dec_gemv    output projection + residual
-//   k_dec_norm    MLP RMSNorm + FiLM
-//   k_dec_gemv    gate/up + SwiGLU (or GELU)
+//   k_dec_gemv    MLP RMSNorm + FiLM, gate/up + SwiGLU (or GELU)
 //   k_dec_gemv    down projection + gated blend
 // A token's rows are few (one per document), so the projections are
-// matrix-vector products bound by reading the weights once: every block
+// matrix-vector products bound by reading the weights once: every wave
 // streams a few weight rows of one expert with 16-byte loads, and all rows
 // (documents) routed to that expert share the read.
 #include <math.h>
@@ -66,25 +65,60 @@ __device__ __forceinline__ int wave_min_i(int v) {
 __device__ __forceinline__ float block_sum(float v, float *red) {
   v = wave_sum(v);
   const int wave = threadIdx.x >> 6;
-  __syncthreads();
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
   return red[0] + red[1] + red[2] + red[3];
 }
 
-// out = FiLM(g * x / sqrt(mean(x^2) + eps)) over one row of d, by a block of
-// 256 threads (paper App. A RMSNorm with the depth FiLM of the review's Eq. 7).
+__device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16_t *p, float a, float b, float c, float d) {
+  uint2 pk;
+  pk.x = (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  pk.y = (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16);
+  *reinterpret_cast<uint2 *>(p) = pk;
+}
+
+// out = FiLM(g * x / sqrt(mean(x^2) + eps)) over one row of d <= 4096, by a
+// block of 256 threads (paper App. A RMSNorm with the depth FiLM of the
+// review's Eq. 7).  Every load of the row, the gain and FiLM is issued
+// before the reduction, so the row costs one memory round trip.
 template <typename act_t>
-__device__ void norm_row(const float *__restrict__ x, int d, const float *__restrict__ g,
-                         const float *__restrict__ fg, const float *__restrict__ fb, float eps,
-                         act_t *__restrict__ out, float *red) {
+__device__ __forceinline__ void norm_row(const float *__restrict__ x, int d,
+                                         const float *__restrict__ g,
+                                         const float *__restrict__ fg,
+                                         const float *__restrict__ fb, float eps,
+                                         act_t *__restrict__ out, float *red) {
+  float4 xv[4], gv[4], av[4], bv[4];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += 256) ss += x[c] * x[c];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = (i * 256 + (int)threadIdx.x) * 4;
+    if (c < d) {
+      xv[i] = *reinterpret_cast<const float4 *>(x + c);
+      gv[i] = *reinterpret_cast<const float4 *>(g + c);
+      if (fg) {
+        av[i] = *reinterpret_cast<const float4 *>(fg + c);
+        bv[i] = *reinterpret_cast<const float4 *>(fb + c);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if ((i * 256 + (int)threadIdx.x) * 4 < d)
+      ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
   const float inv = rsqrtf(block_sum(ss, red) / (float)d + eps);
-  for (int c = threadIdx.x; c < d; c += 256) {
-    float v = x[c] * inv * g[c];
-    if (fg) v = fg[c] * v + fb[c];
-    out[c] = from_f<act_t>(v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = (i * 256 + (int)threadIdx.x) * 4;
+    if (c >= d) continue;
+    float4 v = make_float4(xv[i].x * inv * gv[i].x, xv[i].y * inv * gv[i].y,
+                           xv[i].z * inv * gv[i].z, xv[i].w * inv * gv[i].w);
+    if (fg)
+      v = make_float4(av[i].x * v.x + bv[i].x, av[i].y * v.y + bv[i].y, av[i].z * v.z + bv[i].z,
+                      av[i].w * v.w + bv[i].w);
+    store4(out + c, v.x, v.y, v.z, v.w);
   }
 }
 
@@ -108,15 +142,15 @@ __global__ void k_dec_reset(int32_t *__restrict__ hdr, int32_t *__restrict__ cur
 }
 
 // One block per document.  At position pos of depth index `depth` the token
-// lies in window k, which starts at `start`:
-//  - if the token opens window k (pos == start), window k-1 is closed (its
-//    mean joins the prefix sum), the router input is built (the depth vector
-//    and the token for k = 0, else the mean of the k completed windows'
-//    means), the fp32 router scores it (softmax, lowest index attaining
-//    max(a + bias), gate = a of the applied expert, margin top1 - top2,
-//    forcing), and the open window's running sum restarts at the token;
-//  - else the token joins the open window's running sum;
-//  - then u = FiLM_attn(RMSNorm_e(token)) for the window's expert e.
+// lies in window k:
+//  - if the token opens window k, window k-1 is closed (its mean joins the
+//    prefix sum), the router input is built (the depth vector and the token
+//    for k = 0, else the mean of the k completed windows' means), the fp32
+//    router scores it (softmax, lowest index attaining max(a + bias), gate =
+//    a of the applied expert, margin top1 - top2, forcing), and the open
+//    window's running sum restarts at the token;
+//  - else the token joins the open window's running sum.
+// Then u = FiLM_attn(RMSNorm_e(token)) for the window's expert e.
 // The state's position counter is checked and advanced at depth 0.
 template <typename act_t>
 __global__ void __launch_bounds__(256) k_dec_route(
@@ -141,66 +175,66 @@ __global__ void __launch_bounds__(256) k_dec_route(
     if (hdr[0] != pos) atomicOr(reinterpret_cast<unsigned int *>(hdr + 1), (unsigned)LOL_FLAG_BAD_POS);
     hdr[0] = pos + 1;
   }
-  if (opens) {
-    const float inv_prev = 1.f / (float)max(cur_len[sidx], 1);
-    for (int c = tid; c < d; c += 256) {
-      const float xc = xr[c];
-      const float p = k > 0 ? pre[c] + cs[c] * inv_prev : 0.f;
-      pre[c] = p;
-      s_r[c] = k > 0 ? p / (float)k : 0.5f * (e_vec[c] + xc);
-      cs[c] = xc;
-    }
-    __syncthreads();
-    for (int m = wave; m < L; m += 4) {
-      const float *wm = w_r + (size_t)m * d;
-      float acc = 0.f;
-      for (int c = lane; c < d; c += 64) acc += wm[c] * s_r[c];
-      acc = wave_sum(acc);
-      if (lane == 0) s_z[m] = acc + (b_r ? b_r[m] : 0.f);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const bool live = lane < L;
-      const float zl = live ? s_z[lane] : -INFINITY;
-      const float zmax = wave_max(zl);
-      const float ez = live ? expf(zl - zmax) : 0.f;
-      const float a = ez / wave_sum(ez);
-      const float sc = live ? a + (bias ? bias[lane] : 0.f) : -INFINITY;
-      const float top = wave_max(sc);
-      const int rho = wave_min_i((live && sc == top) ? lane : 64);
-      const float second = wave_max((live && lane != rho) ? sc : -INFINITY);
-      const float margin = L > 1 ? top - second : INFINITY;
-      const size_t pidx = sidx * K_max + k;
-      int chosen = rho;
-      if (forced_e) {
-        const int fe = forced_e[pidx];
-        if (fe >= L) {
-          if (lane == 0) atomicOr(reinterpret_cast<unsigned int *>(hdr + 1), (unsigned)LOL_FLAG_BAD_FORCED_ID);
-        } else if (fe >= 0) {
-          chosen = fe;
-        }
-      }
-      float alpha = __shfl(a, chosen, 64);
-      if (forced_g) {
-        const float fgv = forced_g[pidx];
-        if (!isnan(fgv)) alpha = fgv;
-      }
-      if (lane == 0) {
-        expert[sidx] = chosen;
-        gate[sidx] = alpha;
-        cur_len[sidx] = 1;
-        if (path_e) path_e[pidx] = chosen;
-        if (path_g) path_g[pidx] = alpha;
-        if (path_m) path_m[pidx] = margin;
-        s_e = chosen;
-      }
-    }
-  } else {
+  if (!opens) {
     for (int c = tid; c < d; c += 256) cs[c] += xr[c];
-    if (tid == 0) {
-      cur_len[sidx] += 1;
-      s_e = min(max(expert[sidx], 0), L - 1);
+    const int e = min(max(expert[sidx], 0), L - 1);
+    if (tid == 0) cur_len[sidx] += 1;
+    norm_row<act_t>(xr, d, g_attn + (size_t)e * d, fg ? fg + (size_t)e * film_stride : nullptr,
+                    fb ? fb + (size_t)e * film_stride : nullptr, eps, u + (size_t)b * d, red);
+    return;
+  }
+  const float inv_prev = 1.f / (float)max(cur_len[sidx], 1);
+  for (int c = tid; c < d; c += 256) {
+    const float xc = xr[c];
+    const float p = k > 0 ? pre[c] + cs[c] * inv_prev : 0.f;
+    pre[c] = p;
+    s_r[c] = k > 0 ? p / (float)k : 0.5f * (e_vec[c] + xc);
+    cs[c] = xc;
+  }
+  __syncthreads();
+  for (int m = wave; m < L; m += 4) {
+    const float *wm = w_r + (size_t)m * d;
+    float acc = 0.f;
+    for (int c = lane; c < d; c += 64) acc += wm[c] * s_r[c];
+    acc = wave_sum(acc);
+    if (lane == 0) s_z[m] = acc + (b_r ? b_r[m] : 0.f);
+  }
+  __syncthreads();
+  if (wave == 0) {
+  const bool live = lane < L;
+  const float zl = live ? s_z[lane] : -INFINITY;
+  const float zmax = wave_max(zl);
+  const float ez = live ? expf(zl - zmax) : 0.f;
+  const float a = ez / wave_sum(ez);
+  const float sc = live ? a + (bias ? bias[lane] : 0.f) : -INFINITY;
+  const float top = wave_max(sc);
+  const int rho = wave_min_i((live && sc == top) ? lane : 64);
+  const float second = wave_max((live && lane != rho) ? sc : -INFINITY);
+  const float margin = L > 1 ? top - second : INFINITY;
+  const size_t pidx = sidx * K_max + k;
+  int chosen = rho;
+  if (forced_e) {
+    const int fe = forced_e[pidx];
+    if (fe >= L) {
+      if (lane == 0) atomicOr(reinterpret_cast<unsigned int *>(hdr + 1), (unsigned)LOL_FLAG_BAD_FORCED_ID);
+    } else if (fe >= 0) {
+      chosen = fe;
     }
+  }
+  float alpha = __shfl(a, chosen, 64);
+  if (forced_g) {
+    const float fgv = forced_g[pidx];
+    if (!isnan(fgv)) alpha = fgv;
+  }
+  if (lane == 0) {
+    expert[sidx] = chosen;
+    gate[sidx] = alpha;
+    cur_len[sidx] = 1;
+    if (path_e) path_e[pidx] = chosen;
+    if (path_g) path_g[pidx] = alpha;
+    if (path_m) path_m[pidx] = margin;
+    s_e = chosen;
+  }
   }
   __syncthreads();
   const int e = s_e;
@@ -224,10 +258,10 @@ __global__ void __launch_bounds__(256) k_dec_norm(const float *__restrict__ h, i
                   fb ? fb + (size_t)e * film_stride : nullptr, eps, u + (size_t)b * d, red);
 }
 
-// Sum of the NV x MR values of each lane over the 64 lanes of a wave: every
+// Sum of the N values of each lane over the 64 lanes of a wave: every
 // exchange step halves the values a lane carries (the partner keeps the
 // other half), then plain butterflies finish.  Afterwards a lane holds the
-// total of value index lane >> (6 - log2 N), N = NV MR a power of two <= 64.
+// total of value index lane >> (6 - log2 N), N a power of two <= 64.
 template <int N>
 __device__ __forceinline__ float wave_reduce_many(float (&v)[N], int lane) {
 #pragma unroll
@@ -314,232 +348,260 @@ enum DecEpi { DEC_STORE = 0, DEC_RESID = 1, DEC_SWIGLU = 2, DEC_GELU = 3, DEC_BL
 
 // Grouped matrix-vector products of one depth.  blockIdx.y = g picks the
 // g-th distinct expert among the documents (in order of first appearance);
-// blocks of a g past the distinct count exit.  Each of the 4 waves owns CPW
-// output columns (2 CPW weight rows with SwiGLU: gate row c and up row
-// glu_off + c) and reads them whole, 64 lanes x 16 bytes per load; the
-// documents of the group (up to MR at a time) are staged in LDS in chunks of
-// KC inputs and share every weight load.
-template <typename wt, int CPW, int EPI>
+// blocks of a g past the distinct count exit.  Each wave owns CPW output
+// columns (2 CPW weight rows with SwiGLU: gate row c and up row glu_off + c)
+// and works alone (no block barrier): per chunk of KC inputs it issues every
+// 16-byte weight load of its rows together with the inputs of up to MR
+// documents of the group (from L2, straight into registers), then the
+// products, so a chunk costs one memory round trip.  A lane's sums over its
+// inputs are reduced across the wave once per pass.
+template <typename wt, int CPW, int EPI, int MR, int NT>
 __global__ void __launch_bounds__(256) k_dec_gemv(DecGemv a) {
   constexpr int VEC = 16 / (int)sizeof(wt);
   constexpr int STEP = 64 * VEC;           // inputs one wave load covers
-  constexpr int NT = 4;                    // loads per lane per chunk
-  constexpr int KC = NT * STEP;            // inputs staged per chunk
-  constexpr int MR = 8;                    // documents per pass
+  constexpr int KC = NT * STEP;            // inputs per chunk (NT loads per weight row per lane)
   constexpr bool GLU = EPI == DEC_SWIGLU;
   constexpr int NV = GLU ? 2 * CPW : CPW;  // weight rows per wave
   constexpr int NR = NV * MR;              // sums per lane
-  __shared__ Vec16<wt> s_a[MR * (KC / VEC)];
-  __shared__ float s_res[4][NV][MR];
-  __shared__ int s_rows[64];
-  __shared__ int s_info[2];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col0 = (blockIdx.x * 4 + wave) * CPW;
+  if (col0 >= a.n_cols) return;
 
-  if (wave == 0) {
-    int el = lane < a.B ? min(max(a.expert[lane], 0), a.L - 1) : -1;
-    bool dup = false;
-    for (int j = 0; j < a.B; ++j) {
-      const int ej = __shfl(el, j, 64);
-      if (j < lane && ej == el) dup = true;
-    }
-    const unsigned long long first = __ballot(lane < a.B && !dup);
-    const int g = blockIdx.y;
-    if (__popcll(first) <= g) {
-      if (lane == 0) s_info[0] = 0;
-    } else {
-      unsigned long long mm = first;
-      for (int i = 0; i < g; ++i) mm &= mm - 1;
-      const int leader = __ffsll((long long)mm) - 1;
-      const int e = __shfl(el, leader, 64);
-      const bool mine = lane < a.B && el == e;
-      const unsigned long long rm = __ballot(mine);
-      if (mine) s_rows[__popcll(rm & ((1ull << lane) - 1ull))] = lane;
-      if (lane == 0) {
-        s_info[0] = __popcll(rm);
-        s_info[1] = e;
-      }
-    }
+  // the group: g-th distinct expert, and its documents (bit mask)
+  const int el = lane < a.B ? min(max(a.expert[lane], 0), a.L - 1) : -1;
+  bool dup = false;
+  for (int j = 0; j < a.B; ++j) {
+    const int ej = __shfl(el, j, 64);
+    if (j < lane && ej == el) dup = true;
   }
-  __syncthreads();
-  const int m = s_info[0];
-  if (m == 0) return;
-  const int e = s_info[1];
+  const unsigned long long first = __ballot(lane < a.B && !dup);
+  const int g = blockIdx.y;
+  if (__popcll(first) <= g) return;
+  unsigned long long mm = first;
+  for (int i = 0; i < g; ++i) mm &= mm - 1;
+  const int e = __shfl(el, __ffsll((long long)mm) - 1, 64);
+  unsigned long long rows = __ballot(lane < a.B && el == e);
+
   const int K = a.K;
   const wt *We = static_cast<const wt *>(a.W) + (size_t)e * a.w_estride;
-  const wt *A = static_cast<const wt *>(a.A);
-  const int col_blk = blockIdx.x * 4 * CPW;
   const wt *wrow[NV];
   bool wok[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int j = GLU ? v / 2 : v;
-    const int c = col_blk + wave * CPW + j;
+    const int c = col0 + j;
     wok[v] = c < a.n_cols;
     const int r = (GLU && (v & 1)) ? a.glu_off + c : c;
     wrow[v] = We + (size_t)(wok[v] ? r : 0) * K;
   }
 
-  for (int r0 = 0; r0 < m; r0 += MR) {
-    const int mr = min(MR, m - r0);
+  while (rows) {
+    // the next pass: up to MR documents of the group (padding repeats the first)
+    int rowid[MR];
+    int mr = 0;
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      if (rows) {
+        rowid[r] = __ffsll((long long)rows) - 1;
+        rows &= rows - 1;
+        mr = r + 1;
+      } else {
+        rowid[r] = rowid[0];
+      }
+    }
     float acc[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) acc[i] = 0.f;
-    for (int kc0 = 0; kc0 < K; kc0 += KC) {
-      const int kcl = min(KC, K - kc0);
-      __syncthreads();   // the previous chunk (and pass) is consumed
-      for (int i = tid; i < mr * (KC / VEC); i += 256) {
-        const int r = i / (KC / VEC), q = i % (KC / VEC);
-        if (q * VEC < kcl) s_a[i] = ld16<wt>(A + (size_t)s_rows[r0 + r] * K + kc0 + q * VEC);
-      }
-      __syncthreads();
-      // every weight load of the chunk is issued before the products
+    for (int k0 = 0; k0 < K; k0 += KC) {
       Vec16<wt> w[NT][NV];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int kl = t * STEP + lane * VEC;
+        const int kk = k0 + t * STEP + lane * VEC;
 #pragma unroll
         for (int v = 0; v < NV; ++v)
-          w[t][v] = (wok[v] && kl < kcl) ? ld16<wt>(wrow[v] + kc0 + kl) : zero16<wt>();
+          w[t][v] = (wok[v] && kk < K) ? ld16<wt>(wrow[v] + kk) : zero16<wt>();
       }
+      Vec16<wt> av[NT][MR];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int kl = t * STEP + lane * VEC;
-        if (kl >= kcl) continue;
+        const int kk = k0 + t * STEP + lane * VEC;
+        if (kk < K) {
 #pragma unroll
-        for (int r = 0; r < MR; ++r) {
-          if (r >= mr) break;
-          const Vec16<wt> av = s_a[r * (KC / VEC) + kl / VEC];
+          for (int r = 0; r < MR; ++r)
+            av[t][r] = ld16<wt>(static_cast<const wt *>(a.A) + (size_t)rowid[r] * K + kk);
+        } else {
 #pragma unroll
-          for (int v = 0; v < NV; ++v) acc[v * MR + r] = w[t][v].dot(av, acc[v * MR + r]);
+          for (int r = 0; r < MR; ++r) av[t][r] = zero16<wt>();
         }
       }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+          for (int v = 0; v < NV; ++v) acc[v * MR + r] = w[t][v].dot(av[t][r], acc[v * MR + r]);
     }
     const float tot = wave_reduce_many<NR>(acc, lane);
     constexpr int SH = 6 - Log2<NR>::v;
-    if ((lane & ((1 << SH) - 1)) == 0) {
-      const int idx = lane >> SH;
-      s_res[wave][idx / MR][idx % MR] = tot;
-    }
-    __syncthreads();
-    for (int i = tid; i < 4 * CPW * MR; i += 256) {
-      const int r = i % MR, cj = i / MR;
-      const int wv = cj / CPW, j = cj % CPW;
-      const int c = col_blk + cj;
-      if (r >= mr || c >= a.n_cols) continue;
-      const int row = s_rows[r0 + r];
-      const size_t o = (size_t)row * a.n_cols + c;
-      const float v0 = s_res[wv][GLU ? 2 * j : j][r];
-      if (EPI == DEC_STORE) {
-        a.out[o] = v0;
-      } else if (EPI == DEC_RESID) {
-        a.out[o] = a.x[o] + v0;
-      } else if (EPI == DEC_SWIGLU) {
-        const float up = s_res[wv][2 * j + 1][r];
-        static_cast<wt *>(a.out_act)[o] = from_f<wt>(silu(v0) * up);
-      } else if (EPI == DEC_GELU) {
-        static_cast<wt *>(a.out_act)[o] = from_f<wt>(gelu_erf(v0));
-      } else {
-        const float xv = a.x[o];
-        const float y = a.h[o] + v0;
-        a.out[o] = xv + a.gate[row] * (y - xv);
-      }
+    // SwiGLU: the up row's sum sits MR values (MR << SH lanes) after the gate's
+    const float up = GLU ? __shfl(tot, (lane + (MR << SH)) & 63, 64) : 0.f;
+    const int idx = lane >> SH;
+    const int v = idx / MR, r = idx % MR;
+    if ((lane & ((1 << SH) - 1)) != 0 || r >= mr || (GLU && (v & 1))) continue;
+    const int c = col0 + (GLU ? v / 2 : v);
+    if (c >= a.n_cols) continue;
+    int row = rowid[0];
+#pragma unroll
+    for (int q = 1; q < MR; ++q)
+      if (q == r) row = rowid[q];
+    const size_t o = (size_t)row * a.n_cols + c;
+    if (EPI == DEC_STORE) {
+      a.out[o] = tot;
+    } else if (EPI == DEC_RESID) {
+      a.out[o] = a.x[o] + tot;
+    } else if (EPI == DEC_SWIGLU) {
+      static_cast<wt *>(a.out_act)[o] = from_f<wt>(silu(tot) * up);
+    } else if (EPI == DEC_GELU) {
+      static_cast<wt *>(a.out_act)[o] = from_f<wt>(gelu_erf(tot));
+    } else {
+      const float xv = a.x[o];
+      const float y = a.h[o] + tot;
+      a.out[o] = xv + a.gate[row] * (y - xv);
     }
   }
 }
 
-// Attention of every document's token (block x = document, y = head, one
-// wave) over the open window of one depth: q and k of the token are rotated
+// Attention of every document's token (block x = document, y = head, 4
+// waves) over the open window of one depth: q and k of the token are rotated
 // at its window-local position p (RoPE, rotate-half pairs), rounded to the
 // operand type, k and v are appended to the cache at slot p, and the token
 // attends to slots 0..p (paper Sec. 3.2.1: causal inside the window; review
-// Eq. 1: scores scaled by 1/sqrt(d_head)).
+// Eq. 1: scores scaled by 1/sqrt(d_head)).  One thread per key for the
+// scores; the weighted sum of values splits the keys over the 4 waves.
 template <typename act_t, int DH>
-__global__ void __launch_bounds__(64) k_dec_attn(const float *__restrict__ qkv,
-                                                 act_t *__restrict__ kc, act_t *__restrict__ vc,
-                                                 act_t *__restrict__ o,
-                                                 const float *__restrict__ rope_cs, int d, int H,
-                                                 int W, int p, float scale, int use_rope) {
+__global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
+                                                  act_t *__restrict__ kc, act_t *__restrict__ vc,
+                                                  act_t *__restrict__ o,
+                                                  const float *__restrict__ rope_cs, int d, int H,
+                                                  int W, int p, float scale, int use_rope) {
   extern __shared__ float s_p[];   // [p + 1] scores, then weights
   __shared__ float s_q[DH], s_k[DH], s_v[DH];
+  __shared__ float s_red[4];
+  __shared__ float s_o[4][DH];
   constexpr int HALF = DH / 2;
-  const int b = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float *qr = qkv + (size_t)b * 3 * d + h * DH;
   const size_t cbase = ((size_t)b * H + h) * W * DH;
   act_t *kcache = kc + cbase, *vcache = vc + cbase;
-  if (lane < DH) {
-    float q = qr[lane], k = qr[d + lane];
-    const float v = qr[2 * d + lane];
+  if (tid < DH) {
+    float q = qr[tid], k = qr[d + tid];
+    const float v = qr[2 * d + tid];
     if (use_rope) {
-      const int j = lane % HALF;
+      const int j = tid % HALF;
       const float c = rope_cs[((size_t)p * HALF + j) * 2], s = rope_cs[((size_t)p * HALF + j) * 2 + 1];
-      const int partner = lane < HALF ? lane + HALF : lane - HALF;
+      const int partner = tid < HALF ? tid + HALF : tid - HALF;
       const float qp = qr[partner], kp = qr[d + partner];
-      q = lane < HALF ? q * c - qp * s : q * c + qp * s;
-      k = lane < HALF ? k * c - kp * s : k * c + kp * s;
+      q = tid < HALF ? q * c - qp * s : q * c + qp * s;
+      k = tid < HALF ? k * c - kp * s : k * c + kp * s;
     }
     const act_t qa = from_f<act_t>(q), ka = from_f<act_t>(k), va = from_f<act_t>(v);
-    s_q[lane] = to_f<act_t>(qa);
-    s_k[lane] = to_f<act_t>(ka);
-    s_v[lane] = to_f<act_t>(va);
-    kcache[(size_t)p * DH + lane] = ka;
-    vcache[(size_t)p * DH + lane] = va;
+    s_q[tid] = to_f<act_t>(qa);
+    s_k[tid] = to_f<act_t>(ka);
+    s_v[tid] = to_f<act_t>(va);
+    kcache[(size_t)p * DH + tid] = ka;
+    vcache[(size_t)p * DH + tid] = va;
   }
   __syncthreads();
   float mloc = -INFINITY;
-  for (int j = lane; j <= p; j += 64) {
+  for (int j = tid; j <= p; j += 256) {
     float sc = 0.f;
     if (j == p) {
 #pragma unroll
       for (int t = 0; t < DH; ++t) sc += s_q[t] * s_k[t];
     } else {
+      // the key row in 16-byte loads
       const act_t *kr = kcache + (size_t)j * DH;
+      constexpr int V = 16 / (int)sizeof(act_t);
+      Vec16<act_t> kv[DH / V];
 #pragma unroll
-      for (int t = 0; t < DH; ++t) sc += s_q[t] * to_f<act_t>(kr[t]);
+      for (int t = 0; t < DH / V; ++t) kv[t] = ld16<act_t>(kr + t * V);
+#pragma unroll
+      for (int t = 0; t < DH / V; ++t) {
+        const act_t *kp = reinterpret_cast<const act_t *>(&kv[t].v);
+#pragma unroll
+        for (int i = 0; i < V; ++i) sc += s_q[t * V + i] * to_f<act_t>(kp[i]);
+      }
     }
     sc *= scale;
     s_p[j] = sc;
     mloc = fmaxf(mloc, sc);
   }
-  const float mx = wave_max(mloc);
+  mloc = wave_max(mloc);
+  if (lane == 0) s_red[wave] = mloc;
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   float lsum = 0.f;
-  for (int j = lane; j <= p; j += 64) {
+  for (int j = tid; j <= p; j += 256) {
     const float w = expf(s_p[j] - mx);
     s_p[j] = w;
     lsum += w;
   }
-  const float inv = 1.f / wave_sum(lsum);
-  __syncthreads();
+  lsum = wave_sum(lsum);
+  __syncthreads();   // every score is read, every weight written
+  if (lane == 0) s_red[wave] = lsum;
+  float acc = 0.f;
   if (lane < DH) {
-    float acc = s_p[p] * s_v[lane];
-    int j = 0;
-    for (; j + 4 <= p; j += 4) {
+    int j = wave;
+    for (; j + 12 < p; j += 16) {
       const float v0 = to_f<act_t>(vcache[(size_t)j * DH + lane]);
-      const float v1 = to_f<act_t>(vcache[(size_t)(j + 1) * DH + lane]);
-      const float v2 = to_f<act_t>(vcache[(size_t)(j + 2) * DH + lane]);
-      const float v3 = to_f<act_t>(vcache[(size_t)(j + 3) * DH + lane]);
-      acc += s_p[j] * v0 + s_p[j + 1] * v1 + s_p[j + 2] * v2 + s_p[j + 3] * v3;
+      const float v1 = to_f<act_t>(vcache[(size_t)(j + 4) * DH + lane]);
+      const float v2 = to_f<act_t>(vcache[(size_t)(j + 8) * DH + lane]);
+      const float v3 = to_f<act_t>(vcache[(size_t)(j + 12) * DH + lane]);
+      acc += s_p[j] * v0 + s_p[j + 4] * v1 + s_p[j + 8] * v2 + s_p[j + 12] * v3;
     }
-    for (; j < p; ++j) acc += s_p[j] * to_f<act_t>(vcache[(size_t)j * DH + lane]);
-    o[(size_t)b * d + h * DH + lane] = from_f<act_t>(acc * inv);
+    for (; j < p; j += 4) acc += s_p[j] * to_f<act_t>(vcache[(size_t)j * DH + lane]);
+    if (j == p) acc += s_p[p] * s_v[lane];
+    s_o[wave][lane] = acc;
+  }
+  __syncthreads();
+  if (tid < DH) {
+    const float inv = 1.f / (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+    o[(size_t)b * d + h * DH + tid] =
+        from_f<act_t>((s_o[0][tid] + s_o[1][tid] + s_o[2][tid] + s_o[3][tid]) * inv);
   }
 }
 
-template <typename wt, int CPW, int EPI>
-hipError_t gemv_launch(const DecGemv &a, hipStream_t st) {
-  const int cols = 4 * CPW;
-  dim3 grid((a.n_cols + cols - 1) / cols, min(a.B, a.L));
-  lol_launch(k_dec_gemv<wt, CPW, EPI>, grid, dim3(256), 0, st, a);
+template <typename wt, int CPW, int EPI, int MR, int NT>
+hipError_t gemv_launch_mr(const DecGemv &a, hipStream_t st) {
+  dim3 grid((a.n_cols + 4 * CPW - 1) / (4 * CPW), min(a.B, a.L));
+  lol_launch(k_dec_gemv<wt, CPW, EPI, MR, NT>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
+template <typename wt, int CPW, int EPI, int NT>
+hipError_t gemv_launch(const DecGemv &a, hipStream_t st) {
+  // documents per pass: the batch rounded up to a power of two, at most 8
+  // (8 documents per pass with half the columns per wave: the sums and
+  // inputs of a pass stay in registers)
+  constexpr int CPW8 = CPW > 1 ? CPW / 2 : 1;
+  if (a.B <= 1) return gemv_launch_mr<wt, CPW, EPI, 1, NT>(a, st);
+  if (a.B <= 2) return gemv_launch_mr<wt, CPW, EPI, 2, NT>(a, st);
+  if (a.B <= 4) return gemv_launch_mr<wt, CPW, EPI, 4, NT>(a, st);
+  return gemv_launch_mr<wt, CPW8, EPI, 8, NT>(a, st);
+}
+
+// Columns per wave: enough weight rows per wave (8 KB and more in flight)
+// that one round of waves covers the projection; the down projection reads
+// 4 loads per row per chunk (two chunks at K = 4096).
 template <typename wt>
 hipError_t gemv_typed(const DecGemv &a, int which, bool glu, hipStream_t st) {
   switch (which) {
-    case DEC_QKV: return gemv_launch<wt, 2, DEC_STORE>(a, st);
-    case DEC_O: return gemv_launch<wt, 1, DEC_RESID>(a, st);
+    case DEC_QKV: return gemv_launch<wt, 4, DEC_STORE, 2>(a, st);
+    case DEC_O: return gemv_launch<wt, 1, DEC_RESID, 2>(a, st);
     case DEC_GU:
-      return glu ? gemv_launch<wt, 1, DEC_SWIGLU>(a, st) : gemv_launch<wt, 2, DEC_GELU>(a, st);
-    default: return gemv_launch<wt, 1, DEC_BLEND>(a, st);
+      return glu ? gemv_launch<wt, 2, DEC_SWIGLU, 2>(a, st)
+                 : gemv_launch<wt, 4, DEC_GELU, 2>(a, st);
+    default: return gemv_launch<wt, 1, DEC_BLEND, 4>(a, st);
   }
 }
 
@@ -555,10 +617,10 @@ hipError_t attn_launch(const lol_core_config &c, const DecodeBufs &s, int depth,
   dim3 grid(c.batch, c.n_heads);
   const uint32_t shm = (uint32_t)(p + 1) * sizeof(float);
   if (dh == 64)
-    lol_launch(k_dec_attn<act_t, 64>, grid, dim3(64), shm, st, s.qkv, kc, vc,
+    lol_launch(k_dec_attn<act_t, 64>, grid, dim3(256), shm, st, s.qkv, kc, vc,
                static_cast<act_t *>(s.o), s.rope_cs, c.d, c.n_heads, c.W, p, scale, use_rope);
   else
-    lol_launch(k_dec_attn<act_t, 32>, grid, dim3(64), shm, st, s.qkv, kc, vc,
+    lol_launch(k_dec_attn<act_t, 32>, grid, dim3(256), shm, st, s.qkv, kc, vc,
                static_cast<act_t *>(s.o), s.rope_cs, c.d, c.n_heads, c.W, p, scale, use_rope);
   return hipGetLastError();
 }
@@ -618,6 +680,7 @@ hipError_t launch_dec_route(const lol_core_config &c, const DecodeBufs &s, int d
   const int K_max = (c.n + c.W - 1) / c.W + 1;
   const float *w_r = rt.w_r + (rt.per_depth ? (size_t)depth * L * d : 0);
   const float *b_r = rt.b_r ? rt.b_r + (rt.per_depth ? (size_t)depth * L : 0) : nullptr;
+  // FiLM rows of (depth, attention sublayer): [D][2][d], or [D][L][2][d] per expert
   const size_t film_off = ((size_t)depth * (lib.film_per_expert ? L : 1) * 2 + 0) * d;
   const float *fg = lib.film_gamma ? lib.film_gamma + film_off : nullptr;
   const float *fb = lib.film_beta ? lib.film_beta + film_off : nullptr;
