@@ -364,7 +364,7 @@ __global__ void __launch_bounds__(256) k_dec_gemv(DecGemv a) {
   constexpr int NV = GLU ? 2 * CPW : CPW;  // weight rows per wave
   constexpr int NR = NV * MR;              // sums per lane
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col0 = (blockIdx.x * 4 + wave) * CPW;
+  const int col0 = (blockIdx.x * (blockDim.x >> 6) + wave) * CPW;
   if (col0 >= a.n_cols) return;
 
   // the group: g-th distinct expert, and its documents (bit mask)
@@ -573,8 +573,9 @@ __global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
 
 template <typename wt, int CPW, int EPI, int MR, int NT>
 hipError_t gemv_launch_mr(const DecGemv &a, hipStream_t st) {
-  dim3 grid((a.n_cols + 4 * CPW - 1) / (4 * CPW), min(a.B, a.L));
-  lol_launch(k_dec_gemv<wt, CPW, EPI, MR, NT>, grid, dim3(256), 0, st, a);
+  constexpr int WPB = 4;   // waves per block (they share nothing)
+  dim3 grid((a.n_cols + WPB * CPW - 1) / (WPB * CPW), min(a.B, a.L));
+  lol_launch(k_dec_gemv<wt, CPW, EPI, MR, NT>, grid, dim3(64 * WPB), 0, st, a);
   return hipGetLastError();
 }
 
@@ -590,16 +591,19 @@ hipError_t gemv_launch(const DecGemv &a, hipStream_t st) {
   return gemv_launch_mr<wt, CPW8, EPI, 8, NT>(a, st);
 }
 
-// Columns per wave: enough weight rows per wave (8 KB and more in flight)
-// that one round of waves covers the projection; the down projection reads
-// 4 loads per row per chunk (two chunks at K = 4096).
+// One output column (SwiGLU: one gate/up pair) per wave: with few documents
+// the fixed part of a wave (group lookup, one round trip, the reduction)
+// outweighs its bytes, so more waves in flight hide more of it (measured:
+// 4 columns per wave for QKV and 2 pairs for gate/up were 10-15% slower).
+// The down projection reads 4 loads per row per chunk (two chunks at K =
+// 4096).
 template <typename wt>
 hipError_t gemv_typed(const DecGemv &a, int which, bool glu, hipStream_t st) {
   switch (which) {
-    case DEC_QKV: return gemv_launch<wt, 4, DEC_STORE, 2>(a, st);
+    case DEC_QKV: return gemv_launch<wt, 1, DEC_STORE, 2>(a, st);
     case DEC_O: return gemv_launch<wt, 1, DEC_RESID, 2>(a, st);
     case DEC_GU:
-      return glu ? gemv_launch<wt, 2, DEC_SWIGLU, 2>(a, st)
+      return glu ? gemv_launch<wt, 1, DEC_SWIGLU, 2>(a, st)
                  : gemv_launch<wt, 4, DEC_GELU, 2>(a, st);
     default: return gemv_launch<wt, 1, DEC_BLEND, 4>(a, st);
   }
