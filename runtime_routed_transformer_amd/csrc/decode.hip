@@ -272,8 +272,12 @@ __device__ __forceinline__ float wave_reduce_many(float (&v)[N], int lane) {
       const bool hi = (lane & o) != 0;
 #pragma unroll
       for (int i = 0; i < n2; ++i) {
-        const float send = hi ? v[i] : v[i + n2];
-        const float keep = hi ? v[i + n2] : v[i];
+        float lo_v = v[i], hi_v = v[i + n2];
+        // opaque register values: keeps the compiler from turning the two
+        // selects below into one dynamically indexed (scratch) array access
+        asm volatile("" : "+v"(lo_v), "+v"(hi_v));
+        const float send = hi ? lo_v : hi_v;
+        const float keep = hi ? hi_v : lo_v;
         v[i] = keep + __shfl_xor(send, o, 64);
       }
     } else {
@@ -476,8 +480,11 @@ __global__ void __launch_bounds__(256) k_dec_gemv(DecGemv a) {
 // at its window-local position p (RoPE, rotate-half pairs), rounded to the
 // operand type, k and v are appended to the cache at slot p, and the token
 // attends to slots 0..p (paper Sec. 3.2.1: causal inside the window; review
-// Eq. 1: scores scaled by 1/sqrt(d_head)).  One thread per key for the
-// scores; the weighted sum of values splits the keys over the 4 waves.
+// Eq. 1: scores scaled by 1/sqrt(d_head)).  Keys go one per thread, 256 at
+// a time: the first 256 keys' K and V rows are requested together at the
+// start (16-byte loads), before the token's own projections are read.  The
+// weighted sum of values is one transposed reduction per wave (each lane
+// ends with one dimension's sum), then the 4 waves' sums are added.
 template <typename act_t, int DH>
 __global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
                                                   act_t *__restrict__ kc, act_t *__restrict__ vc,
@@ -489,10 +496,21 @@ __global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
   __shared__ float s_red[4];
   __shared__ float s_o[4][DH];
   constexpr int HALF = DH / 2;
+  constexpr int V = 16 / (int)sizeof(act_t);   // elements per 16-byte load
+  constexpr int NV = DH / V;                   // loads per row
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float *qr = qkv + (size_t)b * 3 * d + h * DH;
   const size_t cbase = ((size_t)b * H + h) * W * DH;
   act_t *kcache = kc + cbase, *vcache = vc + cbase;
+  // keys 0..255 (those before the token): rows requested first
+  Vec16<act_t> k0[NV], v0[NV];
+  if (tid < p) {
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      k0[t] = ld16<act_t>(kcache + (size_t)tid * DH + t * V);
+      v0[t] = ld16<act_t>(vcache + (size_t)tid * DH + t * V);
+    }
+  }
   if (tid < DH) {
     float q = qr[tid], k = qr[d + tid];
     const float v = qr[2 * d + tid];
@@ -512,29 +530,42 @@ __global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
     vcache[(size_t)p * DH + tid] = va;
   }
   __syncthreads();
+  // scores of keys j = tid, tid + 256, ...
+  auto key_dot = [&](const Vec16<act_t> (&kv)[NV]) {
+    float sc = 0.f;
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      const act_t *kp = reinterpret_cast<const act_t *>(&kv[t].v);
+#pragma unroll
+      for (int i = 0; i < V; ++i) sc += s_q[t * V + i] * to_f<act_t>(kp[i]);
+    }
+    return sc;
+  };
   float mloc = -INFINITY;
-  for (int j = tid; j <= p; j += 256) {
+  if (tid <= p) {
+    float sc = 0.f;
+    if (tid == p) {
+#pragma unroll
+      for (int t = 0; t < DH; ++t) sc += s_q[t] * s_k[t];
+    } else {
+      sc = key_dot(k0);
+    }
+    s_p[tid] = sc * scale;
+    mloc = sc * scale;
+  }
+  for (int j = tid + 256; j <= p; j += 256) {
     float sc = 0.f;
     if (j == p) {
 #pragma unroll
       for (int t = 0; t < DH; ++t) sc += s_q[t] * s_k[t];
     } else {
-      // the key row in 16-byte loads
-      const act_t *kr = kcache + (size_t)j * DH;
-      constexpr int V = 16 / (int)sizeof(act_t);
-      Vec16<act_t> kv[DH / V];
+      Vec16<act_t> kv[NV];
 #pragma unroll
-      for (int t = 0; t < DH / V; ++t) kv[t] = ld16<act_t>(kr + t * V);
-#pragma unroll
-      for (int t = 0; t < DH / V; ++t) {
-        const act_t *kp = reinterpret_cast<const act_t *>(&kv[t].v);
-#pragma unroll
-        for (int i = 0; i < V; ++i) sc += s_q[t * V + i] * to_f<act_t>(kp[i]);
-      }
+      for (int t = 0; t < NV; ++t) kv[t] = ld16<act_t>(kcache + (size_t)j * DH + t * V);
+      sc = key_dot(kv);
     }
-    sc *= scale;
-    s_p[j] = sc;
-    mloc = fmaxf(mloc, sc);
+    s_p[j] = sc * scale;
+    mloc = fmaxf(mloc, sc * scale);
   }
   mloc = wave_max(mloc);
   if (lane == 0) s_red[wave] = mloc;
@@ -547,22 +578,42 @@ __global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
     lsum += w;
   }
   lsum = wave_sum(lsum);
-  __syncthreads();   // every score is read, every weight written
+  __syncthreads();   // every thread has read s_red
   if (lane == 0) s_red[wave] = lsum;
-  float acc = 0.f;
-  if (lane < DH) {
-    int j = wave;
-    for (; j + 12 < p; j += 16) {
-      const float v0 = to_f<act_t>(vcache[(size_t)j * DH + lane]);
-      const float v1 = to_f<act_t>(vcache[(size_t)(j + 4) * DH + lane]);
-      const float v2 = to_f<act_t>(vcache[(size_t)(j + 8) * DH + lane]);
-      const float v3 = to_f<act_t>(vcache[(size_t)(j + 12) * DH + lane]);
-      acc += s_p[j] * v0 + s_p[j + 4] * v1 + s_p[j + 8] * v2 + s_p[j + 12] * v3;
+  // sum over keys of w_j v_j: per chunk of 256 keys, this thread's key's
+  // weighted row, reduced over the wave's 64 keys
+  constexpr int SH = 6 - Log2<DH>::v;   // lane >> SH = the dimension a lane ends with
+  float od = 0.f;
+  for (int j0 = 0; j0 <= p; j0 += 256) {
+    const int j = j0 + tid;
+    float val[DH];
+    if (j < p) {
+      const float w = s_p[j];
+      Vec16<act_t> vv[NV];
+      if (j0 == 0) {
+#pragma unroll
+        for (int t = 0; t < NV; ++t) vv[t] = v0[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < NV; ++t) vv[t] = ld16<act_t>(vcache + (size_t)j * DH + t * V);
+      }
+#pragma unroll
+      for (int t = 0; t < NV; ++t) {
+        const act_t *vp = reinterpret_cast<const act_t *>(&vv[t].v);
+#pragma unroll
+        for (int i = 0; i < V; ++i) val[t * V + i] = w * to_f<act_t>(vp[i]);
+      }
+    } else if (j == p) {
+      const float w = s_p[p];
+#pragma unroll
+      for (int i = 0; i < DH; ++i) val[i] = w * s_v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < DH; ++i) val[i] = 0.f;
     }
-    for (; j < p; j += 4) acc += s_p[j] * to_f<act_t>(vcache[(size_t)j * DH + lane]);
-    if (j == p) acc += s_p[p] * s_v[lane];
-    s_o[wave][lane] = acc;
+    od += wave_reduce_many<DH>(val, lane);
   }
+  if ((lane & ((1 << SH) - 1)) == 0) s_o[wave][lane >> SH] = od;
   __syncthreads();
   if (tid < DH) {
     const float inv = 1.f / (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
