@@ -261,7 +261,10 @@ __global__ void __launch_bounds__(256, 3) k_attn_mfma(const bf16_t *__restrict__
   __shared__ __attribute__((aligned(1024))) char lds[2 * KC * RB];
   char *const Kl = lds;
   char *const Vl = lds + KC * RB;
-  const int slot = blockIdx.x, h = blockIdx.y, qc = blockIdx.z;
+  // query chunks in reverse dispatch order: in a window longer than one
+  // chunk the last chunks see the most keys, so they start first and the
+  // light ones fill in behind them
+  const int slot = blockIdx.x, h = blockIdx.y, qc = gridDim.z - 1 - blockIdx.z;
   if (win_exp[slot] < 0) return;
   const int len = win_len[slot];  // tokens of the window (its document's end clips the last one)
   const int q_begin = qc * CH;
