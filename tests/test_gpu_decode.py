@@ -101,6 +101,16 @@ CASES = [
     # one expert (margin +inf, gate 1), no FiLM, no RoPE, S > W
     (CoreConfig("dec_l1_fp32", batch=2, n=40, d=64, n_heads=1, d_ffn=128, L=1, D=2, W=12, S=17,
                 mlp="swiglu", dtype="fp32", seed=62, film=False, rope_theta=0.0), 40, True),
+    # the largest batch (64 documents: passes of 8 per expert group), 6 experts
+    (CoreConfig("dec_b64_bf16", batch=64, n=20, d=128, n_heads=2, d_ffn=256, L=6, D=2, W=8, S=3,
+                mlp="swiglu", dtype="bf16", seed=65), 20, True),
+    # W = 1: every token opens a window at every depth (the router runs on
+    # every token; the cache holds one slot)
+    (CoreConfig("dec_w1_bf16", batch=3, n=12, d=128, n_heads=2, d_ffn=128, L=3, D=3, W=1, S=0,
+                mlp="swiglu", dtype="bf16", seed=66), 12, True),
+    # one-token documents; 5 documents (3 per pass group size rounds up to 8)
+    (CoreConfig("dec_one_token", batch=5, n=1, d=128, n_heads=4, d_ffn=256, L=2, D=3, W=4, S=1,
+                mlp="gelu", dtype="bf16", seed=67), 1, True),
 ]
 
 
