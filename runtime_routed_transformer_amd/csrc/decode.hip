@@ -482,9 +482,9 @@ __global__ void __launch_bounds__(256) k_dec_gemv(DecGemv a) {
 // attends to slots 0..p (paper Sec. 3.2.1: causal inside the window; review
 // Eq. 1: scores scaled by 1/sqrt(d_head)).  Keys go one per thread, 256 at
 // a time: the first 256 keys' K and V rows are requested together at the
-// start (16-byte loads), before the token's own projections are read.  The
-// weighted sum of values is one transposed reduction per wave (each lane
-// ends with one dimension's sum), then the 4 waves' sums are added.
+// start (16-byte loads), before the token's own projections are read; the
+// values are staged in LDS for the weighted sum (lanes over dimensions, keys
+// split over the 4 waves), then the 4 waves' sums are added.
 template <typename act_t, int DH>
 __global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
                                                   act_t *__restrict__ kc, act_t *__restrict__ vc,
@@ -495,6 +495,7 @@ __global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
   __shared__ float s_q[DH], s_k[DH], s_v[DH];
   __shared__ float s_red[4];
   __shared__ float s_o[4][DH];
+  __shared__ __attribute__((aligned(16))) act_t s_vrow[256][DH];   // values of keys 0..255
   constexpr int HALF = DH / 2;
   constexpr int V = 16 / (int)sizeof(act_t);   // elements per 16-byte load
   constexpr int NV = DH / V;                   // loads per row
@@ -580,40 +581,26 @@ __global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
   lsum = wave_sum(lsum);
   __syncthreads();   // every thread has read s_red
   if (lane == 0) s_red[wave] = lsum;
-  // sum over keys of w_j v_j: per chunk of 256 keys, this thread's key's
-  // weighted row, reduced over the wave's 64 keys
-  constexpr int SH = 6 - Log2<DH>::v;   // lane >> SH = the dimension a lane ends with
-  float od = 0.f;
-  for (int j0 = 0; j0 <= p; j0 += 256) {
-    const int j = j0 + tid;
-    float val[DH];
-    if (j < p) {
-      const float w = s_p[j];
-      Vec16<act_t> vv[NV];
-      if (j0 == 0) {
+  // sum over keys of w_j v_j: lanes over dimensions, keys split over the 4
+  // waves; the first 256 keys' values come from LDS (staged from the rows
+  // requested at the start), later ones from the cache
+  if (tid < p) {
 #pragma unroll
-        for (int t = 0; t < NV; ++t) vv[t] = v0[t];
-      } else {
-#pragma unroll
-        for (int t = 0; t < NV; ++t) vv[t] = ld16<act_t>(vcache + (size_t)j * DH + t * V);
-      }
-#pragma unroll
-      for (int t = 0; t < NV; ++t) {
-        const act_t *vp = reinterpret_cast<const act_t *>(&vv[t].v);
-#pragma unroll
-        for (int i = 0; i < V; ++i) val[t * V + i] = w * to_f<act_t>(vp[i]);
-      }
-    } else if (j == p) {
-      const float w = s_p[p];
-#pragma unroll
-      for (int i = 0; i < DH; ++i) val[i] = w * s_v[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < DH; ++i) val[i] = 0.f;
-    }
-    od += wave_reduce_many<DH>(val, lane);
+    for (int t = 0; t < NV; ++t) *reinterpret_cast<decltype(v0[t].v) *>(&s_vrow[tid][t * V]) = v0[t].v;
   }
-  if ((lane & ((1 << SH) - 1)) == 0) s_o[wave][lane >> SH] = od;
+  __syncthreads();
+  if (lane < DH) {
+    float acc = 0.f;
+    const int j1 = min(p, 256);
+    int j = wave;
+    for (; j + 12 < j1; j += 16)
+      acc += s_p[j] * to_f<act_t>(s_vrow[j][lane]) + s_p[j + 4] * to_f<act_t>(s_vrow[j + 4][lane]) +
+             s_p[j + 8] * to_f<act_t>(s_vrow[j + 8][lane]) + s_p[j + 12] * to_f<act_t>(s_vrow[j + 12][lane]);
+    for (; j < j1; j += 4) acc += s_p[j] * to_f<act_t>(s_vrow[j][lane]);
+    for (; j < p; j += 4) acc += s_p[j] * to_f<act_t>(vcache[(size_t)j * DH + lane]);
+    if (j == p) acc += s_p[p] * s_v[lane];
+    s_o[wave][lane] = acc;
+  }
   __syncthreads();
   if (tid < DH) {
     const float inv = 1.f / (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
