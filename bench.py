@@ -36,6 +36,18 @@ def gemm_flops(cfg, tokens=None):
             "gemm_gate_up": 2.0 * T * up * d, "gemm_down": 2.0 * T * d * f}
 
 
+def hbm_bytes(cfg, tokens=None):
+    """Algorithmic HBM bytes per launch (one depth) of the bandwidth-bound
+    kernels, and of the down projection's scatter epilogue (read and write of
+    the fp32 residual rows)."""
+    T, d = (cfg.tokens if tokens is None else tokens), cfg.d
+    act = 2 if cfg.dtype == "bf16" else 4
+    return {"pool": 4.0 * T * d,                        # read s
+            "norm_attn": (4.0 + act) * T * d,           # read s, write u
+            "win_attn": act * 4.0 * T * d,              # read q, k, v; write o
+            "gemm_down (scatter epilogue)": 8.0 * T * d}
+
+
 def cpu_baseline(inp, budget_s=12.0, lengths=None):
     """The oracle, unchanged, on whole documents of the workload, one after
     another until about ``budget_s`` seconds of CPU work are done
@@ -497,6 +509,10 @@ def main(argv=None):
                      "flops_per_launch": flops[dominant]},
         "mfma_util_pct": 100.0 * gemm_tflops / PEAK_BF16_TFLOPS,
         "grouped_gemm_tflops": gemm_tflops,
+        # bandwidth-bound kernels: algorithmic bytes / mean duration (the
+        # scatter entry is a lower bound: the down kernel also does its GEMM)
+        "hbm_gbs": {k: b / (kt[k.split(" ")[0]][0] / max(kt[k.split(" ")[0]][1], 1) / 1e3) / 1e9
+                    for k, b in hbm_bytes(cfg, tokens).items() if kt.get(k.split(" ")[0], (0, 0))[1]},
         "kernels": per_kernel,
     }
     if not args.no_cpu_baseline:
