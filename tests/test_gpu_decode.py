@@ -108,6 +108,12 @@ CASES = [
     # every token; the cache holds one slot)
     (CoreConfig("dec_w1_bf16", batch=3, n=12, d=128, n_heads=2, d_ffn=128, L=3, D=3, W=1, S=0,
                 mlp="swiglu", dtype="bf16", seed=66), 12, True),
+    # windows longer than 256 tokens: keys past the first 256 are read from
+    # the cache inside the score and value loops (d_head 64 and 32)
+    (CoreConfig("dec_w320_bf16", batch=2, n=700, d=128, n_heads=2, d_ffn=256, L=3, D=2, W=320,
+                S=100, mlp="swiglu", dtype="bf16", seed=68), 700, False),
+    (CoreConfig("dec_w300_fp32", batch=1, n=620, d=64, n_heads=2, d_ffn=128, L=2, D=2, W=300,
+                S=77, mlp="gelu", dtype="fp32", seed=69), 620, False),
     # one-token documents; 5 documents (3 per pass group size rounds up to 8)
     (CoreConfig("dec_one_token", batch=5, n=1, d=128, n_heads=4, d_ffn=256, L=2, D=3, W=4, S=1,
                 mlp="gelu", dtype="bf16", seed=67), 1, True),
