@@ -227,8 +227,9 @@ lol_status lol_core_timing_collect(double *ms, int32_t *launches);
 const char *lol_core_kernel_name(int32_t kind);
 
 /* ---- Incremental decode -------------------------------------------------
- * The routed core one token at a time, for `batch` documents in lockstep
- * (every call brings token `pos` of each document).  The review "Library of
+ * The routed core one token at a time, for `batch` documents (every call
+ * brings one token of each document, at the position the state holds for
+ * it).  The review "Library of
  * Layers: Routing Whole Transformer Blocks at Runtime", Deriving prefix-only
  * routing, notes that a window's router reads only earlier, completed
  * windows (window 0: the document's first token and the depth vector), so a
@@ -249,16 +250,30 @@ const char *lol_core_kernel_name(int32_t kind);
  * HOST, pure. */
 size_t lol_decode_state_size(const lol_core_config *cfg);
 
-/* Starts new documents on `state` (DEVICE, state_bytes >= the size above,
- * 256-byte aligned): the next call must bring pos = 0; clears the flags.
- * Asynchronous on stream. */
+/* Starts new documents in every row of `state` (DEVICE, state_bytes >= the
+ * size above, 256-byte aligned): each row's next position is 0; clears the
+ * flags.  Asynchronous on stream. */
 lol_status lol_decode_reset(const lol_core_config *cfg, void *state, size_t state_bytes,
                             void *stream);
 
+/* Starts a new document in row `row` only (0 <= row < batch, else
+ * LOL_EINVAL): its next position is 0; the other rows continue.  For
+ * serving, where documents join and leave the batch at any step.  Launches
+ * one kernel and no memset, so it may be captured in a graph.  Asynchronous
+ * on stream. */
+lol_status lol_decode_reset_row(const lol_core_config *cfg, void *state, size_t state_bytes,
+                                int32_t row, void *stream);
+
 /* One token per document through every routed depth.
- *   pos           the token's position in its document, 0 <= pos < n; calls
- *                 must bring 0, 1, 2, ... after a reset (a call out of turn
- *                 raises LOL_FLAG_BAD_POS and its result is unspecified)
+ *   pos           -1: each row's token is at the row's own next position
+ *                 (0 after its reset, then 1, 2, ...; rows may differ); the
+ *                 call then has no per-call arguments besides the buffers,
+ *                 so it may be captured once in a graph and replayed.
+ *                 0 <= pos < n: every row's token is at pos, which must be
+ *                 each row's next position (lockstep use).  A row whose
+ *                 position differs from pos, or reaches n, raises
+ *                 LOL_FLAG_BAD_POS and its result is unspecified (the
+ *                 kernels stay in bounds)
  *   x             DEVICE [batch][d] fp32, s^(0) of the tokens
  *   lib, rt       as for lol_core_forward
  *   forced_expert, forced_gate
@@ -271,7 +286,7 @@ lol_status lol_decode_reset(const lol_core_config *cfg, void *state, size_t stat
  *                 written (expert, gate, margin); others are left untouched
  *   state         the decode state (DEVICE); its per-call scratch is inside
  * Returns LOL_OK once queued; LOL_EINVAL for NULL inputs or pos outside
- * [0, n); LOL_EWORKSPACE for a state that is missing, too small or not
+ * [-1, n); LOL_EWORKSPACE for a state that is missing, too small or not
  * 256-byte aligned.  Calls on one state must run in order on one stream. */
 lol_status lol_decode_step(const lol_core_config *cfg, int32_t pos, const float *x,
                            const lol_library *lib, const lol_router *rt,

@@ -72,6 +72,8 @@ _SIGNATURES.update({
                               c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "lol_decode_state_size": (c_size_t, [POINTER(lol_core_config)]),
     "lol_decode_reset": (c_int32, [POINTER(lol_core_config), c_void_p, c_size_t, c_void_p]),
+    "lol_decode_reset_row": (c_int32, [POINTER(lol_core_config), c_void_p, c_size_t, c_int32,
+                                       c_void_p]),
     "lol_decode_step": (c_int32, [POINTER(lol_core_config), c_int32, c_void_p,
                                   POINTER(lol_library), POINTER(lol_router), c_void_p, c_void_p,
                                   c_void_p, POINTER(lol_path), c_void_p, c_size_t, c_void_p]),
@@ -159,9 +161,14 @@ def lol_decode_reset(cfg, state, state_bytes, stream) -> int:
     return load().lol_decode_reset(ctypes.byref(cfg), state, state_bytes, stream)
 
 
+def lol_decode_reset_row(cfg, state, state_bytes, row, stream) -> int:
+    return load().lol_decode_reset_row(ctypes.byref(cfg), state, state_bytes, int(row), stream)
+
+
 def lol_decode_step(cfg, pos, x, lib, rt, forced_expert, forced_gate, y, path, state,
                     state_bytes, stream) -> int:
-    """One token per document: x / y are device [batch][d] fp32 addresses."""
+    """One token per document: x / y are device [batch][d] fp32 addresses;
+    pos = -1 takes each row's own next position from the state."""
     return load().lol_decode_step(ctypes.byref(cfg), int(pos), x, ctypes.byref(lib),
                                   ctypes.byref(rt), forced_expert, forced_gate, y,
                                   ctypes.byref(path) if path is not None else None, state,

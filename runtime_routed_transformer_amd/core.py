@@ -151,8 +151,18 @@ class DeviceDecoder:
         if status != B.LOL_OK:
             raise B.LolError(status, "lol_decode_reset")
 
-    def step(self, pos: int, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+    def reset_row(self, row: int, stream: Optional[torch.cuda.Stream] = None) -> None:
+        """Start a new document in one row; the other rows continue."""
+        status = B.lol_decode_reset_row(self.core.ccfg, self.state.data_ptr(), self.state_bytes,
+                                        row, self._stream(stream))
+        if status != B.LOL_OK:
+            raise B.LolError(status, "lol_decode_reset_row")
+
+    def step(self, pos: Optional[int], x: torch.Tensor, y: Optional[torch.Tensor] = None,
              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """pos: every row's position (lockstep), or None for each row's own
+        next position held by the state."""
+        pos = -1 if pos is None else pos
         y = self.y if y is None else y
         for t in (x, y):
             if (t.shape != (self.cfg.batch, self.cfg.d) or t.dtype != torch.float32

@@ -122,17 +122,23 @@ __device__ __forceinline__ void norm_row(const float *__restrict__ x, int d,
   }
 }
 
-__global__ void k_dec_reset(int32_t *__restrict__ hdr, int32_t *__restrict__ cur_len,
-                            int32_t *__restrict__ expert, float *__restrict__ gate, int n_state,
+// Resets rows [row0, row1) of the state: next position 0, window routes to
+// expert 0 (and, with flags, the flag word and the RoPE table).
+__global__ void k_dec_reset(int32_t *__restrict__ hdr, int32_t *__restrict__ row_next,
+                            int32_t *__restrict__ cur_len, int32_t *__restrict__ expert,
+                            float *__restrict__ gate, int B, int D, int row0, int row1, int all,
                             float *__restrict__ cs, int W, int half, double theta, int use_rope) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx < 2) hdr[idx] = 0;
-  if (idx < n_state) {
-    cur_len[idx] = 0;
-    expert[idx] = 0;
-    gate[idx] = 0.f;
+  if (all && idx == 0) hdr[1] = 0;
+  const int nr = row1 - row0;
+  if (idx < nr) row_next[row0 + idx] = 0;
+  if (idx < D * nr) {
+    const int l = idx / nr, b = row0 + idx % nr;
+    cur_len[l * B + b] = 0;
+    expert[l * B + b] = 0;
+    gate[l * B + b] = 0.f;
   }
-  if (use_rope && idx < W * half) {
+  if (all && use_rope && idx < W * half) {
     // cos / sin of p * theta^(-2j/d_head) at window-local position p
     const int p = idx / half, j = idx % half;
     const double ang = (double)p * pow(theta, -2.0 * (double)j / (double)(2 * half));
@@ -141,8 +147,11 @@ __global__ void k_dec_reset(int32_t *__restrict__ hdr, int32_t *__restrict__ cur
   }
 }
 
-// One block per document.  At position pos of depth index `depth` the token
-// lies in window k:
+// One block per document.  At depth 0 the block takes the document's
+// position for this call (`pos` >= 0: every document's, checked against the
+// state; -1: the document's own next position) and advances it; every depth
+// then reads it back.  At position pos of depth index `depth` (window
+// offset delta) the token lies in window k = (pos + delta) / W:
 //  - if the token opens window k, window k-1 is closed (its mean joins the
 //    prefix sum), the router input is built (the depth vector and the token
 //    for k = 0, else the mean of the k completed windows' means), the fp32
@@ -151,11 +160,11 @@ __global__ void k_dec_reset(int32_t *__restrict__ hdr, int32_t *__restrict__ cur
 //    window's running sum restarts at the token;
 //  - else the token joins the open window's running sum.
 // Then u = FiLM_attn(RMSNorm_e(token)) for the window's expert e.
-// The state's position counter is checked and advanced at depth 0.
 template <typename act_t>
 __global__ void __launch_bounds__(256) k_dec_route(
-    const float *__restrict__ x, int d, int L, int B, int depth, int pos, int k, int opens,
-    int K_max, int32_t *__restrict__ hdr, float *__restrict__ prefix, float *__restrict__ cur_sum,
+    const float *__restrict__ x, int d, int L, int B, int depth, int pos_arg, int n, int W,
+    int delta, int K_max, int32_t *__restrict__ hdr, int32_t *__restrict__ row_next,
+    int32_t *__restrict__ row_cur, float *__restrict__ prefix, float *__restrict__ cur_sum,
     int32_t *__restrict__ cur_len, int32_t *__restrict__ expert, float *__restrict__ gate,
     const float *__restrict__ w_r, const float *__restrict__ b_r, const float *__restrict__ e_vec,
     const float *__restrict__ bias, const int32_t *__restrict__ forced_e,
@@ -165,16 +174,34 @@ __global__ void __launch_bounds__(256) k_dec_route(
   extern __shared__ float s_r[];   // [d] router input
   __shared__ float s_z[kMaxExperts];
   __shared__ float red[4];
-  __shared__ int s_e;
+  __shared__ int s_e, s_pos;
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float *xr = x + (size_t)b * d;
   const size_t sidx = (size_t)depth * B + b;
   float *pre = prefix + sidx * d;
   float *cs = cur_sum + sidx * d;
-  if (depth == 0 && b == 0 && tid == 0) {
-    if (hdr[0] != pos) atomicOr(reinterpret_cast<unsigned int *>(hdr + 1), (unsigned)LOL_FLAG_BAD_POS);
-    hdr[0] = pos + 1;
+  if (tid == 0) {
+    int ps;
+    if (depth == 0) {
+      const int nxt = row_next[b];
+      ps = pos_arg >= 0 ? pos_arg : nxt;
+      bool bad = pos_arg >= 0 && nxt != pos_arg;
+      if (ps < 0 || ps >= n) {   // past the document's last slot: stay in bounds
+        bad = true;
+        ps = min(max(ps, 0), n - 1);
+      }
+      if (bad) atomicOr(reinterpret_cast<unsigned int *>(hdr + 1), (unsigned)LOL_FLAG_BAD_POS);
+      row_cur[b] = ps;
+      row_next[b] = ps + 1;
+    } else {
+      ps = row_cur[b];
+    }
+    s_pos = ps;
   }
+  __syncthreads();
+  const int pos = s_pos;
+  const int k = (pos + delta) / W;
+  const bool opens = pos == max(0, k * W - delta);
   if (!opens) {
     for (int c = tid; c < d; c += 256) cs[c] += xr[c];
     const int e = min(max(expert[sidx], 0), L - 1);
@@ -490,8 +517,10 @@ __global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
                                                   act_t *__restrict__ kc, act_t *__restrict__ vc,
                                                   act_t *__restrict__ o,
                                                   const float *__restrict__ rope_cs, int d, int H,
-                                                  int W, int p, float scale, int use_rope) {
-  extern __shared__ float s_p[];   // [p + 1] scores, then weights
+                                                  int W, int delta,
+                                                  const int32_t *__restrict__ row_cur, float scale,
+                                                  int use_rope) {
+  extern __shared__ float s_p[];   // [W] scores, then weights
   __shared__ float s_q[DH], s_k[DH], s_v[DH];
   __shared__ float s_red[4];
   __shared__ float s_o[4][DH];
@@ -500,6 +529,9 @@ __global__ void __launch_bounds__(256) k_dec_attn(const float *__restrict__ qkv,
   constexpr int V = 16 / (int)sizeof(act_t);   // elements per 16-byte load
   constexpr int NV = DH / V;                   // loads per row
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the token's window-local position at this depth
+  const int pos = row_cur[b];
+  const int p = pos - max(0, (pos + delta) / W * W - delta);
   const float *qr = qkv + (size_t)b * 3 * d + h * DH;
   const size_t cbase = ((size_t)b * H + h) * W * DH;
   act_t *kcache = kc + cbase, *vcache = vc + cbase;
@@ -648,7 +680,7 @@ hipError_t gemv_typed(const DecGemv &a, int which, bool glu, hipStream_t st) {
 }
 
 template <typename act_t>
-hipError_t attn_launch(const lol_core_config &c, const DecodeBufs &s, int depth, int p,
+hipError_t attn_launch(const lol_core_config &c, const DecodeBufs &s, int depth, int delta,
                        hipStream_t st) {
   const int dh = c.d / c.n_heads;
   const size_t per_depth = (size_t)c.batch * c.n_heads * c.W * dh;
@@ -657,13 +689,15 @@ hipError_t attn_launch(const lol_core_config &c, const DecodeBufs &s, int depth,
   const float scale = 1.0f / sqrtf((float)dh);
   const int use_rope = c.rope_theta != 0.f ? 1 : 0;
   dim3 grid(c.batch, c.n_heads);
-  const uint32_t shm = (uint32_t)(p + 1) * sizeof(float);
+  const uint32_t shm = (uint32_t)c.W * sizeof(float);   // scores of up to W keys
   if (dh == 64)
     lol_launch(k_dec_attn<act_t, 64>, grid, dim3(256), shm, st, s.qkv, kc, vc,
-               static_cast<act_t *>(s.o), s.rope_cs, c.d, c.n_heads, c.W, p, scale, use_rope);
+               static_cast<act_t *>(s.o), s.rope_cs, c.d, c.n_heads, c.W, delta, s.row_cur, scale,
+               use_rope);
   else
     lol_launch(k_dec_attn<act_t, 32>, grid, dim3(256), shm, st, s.qkv, kc, vc,
-               static_cast<act_t *>(s.o), s.rope_cs, c.d, c.n_heads, c.W, p, scale, use_rope);
+               static_cast<act_t *>(s.o), s.rope_cs, c.d, c.n_heads, c.W, delta, s.row_cur, scale,
+               use_rope);
   return hipGetLastError();
 }
 
@@ -687,6 +721,8 @@ size_t decode_layout(const lol_core_config &c, char *base, DecodeBufs *out) {
   };
   DecodeBufs s;
   s.hdr = (int32_t *)carve(2 * 4);
+  s.row_next = (int32_t *)carve(B * 4);
+  s.row_cur = (int32_t *)carve(B * 4);
   s.prefix = (float *)carve(D * B * d * 4);
   s.cur_sum = (float *)carve(D * B * d * 4);
   s.cur_len = (int32_t *)carve(D * B * 4);
@@ -704,18 +740,19 @@ size_t decode_layout(const lol_core_config &c, char *base, DecodeBufs *out) {
   return off;
 }
 
-hipError_t launch_dec_reset(const lol_core_config &c, const DecodeBufs &s, hipStream_t st) {
+hipError_t launch_dec_reset(const lol_core_config &c, const DecodeBufs &s, int row, hipStream_t st) {
   const int half = c.d / c.n_heads / 2;
-  const int n_state = c.D * c.batch;
-  const int total = max(max(n_state, c.W * half), 2);
-  lol_launch(k_dec_reset, dim3((total + 255) / 256), dim3(256), 0, st, s.hdr, s.cur_len, s.expert,
-             s.gate, n_state, s.rope_cs, c.W, half, (double)c.rope_theta,
-             c.rope_theta != 0.f ? 1 : 0);
+  const bool all = row < 0;
+  const int row0 = all ? 0 : row, row1 = all ? c.batch : row + 1;
+  const int total = max(max(c.D * (row1 - row0), all ? c.W * half : 0), 1);
+  lol_launch(k_dec_reset, dim3((total + 255) / 256), dim3(256), 0, st, s.hdr, s.row_next,
+             s.cur_len, s.expert, s.gate, c.batch, c.D, row0, row1, all ? 1 : 0, s.rope_cs, c.W,
+             half, (double)c.rope_theta, c.rope_theta != 0.f ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_dec_route(const lol_core_config &c, const DecodeBufs &s, int depth, int pos,
-                            int k, int opens, const float *x, const lol_library &lib,
+                            const float *x, const lol_library &lib,
                             const lol_router &rt, const int32_t *forced_e, const float *forced_g,
                             const lol_path *path, hipStream_t st) {
   const int d = c.d, L = c.L;
@@ -730,14 +767,17 @@ hipError_t launch_dec_route(const lol_core_config &c, const DecodeBufs &s, int d
   const uint32_t shm = (uint32_t)d * sizeof(float);
   int32_t *pe = path ? path->expert : nullptr;
   float *pg = path ? path->gate : nullptr, *pm = path ? path->margin : nullptr;
+  const int delta = (int)(((long long)depth * c.S) % c.W);
   if (c.dtype == LOL_BF16)
     lol_launch(k_dec_route<bf16_t>, dim3(c.batch), dim3(256), shm, st, x, d, L, c.batch, depth,
-               pos, k, opens, K_max, s.hdr, s.prefix, s.cur_sum, s.cur_len, s.expert, s.gate, w_r,
+               pos, c.n, c.W, delta, K_max, s.hdr, s.row_next, s.row_cur, s.prefix, s.cur_sum,
+               s.cur_len, s.expert, s.gate, w_r,
                b_r, rt.e_depth + (size_t)depth * d, rt.expert_bias, forced_e, forced_g, pe, pg, pm,
                lib.g_attn, fg, fb, film_stride, c.rms_eps, static_cast<bf16_t *>(s.u));
   else
     lol_launch(k_dec_route<float>, dim3(c.batch), dim3(256), shm, st, x, d, L, c.batch, depth,
-               pos, k, opens, K_max, s.hdr, s.prefix, s.cur_sum, s.cur_len, s.expert, s.gate, w_r,
+               pos, c.n, c.W, delta, K_max, s.hdr, s.row_next, s.row_cur, s.prefix, s.cur_sum,
+               s.cur_len, s.expert, s.gate, w_r,
                b_r, rt.e_depth + (size_t)depth * d, rt.expert_bias, forced_e, forced_g, pe, pg, pm,
                lib.g_attn, fg, fb, film_stride, c.rms_eps, static_cast<float *>(s.u));
   return hipGetLastError();
@@ -760,11 +800,11 @@ hipError_t launch_dec_norm(const lol_core_config &c, const DecodeBufs &s, int de
   return hipGetLastError();
 }
 
-hipError_t launch_dec_attn(const lol_core_config &c, const DecodeBufs &s, int depth, int p,
+hipError_t launch_dec_attn(const lol_core_config &c, const DecodeBufs &s, int depth,
                            hipStream_t st) {
-  if (p < 0 || p >= c.W) return hipErrorInvalidValue;
-  if (c.dtype == LOL_BF16) return attn_launch<bf16_t>(c, s, depth, p, st);
-  return attn_launch<float>(c, s, depth, p, st);
+  const int delta = (int)(((long long)depth * c.S) % c.W);
+  if (c.dtype == LOL_BF16) return attn_launch<bf16_t>(c, s, depth, delta, st);
+  return attn_launch<float>(c, s, depth, delta, st);
 }
 
 hipError_t launch_dec_gemv(const lol_core_config &c, const DecodeBufs &s, int depth, int which,

@@ -388,7 +388,22 @@ lol_status lol_decode_reset(const lol_core_config *cfg, void *state, size_t stat
     return LOL_EWORKSPACE;
   DecodeBufs s;
   decode_layout(*cfg, static_cast<char *>(state), &s);
-  if (launch_dec_reset(*cfg, s, static_cast<hipStream_t>(stream)) != hipSuccess) return LOL_EHIP;
+  if (launch_dec_reset(*cfg, s, -1, static_cast<hipStream_t>(stream)) != hipSuccess) return LOL_EHIP;
+  return LOL_OK;
+}
+
+lol_status lol_decode_reset_row(const lol_core_config *cfg, void *state, size_t state_bytes,
+                                int32_t row, void *stream) {
+  const lol_status vs = validate(cfg);
+  if (vs != LOL_OK) return vs;
+  if (!decode_supported(*cfg)) return LOL_EUNSUPPORTED;
+  if (row < 0 || row >= cfg->batch) return LOL_EINVAL;
+  if (!state || state_bytes < decode_layout(*cfg, nullptr, nullptr) ||
+      (reinterpret_cast<uintptr_t>(state) & 255))
+    return LOL_EWORKSPACE;
+  DecodeBufs s;
+  decode_layout(*cfg, static_cast<char *>(state), &s);
+  if (launch_dec_reset(*cfg, s, row, static_cast<hipStream_t>(stream)) != hipSuccess) return LOL_EHIP;
   return LOL_OK;
 }
 
@@ -406,7 +421,7 @@ lol_status lol_decode_step(const lol_core_config *cfg, int32_t pos, const float 
   if (!rt->w_r || !rt->e_depth) return LOL_EINVAL;
   if ((rt->per_depth != 0 && rt->per_depth != 1) || (lib->film_per_expert != 0 && lib->film_per_expert != 1))
     return LOL_EINVAL;
-  if (pos < 0 || pos >= cfg->n) return LOL_EINVAL;
+  if (pos < -1 || pos >= cfg->n) return LOL_EINVAL;
   if (!state || state_bytes < decode_layout(*cfg, nullptr, nullptr) ||
       (reinterpret_cast<uintptr_t>(state) & 255))
     return LOL_EWORKSPACE;
@@ -429,17 +444,17 @@ lol_status lol_decode_step(const lol_core_config *cfg, int32_t pos, const float 
     err = _l.done(call);                              \
     if (err != hipSuccess) return LOL_EHIP;           \
   } while (0)
+  // each document's position lives on the device (the route kernel of depth
+  // 0 takes it), so the window geometry of every depth is computed there and
+  // a call with pos = -1 has no per-call arguments (it can be captured once
+  // in a graph and replayed)
   for (int l = 0; l < c.D; ++l) {
     cur_depth = l;
-    // the token's window at this depth (partition with offset ((l-1) S) mod W)
-    const int delta = (int)(((long long)l * c.S) % c.W);
-    const int k = (pos + delta) / c.W;
-    const int start = k * c.W - delta > 0 ? k * c.W - delta : 0;
     const float *xin = l == 0 ? x : y;   // depth input; y holds s^(l) afterwards
-    LOL_TRY(KK_ROUTE, launch_dec_route(c, s, l, pos, k, pos == start ? 1 : 0, xin, *lib, *rt,
-                                       forced_expert, forced_gate, path, st));
+    LOL_TRY(KK_ROUTE, launch_dec_route(c, s, l, pos, xin, *lib, *rt, forced_expert, forced_gate,
+                                       path, st));
     LOL_TRY(KK_GEMM_QKV, launch_dec_gemv(c, s, l, DEC_QKV, xin, y, *lib, st));
-    LOL_TRY(KK_ATTN, launch_dec_attn(c, s, l, pos - start, st));
+    LOL_TRY(KK_ATTN, launch_dec_attn(c, s, l, st));
     LOL_TRY(KK_GEMM_O, launch_dec_gemv(c, s, l, DEC_O, xin, y, *lib, st));
     LOL_TRY(KK_NORM_FFN, launch_dec_norm(c, s, l, *lib, st));
     LOL_TRY(KK_GEMM_GATE_UP, launch_dec_gemv(c, s, l, DEC_GU, xin, y, *lib, st));

@@ -172,7 +172,9 @@ hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws,
 // ---- incremental decode (one token per document per call) ----
 // Device buffers carved from the caller's decode state.
 struct DecodeBufs {
-  int32_t *hdr;        // [0] the position the next call must bring, [1] flags
+  int32_t *hdr;        // [1] flags
+  int32_t *row_next;   // [B]        position of each document's next token
+  int32_t *row_cur;    // [B]        position of the token of the call in progress
   float *prefix;       // [D][B][d]  sum of the completed windows' means
   float *cur_sum;      // [D][B][d]  sum of the open window's depth inputs
   int32_t *cur_len;    // [D][B]     tokens in the open window
@@ -191,20 +193,21 @@ enum DecodeProj { DEC_QKV = 0, DEC_O = 1, DEC_GU = 2, DEC_DOWN = 3 };
 // d <= 4096, W <= 8192
 bool decode_supported(const lol_core_config &c);
 size_t decode_layout(const lol_core_config &c, char *base, DecodeBufs *s);
-// position counter and flags to 0, window routes to expert 0, RoPE table
-hipError_t launch_dec_reset(const lol_core_config &c, const DecodeBufs &s, hipStream_t st);
-// window bookkeeping and routing of depth index `depth` for the token at
-// `pos` (in window k; opens = it is the window's first token), then the
-// attention norm into s.u
+// row < 0: every document (positions, routes, flags, RoPE table); else one
+// document: its next position 0 and its window routes
+hipError_t launch_dec_reset(const lol_core_config &c, const DecodeBufs &s, int row, hipStream_t st);
+// window bookkeeping and routing of depth index `depth` for each document's
+// token (pos >= 0: every document at pos; -1: each at its own next
+// position), then the attention norm into s.u
 hipError_t launch_dec_route(const lol_core_config &c, const DecodeBufs &s, int depth, int pos,
-                            int k, int opens, const float *x, const lol_library &lib,
+                            const float *x, const lol_library &lib,
                             const lol_router &rt, const int32_t *forced_e, const float *forced_g,
                             const lol_path *path, hipStream_t st);
 // MLP norm of s.h into s.u
 hipError_t launch_dec_norm(const lol_core_config &c, const DecodeBufs &s, int depth,
                            const lol_library &lib, hipStream_t st);
-// attention at window-local position p (0 <= p < W)
-hipError_t launch_dec_attn(const lol_core_config &c, const DecodeBufs &s, int depth, int p,
+// attention of each document's token over its open window
+hipError_t launch_dec_attn(const lol_core_config &c, const DecodeBufs &s, int depth,
                            hipStream_t st);
 // one projection (DecodeProj) grouped by expert; x = depth input, y = depth output
 hipError_t launch_dec_gemv(const lol_core_config &c, const DecodeBufs &s, int depth, int which,

@@ -168,7 +168,7 @@ def test_decode_sizes_and_host_checks(lib):
         return B.lol_decode_step(c, pos, x, libx, rtx, None, None, y, None, state, nbytes, None)
     assert step(x=None) == B.LOL_EINVAL
     assert step(y=None) == B.LOL_EINVAL
-    assert step(pos=-1) == B.LOL_EINVAL
+    assert step(pos=-2) == B.LOL_EINVAL
     assert step(pos=c.n) == B.LOL_EINVAL
     assert step(nbytes=size - 1) == B.LOL_EWORKSPACE
     assert step(state=None) == B.LOL_EWORKSPACE
@@ -181,3 +181,6 @@ def test_decode_sizes_and_host_checks(lib):
     big = make_config(CONFIG_BY_NAME["tiny_fp32"]); big.d = 8192; big.n_heads = 128
     assert B.lol_decode_reset(big, 256, 1 << 40, None) == B.LOL_EUNSUPPORTED
     assert lib.lol_decode_read_flags(None, None, None) == B.LOL_EINVAL
+    for row in (-1, c.batch):
+        assert B.lol_decode_reset_row(c, 256, size, row, None) == B.LOL_EINVAL
+    assert B.lol_decode_reset_row(c, None, size, 0, None) == B.LOL_EWORKSPACE

@@ -171,3 +171,69 @@ def test_decode_is_deterministic_and_flags_bad_positions():
     got = dec.step(0, core.s0[:, 0].contiguous()).cpu().numpy()
     assert dec.flags() == B.LOL_FLAG_BAD_FORCED_ID
     np.testing.assert_array_equal(got, free)
+
+
+def test_decode_rows_at_their_own_positions():
+    """Serving: every row at its own position (pos = -1).  Rows restart
+    their documents at different steps (lol_decode_reset_row); each row's
+    output at every step equals the oracle's decode of its document at the
+    row's position."""
+    import torch
+    from runtime_routed_transformer_amd.core import DeviceCore, DeviceDecoder
+
+    cfg = CoreConfig("dec_rows", batch=3, n=40, d=128, n_heads=2, d_ffn=256, L=3, D=3, W=8, S=3,
+                     mlp="swiglu", dtype="bf16", seed=70)
+    inp = parity.prepare(cfg)
+    steps, restart = 30, {1: 5, 2: 11}
+    ref = oracle.forward(inp, n_tokens=steps)
+    forced, _ = parity.forced_for_gpu(inp, ref, list(range(cfg.batch)), steps)
+    core = DeviceCore(inp)
+    core.set_forcing(forced_expert=forced)
+    dec = DeviceDecoder(core)
+    start = [0] * cfg.batch
+    got = np.zeros((steps, cfg.batch, cfg.d))
+    want = np.zeros_like(got)
+    for t in range(steps):
+        for b, t0 in restart.items():
+            if t == t0:
+                dec.reset_row(b)
+                start[b] = t
+        pos = [t - start[b] for b in range(cfg.batch)]
+        x = torch.stack([core.s0[b, pos[b]] for b in range(cfg.batch)]).contiguous()
+        got[t] = dec.step(None, x).cpu().numpy()
+        want[t] = np.stack([ref.s64[b, pos[b]] for b in range(cfg.batch)])
+    assert dec.flags() == 0
+    rel = float(np.abs(got - want).max() / np.abs(want).max())
+    print(f"rows at own positions: rel_err={rel:.3e}", flush=True)
+    assert rel <= parity.TOL["bf16"]
+
+
+def test_decode_step_replays_from_a_graph():
+    """With pos = -1 a decode step has no per-call arguments: captured once
+    in a HIP graph (torch.cuda.graph) and replayed per token, it gives the
+    eager steps' outputs bit for bit."""
+    import torch
+    from runtime_routed_transformer_amd.core import DeviceCore, DeviceDecoder
+
+    cfg = CoreConfig("dec_graph", batch=2, n=24, d=128, n_heads=2, d_ffn=256, L=3, D=2, W=8, S=3,
+                     mlp="swiglu", dtype="bf16", seed=71)
+    inp = parity.prepare(cfg)
+    core = DeviceCore(inp)
+    dec = DeviceDecoder(core)
+    eager = [dec.step(None, core.s0[:, p].contiguous()).clone() for p in range(cfg.n)]
+    assert dec.flags() == 0
+    x_in = torch.empty((cfg.batch, cfg.d), dtype=torch.float32, device=core.device)
+    y_out = torch.empty_like(x_in)
+    dec.reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec.step(None, x_in, y=y_out)
+    dec.reset()     # capture ran nothing; start the documents again
+    torch.cuda.synchronize()
+    for p in range(cfg.n):
+        x_in.copy_(core.s0[:, p])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_out, eager[p]), f"position {p}"
+    assert dec.flags() == 0
