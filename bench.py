@@ -341,6 +341,27 @@ def bench_decode(args):
     step_bytes = sum(decode_launch_bytes(cfg, k, n_exp[p, l]) for k in kinds
                      for p in range(steps) for l in range(cfg.D)) / steps
     proj_ms = sum(kt[k][0] for k in kinds) / steps
+    # the same K steps replayed from a HIP graph of one step (each row at its
+    # own position, pos = -1), after the timed region: the host issues one
+    # graph launch and one 16-byte-row input copy per step
+    x_in = torch.empty((cfg.batch, cfg.d), dtype=torch.float32, device=xs.device)
+    y_out = torch.empty_like(x_in)
+    dec.reset(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dec.step(None, x_in, y=y_out)
+    dec.reset(stream)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for p in range(steps):
+        x_in.copy_(xs[p])
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    assert dec.flags() == 0, "decode state flagged an error (graph replay)"
+    graph_ms = g0.elapsed_time(g1) / steps
     result = {
         "metric": DECODE_METRIC, "value": cfg.batch / (ms / 1e3), "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -356,6 +377,7 @@ def bench_decode(args):
                      "kernel_launches_timed": dom_n,
                      "bytes_per_launch_avg": timed_bytes / dom_n},
         "projections_gbs": step_bytes / (proj_ms / 1e3) / 1e9,
+        "graph_replay": {"ms_per_step": graph_ms, "tokens_per_s": cfg.batch / (graph_ms / 1e3)},
         "distinct_experts_per_depth_avg": float(n_exp.mean()),
         "kernels": per_kernel,
     }
