@@ -10,20 +10,22 @@
 // "What it costs": attention stays inside a window, so a depth only needs
 // the open window's keys and values.
 //
-// Per depth and document the state holds: the sum of the completed
-// windows' means, the running sum and length of the open window, its expert
-// and gate, and its keys and values.  One call runs, per depth:
-//   k_dec_route   close/open windows, route a window that opens
-//                 (one block per document)
-//   k_dec_gemv    attention RMSNorm + FiLM, QKV projection (grouped by expert)
+// The state holds each document's next position and, per depth and
+// document, the sum of the completed windows' means, the running sum and
+// length of the open window, its expert and gate, and its keys and values.
+// One call runs, per depth:
+//   k_dec_route   positions (depth 0), close/open windows, route a window
+//                 that opens, attention RMSNorm + FiLM (one block per document)
+//   k_dec_gemv    QKV projection (grouped by expert)
 //   k_dec_attn    RoPE, cache append, attention over the open window
 //   k_dec_gemv    output projection + residual
-//   k_dec_gemv    MLP RMSNorm + FiLM, gate/up + SwiGLU (or GELU)
+//   k_dec_norm    MLP RMSNorm + FiLM
+//   k_dec_gemv    gate/up + SwiGLU (or GELU)
 //   k_dec_gemv    down projection + gated blend
 // A token's rows are few (one per document), so the projections are
 // matrix-vector products bound by reading the weights once: every wave
-// streams a few weight rows of one expert with 16-byte loads, and all rows
-// (documents) routed to that expert share the read.
+// streams one weight row (one gate/up pair) of one expert with 16-byte
+// loads, and all rows (documents) routed to that expert share the read.
 #include <math.h>
 
 #include "lol_internal.h"
