@@ -150,14 +150,18 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 constexpr int TM = 4, TN = 2;           // 32 x 32 blocks per wave: 128 x 64 outputs
 constexpr int BK = 32;
 constexpr int GM = 4;
-// Three shapes of workgroup, WM x WN waves:
+// Four shapes of workgroup, WM x WN waves:
 //   2 x 2: 256 x 128 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
 //   2 x 4: 256 x 256 tile, 8 waves, 4-stage ring of 128 KiB, one per CU
 //          (persistent);
-//   1 x 4: 128 x 256 tile, 4 waves, 3-stage ring of 72 KiB, two per CU.
+//   1 x 4: 128 x 256 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
+//   1 x 8: 128 x 512 tile, 8 waves, 4-stage ring of 160 KiB (all of the
+//          LDS), one per CU (persistent).
 // 2 x 2 and 1 x 4 move the same bytes per MAC (every wave still owns 128 x
-// 64 outputs); 1 x 4 uses the 128-row tile tables, which fit expert row
-// counts that are multiples of 128 without a partial tile.
+// 64 outputs); 1 x 4 and 1 x 8 use the 128-row tile tables, which fit
+// expert row counts that are multiples of 128 without a partial tile, and
+// 1 x 8 loads 1.25x the stage bytes of 2 x 4 per MAC where two 1 x 4
+// workgroups load 1.5x.
 template <int WM, int WN> struct Shape {
   static constexpr int NW = WM * WN;                     // waves
   static constexpr int BMT = 32 * TM * WM;               // rows of A per tile
@@ -1042,9 +1046,10 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
     return hipErrorInvalidValue;  // fp32 mode rotates inside its attention kernel
   if (p.cfg.dtype == LOL_BF16) {
     // 256 x 256 tiles (persistent) when every expert's row count is a
-    // multiple of 256 and such tiles fill the CUs; otherwise 128 x 256 tiles
-    // from the 128-row table, which leave no partial tile when rows come in
-    // multiples of 128 (gate/up measured faster with 256 x 256 either way);
+    // multiple of 256 and such tiles fill the CUs; otherwise tiles from the
+    // 128-row table, which leave no partial tile when rows come in multiples
+    // of 128: 128 x 512 (persistent) when N allows and they fill the CUs,
+    // else 128 x 256 (gate/up measured faster with 256 x 256 either way);
     // 256 x 128 when N is not a multiple of 256
     const int n_w = EPI == EPI_SWIGLU ? 2 * a.N : a.N;   // weight rows
     if (n_w % 256 == 0) {
@@ -1054,6 +1059,8 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
       const bool rows256 = a.len_gcd % kTileM2 == 0 || EPI == EPI_SWIGLU || EPI == EPI_GELU;
       const long long tiles256 = (long long)(p.T / kTileM2) * (n_w / 256);
       if (rows256 && tiles256 >= ncu) return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
+      const long long tiles512 = (long long)(p.T / kTileM) * (n_w / 512);
+      if (n_w % 512 == 0 && tiles512 >= ncu) return launch_shape<EPI, 1, 8>(P, ws, n_w, st);
       return launch_shape<EPI, 1, 4>(P, ws, n_w, st);
     }
     return launch_shape<EPI, 2, 2>(P, ws, n_w, st);
