@@ -1048,8 +1048,11 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
     // 256 x 256 tiles (persistent) when every expert's row count is a
     // multiple of 256 and such tiles fill the CUs; otherwise tiles from the
     // 128-row table, which leave no partial tile when rows come in multiples
-    // of 128: 128 x 512 (persistent) when N allows and they fill the CUs,
-    // else 128 x 256 (gate/up measured faster with 256 x 256 either way);
+    // of 128: 128 x 512 (persistent) for long K (the down projection) when N
+    // allows and they fill the CUs, else 128 x 256 (measured: 128 x 512 is
+    // faster at K = 4096, slower at K = 1024, where the larger tile's
+    // prologue and epilogue weigh more; gate/up measured faster with
+    // 256 x 256 either way);
     // 256 x 128 when N is not a multiple of 256
     const int n_w = EPI == EPI_SWIGLU ? 2 * a.N : a.N;   // weight rows
     if (n_w % 256 == 0) {
@@ -1060,7 +1063,8 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
       const long long tiles256 = (long long)(p.T / kTileM2) * (n_w / 256);
       if (rows256 && tiles256 >= ncu) return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
       const long long tiles512 = (long long)(p.T / kTileM) * (n_w / 512);
-      if (n_w % 512 == 0 && tiles512 >= ncu) return launch_shape<EPI, 1, 8>(P, ws, n_w, st);
+      if (a.K >= 2048 && n_w % 512 == 0 && tiles512 >= ncu)
+        return launch_shape<EPI, 1, 8>(P, ws, n_w, st);
       return launch_shape<EPI, 1, 4>(P, ws, n_w, st);
     }
     return launch_shape<EPI, 2, 2>(P, ws, n_w, st);
