@@ -149,7 +149,7 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 // ---------------------------------------------------------------------------
 constexpr int TM = 4, TN = 2;           // 32 x 32 blocks per wave: 128 x 64 outputs
 constexpr int BK = 32;
-constexpr int GM = 4;
+constexpr int GM = 2;
 // Four shapes of workgroup, WM x WN waves:
 //   2 x 2: 256 x 128 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
 //   2 x 4: 256 x 256 tile, 8 waves, 4-stage ring of 128 KiB, one per CU
