@@ -59,6 +59,7 @@ struct GemmParams {
   int half;                // QKV_ROPE: d_head / 2
   int a_panel_rows;        // 0: A is [rows][K]; else A is in 32-k panels [K/32][a_panel_rows][32]
   int c_panel_rows;        // bf16 store epilogues: 0 = C is [rows][ldc]; else 32-column panels
+  int gm;                  // m-tiles per group of the tile order (see "Tile order")
 };
 
 // Writes 4 consecutive logical columns [col, col+4) of grouped row `row`.
@@ -149,7 +150,11 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 // ---------------------------------------------------------------------------
 constexpr int TM = 4, TN = 2;           // 32 x 32 blocks per wave: 128 x 64 outputs
 constexpr int BK = 32;
-constexpr int GM = 2;
+// m-tiles per group: 4 for the gate/up projection, 2 for the others
+// (same-box A/B at mid_bf16: QKV 124 vs 127 us with 2 rather than 4, gate/up
+// equal in time but with 819 instead of 659 MB of L2-miss traffic; 1 and 8
+// slower)
+constexpr int GM_GATE_UP = 4, GM_OTHER = 2;
 // Four shapes of workgroup, WM x WN waves:
 //   2 x 2: 256 x 128 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
 //   2 x 4: 256 x 256 tile, 8 waves, 4-stage ring of 128 KiB, one per CU
@@ -249,6 +254,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
   auto locate = [&](int uu, int &mt_, int &nt_, int &e_, int &row0_, int &row_end_) -> bool {
     const int t = xcd * per + uu;
     if (uu >= per || t >= R) return false;
+    const int GM = P.gm;
     const int grp = t / (GM * n_nt), within = t - grp * (GM * n_nt);
     const int gm = min(GM, n_mt - grp * GM);
     mt_ = grp * GM + within % gm;
@@ -1040,6 +1046,7 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.half = p.d_head / 2;
   P.a_panel_rows = a.a_panel_rows;
   P.c_panel_rows = a.c_panel_rows;
+  P.gm = (EPI == EPI_SWIGLU || EPI == EPI_GELU) ? GM_GATE_UP : GM_OTHER;
   if ((a.a_panel_rows || a.c_panel_rows) && p.cfg.dtype != LOL_BF16) return hipErrorInvalidValue;
   if (a.c_panel_rows && (EPI == EPI_RESID || EPI == EPI_BLEND || EPI == EPI_ACCUM)) return hipErrorInvalidValue;
   if (EPI == EPI_QKV_ROPE && (p.cfg.dtype != LOL_BF16 || (p.d_head != 32 && p.d_head != 64)))
