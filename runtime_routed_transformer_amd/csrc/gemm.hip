@@ -150,11 +150,11 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 // ---------------------------------------------------------------------------
 constexpr int TM = 4, TN = 2;           // 32 x 32 blocks per wave: 128 x 64 outputs
 constexpr int BK = 32;
-// m-tiles per group: 4 for the gate/up projection, 2 for the others
-// (same-box A/B at mid_bf16: QKV 124 vs 127 us with 2 rather than 4, gate/up
-// equal in time but with 819 instead of 659 MB of L2-miss traffic; 1 and 8
-// slower)
-constexpr int GM_GATE_UP = 4, GM_OTHER = 2;
+// m-tiles per group: 4 for the wide projections (8,192 weight rows and
+// more: gate/up, the vocabulary readout), 2 for the others (same-box A/B at
+// mid_bf16: QKV 124 vs 127 us with 2 rather than 4, gate/up equal in time
+// but with 819 instead of 659 MB of L2-miss traffic; 1 and 8 slower)
+constexpr int GM_WIDE = 4, GM_OTHER = 2;
 // Four shapes of workgroup, WM x WN waves:
 //   2 x 2: 256 x 128 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
 //   2 x 4: 256 x 256 tile, 8 waves, 4-stage ring of 128 KiB, one per CU
@@ -1046,7 +1046,7 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.half = p.d_head / 2;
   P.a_panel_rows = a.a_panel_rows;
   P.c_panel_rows = a.c_panel_rows;
-  P.gm = (EPI == EPI_SWIGLU || EPI == EPI_GELU) ? GM_GATE_UP : GM_OTHER;
+  P.gm = (EPI == EPI_SWIGLU ? 2 * a.N : a.N) >= 8192 ? GM_WIDE : GM_OTHER;
   if ((a.a_panel_rows || a.c_panel_rows) && p.cfg.dtype != LOL_BF16) return hipErrorInvalidValue;
   if (a.c_panel_rows && (EPI == EPI_RESID || EPI == EPI_BLEND || EPI == EPI_ACCUM)) return hipErrorInvalidValue;
   if (EPI == EPI_QKV_ROPE && (p.cfg.dtype != LOL_BF16 || (p.d_head != 32 && p.d_head != 64)))
