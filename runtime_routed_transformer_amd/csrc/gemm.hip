@@ -161,7 +161,9 @@ constexpr int GM_WIDE = 4, GM_OTHER = 2;
 //          (persistent);
 //   1 x 4: 128 x 256 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
 //   1 x 8: 128 x 512 tile, 8 waves, 4-stage ring of 160 KiB (all of the
-//          LDS), one per CU (persistent).
+//          LDS), one per CU (persistent);
+//   1 x 2: 128 x 128 tile, 2 waves, 3-stage ring of 48 KiB, for problems
+//          too small to fill the CUs with larger tiles.
 // 2 x 2 and 1 x 4 move the same bytes per MAC (every wave still owns 128 x
 // 64 outputs); 1 x 4 and 1 x 8 use the 128-row tile tables, which fit
 // expert row counts that are multiples of 128 without a partial tile, and
@@ -1072,6 +1074,10 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
       const long long tiles512 = (long long)(p.T / kTileM) * (n_w / 512);
       if (a.K >= 2048 && n_w % 512 == 0 && tiles512 >= ncu)
         return launch_shape<EPI, 1, 8>(P, ws, n_w, st);
+      // a small problem whose 128 x 256 tiles would fill at most half of the
+      // workgroup slots (two per CU): 128 x 128 tiles double the tile count
+      const long long tiles128x256 = (long long)(p.T / kTileM) * (n_w / 256);
+      if (tiles128x256 <= ncu) return launch_shape<EPI, 1, 2>(P, ws, n_w, st);
       return launch_shape<EPI, 1, 4>(P, ws, n_w, st);
     }
     return launch_shape<EPI, 2, 2>(P, ws, n_w, st);
