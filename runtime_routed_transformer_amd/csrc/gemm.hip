@@ -1069,8 +1069,15 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
       const hipError_t ec = cu_count(&ncu);
       if (ec != hipSuccess) return ec;
       const bool rows256 = a.len_gcd % kTileM2 == 0 || EPI == EPI_SWIGLU || EPI == EPI_GELU;
+      const bool rows128 = a.len_gcd % kTileM == 0;
       const long long tiles256 = (long long)(p.T / kTileM2) * (n_w / 256);
       if (rows256 && tiles256 >= ncu) return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
+      // expert rows that leave partial tiles in either table (windows whose
+      // lengths are not multiples of 128, packed documents): the persistent
+      // 256 x 256 shape, whose waves skip the MFMAs of rows past the expert
+      // (same-box A/B: forced_bf16 down 226 -> 201 us, QKV 151 -> 147 us;
+      // mid_bf16_packed down 284 -> 240 us)
+      if (!rows128 && tiles256 >= ncu) return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
       const long long tiles512 = (long long)(p.T / kTileM) * (n_w / 512);
       if (a.K >= 2048 && n_w % 512 == 0 && tiles512 >= ncu)
         return launch_shape<EPI, 1, 8>(P, ws, n_w, st);
