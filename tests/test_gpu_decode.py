@@ -87,6 +87,9 @@ CASES = [
     (CONFIG_BY_NAME["tiny_fp32"], 64, True),
     (SMALL.scaled(2, 200), 200, False),
     (CONFIG_BY_NAME["mid_bf16"].scaled(2, 300), 300, False),
+    # the benchmark's decode configuration: the 4 documents of the mid
+    # workload (4 per pass), the first 300 positions (two windows at depth 1)
+    (CONFIG_BY_NAME["mid_bf16"].scaled(4, 300).with_(name="mid_bf16_decode@4x300"), 300, False),
     # 32 experts with skewed bias: up to 4 distinct experts per depth
     (CONFIG_BY_NAME["sparse_bf16"].scaled(4, 270), 270, False),
     # every document on one expert per depth: 20 rows share each weight read
