@@ -229,8 +229,8 @@ const char *lol_core_kernel_name(int32_t kind);
 /* ---- Incremental decode -------------------------------------------------
  * The routed core one token at a time, for `batch` documents (every call
  * brings one token of each document, at the position the state holds for
- * it).  The review "Library of
- * Layers: Routing Whole Transformer Blocks at Runtime", Deriving prefix-only
+ * it).  The review "Library of Layers: Routing Whole Transformer Blocks at
+ * Runtime", Deriving prefix-only
  * routing, notes that a window's router reads only earlier, completed
  * windows (window 0: the document's first token and the depth vector), so a
  * window's route and gate are fixed when its first token arrives and a
@@ -241,8 +241,9 @@ const char *lol_core_kernel_name(int32_t kind);
  * the open window's running sum, length, expert and gate, and the open
  * window's keys and values ([W] slots per head).  Feeding tokens 0 .. n-1
  * gives, token by token, the s^(D) rows and path of lol_core_forward on the
- * whole documents, up to rounding (the GEMM operands are rounded at the
- * same points; the sums run in another order).
+ * whole documents, up to rounding (the projections' operands are rounded
+ * to bf16 at the same points, the attention weights stay fp32 here, and
+ * the sums run in another order).
  * Supported: every config lol_core_validate accepts with batch <= 64,
  * d <= 4096 and W <= 8192 (else LOL_EUNSUPPORTED). */
 
