@@ -1,5 +1,5 @@
 """CPU checks of bench.py's host logic: the one-GPU guard and the algorithmic
-work per launch that the roofline fractions are computed from (the survey's
+work per launch that the roofline fractions are computed from (the block's
 per-token FLOP and byte counts, evaluated at the workloads' sizes)."""
 import os
 import subprocess
