@@ -62,6 +62,11 @@ def test_sizes_and_validation(lib):
         assert B.lol_core_workspace_size(c) == 0
     c = make_config(base); c.L = 65
     assert B.lol_core_validate(c) == B.LOL_EUNSUPPORTED
+    # documents x window slots: 64 x 128 = 8,192 is the most one depth takes
+    c = make_config(base); c.L = 64; c.batch = 64; c.n = 254; c.W = 2; c.S = 1
+    assert B.lol_core_k_max(c) == 128 and B.lol_core_validate(c) == B.LOL_OK
+    c.batch = 65
+    assert B.lol_core_validate(c) == B.LOL_EUNSUPPORTED
     c = make_config(base); c.n_heads = 4      # d_head 128
     assert B.lol_core_validate(c) == B.LOL_EUNSUPPORTED
     c = make_config(base); c.d_ffn = 192       # bf16 needs multiples of 128

@@ -117,6 +117,10 @@ CASES = [
                 S=100, mlp="swiglu", dtype="bf16", seed=68), 700, False),
     (CoreConfig("dec_w300_fp32", batch=1, n=620, d=64, n_heads=2, d_ffn=128, L=2, D=2, W=300,
                 S=77, mlp="gelu", dtype="fp32", seed=69), 620, False),
+    # at the decode limits: d = 4,096 (64 heads) and W = 8,192 (a window
+    # longer than the document at both depths)
+    (CoreConfig("dec_limits_d4096_w8192", batch=2, n=40, d=4096, n_heads=64, d_ffn=256, L=3, D=2,
+                W=8192, S=4000, mlp="swiglu", dtype="bf16", seed=70), 40, True),
     # one-token documents; 5 documents (3 per pass group size rounds up to 8)
     (CoreConfig("dec_one_token", batch=5, n=1, d=128, n_heads=4, d_ffn=256, L=2, D=3, W=4, S=1,
                 mlp="gelu", dtype="bf16", seed=67), 1, True),

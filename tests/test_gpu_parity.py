@@ -73,6 +73,16 @@ EDGE = [
                W=16, S=37, mlp="swiglu", dtype="bf16", seed=27),
     CoreConfig("edge_dh32_bf16", batch=2, n=130, d=128, n_heads=4, d_ffn=384, L=5, D=2, W=64,
                S=32, mlp="swiglu", dtype="bf16", seed=28),
+    # at the limits: 64 experts (all used) and 64 documents x 128 window
+    # slots = 8,192 windows per depth, the most one bucketing pass takes;
+    # windows of 1 and 2 tokens, so nearly every M tile is partial (among 64
+    # experts most top-1 margins fall under the near-tie threshold, so most
+    # windows run forced to the oracle's choice; ids are compared on the rest)
+    CoreConfig("edge_limit_experts_slots", batch=64, n=254, d=128, n_heads=2, d_ffn=128, L=64,
+               D=2, W=2, S=1, mlp="swiglu", dtype="bf16", seed=41),
+    # a wide model: d = 4,096 (64 heads), on a short document
+    CoreConfig("edge_limit_wide_d", batch=1, n=40, d=4096, n_heads=64, d_ffn=256, L=2, D=2,
+               W=16, S=8, mlp="swiglu", dtype="bf16", seed=42),
 ]
 
 
