@@ -257,6 +257,43 @@ def test_forced_single_expert_is_looped_model(film):
     assert (res.expert[:, :, 0] == m).all()
 
 
+def test_mixed_forced_path_is_per_window_library_blocks():
+    """Algorithm 1 with a forced path: at every depth each window of the
+    shifted partition runs its own expert's block on its own tokens, and the
+    result is blended with that window's gate (s + alpha (E(s) - s)); here
+    every (depth, window) gets a different expert and gate, and the block is
+    the PyTorch one, so a wrong expert, gate or window boundary anywhere
+    shows up."""
+    cfg = tiny(L=4, D=3, n=40, W=12, S=5, film=True)
+    inp = generate(cfg)
+    rng = np.random.default_rng(5)
+    forced = np.full((cfg.D, cfg.batch, cfg.k_max), -1, np.int32)
+    gate = np.full((cfg.D, cfg.batch, cfg.k_max), np.nan, np.float32)
+    for depth in range(1, cfg.D + 1):
+        for k in range(len(oracle.partition(cfg.n, cfg.W, cfg.S, depth))):
+            for b in range(cfg.batch):
+                forced[depth - 1, b, k] = (3 * depth + 2 * k + b) % cfg.L
+                gate[depth - 1, b, k] = np.float32(rng.uniform(0.1, 0.9))
+    res = oracle.forward(inp, forced_expert=forced, forced_gate=gate)
+    for b in range(cfg.batch):
+        s = inp.s0[b].astype(np.float64)
+        for depth in range(1, cfg.D + 1):
+            nxt = s.copy()
+            film = (inp.film_gamma[depth - 1], inp.film_beta[depth - 1])
+            for k, (a0, a1) in enumerate(oracle.partition(cfg.n, cfg.W, cfg.S, depth)):
+                m = forced[depth - 1, b, k]
+                x = s[a0:a1 + 1]
+                y = torch_block.block(x, inp.wqkv[m], inp.wo[m], inp.w_gu[m], inp.w_down[m],
+                                      inp.g_attn[m], inp.g_ffn[m], cfg.n_heads, "swiglu",
+                                      film=film)
+                nxt[a0:a1 + 1] = x + float(gate[depth - 1, b, k]) * (y - x)
+            s = nxt
+        np.testing.assert_allclose(res.s64[b], s, rtol=0, atol=1e-11)
+    used = forced >= 0
+    np.testing.assert_array_equal(res.expert[used], forced[used])
+    np.testing.assert_array_equal(res.gate[used], gate[used])
+
+
 # ---------------------------------------------------------------- whole-core invariants
 def test_stride_invariants():
     inp = generate(tiny())
