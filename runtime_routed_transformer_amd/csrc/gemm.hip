@@ -218,6 +218,21 @@ __device__ __forceinline__ void reads_then_mfmas() {
   __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // the MFMAs
 }
 
+// Scheduling hint for an MFMA block that also carries N stage loads: N
+// groups of "a share of the M MFMAs, then one load".  Issued as one burst
+// right after the stage barrier, the loads of all waves queue in the CU's
+// memory pipeline together and hold up the MFMAs behind them; spread over
+// the block they enter it one at a time (gate/up main loop 57.9 -> 49.7
+// kilo-clocks per 256 x 256 tile, down 232 -> 202, same-box probe).
+template <int N, int M, int Q = 0>
+__device__ __forceinline__ void mfma_load_groups() {
+  if constexpr (Q < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, (M * (Q + 1)) / N - (M * Q) / N, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    mfma_load_groups<N, M, Q + 1>();
+  }
+}
+
 // silu(x) = x / (1 + e^-x) with the hardware exp2 and reciprocal (about one
 // ulp each, far below the bf16 rounding of the result).
 __device__ __forceinline__ float silu_fast(float x) {
@@ -418,8 +433,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_
         if (ACT) {
           mfmas(fw1, fx1);
           __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // the LDS reads
-          __builtin_amdgcn_sched_group_barrier(0x020, NQ, 0);       // the stage loads
-          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // the MFMAs
+          mfma_load_groups<NQ, TM * TN>();                          // MFMAs, stage loads among them
         }
       }
       // drain: nothing left to load
@@ -814,9 +828,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
 #pragma unroll
       for (int im = 0; im < 2; ++im)
         acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][in], fx[cur][im], acc[in][im], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, NQ, 0);       // the stage loads
     __builtin_amdgcn_sched_group_barrier(0x100, TN + 2, 0);   // the fragment reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * TN, 0);   // the MFMAs
+    mfma_load_groups<NQ, 2 * TN>();                           // MFMAs, stage loads among them
   };
   for (int kt = 0; kt < nk; kt += 2) {
     step(kt, std::integral_constant<int, 0>{});
