@@ -535,9 +535,11 @@ class FullResult:
     coda_out: np.ndarray       # [B][n][d] float64
 
 
-def full_forward(full, core_forced_expert: Optional[np.ndarray] = None) -> FullResult:
+def full_forward(full, core_forced_expert: Optional[np.ndarray] = None,
+                 core_forced_gate: Optional[np.ndarray] = None) -> FullResult:
     """Algorithm 1 end to end: embedding, prelude stack, routed core, coda
-    stack, readout.  ``full`` is a ``FullInputs``."""
+    stack, readout.  ``full`` is a ``FullInputs``; the forcing arrays go to
+    the routed core as in ``forward``."""
     core_cfg = full.core.cfg
     pre = [expert_params(full.prelude, m) for m in range(full.prelude.cfg.L)]
     coda = [expert_params(full.coda, m) for m in range(full.coda.cfg.L)]
@@ -546,7 +548,7 @@ def full_forward(full, core_forced_expert: Optional[np.ndarray] = None) -> FullR
                    for b in range(core_cfg.batch)])
     # the core's input s^(0) is fp32, as on the device
     core_in = dataclasses.replace(full.core, s0=h0.astype(np.float32))
-    res = forward(core_in, forced_expert=core_forced_expert)
+    res = forward(core_in, forced_expert=core_forced_expert, forced_gate=core_forced_gate)
     hD = np.stack([causal_stack(res.s64[b], coda, core_cfg.n_heads, core_cfg.rms_eps,
                                 core_cfg.rope_theta) for b in range(core_cfg.batch)])
     logits = np.stack([lm_head(hD[b], full.g_final, full.w_vocab, core_cfg.rms_eps)

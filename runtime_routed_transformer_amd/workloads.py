@@ -65,6 +65,7 @@ class CoreConfig:
     path_mode: str = "free"      # "free" | "forced_seq" (one id sequence for all windows)
     router: str = "tied"         # "tied" | "per_depth" (one router per routed depth)
     film_mode: str = "depth"     # "depth" (shared by experts) | "depth_expert"
+    router_std: float = WEIGHT_STD   # std of W_r; larger values give peaked routes with clear margins
 
     @property
     def d_head(self) -> int:
@@ -166,7 +167,8 @@ def generate(cfg: CoreConfig) -> CoreInputs:
     Order of draws: s0; then per expert wqkv, wo, w_gu (or w_1), w_down
     (or w_2), g_attn, g_ffn; then FiLM gamma, beta; then W_r and e_depth;
     then, for the forced-sequence workload, the per-depth expert ids.
-    Projections, W_r and e_depth are N(0, 0.02^2); gains and FiLM gamma are
+    Projections, W_r and e_depth are N(0, 0.02^2) (W_r: N(0, router_std^2),
+    0.02 unless a test asks for peaked routes); gains and FiLM gamma are
     1 + N(0, 0.02^2); FiLM beta is N(0, 0.02^2); b_r = 0; expert_bias = 0
     (the skewed workload's bias is calibrated afterwards by the test harness).
     """
@@ -196,7 +198,7 @@ def generate(cfg: CoreConfig) -> CoreInputs:
     else:
         film_gamma = film_beta = None
     per_depth = cfg.router == "per_depth"
-    w_r = _normal(rng, (D, L, d) if per_depth else (L, d), WEIGHT_STD)
+    w_r = _normal(rng, (D, L, d) if per_depth else (L, d), cfg.router_std)
     e_depth = _normal(rng, (D, d), WEIGHT_STD)
     b_r = np.zeros((D, L) if per_depth else L, np.float32)
     expert_bias = np.zeros(L, np.float32)

@@ -115,6 +115,23 @@ def test_parity_edge_cases(cfg):
     _report(parity.run(parity.prepare(cfg)))
 
 
+def test_parity_many_experts_clear_margins():
+    """Free routing over 32 experts with every route clear of the near-tie
+    threshold: W_r drawn with std 1.0 instead of 0.02 makes the router's
+    probabilities peaked (at 0.02 most margins among 32 experts fall under
+    1e-3 and those windows run forced).  All 144 windows' ids, gates and
+    margins are compared and none is forced; 16 to 19 experts are used per
+    depth.  The 50x larger router weights carry the bf16 states' rounding
+    50x into the later depths' logits, so those gates get 50x the usual
+    bound; depth 1, which routes the same s^(0) on both sides, keeps 1e-5."""
+    cfg = CoreConfig("free_L32_clear_margins", batch=8, n=1024, d=1024, n_heads=16, d_ffn=4096,
+                     L=32, D=4, W=256, S=128, mlp="swiglu", dtype="bf16", seed=43, router_std=1.0)
+    print(f"[parity] {cfg.name}", flush=True)
+    rep = parity.run(parity.prepare(cfg), gate_tol_scale=1.0 / 0.02)
+    _report(rep)
+    assert rep.forced_windows == 0 and rep.ids_compared == 144, str(rep)
+
+
 def test_gate_zero_identity_and_determinism_and_inplace():
     import torch
     from runtime_routed_transformer_amd.core import DeviceCore

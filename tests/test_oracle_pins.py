@@ -501,6 +501,60 @@ def test_causal_stack_is_the_ordinary_decoder_stack():
         np.testing.assert_allclose(res.s64[b], want, rtol=0, atol=1e-11)
 
 
+def test_full_forward_is_embedding_prelude_core_coda_readout():
+    """Algorithm 1 end to end (paper App. A: prelude on the tokens, routed
+    core, coda, vocabulary readout), composed from PyTorch library routines.
+    With one window per document (W = n, S = 0) and every core window forced
+    to expert m with gate 1, the core is D applications of block m, each
+    with its depth's FiLM, so the whole forward is embedding -> prelude
+    blocks -> core blocks -> coda blocks -> rms_norm -> linear.  The expert
+    and the depths' FiLM rows differ, so feeding the coda the prelude's
+    output, skipping a depth, taking the wrong depth's FiLM or the wrong
+    expert all fail.  A gate-0 core is the identity between the stacks."""
+    import torch
+    import torch.nn.functional as F
+    from runtime_routed_transformer_amd.workloads import FullConfig, generate_full
+    n = 24
+    full = generate_full(FullConfig("pin_full_fwd", tiny(n=n, W=n, S=0, D=2), vocab=57, prelude=2,
+                                    coda=2, seed=13))
+    cfg, m = full.core.cfg, 1
+    shape = (cfg.D, cfg.batch, cfg.k_max)
+    forced = np.full(shape, m, np.int32)
+    got = oracle.full_forward(full, core_forced_expert=forced,
+                              core_forced_gate=np.ones(shape, np.float32))
+
+    def stack(x, part, film_of=None, experts=None):
+        for l, e in enumerate(experts if experts is not None else range(part.cfg.L)):
+            x = torch_block.block(x, part.wqkv[e], part.wo[e], part.w_gu[e], part.w_down[e],
+                                  part.g_attn[e], part.g_ffn[e], cfg.n_heads, cfg.mlp,
+                                  eps=cfg.rms_eps, theta=cfg.rope_theta,
+                                  film=None if film_of is None else film_of(l))
+        return x
+
+    core = full.core
+    film = lambda l: (core.film_gamma[l], core.film_beta[l])
+    emb = F.embedding(torch.from_numpy(full.tokens.astype(np.int64)),
+                      torch.from_numpy(full.embedding.astype(np.float64))).numpy()
+    for b in range(cfg.batch):
+        h0 = stack(emb[b], full.prelude)
+        np.testing.assert_allclose(got.prelude_out[b], h0, rtol=0, atol=1e-11)
+        # the core's input is rounded to fp32 (its storage type), as in full_forward
+        hc = stack(h0.astype(np.float32).astype(np.float64), core, film, [m] * cfg.D)
+        hD = stack(hc, full.coda)
+        np.testing.assert_allclose(got.coda_out[b], hD, rtol=0, atol=1e-10)
+        logits = F.linear(F.rms_norm(torch.from_numpy(hD), (cfg.d,),
+                                     weight=torch.from_numpy(full.g_final.astype(np.float64)),
+                                     eps=cfg.rms_eps),
+                          torch.from_numpy(full.w_vocab.astype(np.float64))).numpy()
+        np.testing.assert_allclose(got.logits[b], logits, rtol=0, atol=1e-10)
+    # gate 0: the core passes its (fp32) input through
+    ident = oracle.full_forward(full, core_forced_expert=forced,
+                                core_forced_gate=np.zeros(shape, np.float32))
+    for b in range(cfg.batch):
+        h0 = stack(emb[b], full.prelude).astype(np.float32).astype(np.float64)
+        np.testing.assert_allclose(ident.coda_out[b], stack(h0, full.coda), rtol=0, atol=1e-10)
+
+
 # ---------------------------------------------------------------- packed documents
 def test_packed_documents_route_from_their_own_prefix():
     """Packed documents (blog 'The forward pass, term by term': the router's
