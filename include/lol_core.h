@@ -91,12 +91,22 @@ typedef struct {
  *                               (the paper's gamma_{l,s}, beta_{l,s});
  *                            1: [D][L][2][d], per depth and expert (the
  *                               released configs' depth_expert_film): a
- *                               window uses the FiLM of its chosen expert. */
+ *                               window uses the FiLM of its chosen expert.
+ *   wo_panels              NULL, or W_o already rearranged by
+ *                          lol_prepare_wo_panels (see there).  When the
+ *                          forward's fused output projection is used (bf16,
+ *                          d a multiple of 256 up to 1024) and this is NULL,
+ *                          every forward rearranges W_o into its workspace
+ *                          first; given, the forward reads it and does not.
+ *                          Must hold the panels of the same wo.
+ * Callers that build this struct must set every member (NULL / 0 where not
+ * used). */
 typedef struct {
   const void *wqkv, *wo, *w_gu, *w_down;
   const float *g_attn, *g_ffn;
   const float *film_gamma, *film_beta;
   int32_t film_per_expert;
+  const void *wo_panels;
 } lol_library;
 
 /* The router (DEVICE, fp32):
@@ -116,11 +126,17 @@ typedef struct {
  * document and window ordinal; slots k >= K_l hold expert -1, gate 0,
  * margin 0.  expert: chosen library index; gate: alpha applied to the
  * update; margin: (a+b)_top1 - (a+b)_top2 of the free router (+inf when
- * L = 1).  Any member may be NULL (not written). */
+ * L = 1).
+ * util (DEVICE [D][L] int32): the number of windows routed to each expert
+ * at each depth, the per-depth expert utilisation the paper plots as a
+ * heat map (Sec. 4.2, Fig. 4); written by the forwards, not by decode.
+ * Any member may be NULL (not written); callers that build this struct
+ * must set every member. */
 typedef struct {
   int32_t *expert;
   float *gate;
   float *margin;
+  int32_t *util;
 } lol_path;
 
 /* ceil(n / W) + 1, or -1 for an invalid config.  HOST, pure. */
@@ -193,6 +209,52 @@ lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
                                  const int32_t *forced_expert, const float *forced_gate,
                                  float *s_out, const lol_path *path,
                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- Static weight preparation ------------------------------------------
+ * The fused output projection reads W_o in 16-k panels, [L][d/16][d][16]:
+ * panel p of expert e holds W_o[e][j][16 p .. 16 p + 15] for every output
+ * row j in order, so that one 16-column step of an expert's W_o is one
+ * contiguous block.  The weights do not change between forwards, so a
+ * caller can rearrange them once and pass the result as
+ * lol_library.wo_panels.
+ * lol_prepare_wo_panels_size: bytes of that buffer for cfg, or 0 when cfg
+ * does not use the fused output projection (fp32, or d not a multiple of
+ * 256, or d > 1024) or is invalid.  HOST, pure.
+ * lol_prepare_wo_panels: wo (DEVICE [L][d][d] bf16) -> wo_panels (DEVICE,
+ * the size above, 16-byte aligned; must not overlap wo).  Asynchronous on
+ * stream.  LOL_EUNSUPPORTED when the size above is 0, LOL_EINVAL for NULL
+ * or misaligned pointers. */
+size_t lol_prepare_wo_panels_size(const lol_core_config *cfg);
+lol_status lol_prepare_wo_panels(const lol_core_config *cfg, const void *wo, void *wo_panels,
+                                 void *stream);
+
+/* ---- Expert bucketing of the last routed depth --------------------------
+ * A forward groups every depth's windows by chosen expert (the grouped
+ * dispatch of the explainer "Library of Layers: a transformer that picks
+ * its own layer order", What it costs): windows routed to expert e, in
+ * (document, window) order, form one contiguous range of "grouped rows",
+ * one row per token, and the expert GEMMs walk that range in tiles of 128
+ * or 256 rows.  lol_core_read_buckets copies those tables, as the workspace
+ * holds them after the last routed depth of the most recent forward on it,
+ * into `out` (DEVICE int32, lol_core_buckets_size(cfg) entries), laid out
+ * back to back as
+ *   counts   [L]            windows routed to each expert
+ *   row_off  [L + 1]        first grouped row of each expert; row_off[L] =
+ *                           tokens routed
+ *   win_row0 [batch K_max]  first grouped row of window slot b K_max + k,
+ *                           -1 for a slot without a window
+ *   n_tiles  [2]            tiles in use in the 128- and 256-row tables
+ *   tiles128 [M128][2]      (expert, first grouped row) per 128-row tile:
+ *                           every expert's full tiles in expert order, then
+ *                           each expert's partial last tile in expert
+ *                           order; unused entries (-1, 0)
+ *   tiles256 [M256][2]      the same for 256-row tiles
+ * with M128 = ceil(batch n / 128) + L and M256 = ceil(batch n / 256) + L.
+ * Asynchronous on stream (device-to-device copies).  For inspection and
+ * tests; the forward does not need it. */
+size_t lol_core_buckets_size(const lol_core_config *cfg);
+lol_status lol_core_read_buckets(const lol_core_config *cfg, const void *workspace,
+                                 size_t workspace_bytes, int32_t *out, void *stream);
 
 /* Device-side error flags of the last forward that used `workspace` (and,
  * LOL_FLAG_BAD_POS, of decode calls on a decode state). */

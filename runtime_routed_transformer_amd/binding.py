@@ -39,7 +39,7 @@ class lol_core_config(ctypes.Structure):
 class lol_library(ctypes.Structure):
     _fields_ = [(name, c_void_p) for name in
                 ("wqkv", "wo", "w_gu", "w_down", "g_attn", "g_ffn", "film_gamma", "film_beta")] + \
-               [("film_per_expert", c_int32)]
+               [("film_per_expert", c_int32), ("wo_panels", c_void_p)]
 
 
 class lol_router(ctypes.Structure):
@@ -48,7 +48,7 @@ class lol_router(ctypes.Structure):
 
 
 class lol_path(ctypes.Structure):
-    _fields_ = [(name, c_void_p) for name in ("expert", "gate", "margin")]
+    _fields_ = [(name, c_void_p) for name in ("expert", "gate", "margin", "util")]
 
 
 _SIGNATURES.update({
@@ -63,6 +63,11 @@ _SIGNATURES.update({
                                         POINTER(lol_router), c_void_p, c_void_p, c_void_p,
                                         POINTER(lol_path), c_void_p, c_size_t, c_void_p]),
     "lol_core_read_flags": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
+    "lol_prepare_wo_panels_size": (c_size_t, [POINTER(lol_core_config)]),
+    "lol_prepare_wo_panels": (c_int32, [POINTER(lol_core_config), c_void_p, c_void_p, c_void_p]),
+    "lol_core_buckets_size": (c_size_t, [POINTER(lol_core_config)]),
+    "lol_core_read_buckets": (c_int32, [POINTER(lol_core_config), c_void_p, c_size_t, c_void_p,
+                                        c_void_p]),
     "lol_core_timing_enable": (c_int32, [c_uint32]),
     "lol_core_timing_depth": (c_int32, [c_int32]),
     "lol_embed": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
@@ -151,6 +156,22 @@ def lol_core_read_flags(workspace, stream) -> int:
     out = c_uint32(0)
     _check(load().lol_core_read_flags(workspace, ctypes.byref(out), stream), "lol_core_read_flags")
     return int(out.value)
+
+
+def lol_prepare_wo_panels_size(cfg: lol_core_config) -> int:
+    return load().lol_prepare_wo_panels_size(ctypes.byref(cfg))
+
+
+def lol_prepare_wo_panels(cfg, wo, wo_panels, stream) -> int:
+    return load().lol_prepare_wo_panels(ctypes.byref(cfg), wo, wo_panels, stream)
+
+
+def lol_core_buckets_size(cfg: lol_core_config) -> int:
+    return load().lol_core_buckets_size(ctypes.byref(cfg))
+
+
+def lol_core_read_buckets(cfg, workspace, workspace_bytes, out, stream) -> int:
+    return load().lol_core_read_buckets(ctypes.byref(cfg), workspace, workspace_bytes, out, stream)
 
 
 def lol_decode_state_size(cfg: lol_core_config) -> int:

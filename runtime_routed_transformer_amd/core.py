@@ -51,11 +51,23 @@ class DeviceCore:
         self.film_gamma, self.film_beta = f32(inp.film_gamma), f32(inp.film_beta)
         self.w_r, self.b_r = f32(inp.w_r), f32(inp.b_r)
         self.e_depth, self.expert_bias = f32(inp.e_depth), f32(inp.expert_bias)
+        # W_o in the fused output projection's panel layout, rearranged once
+        # here rather than in every forward (None where the config does not
+        # use it)
+        self.wo_panels = None
+        panel_bytes = B.lol_prepare_wo_panels_size(self.ccfg)
+        if panel_bytes:
+            self.wo_panels = torch.empty(panel_bytes, dtype=torch.uint8, device=dev)
+            status = B.lol_prepare_wo_panels(self.ccfg, _ptr(self.w["wo"]), _ptr(self.wo_panels),
+                                             torch.cuda.current_stream(dev).cuda_stream)
+            if status != B.LOL_OK:
+                raise B.LolError(status, "lol_prepare_wo_panels")
         self.lib = B.lol_library(
             wqkv=_ptr(self.w["wqkv"]), wo=_ptr(self.w["wo"]), w_gu=_ptr(self.w["w_gu"]),
             w_down=_ptr(self.w["w_down"]), g_attn=_ptr(self.g_attn), g_ffn=_ptr(self.g_ffn),
             film_gamma=_ptr(self.film_gamma), film_beta=_ptr(self.film_beta),
-            film_per_expert=1 if self.cfg.film_mode == "depth_expert" else 0)
+            film_per_expert=1 if self.cfg.film_mode == "depth_expert" else 0,
+            wo_panels=_ptr(self.wo_panels))
         self.rt = B.lol_router(w_r=_ptr(self.w_r), b_r=_ptr(self.b_r), e_depth=_ptr(self.e_depth),
                                expert_bias=_ptr(self.expert_bias),
                                per_depth=1 if self.cfg.router == "per_depth" else 0)
@@ -66,8 +78,9 @@ class DeviceCore:
         self.path_expert = torch.empty(shape, dtype=torch.int32, device=dev)
         self.path_gate = torch.empty(shape, dtype=torch.float32, device=dev)
         self.path_margin = torch.empty(shape, dtype=torch.float32, device=dev)
+        self.path_util = torch.empty((self.cfg.D, self.cfg.L), dtype=torch.int32, device=dev)
         self.path = B.lol_path(expert=_ptr(self.path_expert), gate=_ptr(self.path_gate),
-                               margin=_ptr(self.path_margin))
+                               margin=_ptr(self.path_margin), util=_ptr(self.path_util))
         self.s_out = torch.empty_like(self.s0)
         self.forced_expert = None
         self.forced_gate = None
@@ -115,6 +128,33 @@ class DeviceCore:
         if status != B.LOL_OK:
             raise B.LolError(status, "lol_core_forward_docs")
         return s_out
+
+    def read_buckets(self, stream: Optional[torch.cuda.Stream] = None) -> dict:
+        """The last routed depth's expert bucketing of the most recent forward
+        (``lol_core_read_buckets``), split into its named tables (numpy)."""
+        n = B.lol_core_buckets_size(self.ccfg)
+        out = torch.empty(n, dtype=torch.int32, device=self.device)
+        st = (stream or torch.cuda.current_stream(self.device)).cuda_stream
+        status = B.lol_core_read_buckets(self.ccfg, self.workspace.data_ptr(), self.ws_bytes,
+                                         out.data_ptr(), st)
+        if status != B.LOL_OK:
+            raise B.LolError(status, "lol_core_read_buckets")
+        torch.cuda.synchronize(self.device)
+        a = out.cpu().numpy()
+        L, slots = self.cfg.L, self.cfg.batch * self.k_max
+        m128 = -(-self.cfg.batch * self.cfg.n // 128) + L
+        m256 = -(-self.cfg.batch * self.cfg.n // 256) + L
+        sizes = (("counts", L), ("row_off", L + 1), ("win_row0", slots), ("n_tiles", 2),
+                 ("tiles128", 2 * m128), ("tiles256", 2 * m256))
+        if sum(sz for _, sz in sizes) != n:
+            raise RuntimeError("lol_core_buckets_size disagrees with the documented layout")
+        res, off = {}, 0
+        for name, sz in sizes:
+            res[name] = a[off:off + sz].copy()
+            off += sz
+        res["tiles128"] = res["tiles128"].reshape(m128, 2)
+        res["tiles256"] = res["tiles256"].reshape(m256, 2)
+        return res
 
     def flags(self, stream: Optional[torch.cuda.Stream] = None) -> int:
         st = (stream or torch.cuda.current_stream(self.device)).cuda_stream

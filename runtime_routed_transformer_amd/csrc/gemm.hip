@@ -1140,7 +1140,8 @@ hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws,
   const int d = p.cfg.d;
   ONormParams P;
   P.A = reinterpret_cast<const bf16_t *>(ws.o);
-  P.Wp = ws.wo_p;
+  // W_o in panels: the caller's (prepared once) or the forward's own copy
+  P.Wp = lib.wo_panels ? reinterpret_cast<const bf16_t *>(lib.wo_panels) : ws.wo_p;
   P.mtile = ws.mtile;
   P.mcount = ws.mcount;
   P.toff = ws.toff;
@@ -1167,12 +1168,12 @@ hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws,
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_pack_wo(const Plan &p, const Workspace &ws, const lol_library &lib, hipStream_t st) {
-  if (!ws.wo_p) return hipErrorInvalidValue;
-  const int d = p.cfg.d;
-  const long long pieces = (long long)p.cfg.L * d * d / 8;   // 16-byte pieces
+hipError_t launch_pack_wo(const lol_core_config &c, const void *wo, void *wo_p, hipStream_t st) {
+  if (!wo || !wo_p) return hipErrorInvalidValue;
+  const int d = c.d;
+  const long long pieces = (long long)c.L * d * d / 8;   // 16-byte pieces
   lol_launch(k_pack_panels, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const bf16_t *>(lib.wo), ws.wo_p, d, pieces);
+                     reinterpret_cast<const bf16_t *>(wo), reinterpret_cast<bf16_t *>(wo_p), d, pieces);
   return hipGetLastError();
 }
 

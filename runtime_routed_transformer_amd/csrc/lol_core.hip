@@ -291,7 +291,9 @@ lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
   const bool qkv_panels = bf16;    // u from the attention norm
   const bool down_panels = bf16;   // hid from the gate/up epilogue
   LOL_TRY(KK_SETUP, launch_setup(p, ws, st));
-  if (fused_o) LOL_TRY(KK_SETUP, launch_pack_wo(p, ws, *lib, st));
+  // W_o in 16-k panels for the fused output projection, unless the caller
+  // prepared them once (lol_prepare_wo_panels)
+  if (fused_o && !lib->wo_panels) LOL_TRY(KK_SETUP, launch_pack_wo(c, lib->wo, ws.wo_p, st));
   for (int l = 0; l < c.D; ++l) {
     cur_depth = l;
     const float *s = l == 0 ? s0 : s_out;   // depth input
@@ -473,6 +475,61 @@ lol_status lol_decode_read_flags(void *state, uint32_t *flags, void *stream) {
   if (hipStreamSynchronize(st) != hipSuccess) return LOL_EHIP;
   if (hipMemsetAsync(dflags, 0, sizeof(uint32_t), st) != hipSuccess) return LOL_EHIP;
   if (hipStreamSynchronize(st) != hipSuccess) return LOL_EHIP;
+  return LOL_OK;
+}
+
+size_t lol_prepare_wo_panels_size(const lol_core_config *cfg) {
+  if (validate(cfg) != LOL_OK || !o_norm_eligible(*cfg)) return 0;
+  return (size_t)cfg->L * cfg->d * cfg->d * 2;
+}
+
+lol_status lol_prepare_wo_panels(const lol_core_config *cfg, const void *wo, void *wo_panels,
+                                 void *stream) {
+  const lol_status vs = validate(cfg);
+  if (vs != LOL_OK) return vs;
+  if (!o_norm_eligible(*cfg)) return LOL_EUNSUPPORTED;
+  if (!wo || !wo_panels || (reinterpret_cast<uintptr_t>(wo) & 15) ||
+      (reinterpret_cast<uintptr_t>(wo_panels) & 15))
+    return LOL_EINVAL;
+  const size_t bytes = lol_prepare_wo_panels_size(cfg);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(wo), b = reinterpret_cast<uintptr_t>(wo_panels);
+  if (a < b + bytes && b < a + bytes) return LOL_EINVAL;   // overlapping buffers
+  if (launch_pack_wo(*cfg, wo, wo_panels, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LOL_EHIP;
+  return LOL_OK;
+}
+
+size_t lol_core_buckets_size(const lol_core_config *cfg) {
+  if (validate(cfg) != LOL_OK) return 0;
+  const Plan p = make_plan(cfg);
+  Workspace w;
+  workspace_layout(p, nullptr, &w);
+  return (size_t)cfg->L + (cfg->L + 1) + (size_t)p.n_slots + 2 + 2 * (size_t)w.max_mtiles +
+         2 * (size_t)w.max_mtiles2;
+}
+
+lol_status lol_core_read_buckets(const lol_core_config *cfg, const void *workspace,
+                                 size_t workspace_bytes, int32_t *out, void *stream) {
+  const lol_status vs = validate(cfg);
+  if (vs != LOL_OK) return vs;
+  if (!out) return LOL_EINVAL;
+  const Plan p = make_plan(cfg);
+  if (!workspace || workspace_bytes < workspace_layout(p, nullptr, nullptr) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return LOL_EWORKSPACE;
+  Workspace w;
+  workspace_layout(p, static_cast<char *>(const_cast<void *>(workspace)), &w);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t L = cfg->L;
+  struct Piece { const int32_t *src; size_t count; } pieces[] = {
+      {w.ecount, L}, {w.toff, L + 1}, {w.win_row0, (size_t)p.n_slots}, {w.mcount, 2},
+      {w.mtile, 2 * (size_t)w.max_mtiles}, {w.mtile2, 2 * (size_t)w.max_mtiles2}};
+  int32_t *dst = out;
+  for (const Piece &pc : pieces) {
+    if (hipMemcpyAsync(dst, pc.src, pc.count * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return LOL_EHIP;
+    dst += pc.count;
+  }
   return LOL_OK;
 }
 

@@ -163,7 +163,7 @@ bool o_norm_eligible(const lol_core_config &c);   // bf16, d a multiple of 256 u
 bool o_norm_fused(const Plan &p);                  // eligible and the device's LDS holds the ring
 // W_o [L][d][d] -> 16-k panels [L][d/16][d][16]: one 16-k stage of all d
 // rows of an expert becomes one contiguous block
-hipError_t launch_pack_wo(const Plan &p, const Workspace &ws, const lol_library &lib, hipStream_t st);
+hipError_t launch_pack_wo(const lol_core_config &c, const void *wo, void *wo_p, hipStream_t st);
 // u_panel_rows > 0 writes u in 32-k panels [d/32][u_panel_rows][32] (the
 // A layout the next GEMM reads with GemmArgs::a_panel_rows)
 hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws, const float *s_in,

@@ -162,7 +162,8 @@ __global__ void __launch_bounds__(1024) k_route_all(
     int32_t *__restrict__ row_tok, int32_t *__restrict__ row_pos, int32_t *__restrict__ row_exp,
     float *__restrict__ row_gate, float *__restrict__ zlog_g, int n, int nch, int L, int W, int delta,
     int K, int K_max, int B, int depth, int32_t *__restrict__ win_len,
-    const int32_t *__restrict__ doc_start, const int32_t *__restrict__ doc_len, int n_tokens) {
+    const int32_t *__restrict__ doc_start, const int32_t *__restrict__ doc_len, int n_tokens,
+    int32_t *__restrict__ path_util) {
   __shared__ int s_exp[kMaxSlots];
   __shared__ int s_len[kMaxSlots];
   __shared__ int cnt_w[kMaxExperts], cnt_t[kMaxExperts];
@@ -316,7 +317,10 @@ __global__ void __launch_bounds__(1024) k_route_all(
   }
   __syncthreads();
   for (int e = tid; e <= L; e += blockDim.x) toff_out[e] = toff[e];
-  for (int e = tid; e < L; e += blockDim.x) ecount[e] = cnt_w[e];
+  for (int e = tid; e < L; e += blockDim.x) {
+    ecount[e] = cnt_w[e];
+    if (path_util) path_util[(size_t)depth * L + e] = cnt_w[e];
+  }
   // first grouped row of every window: one wave per expert walks the slots in
   // order, 64 at a time, with an exclusive scan of the lengths
   for (int e = wave; e < L; e += 16) {
@@ -444,7 +448,7 @@ hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const
                      ws.max_mtiles, ws.mtile2, ws.max_mtiles2, ws.mcount, ws.row_tok, ws.row_pos,
                      ws.row_exp, ws.row_gate, ws.zlog, p.cfg.n, p.cfg.d / 64, p.cfg.L, p.cfg.W,
                      g.delta, g.K, p.K_max, p.cfg.batch, g.depth, ws.win_len, p.doc_start,
-                     p.doc_len, p.n_tokens);
+                     p.doc_len, p.n_tokens, path ? path->util : nullptr);
   return hipGetLastError();
 }
 

@@ -189,3 +189,45 @@ def test_decode_sizes_and_host_checks(lib):
     for row in (-1, c.batch):
         assert B.lol_decode_reset_row(c, 256, size, row, None) == B.LOL_EINVAL
     assert B.lol_decode_reset_row(c, None, size, 0, None) == B.LOL_EWORKSPACE
+
+
+def test_prepared_wo_panels_sizes_and_rejections(lib):
+    """lol_prepare_wo_panels: a buffer of L d d bf16 values where the fused
+    output projection is used (bf16, d a multiple of 256 up to 1024), none
+    elsewhere; bad arguments are refused before anything is launched."""
+    for cfg in CONFIGS:
+        c = make_config(cfg)
+        want = cfg.L * cfg.d * cfg.d * 2 if (cfg.dtype == "bf16" and cfg.d % 256 == 0
+                                             and cfg.d <= 1024) else 0
+        assert B.lol_prepare_wo_panels_size(c) == want, cfg.name
+    tiny = make_config(CONFIG_BY_NAME["tiny_fp32"])
+    assert B.lol_prepare_wo_panels(tiny, 4096, 1 << 20, None) == B.LOL_EUNSUPPORTED
+    mid = make_config(CONFIG_BY_NAME["mid_bf16"])
+    size = B.lol_prepare_wo_panels_size(mid)
+    assert B.lol_prepare_wo_panels(mid, None, 4096, None) == B.LOL_EINVAL
+    assert B.lol_prepare_wo_panels(mid, 4096, None, None) == B.LOL_EINVAL
+    assert B.lol_prepare_wo_panels(mid, 4096 + 8, 1 << 40, None) == B.LOL_EINVAL   # misaligned
+    assert B.lol_prepare_wo_panels(mid, 4096, 4096 + size - 16, None) == B.LOL_EINVAL  # overlap
+    bad = make_config(CONFIG_BY_NAME["mid_bf16"]); bad.W = 0
+    assert B.lol_prepare_wo_panels_size(bad) == 0
+    assert B.lol_prepare_wo_panels(bad, 4096, 1 << 40, None) == B.LOL_EINVAL
+
+
+def test_buckets_size_matches_the_documented_layout(lib):
+    """counts [L], row_off [L + 1], win_row0 [batch K_max], n_tiles [2],
+    tiles128 [ceil(T / 128) + L][2], tiles256 [ceil(T / 256) + L][2]."""
+    for cfg in CONFIGS:
+        c = make_config(cfg)
+        T = cfg.batch * cfg.n
+        want = (cfg.L + cfg.L + 1 + cfg.batch * cfg.k_max + 2 + 2 * (-(-T // 128) + cfg.L)
+                + 2 * (-(-T // 256) + cfg.L))
+        assert B.lol_core_buckets_size(c) == want, cfg.name
+    mid = make_config(CONFIG_BY_NAME["mid_bf16"])
+    ws = B.lol_core_workspace_size(mid)
+    assert B.lol_core_read_buckets(mid, 1 << 20, ws, None, None) == B.LOL_EINVAL
+    assert B.lol_core_read_buckets(mid, None, ws, 4096, None) == B.LOL_EWORKSPACE
+    assert B.lol_core_read_buckets(mid, 1 << 20, ws - 1, 4096, None) == B.LOL_EWORKSPACE
+    assert B.lol_core_read_buckets(mid, (1 << 20) + 16, ws, 4096, None) == B.LOL_EWORKSPACE
+    bad = make_config(CONFIG_BY_NAME["mid_bf16"]); bad.D = 0
+    assert B.lol_core_buckets_size(bad) == 0
+    assert B.lol_core_read_buckets(bad, 1 << 20, ws, 4096, None) == B.LOL_EINVAL
