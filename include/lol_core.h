@@ -173,6 +173,29 @@ lol_status lol_core_forward(const lol_core_config *cfg, const float *s0,
                             float *s_out, const lol_path *path,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* The same forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument; the forward uses a buffer inside the
+ * library instead, LOL_STATIC_SCRATCH_BYTES of device memory that each GPU
+ * the library runs on holds from the library's load until the process
+ * ends.  Arguments, results and errors as lol_core_forward, plus:
+ *   LOL_EWORKSPACE  when lol_core_workspace_size(cfg) exceeds
+ *                   LOL_STATIC_SCRATCH_BYTES (checked before any launch);
+ *   LOL_EHIP        when the buffer's device address cannot be obtained.
+ * Every call on one GPU shares the one buffer, which keeps the last call's
+ * contents: calls that overlap on a GPU (other streams, other host
+ * threads) race and give unspecified results; calls queued in order on one
+ * stream are safe.  The device flags of these calls are cleared at the
+ * start of each call and cannot be read (a bad forced id is still treated
+ * as free).  Kernel timing (lol_core_timing_enable) does not apply.  It
+ * calls no allocating routine: hipMalloc, hipFree and event creation are
+ * never reached. */
+#define LOL_STATIC_SCRATCH_BYTES (64u << 20)
+lol_status lol_core_forward_static(const lol_core_config *cfg, const float *s0,
+                                   const lol_library *lib, const lol_router *rt,
+                                   const int32_t *forced_expert, const float *forced_gate,
+                                   float *s_out, const lol_path *path, void *stream);
+
 /* Packed documents: the same forward over a batch of documents of
  * different lengths laid out back to back in one token stream.  Each
  * document is partitioned into windows, routed and attended exactly as if

@@ -63,6 +63,9 @@ _SIGNATURES.update({
                                         POINTER(lol_router), c_void_p, c_void_p, c_void_p,
                                         POINTER(lol_path), c_void_p, c_size_t, c_void_p]),
     "lol_core_read_flags": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
+    "lol_core_forward_static": (c_int32, [POINTER(lol_core_config), c_void_p,
+                                          POINTER(lol_library), POINTER(lol_router), c_void_p,
+                                          c_void_p, c_void_p, POINTER(lol_path), c_void_p]),
     "lol_prepare_wo_panels_size": (c_size_t, [POINTER(lol_core_config)]),
     "lol_prepare_wo_panels": (c_int32, [POINTER(lol_core_config), c_void_p, c_void_p, c_void_p]),
     "lol_core_buckets_size": (c_size_t, [POINTER(lol_core_config)]),
@@ -150,6 +153,18 @@ def lol_core_forward_docs(cfg, n_tokens, doc_start, doc_len, s0, lib, rt, forced
                                         forced_gate, s_out,
                                         ctypes.byref(path) if path is not None else None,
                                         workspace, workspace_bytes, stream)
+
+
+LOL_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def lol_core_forward_static(cfg, s0, lib, rt, forced_expert, forced_gate, s_out, path,
+                            stream) -> int:
+    """The forward without a workspace argument (the library's own buffer)."""
+    return load().lol_core_forward_static(ctypes.byref(cfg), s0, ctypes.byref(lib),
+                                          ctypes.byref(rt), forced_expert, forced_gate, s_out,
+                                          ctypes.byref(path) if path is not None else None,
+                                          stream)
 
 
 def lol_core_read_flags(workspace, stream) -> int:

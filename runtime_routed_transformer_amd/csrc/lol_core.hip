@@ -202,6 +202,14 @@ size_t workspace_layout(const Plan &p, char *base, Workspace *ws) {
   return off;
 }
 
+namespace {
+lol_status forward_impl(const lol_core_config *cfg, int64_t n_tokens, const int32_t *doc_start,
+                        const int32_t *doc_len, const float *s0, const lol_library *lib,
+                        const lol_router *rt, const int32_t *forced_expert,
+                        const float *forced_gate, float *s_out, const lol_path *path,
+                        void *workspace, size_t workspace_bytes, void *stream, bool allow_timing);
+hipError_t scratch_address(void **out);
+}  // namespace
 }  // namespace lol
 
 using namespace lol;
@@ -237,6 +245,22 @@ lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
                                  const int32_t *forced_expert, const float *forced_gate,
                                  float *s_out, const lol_path *path, void *workspace,
                                  size_t workspace_bytes, void *stream) {
+  return forward_impl(cfg, n_tokens, doc_start, doc_len, s0, lib, rt, forced_expert, forced_gate,
+                      s_out, path, workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace lol {
+namespace {
+// The routed-core forward behind every entry point.  allow_timing = false
+// leaves the timing instrumentation off for this call (it creates HIP
+// events on first use).
+lol_status forward_impl(const lol_core_config *cfg, int64_t n_tokens, const int32_t *doc_start,
+                        const int32_t *doc_len, const float *s0, const lol_library *lib,
+                        const lol_router *rt, const int32_t *forced_expert,
+                        const float *forced_gate, float *s_out, const lol_path *path,
+                        void *workspace, size_t workspace_bytes, void *stream, bool allow_timing) {
   const lol_status vs = validate(cfg);
   if (vs != LOL_OK) return vs;
   if (!s0 || !s_out || !lib || !rt) return LOL_EINVAL;
@@ -263,7 +287,7 @@ lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
   int32_t timing_depth;
   {
     std::lock_guard<std::mutex> lk(g_tmu);
-    timing = g_timing;
+    timing = allow_timing ? g_timing : 0u;
     timing_depth = g_timing_depth;
   }
   int cur_depth = -1;   // depth index of the launches below (-1: before the first depth)
@@ -373,6 +397,54 @@ lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
   }
 #undef LOL_TRY
   return LOL_OK;
+}
+
+// ---- The forward without a workspace argument ----
+// Callers that cannot allocate (inside HIP graph capture, in tight serving
+// loops) use a workspace that lives in the library itself: one array per
+// device, allocated when the code object is loaded and held until the
+// process ends.  Every call on a device shares it.
+static __device__ __align__(256) char scratch[LOL_STATIC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress): the host-side name is only a stand-in.
+hipError_t scratch_address(void **out) {
+  static std::mutex mu;
+  static void *addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+}  // namespace
+}  // namespace lol
+
+extern "C" {
+
+lol_status lol_core_forward_static(const lol_core_config *cfg, const float *s0,
+                                   const lol_library *lib, const lol_router *rt,
+                                   const int32_t *forced_expert, const float *forced_gate,
+                                   float *s_out, const lol_path *path, void *stream) {
+  const lol_status vs = validate(cfg);
+  if (vs != LOL_OK) return vs;
+  const size_t need = lol_core_workspace_size(cfg);
+  if (need > (size_t)LOL_STATIC_SCRATCH_BYTES) return LOL_EWORKSPACE;
+  if (!s0 || !s_out || !lib || !rt) return LOL_EINVAL;
+  void *ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return LOL_EHIP;
+  return forward_impl(cfg, (int64_t)cfg->batch * cfg->n, nullptr, nullptr, s0, lib, rt,
+                      forced_expert, forced_gate, s_out, path, ws, LOL_STATIC_SCRATCH_BYTES,
+                      stream, false);
 }
 
 size_t lol_decode_state_size(const lol_core_config *cfg) {
