@@ -48,17 +48,29 @@ def hbm_bytes(cfg, tokens=None):
             "gemm_down (scatter epilogue)": 8.0 * T * d}
 
 
+def oracle_threads():
+    """(threads the oracle's numpy/BLAS calls use, host cores this process
+    may run on).  The oracle is numpy float64; its matrix products run on
+    the BLAS thread pool, everything else on one thread."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    try:
+        host = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        host = os.cpu_count() or 1
+    return int(threads), int(host)
+
+
 def cpu_baseline(inp, budget_s=12.0, lengths=None):
     """The oracle, unchanged, on whole documents of the workload, one after
     another until about ``budget_s`` seconds of CPU work are done
     (``lengths``: packed documents, document b = the first lengths[b]
     tokens of row b)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads, host = oracle_threads()
     cfg = inp.cfg
     lens = [cfg.n] * cfg.batch if lengths is None else [int(x) for x in lengths]
     done, tokens, t0 = 0, 0, time.perf_counter()
@@ -69,9 +81,11 @@ def cpu_baseline(inp, budget_s=12.0, lengths=None):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "host_cores": host,
+            "kind": "oracle",
             "sample": f"{done} of {cfg.batch} documents of {cfg.name} ({tokens} tokens x "
-                      f"{cfg.D} depths), numpy float64, {dt:.1f} s"}
+                      f"{cfg.D} depths), numpy float64 (BLAS on {threads} threads, the rest on "
+                      f"one), {dt:.1f} s"}
 
 
 # source files that define each kernel kind's code and launch shape
@@ -120,7 +134,6 @@ def bench_full(args):
     protocol as the routed core, with the readout GEMM among the candidates
     for the dominant kernel."""
     import torch
-    import oracle
     from runtime_routed_transformer_amd import binding as B
     from runtime_routed_transformer_amd.model import DeviceModel
     from runtime_routed_transformer_amd.workloads import FULL_BY_NAME, FullConfig, generate_full
@@ -226,16 +239,13 @@ def bench_full(args):
         sample = FullConfig(f"{fcfg.name}@1x{n_s}", cc.scaled(1, n_s), fcfg.vocab, fcfg.prelude,
                             fcfg.coda, fcfg.seed)
         full = generate_full(sample)
+        import oracle
+        threads, host = oracle_threads()
         t0 = time.perf_counter()
         oracle.full_forward(full, core_forced_expert=full.core.forced_expert)
         dt = time.perf_counter() - t0
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover
-            threads = os.cpu_count() or 1
-        result["cpu_baseline"] = {"value": n_s / dt, "unit": "tokens/s", "cores": int(threads),
-                                  "kind": "oracle",
+        result["cpu_baseline"] = {"value": n_s / dt, "unit": "tokens/s", "cores": threads,
+                                  "host_cores": host, "kind": "oracle",
                                   "sample": f"one {n_s}-token document of {fcfg.name}, numpy "
                                             f"float64, {dt:.1f} s"}
     print(json.dumps(result), flush=True)
@@ -274,17 +284,14 @@ def bench_decode(args):
     dominant projection is timed with HIP events at one depth per step."""
     import numpy as np
     import torch
-    import oracle
     from runtime_routed_transformer_amd import binding as B
     from runtime_routed_transformer_amd.core import DeviceCore, DeviceDecoder
-    from runtime_routed_transformer_amd.workloads import CONFIG_BY_NAME, generate
+    from runtime_routed_transformer_amd.workloads import CONFIG_BY_NAME, generate, load_skewed_bias
 
     base = args.workload[: -len("_decode")]
     inp = generate(CONFIG_BY_NAME[base])
     cfg = inp.cfg
-    if cfg.bias_mode == "skewed":
-        from oracle.calibrate import apply_skew  # input preparation only
-        apply_skew(inp)
+    load_skewed_bias(inp)   # the stored calibrated bias (skewed workloads only)
     steps = args.steps if args.steps is not None else min(cfg.n, 2 * cfg.W)
     if steps > cfg.n or args.warmup > cfg.n:
         raise SystemExit(f"--steps and --warmup must be at most n = {cfg.n} positions")
@@ -382,11 +389,8 @@ def bench_decode(args):
         "kernels": per_kernel,
     }
     if not args.no_cpu_baseline:
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover
-            threads = os.cpu_count() or 1
+        import oracle
+        threads, host = oracle_threads()
         # the oracle's decode on document 0, a growing prefix until ~10 s of work
         n_s, dt = 8, 0.0
         while True:
@@ -396,8 +400,8 @@ def bench_decode(args):
             if dt >= 5.0 or n_s >= steps:
                 break
             n_s = min(steps, n_s * 2)
-        result["cpu_baseline"] = {"value": n_s / dt, "unit": "tokens/s", "cores": int(threads),
-                                  "kind": "oracle",
+        result["cpu_baseline"] = {"value": n_s / dt, "unit": "tokens/s", "cores": threads,
+                                  "host_cores": host, "kind": "oracle",
                                   "sample": f"oracle.decode of positions 0..{n_s - 1} of document "
                                             f"0 of {base}, numpy float64, {dt:.1f} s"}
     print(json.dumps(result), flush=True)
@@ -432,7 +436,8 @@ def main(argv=None):
     from runtime_routed_transformer_amd import binding as B
     from runtime_routed_transformer_amd.core import DeviceCore
     from runtime_routed_transformer_amd.workloads import (CONFIG_BY_NAME, PACKED_BY_NAME,
-                                                          generate, generate_packed)
+                                                          generate, generate_packed,
+                                                          load_skewed_bias)
 
     packed = None
     if args.workload in PACKED_BY_NAME:
@@ -442,9 +447,7 @@ def main(argv=None):
     else:
         inp = generate(CONFIG_BY_NAME[args.workload])
     cfg = inp.cfg
-    if cfg.bias_mode == "skewed":
-        from oracle.calibrate import apply_skew  # input preparation only
-        apply_skew(inp)
+    load_skewed_bias(inp)   # the stored calibrated bias (skewed workloads only)
     core = DeviceCore(inp, "cuda:0")
     core.set_forcing(inp.forced_expert)
     stream = torch.cuda.current_stream()

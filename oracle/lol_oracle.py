@@ -18,10 +18,11 @@ Sources (the four pages on the method):
            (zhongzhuzhou.org): Eqs. (1)-(5), (7) and the reader's Algorithm 1.
 
 Arithmetic: everything in float64 (inputs are fp32 or bf16-exact fp32 values,
-upcast exactly), except the router's score-and-select step, which the blog's
-quoted code runs in fp32 (``self.c_fc(x.float())``) and which this oracle
-therefore also evaluates in fp32 so that both sides decide the argmax in the
-same precision.  Activations are never rounded to bf16.
+upcast exactly), except the router's score-and-select step: the blog ("How
+the order is chosen") states that the router casts its input to fp32 before
+its linear layer, so this oracle also evaluates that step in fp32 and both
+sides decide the argmax in the same precision.  Activations are never
+rounded to bf16.
 
 Readings of points the pages leave open:
   * RMSNorm eps = 1e-6; Norm_s(x) = g_s * x / sqrt(mean(x^2) + eps) with a
@@ -117,9 +118,9 @@ def router_inputs(s_row: np.ndarray, windows, e_depth: np.ndarray) -> np.ndarray
 
 # --------------------------------------------------------------------------
 # a4. Score and select
-#   [blog] "The forward pass, term by term", steps 3 and 4, and the quoted
-#   router code: logits = c_fc(x.float()) in fp32, softmax, biased top-1
-#   whose weight is the unbiased score.  [paper] App. A (loss-free
+#   [blog] "The forward pass, term by term", steps 3 and 4, and "How the
+#   order is chosen": the router's linear layer runs in fp32, then a
+#   softmax and a biased top-1 whose weight is the unbiased score.  [paper] App. A (loss-free
 #   balancing): rho = argmax_m (a_m + b_m), alpha = a_rho.  [review] Eq. (5).
 #   Training noise is off at inference ([review] reader's Algorithm 1 note).
 # --------------------------------------------------------------------------

@@ -35,6 +35,8 @@ bf16 workloads round every block matrix to bf16 once (round to nearest even);
 from __future__ import annotations
 
 import dataclasses
+import json
+import os
 from dataclasses import dataclass
 from typing import Optional
 
@@ -210,6 +212,28 @@ def generate(cfg: CoreConfig) -> CoreInputs:
         wqkv, wo, w_gu, w_down = (bf16_round(w) for w in (wqkv, wo, w_gu, w_down))
     return CoreInputs(cfg, s0, wqkv, wo, w_gu, w_down, g_attn, g_ffn,
                       film_gamma, film_beta, w_r, b_r, e_depth, expert_bias, forced)
+
+
+# The skewed workloads' balancing bias, calibrated once against target loads
+# (a frozen input of those workloads) and stored by ``oracle/write_bias_fixture.py``.
+SKEWED_BIAS_FIXTURE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "data",
+                                   "skewed_bias.json")
+
+
+def load_skewed_bias(inp: "CoreInputs") -> None:
+    """Set ``inp.expert_bias`` from the stored fixture for a skewed workload
+    (raises if the fixture has no entry for exactly this config)."""
+    cfg = inp.cfg
+    if cfg.bias_mode != "skewed":
+        return
+    with open(SKEWED_BIAS_FIXTURE) as fh:
+        table = json.load(fh)
+    entry = table.get(cfg.name)
+    if entry is None or entry["config"] != dataclasses.asdict(cfg):
+        raise KeyError(f"no stored skewed bias for config {cfg.name} (run "
+                       "`python -m oracle.write_bias_fixture`)")
+    bits = np.array([int(h, 16) for h in entry["bias_f32_bits"]], np.uint32)
+    inp.expert_bias = bits.view(np.float32).copy()
 
 
 # --------------------------------------------------------------------------

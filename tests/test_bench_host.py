@@ -75,3 +75,35 @@ def test_stored_traffic_is_ignored_once_sources_change(tmp_path, monkeypatch):
     (prof / "gemm_qkv_mid_bf16_traffic.md").write_text(
         'x\n```json\n{"bytes_per_launch": 123.0, "sources_sha256": "%s"}\n```\n' % digest)
     assert bench.stored_traffic("gemm_qkv", "mid_bf16") == pytest.approx(123.0)
+
+
+def test_stored_skewed_bias_equals_a_fresh_calibration():
+    """The benchmark reads the skewed workloads' balancing bias from a
+    fixture written by oracle/write_bias_fixture.py (so its GPU legs never
+    run the oracle); the fixture must still be what the calibration gives
+    for the current config, bit for bit."""
+    import numpy as np
+    from oracle import write_bias_fixture as wbf
+    from runtime_routed_transformer_amd.workloads import generate, load_skewed_bias
+    cfgs = wbf.fixture_configs()
+    assert cfgs, "no skewed workload"
+    for cfg in cfgs:
+        inp = generate(cfg)
+        load_skewed_bias(inp)
+        np.testing.assert_array_equal(inp.expert_bias.view(np.uint32),
+                                      wbf.calibrated(cfg).view(np.uint32), err_msg=cfg.name)
+
+
+def test_bench_gpu_legs_do_not_import_the_oracle():
+    """Only the cpu_baseline code of bench.py may import oracle/: every
+    import of it sits inside a baseline block."""
+    import ast
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    tree = ast.parse(src)
+    for node in ast.walk(tree):
+        if isinstance(node, (ast.Import, ast.ImportFrom)):
+            names = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
+            if any(n == "oracle" or n.startswith("oracle.") for n in names):
+                line = src.splitlines()[node.lineno - 1]
+                ctx = "\n".join(src.splitlines()[max(0, node.lineno - 12):node.lineno])
+                assert "cpu_baseline" in ctx or "no_cpu_baseline" in ctx, line
