@@ -48,6 +48,37 @@ def hbm_bytes(cfg, tokens=None):
             "gemm_down (scatter epilogue)": 8.0 * T * d}
 
 
+def measure_ceilings(torch, B):
+    """What this GPU sustains, measured before the timed region: the bf16
+    matrix cores on register-only operands, identical and random (the clock
+    follows the power draw, which follows the operands' bit activity), and a
+    plain device-to-device copy of 1 GiB (read + written bytes / time)."""
+    out = {}
+    nbytes = B.load().lol_measure_mfma_bf16_scratch_size()
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    for name, rnd in (("mfma_bf16_identical_operands", False), ("mfma_bf16_random_operands", True)):
+        tf, ghz = B.lol_measure_mfma_bf16(rnd, 20000, scratch.data_ptr(), nbytes, st)
+        out[name] = {"tflops": tf, "clock_ghz": ghz}
+    del scratch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3
+        best = t if best is None else min(best, t)
+    out["hbm_copy_gbs"] = 2 * src.numel() / best / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def oracle_threads():
     """(threads the oracle's numpy/BLAS calls use, host cores this process
     may run on).  The oracle is numpy float64; its matrix products run on
@@ -92,7 +123,8 @@ def cpu_baseline(inp, budget_s=12.0, lengths=None):
 KERNEL_SOURCES = {
     "gemm_qkv": ("gemm.hip", "lol_internal.h"), "gemm_o": ("gemm.hip", "lol_internal.h"),
     "gemm_gate_up": ("gemm.hip", "lol_internal.h"), "gemm_down": ("gemm.hip", "lol_internal.h"),
-    "win_attn": ("block.hip", "lol_internal.h"),
+    "win_attn": ("block.hip", "lol_internal.h"), "norm_attn": ("block.hip", "lol_internal.h"),
+    "pool": ("route.hip", "lol_internal.h"), "route": ("route.hip", "lol_internal.h"),
 }
 
 
@@ -416,6 +448,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mid_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the matrix-core and copy ceilings measured before the timed region")
     ap.add_argument("--timing-steps", type=int, default=3)
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -470,6 +504,7 @@ def main(argv=None):
     # kernel that the HBM-traffic counters of the profiles are scaled by
     s_ref = core.s0 if packed is None else p_in
     torch.empty_like(s_ref).copy_(s_ref)
+    ceilings = None if args.no_ceilings else measure_ceilings(torch, B)
 
     for _ in range(args.warmup):
         forward()
@@ -531,7 +566,12 @@ def main(argv=None):
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "kernel_ms_avg": dom_ms, "kernel_launches_timed": dom_n,
-                     "flops_per_launch": flops[dominant]},
+                     "flops_per_launch": flops[dominant],
+                     # the same kernel against the matrix-core rate this GPU
+                     # sustains on random operands (measured below)
+                     "frac_of_measured_ceiling": None if ceilings is None else
+                     achieved / ceilings["mfma_bf16_random_operands"]["tflops"]},
+        "ceilings": ceilings,
         "mfma_util_pct": 100.0 * gemm_tflops / PEAK_BF16_TFLOPS,
         "grouped_gemm_tflops": gemm_tflops,
         # bandwidth-bound kernels: algorithmic bytes / mean duration (the
@@ -540,6 +580,9 @@ def main(argv=None):
                     for k, b in hbm_bytes(cfg, tokens).items() if kt.get(k.split(" ")[0], (0, 0))[1]},
         "kernels": per_kernel,
     }
+    if ceilings is not None:
+        result["hbm_frac_of_copy"] = {k: v / ceilings["hbm_copy_gbs"]
+                                      for k, v in result["hbm_gbs"].items()}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, lengths=None if packed is None else packed.length)
     print(json.dumps(result), flush=True)

@@ -605,6 +605,48 @@ lol_status lol_core_read_buckets(const lol_core_config *cfg, const void *workspa
   return LOL_OK;
 }
 
+size_t lol_measure_mfma_bf16_scratch_size(void) {
+  int ncu = 0;
+  if (cu_count(&ncu) != hipSuccess || ncu < 1) return 0;
+  return mfma_ceiling_scratch_bytes(ncu);
+}
+
+lol_status lol_measure_mfma_bf16(int32_t random_operands, int32_t iters, void *scratch,
+                                 size_t scratch_bytes, double *tflops, double *ghz,
+                                 void *stream) {
+  if (!scratch || !tflops || !ghz || iters < 1 || iters > (1 << 24) ||
+      (random_operands != 0 && random_operands != 1) ||
+      (reinterpret_cast<uintptr_t>(scratch) & 255))
+    return LOL_EINVAL;
+  int ncu = 0;
+  if (cu_count(&ncu) != hipSuccess || ncu < 1) return LOL_EHIP;
+  if (scratch_bytes < mfma_ceiling_scratch_bytes(ncu)) return LOL_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // one untimed launch (clocks ramp up, code is loaded), then the measured one
+  for (int rep = 0; rep < 2; ++rep)
+    if (launch_mfma_ceiling(ncu, rep == 0 ? (iters + 7) / 8 : iters, random_operands, scratch, st) !=
+        hipSuccess)
+      return LOL_EHIP;
+  std::vector<long long> clk((size_t)ncu * 2);
+  const char *src = static_cast<const char *>(scratch) + (size_t)ncu * 512 * sizeof(float);
+  if (hipMemcpyAsync(clk.data(), src, clk.size() * sizeof(long long), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return LOL_EHIP;
+  long long longest = 0;
+  double clock_sum = 0.0;
+  for (int b = 0; b < ncu; ++b) {
+    const long long cyc = clk[2 * b], ref = clk[2 * b + 1];
+    if (ref <= 0) return LOL_EHIP;
+    longest = ref > longest ? ref : longest;
+    clock_sum += (double)cyc / (double)ref * 0.1;   // s_memrealtime ticks at 100 MHz
+  }
+  const double seconds = (double)longest * 1e-8;
+  *tflops = mfma_ceiling_flops_per_block(iters) * ncu / seconds * 1e-12;
+  *ghz = clock_sum / ncu;
+  return LOL_OK;
+}
+
 lol_status lol_core_read_flags(void *workspace, uint32_t *flags, void *stream) {
   if (!workspace || !flags) return LOL_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);

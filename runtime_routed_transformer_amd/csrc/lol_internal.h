@@ -169,6 +169,11 @@ hipError_t launch_pack_wo(const lol_core_config &c, const void *wo, void *wo_p, 
 hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws, const float *s_in,
                          float *s, const lol_library &lib, int u_panel_rows, hipStream_t st);
 
+// ---- measurement: the matrix cores' sustained bf16 rate (ceiling.hip) ----
+size_t mfma_ceiling_scratch_bytes(int blocks);
+hipError_t launch_mfma_ceiling(int blocks, int iters, int random, void *scratch, hipStream_t st);
+double mfma_ceiling_flops_per_block(int iters);
+
 // ---- incremental decode (one token per document per call) ----
 // Device buffers carved from the caller's decode state.
 struct DecodeBufs {

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "lol_core.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lol_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lol_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -231,3 +231,14 @@ def test_buckets_size_matches_the_documented_layout(lib):
     bad = make_config(CONFIG_BY_NAME["mid_bf16"]); bad.D = 0
     assert B.lol_core_buckets_size(bad) == 0
     assert B.lol_core_read_buckets(bad, 1 << 20, ws, 4096, None) == B.LOL_EINVAL
+
+
+def test_mfma_measurement_rejects_bad_arguments(lib):
+    import ctypes
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    f = lib.lol_measure_mfma_bf16
+    assert f(2, 10, 4096, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(1, 0, 4096, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(1, 10, None, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(1, 10, 4096 + 16, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(1, 10, 4096, 1 << 20, None, ctypes.byref(ghz), None) == B.LOL_EINVAL
