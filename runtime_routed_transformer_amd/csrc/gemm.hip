@@ -148,7 +148,7 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 // ranges (workgroup i runs on XCD i mod 8), so that tiles sharing an A or B
 // slice run close together in time on one XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int TM = 4, TN = 2;           // 32 x 32 blocks per wave: 128 x 64 outputs
+constexpr int TN = 2;                   // 32 x 32 blocks per wave along N: 64 output columns
 constexpr int BK = 32;
 // m-tiles per group: 4 for the wide projections (8,192 weight rows and
 // more: gate/up, the vocabulary readout), 2 for the others (same-box A/B at
@@ -162,21 +162,29 @@ constexpr int GM_WIDE = 4, GM_OTHER = 2;
 //   1 x 4: 128 x 256 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
 //   1 x 8: 128 x 512 tile, 8 waves, 4-stage ring of 160 KiB (all of the
 //          LDS), one per CU (persistent);
-//   1 x 2: 128 x 128 tile, 2 waves, 3-stage ring of 48 KiB, for problems
-//          too small to fill the CUs with larger tiles.
-// 2 x 2 and 1 x 4 move the same bytes per MAC (every wave still owns 128 x
-// 64 outputs); 1 x 4 and 1 x 8 use the 128-row tile tables, which fit
-// expert row counts that are multiples of 128 without a partial tile, and
-// 1 x 8 loads 1.25x the stage bytes of 2 x 4 per MAC where two 1 x 4
-// workgroups load 1.5x.
-template <int WM, int WN> struct Shape {
+//   2 x 2 with 64 x 64 per wave (TM = 2): 128 x 128 tile, 4 waves, 3-stage
+//          ring of 48 KiB, three per CU, for problems too small to fill the
+//          CUs with larger tiles: all four SIMDs of a CU work even when
+//          there is one tile per CU (small_bf16's down projection, 256
+//          tiles, ran on two-wave 128 x 128 tiles with two SIMDs idle).
+// Every other shape gives each wave 128 x 64 outputs (TM = 4): 2 x 2 and
+// 1 x 4 move the same bytes per MAC; 1 x 4 and 1 x 8 use the 128-row tile
+// tables, which fit expert row counts that are multiples of 128 without a
+// partial tile, and 1 x 8 loads 1.25x the stage bytes of 2 x 4 per MAC
+// where two 1 x 4 workgroups load 1.5x.
+// NSV > 0 overrides the ring depth (and gives the workgroup the CU alone):
+// the 128 x 128 shape with an 8-stage ring for problems with at most one
+// tile per CU, where a stage's matrix work (256 clocks per wave) is far
+// shorter than a load's latency and only a deep ring keeps it fed.
+template <int WM, int WN, int TMV = 4, int NSV = 0> struct Shape {
+  static constexpr int TM = TMV;                         // 32 x 32 blocks per wave along M
   static constexpr int NW = WM * WN;                     // waves
   static constexpr int BMT = 32 * TM * WM;               // rows of A per tile
   static constexpr int BNT = 32 * TN * WN;               // weight rows per tile
-  static constexpr int NSTAGE = NW == 8 ? 4 : 3;
+  static constexpr int NSTAGE = NSV ? NSV : (NW == 8 ? 4 : 3);
   static constexpr int STAGE_BYTES = (BMT + BNT) * BK * 2;
   static constexpr int LDS = NSTAGE * STAGE_BYTES;
-  static constexpr int PER_CU = NW == 8 ? 1 : 2;
+  static constexpr int PER_CU = NSV ? 1 : NW == 8 ? 1 : (TM == 2 ? 3 : 2);
   // one workgroup per CU walks a range of tiles (see "Persistent tiles")
   static constexpr bool PERSIST = NW == 8;
   static_assert(BMT == kTileM || BMT == kTileM2, "M tiles come from the 128- or 256-row tables");
@@ -246,9 +254,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int EPI, int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN>::PER_CU)) k_gemm_bf16(GemmParams P) {
-  using S = Shape<WM, WN>;
+template <int EPI, int WM, int WN, int TMV, int NSV>
+__global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU)) k_gemm_bf16(GemmParams P) {
+  using S = Shape<WM, WN, TMV, NSV>;
+  constexpr int TM = S::TM;
   constexpr int NW = S::NW, BMT = S::BMT, BNT = S::BNT, NSTAGE = S::NSTAGE;
   constexpr int STAGE_BYTES = S::STAGE_BYTES;
   constexpr int A_BYTES = BMT * BK * 2;
@@ -1014,14 +1023,14 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmParams P) {
 }
 
 
-template <int EPI, int WM, int WN>
+template <int EPI, int WM, int WN, int TMV = 4, int NSV = 0>
 hipError_t launch_shape(GemmParams P, const Workspace &ws, int n_w, hipStream_t st) {
-  using S = Shape<WM, WN>;
+  using S = Shape<WM, WN, TMV, NSV>;
   const bool tall = S::BMT == kTileM2;
   P.mtile = tall ? ws.mtile2 : ws.mtile;
   P.mcount = tall ? ws.mcount + 1 : ws.mcount;
   P.n_tiles_n = n_w / S::BNT;
-  const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, WM, WN>,
+  const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, WM, WN, TMV, NSV>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
   if (e != hipSuccess) return e;
   int grid = (((tall ? ws.max_mtiles2 : ws.max_mtiles) * P.n_tiles_n + 7) / 8) * 8;
@@ -1032,7 +1041,7 @@ hipError_t launch_shape(GemmParams P, const Workspace &ws, int n_w, hipStream_t 
     if (ec != hipSuccess) return ec;
     grid = min(grid, max(8, ncu / 8 * 8));
   }
-  lol_launch((k_gemm_bf16<EPI, WM, WN>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
+  lol_launch((k_gemm_bf16<EPI, WM, WN, TMV, NSV>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
   return hipGetLastError();
 }
 
@@ -1094,10 +1103,13 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
       const long long tiles512 = (long long)(p.T / kTileM) * (n_w / 512);
       if (a.K >= 2048 && n_w % 512 == 0 && tiles512 >= ncu)
         return launch_shape<EPI, 1, 8>(P, ws, n_w, st);
-      // a small problem whose 128 x 256 tiles would fill at most half of the
-      // workgroup slots (two per CU): 128 x 128 tiles double the tile count
+      // a small problem whose 128 x 256 tiles would not fill the workgroup
+      // slots (two per CU) in one round: 128 x 128 tiles of four 64 x 64
+      // waves, three per CU, double the tile count and keep every SIMD busy
       const long long tiles128x256 = (long long)(p.T / kTileM) * (n_w / 256);
-      if (tiles128x256 <= ncu) return launch_shape<EPI, 1, 2>(P, ws, n_w, st);
+      const long long tiles128x128 = 2 * tiles128x256;
+      if (tiles128x128 <= ncu) return launch_shape<EPI, 2, 2, 2, 8>(P, ws, n_w, st);
+      if (tiles128x256 < 2LL * ncu) return launch_shape<EPI, 2, 2, 2>(P, ws, n_w, st);
       return launch_shape<EPI, 1, 4>(P, ws, n_w, st);
     }
     return launch_shape<EPI, 2, 2>(P, ws, n_w, st);
