@@ -60,7 +60,8 @@ __global__ void __launch_bounds__(256) k_norm(const float *__restrict__ src,
                                               const float *__restrict__ fb, act_t *__restrict__ u,
                                               const int32_t *__restrict__ n_rows, int d, float eps,
                                               int panel_rows, int film_stride) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // the row is wave-uniform: its metadata arrive through scalar loads
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // grouped rows in use this depth (the grid covers the most there can be;
   // packed documents fill fewer, and the rows past them hold no metadata)
   if (row >= *n_rows) return;
@@ -271,7 +272,8 @@ __global__ void __launch_bounds__(256, 3) k_attn_mfma(const bf16_t *__restrict__
   if (q_begin >= len) return;
   const int base = win_row0[slot];
   const size_t ld3 = (size_t)3 * d;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar LDS addresses
   const int hl = lane >> 5, col = lane & 31;
 
   // ---- this wave's two query blocks: Q fragments straight from HBM

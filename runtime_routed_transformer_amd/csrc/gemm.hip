@@ -295,7 +295,8 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   if (!locate(u, mt, nt, e, row0, row_end)) return;
   const int K = P.K;
   const bf16_t *A = reinterpret_cast<const bf16_t *>(P.A);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar LDS addresses
 
   // ---- per-lane global sources of this wave's load instructions
   const int lrow = lane >> 2, lchunk = lane & 3;
@@ -387,7 +388,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   // front of the MFMAs.
   const int nk = K / BK;
   int gb = 0;   // ring slot of the tile's stage 0 (rotates from tile to tile)
-  auto slot = [&](int st) { return (gb + st) % NSTAGE; };
+  auto slot = [&](int st) { return (int)((unsigned)(gb + st) % NSTAGE); };
 #pragma unroll
   for (int st = 0; st < NSTAGE - 1; ++st)
     if (st < nk) issue(st, slot(st));
@@ -472,7 +473,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
     // under this tile's epilogue, which stages through the other two slots
     int mt2 = 0, nt2 = 0, e2 = 0, r02 = 0, re2 = 0;
     const bool more = PERSIST && locate(u + ustep, mt2, nt2, e2, r02, re2);
-    const int gb2 = (gb + nk) % NSTAGE;
+    const int gb2 = (int)((unsigned)(gb + nk) % NSTAGE);
     if (PERSIST && more) {
       set_src(e2, r02, re2, nt2);
 #pragma unroll
@@ -766,7 +767,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
   const int row_end = P.toff[e + 1];
   if (row0 >= row_end) return;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar LDS addresses
 
   // ---- load sources.  Activations: wave w fetches rows 8 w .. 8 w + 7, 4
   // bytes per lane (lane -> row 8 w + lane / 8, dword lane % 8 of the row's
@@ -830,8 +832,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
   auto step = [&](int kt, auto cur_tag) {
     constexpr int cur = decltype(cur_tag)::value;
     stage_barrier<NQ * 2, 0>();
-    issue(min(kt + NS, nk - 1), kt % NS);
-    read_frags(cur ^ 1, (kt + 1) % NS);
+    issue(min(kt + NS, nk - 1), (int)((unsigned)kt % NS));
+    read_frags(cur ^ 1, (int)((unsigned)(kt + 1) % NS));
 #pragma unroll
     for (int in = 0; in < TN; ++in)
 #pragma unroll
