@@ -33,7 +33,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // u[row] = gamma * (g_e * x / sqrt(mean(x^2) + eps)) + beta, one wave per row.
-// FROM_S: x = s[row_tok[row]] (attention sublayer); else x = h[row] (MLP).
+// FROM_S (attention sublayer): blocks walk the windows (block (c, slot) takes
+// positions 4c .. 4c + 3 of window slot `slot`), x = s[token], and the wave
+// also writes the grouped row's metadata (token, window-local position,
+// expert, gate) for the kernels after it.  Else (MLP) x = h[row], rows in
+// grouped order.
 // NCH > 0: d = 256 NCH; every lane keeps its NCH float4 chunks of the row in
 // registers (read once, 16-byte loads) and stores 4 outputs per chunk.
 // NCH = 0: any d (multiple of 64), element-wise.
@@ -51,22 +55,56 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t *p, float a, float b, floa
   *reinterpret_cast<uint2 *>(p) = pk;
 }
 
+// Window geometry and grouped-row metadata for the attention norm.
+struct NormWin {
+  const int32_t *win_exp, *win_len, *win_row0;
+  const float *win_gate;
+  const int32_t *doc_start, *doc_len;   // packed documents, or NULL
+  int W, delta, K_max, n, n_tokens;
+  int32_t *row_tok, *row_pos, *row_exp;
+  float *row_gate;
+};
+
 template <typename act_t, bool FROM_S, int NCH>
 __global__ void __launch_bounds__(256) k_norm(const float *__restrict__ src,
-                                              const int32_t *__restrict__ row_tok,
-                                              const int32_t *__restrict__ row_exp,
+                                              const int32_t *__restrict__ row_exp_in,
                                               const float *__restrict__ gain,
                                               const float *__restrict__ fg,
                                               const float *__restrict__ fb, act_t *__restrict__ u,
                                               const int32_t *__restrict__ n_rows, int d, float eps,
-                                              int panel_rows, int film_stride) {
+                                              int panel_rows, int film_stride, NormWin nw) {
   // the row is wave-uniform: its metadata arrive through scalar loads
-  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  // grouped rows in use this depth (the grid covers the most there can be;
-  // packed documents fill fewer, and the rows past them hold no metadata)
-  if (row >= *n_rows) return;
-  const float *x = src + (FROM_S ? (size_t)row_tok[row] : (size_t)row) * d;
-  const int e = row_exp[row];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  int row, e;
+  const float *x;
+  if constexpr (FROM_S) {
+    const int slot = blockIdx.y, p = blockIdx.x * 4 + wave;
+    e = nw.win_exp[slot];
+    if (e < 0 || p >= nw.win_len[slot]) return;
+    row = nw.win_row0[slot] + p;
+    const int b = slot / nw.K_max, k = slot - b * nw.K_max;
+    // document b's first token (clamped into the stream like the router's)
+    int d0 = b * nw.n;
+    if (nw.doc_len) {
+      const int len = min(min(max(nw.doc_len[b], 1), nw.n), nw.n_tokens);
+      d0 = min(max(nw.doc_start[b], 0), nw.n_tokens - len);
+    }
+    const int tok = d0 + max(0, k * nw.W - nw.delta) + p;
+    if (lane == 0) {
+      nw.row_tok[row] = tok;
+      nw.row_pos[row] = p;
+      nw.row_exp[row] = e;
+      nw.row_gate[row] = nw.win_gate[slot];
+    }
+    x = src + (size_t)tok * d;
+  } else {
+    row = blockIdx.x * 4 + wave;
+    // grouped rows in use this depth (the grid covers the most there can be;
+    // packed documents fill fewer, and the rows past them hold no metadata)
+    if (row >= *n_rows) return;
+    x = src + (size_t)row * d;
+    e = row_exp_in[row];
+  }
   const float *g = gain + (size_t)e * d;
   // FiLM of this depth and sublayer; per expert when film_stride > 0
   if (fg) {
@@ -434,23 +472,26 @@ __global__ void __launch_bounds__(256, 3) k_attn_mfma(const bf16_t *__restrict__
 
 template <typename act_t, int NCH>
 void norm_launch(const Plan &p, int which, const float *s, const lol_library &lib,
-                 const Workspace &ws, const float *fg, const float *fb, int panel_rows, hipStream_t st) {
-  dim3 grid((p.T + 3) / 4);
+                 const Workspace &ws, const float *fg, const float *fb, int panel_rows, int delta,
+                 hipStream_t st) {
   const int film_stride = lib.film_per_expert ? 2 * p.cfg.d : 0;
   const int32_t *n_rows = ws.toff + p.cfg.L;   // total grouped rows, written by the router
+  NormWin nw{ws.win_exp, ws.win_len, ws.win_row0, ws.win_gate, p.doc_start, p.doc_len,
+             p.cfg.W, delta, p.K_max, p.cfg.n, p.n_tokens, ws.row_tok, ws.row_pos, ws.row_exp,
+             ws.row_gate};
   if (which == 0)
-    lol_launch((k_norm<act_t, true, NCH>), grid, dim3(256), 0, st, s, ws.row_tok,
+    lol_launch((k_norm<act_t, true, NCH>), dim3((p.cfg.W + 3) / 4, p.n_slots), dim3(256), 0, st, s,
                        ws.row_exp, lib.g_attn, fg, fb, reinterpret_cast<act_t *>(ws.u), n_rows,
-                       p.cfg.d, p.cfg.rms_eps, panel_rows, film_stride);
+                       p.cfg.d, p.cfg.rms_eps, panel_rows, film_stride, nw);
   else
-    lol_launch((k_norm<act_t, false, NCH>), grid, dim3(256), 0, st, ws.h, ws.row_tok,
+    lol_launch((k_norm<act_t, false, NCH>), dim3((p.T + 3) / 4), dim3(256), 0, st, ws.h,
                        ws.row_exp, lib.g_ffn, fg, fb, reinterpret_cast<act_t *>(ws.u), n_rows,
-                       p.cfg.d, p.cfg.rms_eps, panel_rows, film_stride);
+                       p.cfg.d, p.cfg.rms_eps, panel_rows, film_stride, nw);
 }
 
 template <typename act_t>
 hipError_t norm_typed(const Plan &p, int which, const float *s, const lol_library &lib,
-                      const Workspace &ws, int depth, int panel_rows, hipStream_t st) {
+                      const Workspace &ws, int depth, int delta, int panel_rows, hipStream_t st) {
   const int d = p.cfg.d;
   // FiLM rows of (depth, sublayer): [D][2][d], or [D][L][2][d] per expert
   // (then the kernel adds expert * 2d)
@@ -458,15 +499,15 @@ hipError_t norm_typed(const Plan &p, int which, const float *s, const lol_librar
   const float *fg = lib.film_gamma ? lib.film_gamma + film_off : nullptr;
   const float *fb = lib.film_beta ? lib.film_beta + film_off : nullptr;
   switch ((d % 256 == 0) ? d / 256 : 0) {
-    case 1: norm_launch<act_t, 1>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
-    case 2: norm_launch<act_t, 2>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
-    case 3: norm_launch<act_t, 3>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
-    case 4: norm_launch<act_t, 4>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
-    case 5: norm_launch<act_t, 5>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
-    case 6: norm_launch<act_t, 6>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
-    case 7: norm_launch<act_t, 7>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
-    case 8: norm_launch<act_t, 8>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
-    default: norm_launch<act_t, 0>(p, which, s, lib, ws, fg, fb, panel_rows, st); break;
+    case 1: norm_launch<act_t, 1>(p, which, s, lib, ws, fg, fb, panel_rows, delta, st); break;
+    case 2: norm_launch<act_t, 2>(p, which, s, lib, ws, fg, fb, panel_rows, delta, st); break;
+    case 3: norm_launch<act_t, 3>(p, which, s, lib, ws, fg, fb, panel_rows, delta, st); break;
+    case 4: norm_launch<act_t, 4>(p, which, s, lib, ws, fg, fb, panel_rows, delta, st); break;
+    case 5: norm_launch<act_t, 5>(p, which, s, lib, ws, fg, fb, panel_rows, delta, st); break;
+    case 6: norm_launch<act_t, 6>(p, which, s, lib, ws, fg, fb, panel_rows, delta, st); break;
+    case 7: norm_launch<act_t, 7>(p, which, s, lib, ws, fg, fb, panel_rows, delta, st); break;
+    case 8: norm_launch<act_t, 8>(p, which, s, lib, ws, fg, fb, panel_rows, delta, st); break;
+    default: norm_launch<act_t, 0>(p, which, s, lib, ws, fg, fb, panel_rows, delta, st); break;
   }
   return hipGetLastError();
 }
@@ -498,8 +539,9 @@ hipError_t attn_mfma(const Plan &p, const DepthGeom &g, const Workspace &ws, hip
 hipError_t launch_norm(const Plan &p, const DepthGeom &g, int which, const float *s,
                        const lol_library &lib, const Workspace &ws, int panel_rows, hipStream_t st) {
   if (panel_rows && (p.cfg.dtype != LOL_BF16 || p.cfg.d % 32 != 0)) return hipErrorInvalidValue;
-  if (p.cfg.dtype == LOL_BF16) return norm_typed<bf16_t>(p, which, s, lib, ws, g.depth, panel_rows, st);
-  return norm_typed<float>(p, which, s, lib, ws, g.depth, 0, st);
+  if (p.cfg.dtype == LOL_BF16)
+    return norm_typed<bf16_t>(p, which, s, lib, ws, g.depth, g.delta, panel_rows, st);
+  return norm_typed<float>(p, which, s, lib, ws, g.depth, g.delta, 0, st);
 }
 
 hipError_t launch_attention(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {

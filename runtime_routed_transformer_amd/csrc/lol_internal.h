@@ -109,14 +109,16 @@ hipError_t cu_count(int *n);
 // window means, contracted with the router weights per 64-column chunk
 hipError_t launch_pool(const Plan &p, const DepthGeom &g, const float *s, const Workspace &ws,
                        const lol_router &rt, hipStream_t st);
-// router (logits of the prefix inputs, softmax, choice, forcing), expert
-// bucketing and grouped-row metadata
+// router (logits of the prefix inputs, softmax, choice, forcing) and expert
+// bucketing (the grouped-row metadata come from the attention norm)
 hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const Workspace &ws,
                         const lol_router &rt, const int32_t *forced_expert, const float *forced_gate,
                         const lol_path *path, hipStream_t st);
 // clears the flag word and builds the RoPE table
 hipError_t launch_setup(const Plan &p, const Workspace &ws, hipStream_t st);
-// which = 0: u = FiLM(Norm_attn(s[row_tok])) ; which = 1: u = FiLM(Norm_ffn(h)).
+// which = 0: walks every window's tokens: u = FiLM(Norm_attn(s[token])) at the
+// token's grouped row, and the grouped-row metadata (row_tok, row_pos,
+// row_exp, row_gate) the later kernels read; which = 1: u = FiLM(Norm_ffn(h)).
 // panel_rows > 0 (bf16) writes u in 32-column panels [d/32][panel_rows][32].
 hipError_t launch_norm(const Plan &p, const DepthGeom &g, int which, const float *s,
                        const lol_library &lib, const Workspace &ws, int panel_rows, hipStream_t st);

@@ -147,8 +147,9 @@ __global__ void __launch_bounds__(256) k_pool(const float *__restrict__ s,
 //     rows; per-expert counts and row offsets, the first grouped row of every
 //     window, and the M-tile tables (expert, first row) for kTileM- and
 //     kTileM2-row tiles;
-//  4. grouped-row metadata: token, window-local position, expert and gate of
-//     every grouped row.
+// The grouped-row metadata (token, window-local position, expert and gate of
+// every grouped row) are written by the attention norm, which visits every
+// window's rows anyway.
 // Integer counts only (LDS atomics on integers), so the result does not
 // depend on thread timing.
 __global__ void __launch_bounds__(1024) k_route_all(
@@ -159,8 +160,7 @@ __global__ void __launch_bounds__(1024) k_route_all(
     float *__restrict__ path_m, uint32_t *__restrict__ flags, int32_t *__restrict__ ecount,
     int32_t *__restrict__ toff_out, int32_t *__restrict__ mtile, int max_mtiles,
     int32_t *__restrict__ mtile2, int max_mtiles2, int32_t *__restrict__ mcount,
-    int32_t *__restrict__ row_tok, int32_t *__restrict__ row_pos, int32_t *__restrict__ row_exp,
-    float *__restrict__ row_gate, float *__restrict__ zlog_g, int n, int nch, int L, int W, int delta,
+    float *__restrict__ zlog_g, int n, int nch, int L, int W, int delta,
     int K, int K_max, int B, int depth, int32_t *__restrict__ win_len,
     const int32_t *__restrict__ doc_start, const int32_t *__restrict__ doc_len, int n_tokens,
     int32_t *__restrict__ path_util) {
@@ -174,6 +174,12 @@ __global__ void __launch_bounds__(1024) k_route_all(
   __shared__ int fo[kMaxExperts + 1], po[kMaxExperts + 1], fo2[kMaxExperts + 1], po2[kMaxExperts + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n_slots = B * K_max;
+  // the router's own bias and the balancing bias, read once
+  __shared__ float s_br[kMaxExperts], s_bias[kMaxExperts];
+  if (tid < L) {
+    s_br[tid] = b_r ? b_r[tid] : 0.f;
+    s_bias[tid] = bias ? bias[tid] : 0.f;
+  }
   // window logits live in LDS when they fit, else in the workspace
   __shared__ float s_zlog[kZlogLds];
   float *const zlog = (size_t)n_slots * L <= kZlogLds ? s_zlog : zlog_g;
@@ -198,24 +204,34 @@ __global__ void __launch_bounds__(1024) k_route_all(
     zlog[((size_t)b * K_max + k) * L + m] = y;
   }
   __syncthreads();
-  for (int bm = wave; bm < B * L; bm += 16) {
-    const int b = bm / L, m = bm % L;
-    const float br = b_r ? b_r[m] : 0.f;
-    float carry = 0.f;
-    for (int k0 = 0; k0 < K; k0 += 64) {
-      const int k = k0 + lane;
-      float *zp = zlog + ((size_t)b * K_max + k) * L + m;
-      const float y = k < K ? *zp : 0.f;
-      // inclusive scan of Y over k >= 1 (slot 0 is not part of the prefix)
-      float v = (k >= 1) ? y : 0.f;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
+  // segments of SEG lanes, one (document, expert) each: 4 per wave when a
+  // document has at most 16 windows, 2 up to 32, else one per wave with a
+  // carry across passes of 64 windows (the per-element sums are the same
+  // for every segment width)
+  {
+    const int SEG = K <= 16 ? 16 : (K <= 32 ? 32 : 64);
+    const int pw = 64 / SEG, sl = lane & (SEG - 1), sp = lane / SEG;
+    for (int bm0 = wave * pw; bm0 < B * L; bm0 += 16 * pw) {
+      const int bm = bm0 + sp;
+      const bool okp = bm < B * L;
+      const int b = okp ? bm / L : 0, m = okp ? bm % L : 0;
+      const float br = s_br[m];
+      float carry = 0.f;
+      for (int k0 = 0; k0 < K; k0 += SEG) {
+        const int k = k0 + sl;
+        const bool okk = okp && k < K;
+        float *zp = zlog + ((size_t)b * K_max + k) * L + m;
+        const float y = okk ? *zp : 0.f;
+        // inclusive scan of Y over k >= 1 (slot 0 is not part of the prefix)
+        float v = (k >= 1) ? y : 0.f;
+        for (int o = 1; o < SEG; o <<= 1) {
+          const float t = __shfl_up(v, o, SEG);
+          if (sl >= o) v += t;
+        }
+        v += carry;
+        if (okk) *zp = (k == 0 ? y : v / (float)k) + br;
+        carry = __shfl(v, SEG - 1, SEG);
       }
-      v += carry;
-      if (k < K) *zp = (k == 0 ? y : v / (float)k) + br;
-      carry = __shfl(v, 63, 64);
     }
   }
   for (int i = tid; i < kMaxExperts; i += blockDim.x) { cnt_w[i] = 0; cnt_t[i] = 0; }
@@ -247,7 +263,7 @@ __global__ void __launch_bounds__(1024) k_route_all(
     const float zmax = group_max(zl, G);
     const float ez = live ? expf(zl - zmax) : 0.f;
     const float a = ez / group_sum(ez, G);
-    const float sc = live ? a + (bias ? bias[gl] : 0.f) : -INFINITY;
+    const float sc = live ? a + s_bias[gl] : -INFINITY;
     const float top = group_max(sc, G);
     // lowest index attaining the maximum
     const int rho = group_min((live && sc == top) ? gl : 64, G);
@@ -370,42 +386,6 @@ __global__ void __launch_bounds__(1024) k_route_all(
     mtile2[2 * i] = e;
     mtile2[2 * i + 1] = row0;
   }
-  __syncthreads();  // win_row0 complete
-
-  // 4. grouped-row metadata, one wave per window.  A wave takes windows
-  // wave, wave + 16, ...: lane j first fetches the first row and gate of its
-  // j-th window (one round trip for up to 64 windows), then the wave walks
-  // them with shuffles.
-  for (int r0 = wave; r0 < n_slots; r0 += 16 * 64) {
-    const int my_slot = r0 + 16 * lane;
-    int my_e = -1, my_len = 0, my_row0 = 0;
-    float my_gate = 0.f;
-    if (my_slot < n_slots) {
-      my_e = s_exp[my_slot];
-      my_len = s_len[my_slot];
-      if (my_e >= 0) {
-        my_row0 = win_row0[my_slot];
-        my_gate = win_gate[my_slot];
-      }
-    }
-    for (int j = 0; j < 64; ++j) {
-      const int slot = r0 + 16 * j;
-      if (slot >= n_slots) break;
-      const int e = __shfl(my_e, j, 64);
-      if (e < 0) continue;
-      const int len = __shfl(my_len, j, 64), base = __shfl(my_row0, j, 64);
-      const float g = __shfl(my_gate, j, 64);
-      const int b = slot / K_max, k = slot % K_max;
-      const int tok0 = doc_span(doc_start, doc_len, b, n, n_tokens).start + win_start(k, W, delta);
-      for (int p = lane; p < len; p += 64) {
-        const int row = base + p;
-        row_tok[row] = tok0 + p;
-        row_pos[row] = p;
-        row_exp[row] = e;
-        row_gate[row] = g;
-      }
-    }
-  }
 }
 
 // Per-call set-up: clears the device flag word and fills the RoPE table
@@ -445,8 +425,8 @@ hipError_t launch_route(const Plan &p, const DepthGeom &g, const float *s, const
                      rt.expert_bias, forced_expert, forced_gate, ws.win_exp, ws.win_gate,
                      ws.win_row0, path ? path->expert : nullptr, path ? path->gate : nullptr,
                      path ? path->margin : nullptr, ws.flags, ws.ecount, ws.toff, ws.mtile,
-                     ws.max_mtiles, ws.mtile2, ws.max_mtiles2, ws.mcount, ws.row_tok, ws.row_pos,
-                     ws.row_exp, ws.row_gate, ws.zlog, p.cfg.n, p.cfg.d / 64, p.cfg.L, p.cfg.W,
+                     ws.max_mtiles, ws.mtile2, ws.max_mtiles2, ws.mcount, ws.zlog, p.cfg.n,
+                     p.cfg.d / 64, p.cfg.L, p.cfg.W,
                      g.delta, g.K, p.K_max, p.cfg.batch, g.depth, ws.win_len, p.doc_start,
                      p.doc_len, p.n_tokens, path ? path->util : nullptr);
   return hipGetLastError();
