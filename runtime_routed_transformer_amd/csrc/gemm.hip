@@ -191,13 +191,16 @@ template <int WM, int WN, int TMV = 4, int NSV = 0> struct Shape {
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
-__device__ __forceinline__ void lds_dma16(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)lds, 16, 0, 0);
+// Direct global-to-LDS load of 16 bytes per lane through a buffer resource:
+// per-lane byte offset voff plus a wave-uniform byte offset soff, so that a
+// stage needs no per-lane 64-bit address arithmetic
+constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format, no swizzle
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, void *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, (int)voff, soff, 0, 0);
 }
 
 // Stage barrier: wait until at most VM vector-memory operations (the
@@ -302,20 +305,26 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   const int lrow = lane >> 2, lchunk = lane & 3;
   // sources: a per-tile base (wave-uniform) plus a 32-bit element offset per
   // lane and load instruction
-  const bf16_t *a_base, *b_base;
+  // buffer resources (base = this tile's first A row / its expert's weights;
+  // 2^32 - 1 bytes of range, the offsets stay inside the operands) and
+  // per-lane byte offsets; a stage adds a scalar offset
+  __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc;
   uint32_t soff[NQ];
   // A row stride and per-stage step: row-major, or 32-k panels (a stage of
   // the tile is then one contiguous block of whole lines)
   const int a_rs = P.a_panel_rows ? BK : K;
   const size_t a_ks = P.a_panel_rows ? (size_t)P.a_panel_rows * BK : BK;
   auto set_src = [&](int e_, int row0_, int row_end_, int nt_) {
-    a_base = A + (size_t)row0_ * a_rs;
-    b_base = reinterpret_cast<const bf16_t *>(P.Wt) + (size_t)e_ * P.w_stride;
+    a_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(A + (size_t)row0_ * a_rs), 0, -1,
+                                               kBufferFlags);
+    b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t *>(reinterpret_cast<const bf16_t *>(P.Wt) + (size_t)e_ * P.w_stride), 0, -1,
+        kBufferFlags);
     const int last = row_end_ - 1 - row0_;                   // last valid row of the A tile
 #pragma unroll
     for (int i = 0; i < AQ; ++i) {
       const int r = (wave + NW * i) * 16 + lrow;             // row inside the A tile
-      soff[i] = (uint32_t)min(r, last) * a_rs + ((lchunk ^ swz(r)) << 3);
+      soff[i] = ((uint32_t)min(r, last) * a_rs + ((lchunk ^ swz(r)) << 3)) * 2;   // bytes
     }
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
@@ -330,19 +339,18 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
       } else {
         wrow = nt_ * BNT + r;
       }
-      soff[AQ + i] = (uint32_t)wrow * K + ((lchunk ^ swz(r)) << 3);
+      soff[AQ + i] = ((uint32_t)wrow * K + ((lchunk ^ swz(r)) << 3)) * 2;   // bytes
     }
   };
   set_src(e, row0, row_end, nt);
   auto issue = [&](int stage, int slot) {
     char *base = smem + slot * STAGE_BYTES;
-    const int koff = stage * BK;
-    const bf16_t *ap = a_base + stage * a_ks;
+    const int a_so = (int)(stage * a_ks * 2), b_so = stage * BK * 2;   // bytes
 #pragma unroll
-    for (int i = 0; i < AQ; ++i) lds_dma16(ap + soff[i], base + (wave + NW * i) * 1024);
+    for (int i = 0; i < AQ; ++i) lds_dma16_buf(a_rsrc, soff[i], a_so, base + (wave + NW * i) * 1024);
 #pragma unroll
     for (int i = 0; i < BQ; ++i)
-      lds_dma16(b_base + soff[AQ + i] + koff, base + A_BYTES + (wave + NW * i) * 1024);
+      lds_dma16_buf(b_rsrc, soff[AQ + i], b_so, base + A_BYTES + (wave + NW * i) * 1024);
   };
 
   // ---- fragment addresses: lane reads row (lane & 31) of each 32-row block
@@ -736,8 +744,8 @@ template <int TN> struct ONormShape {
   static_assert(32 * D * 4 <= LDS, "epilogue staging of 32 fp32 rows fits in the ring");
 };
 
-__device__ __forceinline__ void lds_dma4(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)lds, 4, 0, 0);
+__device__ __forceinline__ void lds_dma4_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, void *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 4, (int)voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ float wave_sum64(float v) {
@@ -777,22 +785,25 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
   const int last = row_end - 1 - row0;
   const int ar = wave * 8 + (lane >> 3);
   const int a_chunk = ((lane >> 2) & 1) ^ ((ar >> 3) & 1);
-  const bf16_t *a_src = P.A + (size_t)(row0 + min(ar, last)) * D + a_chunk * 8 + (lane & 3) * 2;
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(P.A + (size_t)row0 * D), 0, -1, kBufferFlags);
+  const uint32_t a_off = ((uint32_t)min(ar, last) * D + a_chunk * 8 + (lane & 3) * 2) * 2;   // bytes
   // weights in 16-k panels: stage k0 / 16 of expert e is the contiguous
   // block Wp[e][k0 / 16][0 .. d)[0 .. 16), so every request is a whole line
-  const bf16_t *b_base = P.Wp + (size_t)e * D * D;
+  const __amdgpu_buffer_rsrc_t b_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(P.Wp + (size_t)e * D * D), 0, -1, kBufferFlags);
   uint32_t boff[TN];
 #pragma unroll
   for (int q = 0; q < TN; ++q) {
     const int br = (wave + 8 * q) * 32 + (lane >> 1);
-    boff[q] = (uint32_t)br * kONormBK + (((lane & 1) ^ ((br >> 3) & 1)) << 3);
+    boff[q] = ((uint32_t)br * kONormBK + (((lane & 1) ^ ((br >> 3) & 1)) << 3)) * 2;   // bytes
   }
   auto issue = [&](int stage, int slot) {
     char *base = smem + slot * STAGE;
-    lds_dma4(a_src + stage * kONormBK, base + wave * 256);
-    const bf16_t *bp = b_base + (size_t)stage * (D * kONormBK);
+    lds_dma4_buf(a_rsrc, a_off, stage * kONormBK * 2, base + wave * 256);
+    const int b_so = stage * (D * kONormBK) * 2;
 #pragma unroll
-    for (int q = 0; q < TN; ++q) lds_dma16(bp + boff[q], base + A_STAGE + (wave + 8 * q) * 1024);
+    for (int q = 0; q < TN; ++q) lds_dma16_buf(b_rsrc, boff[q], b_so, base + A_STAGE + (wave + 8 * q) * 1024);
   };
 
   // ---- fragments: lane reads row (lane & 31) of each 32-row block at logical
