@@ -435,41 +435,64 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
       else
         stage_barrier<0, 0>();
       if (ACT) read_frags(fw0, fx0, slot(0), coff0);
-      int kt = 0;
-      // steady state: at the barrier stages kt+2 .. kt+NSTAGE-2 may still be in
-      // flight; stage kt+NSTAGE-1 goes into the slot of stage kt-1
-      for (; kt + NSTAGE - 1 < nk; ++kt) {
+      // one 32-k stage: its second 16-k step's fragments are read under the
+      // first step's MFMAs; after the barrier the next stage's first-step
+      // fragments are read and (LOAD) stage kt+NSTAGE-1 is requested, under
+      // the second step's MFMAs
+      auto stage_step = [&](int kt, int s_kt, int s_next, int s_load, auto load_tag) {
+        constexpr bool LOAD = decltype(load_tag)::value;
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): also settles scalar loads
         if (ACT) {
-          read_frags(fw1, fx1, slot(kt), coff1);
+          read_frags(fw1, fx1, s_kt, coff1);
           mfmas(fw0, fx0);
           reads_then_mfmas<NR, TM * TN>();
         }
-        stage_barrier<NQ * (NSTAGE - 3), 0>();
-        if (ACT) read_frags(fw0, fx0, slot(kt + 1), coff0);
-        issue(kt + NSTAGE - 1, slot(kt + NSTAGE - 1));
-        if (ACT) {
-          mfmas(fw1, fx1);
-          __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // the LDS reads
-          mfma_load_groups<NQ, TM * TN>();                          // MFMAs, stage loads among them
+        if (LOAD) {
+          // at the barrier stages kt+2 .. kt+NSTAGE-2 may still be in flight;
+          // stage kt+NSTAGE-1 goes into the slot of stage kt-1
+          stage_barrier<NQ * (NSTAGE - 3), 0>();
+          if (ACT) read_frags(fw0, fx0, s_next, coff0);
+          issue(kt + NSTAGE - 1, s_load);
+          if (ACT) {
+            mfmas(fw1, fx1);
+            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // the LDS reads
+            mfma_load_groups<NQ, TM * TN>();                          // MFMAs, stage loads among them
+          }
+        } else {
+          // drain: nothing left to load
+          stage_barrier<0, 0>();
+          if (ACT) {
+            // (on the last stage this reads a stale slot, unused)
+            read_frags(fw0, fx0, s_next, coff0);
+            mfmas(fw1, fx1);
+            reads_then_mfmas<NR, TM * TN>();
+          }
+        }
+      };
+      // (not for the RoPE and blend epilogues, whose registers it would spill)
+      if constexpr (NSTAGE == 4 && EPI != EPI_QKV_ROPE && EPI != EPI_BLEND) {
+        if ((nk & 3) == 0) {
+          // K a multiple of 4 stages: every tile starts in ring slot 0, so the
+          // loop unrolled by the ring's 4 slots has constant slots (immediate
+          // LDS offsets, no slot arithmetic)
+          int kt = 0;
+          for (; kt + 4 < nk; kt += 4) {
+            stage_step(kt, 0, 1, 3, std::true_type{});
+            stage_step(kt + 1, 1, 2, 0, std::true_type{});
+            stage_step(kt + 2, 2, 3, 1, std::true_type{});
+            stage_step(kt + 3, 3, 0, 2, std::true_type{});
+          }
+          stage_step(kt, 0, 1, 3, std::true_type{});   // requests the last stage
+          stage_step(kt + 1, 1, 2, 0, std::false_type{});
+          stage_step(kt + 2, 2, 3, 0, std::false_type{});
+          stage_step(kt + 3, 3, 0, 0, std::false_type{});
+          return;
         }
       }
-      // drain: nothing left to load
-      for (; kt < nk; ++kt) {
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        if (ACT) {
-          read_frags(fw1, fx1, slot(kt), coff1);
-          mfmas(fw0, fx0);
-          reads_then_mfmas<NR, TM * TN>();
-        }
-        stage_barrier<0, 0>();
-        if (ACT) {
-          // (on the last stage this reads a stale slot, unused)
-          read_frags(fw0, fx0, slot(kt + 1), coff0);
-          mfmas(fw1, fx1);
-          reads_then_mfmas<NR, TM * TN>();
-        }
-      }
+      int kt = 0;
+      for (; kt + NSTAGE - 1 < nk; ++kt)
+        stage_step(kt, slot(kt), slot(kt + 1), slot(kt + NSTAGE - 1), std::true_type{});
+      for (; kt < nk; ++kt) stage_step(kt, slot(kt), slot(kt + 1), 0, std::false_type{});
     };
     if (active)
       main_loop(std::true_type{});
