@@ -25,6 +25,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 __device__ __forceinline__ bf16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
@@ -266,7 +267,6 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   constexpr int A_BYTES = BMT * BK * 2;
   constexpr int AQ = BMT / 16 / NW, BQ = BNT / 16 / NW;  // 1-KiB load instructions per wave per stage
   constexpr int NQ = AQ + BQ;
-  constexpr int NR = TM + TN;                  // fragment reads per 16-k step
 
   constexpr bool PERSIST = S::PERSIST;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -353,43 +353,89 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
       lds_dma16_buf(b_rsrc, soff[AQ + i], b_so, base + A_BYTES + (wave + NW * i) * 1024);
   };
 
-  // ---- fragment addresses: lane reads row (lane & 31) of each 32-row block
-  // at logical chunk 2 kk + (lane >> 5)
+  // ---- fragments.  v_mfma_f32_16x16x32_bf16 with the weights as operand A:
+  // lane l holds row l % 16 of a 16-row block at logical 16-byte chunk l / 16
+  // (k 8 (l / 16) .. + 7) of both operands, and ends with
+  // C[m = l % 16][n = 4 (l / 16) + j], j < 4, of its 16 x 16 block: four
+  // consecutive output columns per lane.  (The 32 x 32 x 16 instruction
+  // moves twice the accumulator bytes per MAC and, on random operands,
+  // draws enough more power to run these GEMMs 6-12% slower.)  A wave's
+  // 64 x 128 (columns x rows) block is NWB x NXB such blocks; a stage's
+  // MFMAs run in four quarters: weight blocks 0-1 or 2-3 times activation
+  // blocks 0 .. HX-1 or HX .. NXB-1.
+  constexpr int NWB = 2 * TN;   // 16-row weight blocks per wave
+  constexpr int NXB = 2 * TM;   // 16-row activation blocks per wave
+  constexpr int HX = TM;        // activation blocks per half-stage
   const int wm = wave / WN, wn = wave % WN;
-  const int frow = lane & 31;
-  const int sw = swz(frow);
-  const int coff0 = ((lane >> 5) ^ sw) << 4, coff1 = ((2 + (lane >> 5)) ^ sw) << 4;
-  const int a_frag = (wm * TM * 32 + frow) * 64;            // byte offset inside the A part
-  const int b_frag = A_BYTES + (wn * TN * 32 + frow) * 64;  // inside the B part
+  const int frow = lane & 15;
+  const int coff = ((lane >> 4) ^ swz(frow)) << 4;          // swz of every row of the block
+  const int a_frag = (wm * NXB * 16 + frow) * 64 + coff;    // byte offset inside the A part
+  const int b_frag = A_BYTES + (wn * NWB * 16 + frow) * 64 + coff;   // inside the B part
 
-  f32x16 acc[TN][TM];
+  f32x4 acc[NWB][NXB];
 
-  bf16x8 fw0[TN], fx0[TM], fw1[TN], fx1[TM];
-  auto read_frags = [&](bf16x8 *fw, bf16x8 *fx, int slot, int coff) {
+  bf16x8 fw[NWB], fx0[HX], fx1[HX];   // the stage's weights and its two activation halves
+  // TM == 2 (64 x 64 waves: the small-problem shapes, up to one wave per
+  // SIMD, where the loop waits on LDS latency): v_mfma_f32_32x32x16_bf16
+  // with two 16-k steps per stage, each with 4 MFMAs of 32 cycles covering
+  // the next step's fragment reads, measured faster there than the 16 x 16
+  // schedule.  Lane l reads row l % 32 of a 32-row block at logical chunk
+  // 2 kk + l / 32 and ends with C[m = l % 32][n = 8 g + 4 (l / 32) + j],
+  // g, j < 4, of its 32 x 32 block.
+  constexpr bool M32 = TM == 2;
+  const int frow32 = lane & 31;
+  const int coff32_0 = ((lane >> 5) ^ swz(frow32)) << 4, coff32_1 = ((2 + (lane >> 5)) ^ swz(frow32)) << 4;
+  const int a_frag32 = (wm * TM * 32 + frow32) * 64;
+  const int b_frag32 = A_BYTES + (wn * TN * 32 + frow32) * 64;
+  f32x16 acc32[M32 ? TN : 1][M32 ? TM : 1];
+  bf16x8 gw0[M32 ? TN : 1], gx0[M32 ? TM : 1], gw1[M32 ? TN : 1], gx1[M32 ? TM : 1];
+  auto read_frags32 = [&](bf16x8 *w, bf16x8 *x, int slot, int co) {
     const char *base = smem + slot * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
-      fw[i] = *reinterpret_cast<const bf16x8 *>(base + b_frag + i * 32 * 64 + coff);
+    for (int i = 0; i < TN; ++i) w[i] = *reinterpret_cast<const bf16x8 *>(base + b_frag32 + i * 32 * 64 + co);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      fx[i] = *reinterpret_cast<const bf16x8 *>(base + a_frag + i * 32 * 64 + coff);
+    for (int i = 0; i < TM; ++i) x[i] = *reinterpret_cast<const bf16x8 *>(base + a_frag32 + i * 32 * 64 + co);
   };
-  auto mfmas = [&](const bf16x8 *fw, const bf16x8 *fx) {
+  auto mfmas32 = [&](const bf16x8 *w, const bf16x8 *x) {
 #pragma unroll
-    for (int in = 0; in < TN; ++in)
+    for (int in = 0; in < (M32 ? TN : 1); ++in)
 #pragma unroll
-      for (int im = 0; im < TM; ++im)
-        acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[in], fx[im], acc[in][im], 0, 0, 0);
+      for (int im = 0; im < (M32 ? TM : 1); ++im)
+        acc32[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[in], x[im], acc32[in][im], 0, 0, 0);
+  };
+  // weight blocks 2 wh, 2 wh + 1
+  auto read_w = [&](int slot, int wh) {
+    const char *base = smem + slot * STAGE_BYTES + wh * 2 * 16 * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      fw[2 * wh + i] = *reinterpret_cast<const bf16x8 *>(base + b_frag + i * 16 * 64);
+  };
+  auto read_x = [&](bf16x8 *x, int slot, int half) {
+    const char *base = smem + slot * STAGE_BYTES + half * HX * 16 * 64;
+#pragma unroll
+    for (int i = 0; i < HX; ++i) x[i] = *reinterpret_cast<const bf16x8 *>(base + a_frag + i * 16 * 64);
+  };
+  // quarter (WH, XH): weight blocks 2 WH, 2 WH + 1 times activation half XH
+  auto mfmas = [&](const bf16x8 *x, auto wh_tag, auto xh_tag) {
+    constexpr int WH = decltype(wh_tag)::value, XH = decltype(xh_tag)::value;
+#pragma unroll
+    for (int jn = 2 * WH; jn < 2 * WH + 2; ++jn)
+#pragma unroll
+      for (int i = 0; i < HX; ++i)
+        acc[jn][XH * HX + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[jn], x[i], acc[jn][XH * HX + i], 0, 0, 0);
   };
 
   // Order inside iteration kt (stage kt in slot kt % NSTAGE):
-  //   wait for the first-step fragments of stage kt (read one MFMA block
-  //   ago); read the second-step fragments; MFMAs of the first step;
+  //   wait for activation half 0 and weight blocks 0-1 of stage kt; read
+  //   activation half 1; quarter (0, 0); wait for weight blocks 2-3;
+  //   quarter (1, 0);
   //   barrier: stage kt+1 has landed and every fragment read of this wave
-  //   is done (they too had a whole MFMA block), so after it the slot of
-  //   stage kt-1 is free on every wave;
-  //   read the first-step fragments of stage kt+1; load stage kt+NSTAGE-1
-  //   into the free slot; MFMAs of the second step.
+  //   is done, so after it the slot of stage kt-1 is free on every wave;
+  //   read activation half 0 of stage kt+1; load stage kt+NSTAGE-1 into
+  //   the free slot; quarter (0, 1); read weight blocks 0-1 of stage kt+1;
+  //   quarter (1, 1); read its weight blocks 2-3.
+  // Every read has at least 8 MFMAs (a quarter) to arrive before its first
+  // use, and the fragments take 48 registers.
   // (Requesting stages one iteration earlier, into the slot of stage kt,
   // measured no faster.)  The explicit LDS waits sit where the reads have
   // had an MFMA block to arrive, so the compiler needs none of its own in
@@ -401,26 +447,36 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   for (int st = 0; st < NSTAGE - 1; ++st)
     if (st < nk) issue(st, slot(st));
   const int out_cols = (EPI == EPI_SWIGLU) ? BNT / 2 : BNT;
-  int rpos[EPI == EPI_QKV_ROPE ? TM : 1];
-  float4 tq[EPI == EPI_QKV_ROPE ? 4 : 1][2];
-  // (cos, sin) of frequencies jb .. jb + 3 at position pos, jb = 8 g + 4 (lane / 32)
-  auto rope_table = [&](int pos, float4 (&t)[EPI == EPI_QKV_ROPE ? 4 : 1][2]) {
-    const float *cs = P.rope_cs + (size_t)pos * P.half * 2 + 8 * (lane >> 5);
+  constexpr bool ROPE = EPI == EPI_QKV_ROPE;
+  int rpos[ROPE ? NXB : 1];
+  // (cos, sin) of frequencies f .. f + 3 at position pos, f = 16 q + 4 (lane / 16)
+  // (q = 0, and q = 1 for d_head = 64), for each 16-row half of a 32-row block
+  float4 tq[ROPE ? 2 : 1][2][2];
+  auto rope_table = [&](int pos, float4 (&t)[2][2]) {
+    const float *cs = P.rope_cs + (size_t)pos * P.half * 2 + 8 * (lane >> 4);
 #pragma unroll
-    for (int g = 0; g < (EPI == EPI_QKV_ROPE ? 4 : 1); ++g) {
-      if (g < 2 || P.half == 32) {
-        t[g][0] = *reinterpret_cast<const float4 *>(cs + 16 * g);
-        t[g][1] = *reinterpret_cast<const float4 *>(cs + 16 * g + 4);
+    for (int q = 0; q < 2; ++q) {
+      if (q == 0 || P.half == 32) {
+        t[q][0] = *reinterpret_cast<const float4 *>(cs + 32 * q);
+        t[q][1] = *reinterpret_cast<const float4 *>(cs + 32 * q + 4);
       }
     }
   };
   for (;;) {
 #pragma unroll
-    for (int a = 0; a < TN; ++a)
+    for (int a = 0; a < NWB; ++a)
 #pragma unroll
-      for (int b = 0; b < TM; ++b)
+      for (int b = 0; b < NXB; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+        for (int i = 0; i < 4; ++i) acc[a][b][i] = 0.f;
+    if constexpr (M32) {
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc32[a][b][i] = 0.f;
+    }
     // A wave whose 128 rows all lie past the expert's last row (the second
     // wave row of a partial tile with at most 128 rows) skips its fragment
     // reads and MFMAs and only keeps the barriers and its share of the loads.
@@ -434,61 +490,82 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
         stage_barrier<NQ * (NSTAGE - 2), 0>();
       else
         stage_barrier<0, 0>();
-      if (ACT) read_frags(fw0, fx0, slot(0), coff0);
-      // one 32-k stage: its second 16-k step's fragments are read under the
-      // first step's MFMAs; after the barrier the next stage's first-step
-      // fragments are read and (LOAD) stage kt+NSTAGE-1 is requested, under
-      // the second step's MFMAs
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      if constexpr (M32) {
+        if (ACT) read_frags32(gw0, gx0, slot(0), coff32_0);
+        auto step32 = [&](int kt, int s_kt, int s_next, int s_load, auto load_tag) {
+          constexpr bool LOAD = decltype(load_tag)::value;
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+          if (ACT) {
+            read_frags32(gw1, gx1, s_kt, coff32_1);
+            mfmas32(gw0, gx0);
+            reads_then_mfmas<TM + TN, TM * TN>();
+          }
+          if (LOAD)
+            stage_barrier<NQ * (NSTAGE - 3), 0>();
+          else
+            stage_barrier<0, 0>();
+          if (ACT) read_frags32(gw0, gx0, s_next, coff32_0);   // (last stage: a stale slot, unused)
+          if (LOAD) issue(kt + NSTAGE - 1, s_load);
+          if (ACT) {
+            mfmas32(gw1, gx1);
+            __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+            if (LOAD)
+              mfma_load_groups<NQ, TM * TN>();
+            else
+              __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+          }
+        };
+        int kt = 0;
+        for (; kt + NSTAGE - 1 < nk; ++kt)
+          step32(kt, slot(kt), slot(kt + 1), slot(kt + NSTAGE - 1), std::true_type{});
+        for (; kt < nk; ++kt) step32(kt, slot(kt), slot(kt + 1), 0, std::false_type{});
+        return;
+      }
+      if (ACT) {
+        // in the order the steady state leaves its reads in flight
+        read_x(fx0, slot(0), 0);
+        read_w(slot(0), 0);
+        read_w(slot(0), 1);
+      }
       auto stage_step = [&](int kt, int s_kt, int s_next, int s_load, auto load_tag) {
         constexpr bool LOAD = decltype(load_tag)::value;
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): also settles scalar loads
+        // activation half 0 and weight blocks 0-1 landed (blocks 2-3 may not)
+        __builtin_amdgcn_s_waitcnt(0xc07f | (2 << 8));
         if (ACT) {
-          read_frags(fw1, fx1, s_kt, coff1);
-          mfmas(fw0, fx0);
-          reads_then_mfmas<NR, TM * TN>();
+          read_x(fx1, s_kt, 1);
+          mfmas(fx0, I0{}, I0{});
+          reads_then_mfmas<HX, 2 * HX>();
         }
-        if (LOAD) {
+        // weight blocks 2-3 landed (activation half 1 may not)
+        __builtin_amdgcn_s_waitcnt(0xc07f | (HX << 8));
+        if (ACT) {
+          mfmas(fx0, I1{}, I0{});
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * HX, 0);
+        }
+        if (LOAD)
           // at the barrier stages kt+2 .. kt+NSTAGE-2 may still be in flight;
           // stage kt+NSTAGE-1 goes into the slot of stage kt-1
           stage_barrier<NQ * (NSTAGE - 3), 0>();
-          if (ACT) read_frags(fw0, fx0, s_next, coff0);
-          issue(kt + NSTAGE - 1, s_load);
-          if (ACT) {
-            mfmas(fw1, fx1);
-            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // the LDS reads
-            mfma_load_groups<NQ, TM * TN>();                          // MFMAs, stage loads among them
-          }
-        } else {
-          // drain: nothing left to load
-          stage_barrier<0, 0>();
-          if (ACT) {
-            // (on the last stage this reads a stale slot, unused)
-            read_frags(fw0, fx0, s_next, coff0);
-            mfmas(fw1, fx1);
-            reads_then_mfmas<NR, TM * TN>();
-          }
+        else
+          stage_barrier<0, 0>();   // drain: nothing left to load
+        if (ACT) read_x(fx0, s_next, 0);   // (on the last stage a stale slot, unused)
+        if (LOAD) issue(kt + NSTAGE - 1, s_load);
+        if (ACT) {
+          mfmas(fx1, I0{}, I1{});
+          __builtin_amdgcn_sched_group_barrier(0x100, HX, 0);        // the LDS reads
+          if (LOAD)
+            mfma_load_groups<NQ, 2 * HX>();                          // MFMAs, stage loads among them
+          else
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * HX, 0);
+          read_w(s_next, 0);
+          mfmas(fx1, I1{}, I1{});
+          reads_then_mfmas<2, 2 * HX>();
+          read_w(s_next, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
       };
-      // (not for the RoPE and blend epilogues, whose registers it would spill)
-      if constexpr (NSTAGE == 4 && EPI != EPI_QKV_ROPE && EPI != EPI_BLEND) {
-        if ((nk & 3) == 0) {
-          // K a multiple of 4 stages: every tile starts in ring slot 0, so the
-          // loop unrolled by the ring's 4 slots has constant slots (immediate
-          // LDS offsets, no slot arithmetic)
-          int kt = 0;
-          for (; kt + 4 < nk; kt += 4) {
-            stage_step(kt, 0, 1, 3, std::true_type{});
-            stage_step(kt + 1, 1, 2, 0, std::true_type{});
-            stage_step(kt + 2, 2, 3, 1, std::true_type{});
-            stage_step(kt + 3, 3, 0, 2, std::true_type{});
-          }
-          stage_step(kt, 0, 1, 3, std::true_type{});   // requests the last stage
-          stage_step(kt + 1, 1, 2, 0, std::false_type{});
-          stage_step(kt + 2, 2, 3, 0, std::false_type{});
-          stage_step(kt + 3, 3, 0, 0, std::false_type{});
-          return;
-        }
-      }
       int kt = 0;
       for (; kt + NSTAGE - 1 < nk; ++kt)
         stage_step(kt, slot(kt), slot(kt + 1), slot(kt + NSTAGE - 1), std::true_type{});
@@ -512,10 +589,10 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
         if (st < nk) issue(st, (gb2 + st) % NSTAGE);
     }
 
-    // ---- epilogue.  acc[in][im] holds C[m = im*32 + lane%32][n = in*32 + g*8
-    // + 4*(lane/32) + j] (g, j < 4) of this wave's 128 x 64 block.  SwiGLU:
-    // acc[0] is the gate and acc[1] the up projection of the same 32 hidden
-    // columns.
+    // ---- epilogue.  acc[jn][xb] holds C[m = xb*16 + lane%16][n = jn*16 +
+    // 4*(lane/16) + j] (j < 4) of this wave's 128 x 64 block.  SwiGLU:
+    // acc[0], acc[1] are the gate and acc[2], acc[3] the up projection of the
+    // same 32 hidden columns.
     // the lane index, opaque to the compiler: keeps the epilogue's address
     // arithmetic from being hoisted out of the tile loop (registers are
     // short across the main loop)
@@ -537,70 +614,134 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
     const int col_base = nt * out_cols + wn * NC;
     // RoPE: window positions of this lane's rows and the (cos, sin) table
     // entries of its first 32-row block
-    const bool rope = EPI == EPI_QKV_ROPE && col_base < P.rope_cols;
-    if (EPI == EPI_QKV_ROPE && rope) {
+    const bool rope = ROPE && col_base < P.rope_cols;
+    if (ROPE && rope && !M32) {
 #pragma unroll
-      for (int im = 0; im < TM; ++im)
-        rpos[im] = P.row_pos[min(row0 + wm * TM * 32 + im * 32 + (lane_e & 31), row_end - 1)];
-      rope_table(rpos[0], tq);
+      for (int xb = 0; xb < NXB; ++xb)
+        rpos[xb] = P.row_pos[min(row0 + wm * NXB * 16 + xb * 16 + (lane_e & 15), row_end - 1)];
+      rope_table(rpos[0], tq[0]);
+      rope_table(rpos[1], tq[1]);
     }
     // RoPE (QKV, q and k columns): before staging, every lane_e holds one row of
-    // each 32-row block and, for each of its columns in the low half of a
-    // head, also the partner column d_head/2 to the right: acc[0] / acc[1] for
-    // d_head = 64 (the wave's 64 columns are one head), blocks g and g + 2 of
-    // the same acc for d_head = 32 (two heads).  The rotation is done there, on
-    // the fp32 accumulators.
+    // each 16-row block and, for each of its columns in the low half of a
+    // head, also the partner column d_head/2 to the right, in the same
+    // register of another block: acc[q] / acc[q + 2] for d_head = 64 (the
+    // wave's 64 columns are one head), acc[2 h] / acc[2 h + 1] for d_head = 32
+    // (two heads).  The rotation is done there, on the fp32 accumulators.
 #pragma unroll
     for (int im = 0; im < TM; ++im) {
-      if (EPI == EPI_QKV_ROPE && rope) {
-        if (im > 0) rope_table(rpos[im], tq);
-        // pair (x, y) at frequency j: x' = x cos - y sin, y' = x sin + y cos
-        auto rot = [](f32x16 &a, int i, f32x16 &b, int k, float c, float sn) {
-          const float x = a[i], y = b[k];
-          a[i] = x * c - y * sn;
-          b[k] = x * sn + y * c;
+      if (ROPE && rope && !M32) {
+        if (im > 0) {
+          rope_table(rpos[2 * im], tq[0]);
+          rope_table(rpos[2 * im + 1], tq[1]);
+        }
+        // pair (x, y) at frequency f: x' = x cos - y sin, y' = x sin + y cos
+        auto rot = [](f32x4 &a, f32x4 &b, int j, float c, float sn) {
+          const float x = a[j], y = b[j];
+          a[j] = x * c - y * sn;
+          b[j] = x * sn + y * c;
         };
-        if (P.half == 32) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            rot(acc[0][im], 4 * g + 0, acc[1][im], 4 * g + 0, tq[g][0].x, tq[g][0].y);
-            rot(acc[0][im], 4 * g + 1, acc[1][im], 4 * g + 1, tq[g][0].z, tq[g][0].w);
-            rot(acc[0][im], 4 * g + 2, acc[1][im], 4 * g + 2, tq[g][1].x, tq[g][1].y);
-            rot(acc[0][im], 4 * g + 3, acc[1][im], 4 * g + 3, tq[g][1].z, tq[g][1].w);
-          }
-        } else {  // d_head = 32
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int xb = 2 * im + h2;
+          const float4(&t)[2][2] = tq[h2];
+          if (P.half == 32) {
 #pragma unroll
-          for (int in = 0; in < TN; ++in)
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-              rot(acc[in][im], 4 * g + 0, acc[in][im], 4 * g + 8, tq[g][0].x, tq[g][0].y);
-              rot(acc[in][im], 4 * g + 1, acc[in][im], 4 * g + 9, tq[g][0].z, tq[g][0].w);
-              rot(acc[in][im], 4 * g + 2, acc[in][im], 4 * g + 10, tq[g][1].x, tq[g][1].y);
-              rot(acc[in][im], 4 * g + 3, acc[in][im], 4 * g + 11, tq[g][1].z, tq[g][1].w);
+            for (int q = 0; q < 2; ++q) {
+              rot(acc[q][xb], acc[q + 2][xb], 0, t[q][0].x, t[q][0].y);
+              rot(acc[q][xb], acc[q + 2][xb], 1, t[q][0].z, t[q][0].w);
+              rot(acc[q][xb], acc[q + 2][xb], 2, t[q][1].x, t[q][1].y);
+              rot(acc[q][xb], acc[q + 2][xb], 3, t[q][1].z, t[q][1].w);
             }
+          } else {  // d_head = 32
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              rot(acc[2 * hh][xb], acc[2 * hh + 1][xb], 0, t[0][0].x, t[0][0].y);
+              rot(acc[2 * hh][xb], acc[2 * hh + 1][xb], 1, t[0][0].z, t[0][0].w);
+              rot(acc[2 * hh][xb], acc[2 * hh + 1][xb], 2, t[0][1].x, t[0][1].y);
+              rot(acc[2 * hh][xb], acc[2 * hh + 1][xb], 3, t[0][1].z, t[0][1].w);
+            }
+          }
         }
       }
-      // stage this 32-row block
+      if constexpr (M32) {
+        // RoPE (d_head 64: acc32[0] / acc32[1]; 32: blocks g and g + 2 of one
+        // acc32), with the (cos, sin) entries of this lane's row
+        if (ROPE && rope) {
+          const int pos = P.row_pos[min(row0 + wm * TM * 32 + im * 32 + (lane_e & 31), row_end - 1)];
+          const float *cs = P.rope_cs + (size_t)pos * P.half * 2 + 8 * (lane_e >> 5);
+          auto rot = [](f32x16 &a, int i, f32x16 &b, int k, float c, float sn) {
+            const float x = a[i], y = b[k];
+            a[i] = x * c - y * sn;
+            b[k] = x * sn + y * c;
+          };
 #pragma unroll
-      for (int in = 0; in < (EPI == EPI_SWIGLU ? 1 : TN); ++in)
+          for (int g = 0; g < 4; ++g) {
+            if (g >= 2 && P.half != 32) break;
+            const float4 t0 = *reinterpret_cast<const float4 *>(cs + 16 * g);
+            const float4 t1 = *reinterpret_cast<const float4 *>(cs + 16 * g + 4);
+            if (P.half == 32) {
+              rot(acc32[0][im], 4 * g + 0, acc32[1][im], 4 * g + 0, t0.x, t0.y);
+              rot(acc32[0][im], 4 * g + 1, acc32[1][im], 4 * g + 1, t0.z, t0.w);
+              rot(acc32[0][im], 4 * g + 2, acc32[1][im], 4 * g + 2, t1.x, t1.y);
+              rot(acc32[0][im], 4 * g + 3, acc32[1][im], 4 * g + 3, t1.z, t1.w);
+            } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+              for (int in = 0; in < TN; ++in) {
+                rot(acc32[in][im], 4 * g + 0, acc32[in][im], 4 * g + 8, t0.x, t0.y);
+                rot(acc32[in][im], 4 * g + 1, acc32[in][im], 4 * g + 9, t0.z, t0.w);
+                rot(acc32[in][im], 4 * g + 2, acc32[in][im], 4 * g + 10, t1.x, t1.y);
+                rot(acc32[in][im], 4 * g + 3, acc32[in][im], 4 * g + 11, t1.z, t1.w);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int in = 0; in < (EPI == EPI_SWIGLU ? 1 : TN); ++in)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float4 v;
+            if (EPI == EPI_SWIGLU) {
+              v.x = silu_fast(acc32[0][im][4 * g + 0]) * acc32[1][im][4 * g + 0];
+              v.y = silu_fast(acc32[0][im][4 * g + 1]) * acc32[1][im][4 * g + 1];
+              v.z = silu_fast(acc32[0][im][4 * g + 2]) * acc32[1][im][4 * g + 2];
+              v.w = silu_fast(acc32[0][im][4 * g + 3]) * acc32[1][im][4 * g + 3];
+            } else {
+              v = make_float4(acc32[in][im][4 * g], acc32[in][im][4 * g + 1], acc32[in][im][4 * g + 2],
+                              acc32[in][im][4 * g + 3]);
+              if (EPI == EPI_GELU) {
+                v.x = gelu_erf(v.x); v.y = gelu_erf(v.y); v.z = gelu_erf(v.z); v.w = gelu_erf(v.w);
+              }
+            }
+            const int c = in * 8 + 2 * g + (lane_e >> 5);
+            *reinterpret_cast<float4 *>(stage_f + sslot(lane_e & 31, c) * 4) = v;
+          }
+      }
+      // stage this 32-row block: its two 16-row blocks, four columns per lane
+      // and block
+#pragma unroll
+      for (int h2 = 0; h2 < (M32 ? 0 : 2); ++h2) {
+        const int xb = 2 * im + h2;
+        const int r = 16 * h2 + (lane_e & 15);
+#pragma unroll
+        for (int jn = 0; jn < (EPI == EPI_SWIGLU ? NWB / 2 : NWB); ++jn) {
           float4 v;
           if (EPI == EPI_SWIGLU) {
-            v.x = silu_fast(acc[0][im][4 * g + 0]) * acc[1][im][4 * g + 0];
-            v.y = silu_fast(acc[0][im][4 * g + 1]) * acc[1][im][4 * g + 1];
-            v.z = silu_fast(acc[0][im][4 * g + 2]) * acc[1][im][4 * g + 2];
-            v.w = silu_fast(acc[0][im][4 * g + 3]) * acc[1][im][4 * g + 3];
+            const f32x4 g = acc[jn][xb], up = acc[jn + NWB / 2][xb];
+            v.x = silu_fast(g[0]) * up[0];
+            v.y = silu_fast(g[1]) * up[1];
+            v.z = silu_fast(g[2]) * up[2];
+            v.w = silu_fast(g[3]) * up[3];
           } else {
-            v = make_float4(acc[in][im][4 * g], acc[in][im][4 * g + 1], acc[in][im][4 * g + 2],
-                            acc[in][im][4 * g + 3]);
+            v = make_float4(acc[jn][xb][0], acc[jn][xb][1], acc[jn][xb][2], acc[jn][xb][3]);
             if (EPI == EPI_GELU) {
               v.x = gelu_erf(v.x); v.y = gelu_erf(v.y); v.z = gelu_erf(v.z); v.w = gelu_erf(v.w);
             }
           }
-          const int c = in * 8 + 2 * g + (lane_e >> 5);   // logical 16-byte slot of the row
-          *reinterpret_cast<float4 *>(stage_f + sslot(lane_e & 31, c) * 4) = v;
+          const int c = jn * 4 + (lane_e >> 4);   // logical 16-byte slot of the row
+          *reinterpret_cast<float4 *>(stage_f + sslot(r, c) * 4) = v;
         }
+      }
       // read back whole rows: lane_e -> row rr (+ RPP * pass), 8 columns from 4 * cc
       constexpr int NP = 32 / RPP;
       const int col = col_base + cc * 4;
@@ -1111,6 +1252,9 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   if (a.c_panel_rows && (EPI == EPI_RESID || EPI == EPI_BLEND || EPI == EPI_ACCUM)) return hipErrorInvalidValue;
   if (EPI == EPI_QKV_ROPE && (p.cfg.dtype != LOL_BF16 || (p.d_head != 32 && p.d_head != 64)))
     return hipErrorInvalidValue;  // fp32 mode rotates inside its attention kernel
+  // the bf16 kernel takes K in groups of 4 32-k stages (d and d_ffn are
+  // multiples of 128 in bf16 mode)
+  if (p.cfg.dtype == LOL_BF16 && a.K % (4 * BK) != 0) return hipErrorInvalidValue;
   if (p.cfg.dtype == LOL_BF16) {
     // 256 x 256 tiles (persistent) when every expert's row count is a
     // multiple of 256 and such tiles fill the CUs; otherwise tiles from the
