@@ -313,10 +313,12 @@ const char *lol_core_kernel_name(int32_t kind);
 
 /* Measurement only: the bf16 matrix-core rate this GPU sustains, for the
  * roofline's ceiling beside the datasheet peak.  One workgroup of 8 waves
- * per compute unit issues nothing but v_mfma_f32_32x32x16_bf16 on operands
- * held in registers (no memory traffic), `iters` x 8 instructions per wave,
- * on operands that are identical in every instruction (random_operands = 0)
- * or random bf16 values of GEMM-like size (1).  The chip's clock follows
+ * per compute unit issues nothing but one bf16 MFMA shape on operands held
+ * in registers (no memory traffic): shape 32 = v_mfma_f32_32x32x16_bf16,
+ * `iters` x 8 instructions per wave; shape 16 = v_mfma_f32_16x16x32_bf16
+ * (the grouped GEMMs' instruction), twice as many for the same MACs; in
+ * either case on operands that are identical in every instruction
+ * (random_operands = 0) or random bf16 values of GEMM-like size (1).  The chip's clock follows
  * its power draw, which depends on how many multiplier bits the operands
  * toggle, so the two settings bracket what a GEMM can reach.
  *   scratch   DEVICE, >= lol_measure_mfma_bf16_scratch_size() bytes,
@@ -325,11 +327,11 @@ const char *lol_core_kernel_name(int32_t kind);
  *   ghz       HOST, receives the mean shader clock during the run (s_memtime
  *             cycles over the 100 MHz s_memrealtime ticks)
  * Launches twice (a short untimed run, then the measured one) and
- * synchronises stream.  LOL_EINVAL for bad arguments, LOL_EWORKSPACE for a
- * small scratch. */
+ * synchronises stream.  LOL_EINVAL for bad arguments (shape other than 16
+ * or 32 included), LOL_EWORKSPACE for a small scratch. */
 size_t lol_measure_mfma_bf16_scratch_size(void);
-lol_status lol_measure_mfma_bf16(int32_t random_operands, int32_t iters, void *scratch,
-                                 size_t scratch_bytes, double *tflops, double *ghz,
+lol_status lol_measure_mfma_bf16(int32_t shape, int32_t random_operands, int32_t iters,
+                                 void *scratch, size_t scratch_bytes, double *tflops, double *ghz,
                                  void *stream);
 
 /* ---- Incremental decode -------------------------------------------------

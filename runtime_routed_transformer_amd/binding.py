@@ -89,7 +89,7 @@ _SIGNATURES.update({
     "lol_core_timing_collect": (c_int32, [POINTER(c_double), POINTER(c_int32)]),
     "lol_core_kernel_name": (c_char_p, [c_int32]),
     "lol_measure_mfma_bf16_scratch_size": (c_size_t, []),
-    "lol_measure_mfma_bf16": (c_int32, [c_int32, c_int32, c_void_p, c_size_t, POINTER(c_double),
+    "lol_measure_mfma_bf16": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_size_t, POINTER(c_double),
                                         POINTER(c_double), c_void_p]),
     "lol_status_str": (c_char_p, [c_int32]),
 })
@@ -244,10 +244,12 @@ def lol_core_timing_collect():
     return {lol_core_kernel_name(k): (float(ms[k]), int(cnt[k])) for k in range(LOL_KERNEL_KINDS)}
 
 
-def lol_measure_mfma_bf16(random_operands: bool, iters: int, scratch, scratch_bytes, stream):
-    """(TFLOP/s, GHz) of the register-only bf16 MFMA loop (measurement only)."""
+def lol_measure_mfma_bf16(shape: int, random_operands: bool, iters: int, scratch, scratch_bytes,
+                          stream):
+    """(TFLOP/s, GHz) of the register-only bf16 MFMA loop (measurement only);
+    shape 32 = 32x32x16, 16 = 16x16x32."""
     tf, ghz = c_double(0.0), c_double(0.0)
-    _check(load().lol_measure_mfma_bf16(1 if random_operands else 0, int(iters), scratch,
+    _check(load().lol_measure_mfma_bf16(int(shape), 1 if random_operands else 0, int(iters), scratch,
                                         scratch_bytes, ctypes.byref(tf), ctypes.byref(ghz), stream),
            "lol_measure_mfma_bf16")
     return float(tf.value), float(ghz.value)

@@ -611,10 +611,10 @@ size_t lol_measure_mfma_bf16_scratch_size(void) {
   return mfma_ceiling_scratch_bytes(ncu);
 }
 
-lol_status lol_measure_mfma_bf16(int32_t random_operands, int32_t iters, void *scratch,
-                                 size_t scratch_bytes, double *tflops, double *ghz,
+lol_status lol_measure_mfma_bf16(int32_t shape, int32_t random_operands, int32_t iters,
+                                 void *scratch, size_t scratch_bytes, double *tflops, double *ghz,
                                  void *stream) {
-  if (!scratch || !tflops || !ghz || iters < 1 || iters > (1 << 24) ||
+  if (!scratch || !tflops || !ghz || iters < 1 || iters > (1 << 24) || (shape != 16 && shape != 32) ||
       (random_operands != 0 && random_operands != 1) ||
       (reinterpret_cast<uintptr_t>(scratch) & 255))
     return LOL_EINVAL;
@@ -624,7 +624,7 @@ lol_status lol_measure_mfma_bf16(int32_t random_operands, int32_t iters, void *s
   hipStream_t st = static_cast<hipStream_t>(stream);
   // one untimed launch (clocks ramp up, code is loaded), then the measured one
   for (int rep = 0; rep < 2; ++rep)
-    if (launch_mfma_ceiling(ncu, rep == 0 ? (iters + 7) / 8 : iters, random_operands, scratch, st) !=
+    if (launch_mfma_ceiling(shape, ncu, rep == 0 ? (iters + 7) / 8 : iters, random_operands, scratch, st) !=
         hipSuccess)
       return LOL_EHIP;
   std::vector<long long> clk((size_t)ncu * 2);

@@ -173,7 +173,9 @@ hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws,
 
 // ---- measurement: the matrix cores' sustained bf16 rate (ceiling.hip) ----
 size_t mfma_ceiling_scratch_bytes(int blocks);
-hipError_t launch_mfma_ceiling(int blocks, int iters, int random, void *scratch, hipStream_t st);
+// shape 32: v_mfma_f32_32x32x16_bf16; 16: v_mfma_f32_16x16x32_bf16
+hipError_t launch_mfma_ceiling(int shape, int blocks, int iters, int random, void *scratch,
+                               hipStream_t st);
 double mfma_ceiling_flops_per_block(int iters);
 
 // ---- incremental decode (one token per document per call) ----

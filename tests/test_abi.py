@@ -237,8 +237,10 @@ def test_mfma_measurement_rejects_bad_arguments(lib):
     import ctypes
     tf, ghz = ctypes.c_double(), ctypes.c_double()
     f = lib.lol_measure_mfma_bf16
-    assert f(2, 10, 4096, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
-    assert f(1, 0, 4096, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
-    assert f(1, 10, None, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
-    assert f(1, 10, 4096 + 16, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
-    assert f(1, 10, 4096, 1 << 20, None, ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(16, 2, 10, 4096, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(16, 1, 0, 4096, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(16, 1, 10, None, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(16, 1, 10, 4096 + 16, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(16, 1, 10, 4096, 1 << 20, None, ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(8, 1, 10, 4096, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
+    assert f(64, 1, 10, 4096, 1 << 20, ctypes.byref(tf), ctypes.byref(ghz), None) == B.LOL_EINVAL
