@@ -110,28 +110,30 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel.  A workgroup computes a 256 x 128 tile (rows x output
-// columns of W) with 4 waves in a 2 x 2 grid, each wave 128 x 64 = 4 x 2
-// blocks of v_mfma_f32_32x32x16_bf16.  Two workgroups share a CU (LDS 72
-// KiB, at most 256 registers per lane each), so one workgroup's barriers,
-// prologue and epilogue overlap the other's matrix work.
+// bf16 MFMA kernel.  A workgroup of WM x WN waves computes one tile (rows x
+// output columns of W); each wave owns 128 x 64 outputs as 16 x 16 blocks of
+// v_mfma_f32_16x16x32_bf16, or 64 x 64 as 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16 in the small-problem shapes (the shape table
+// below).
 //
 // Main loop: k advances by BK = 32 per stage through a ring of NSTAGE LDS
 // stages filled by direct global-to-LDS loads (16 bytes per lane, no
-// register staging).  Inside a stage the fragments of the second 16-k step
-// are read while the first step's MFMAs run, and the first step of the next
-// stage right after the stage barrier.
+// register staging).  Fragment reads of the next stage start right after
+// the stage barrier, under the MFMAs of the current one.
 //
 // LDS layout of one operand in one stage: rows of 32 k = 64 bytes, four
 // 16-byte chunks per row; logical chunk c of row r sits at chunk
 // c ^ swz(r), swz(r) = (r >> 2) & 3.  One load instruction fills 16
 // consecutive rows (1 KiB); the swizzle is applied on the global side (each
-// lane picks which chunk of its row to fetch).  A 128-bit LDS read is served
-// 16 lanes at a time over 64 four-byte banks; with this swizzle the 16 lanes
-// of an MFMA fragment read (16 consecutive rows, one logical chunk) cover
-// all 64 banks, and the hardware's bank-conflict counter reads zero for
-// every fragment read of the kernel (measured for each 32-row block and
-// chunk pair).
+// lane picks which chunk of its row to fetch).  A fragment read has every
+// quarter-wave read one logical chunk of 16 consecutive rows; with the
+// swizzle these 16 lanes cover all 64 four-byte banks.  The read runs at
+// the full rate (4 clocks per 128-bit instruction, measured) only when, in
+// addition, lanes l and l + 16 read 16-byte slots whose index XOR has even
+// parity; an odd XOR costs 2 more clocks per half-wave.  The 32 x 32
+// fragments (lanes l and l + 16 read the same chunk of rows 16 apart)
+// satisfy this as they are; the 16 x 16 fragments order their k-chunks
+// for it.
 //
 // Epilogue: each wave stages 32 rows of its results at a time in LDS (fp32,
 // XOR-swizzled 16-byte slots) and reads them back row-wise, so that every
@@ -368,7 +370,12 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   constexpr int HX = TM;        // activation blocks per half-stage
   const int wm = wave / WN, wn = wave % WN;
   const int frow = lane & 15;
-  const int coff = ((lane >> 4) ^ swz(frow)) << 4;          // swz of every row of the block
+  // quarter q of the wave (lanes 16 q .. 16 q + 15) takes logical k-chunk
+  // pi(q) = 0, 3, 1, 2 of both operands (the MFMA's k order is free as long
+  // as both operands share it): a 128-bit read runs at full rate only when
+  // lanes l and l + 16 sit at 16-byte slots whose XOR has even parity
+  const int kq = (lane >> 5) ^ (((lane >> 4) & 1) * 3);
+  const int coff = (kq ^ swz(frow)) << 4;                    // swz of every row of the block
   const int a_frag = (wm * NXB * 16 + frow) * 64 + coff;    // byte offset inside the A part
   const int b_frag = A_BYTES + (wn * NWB * 16 + frow) * 64 + coff;   // inside the B part
 
