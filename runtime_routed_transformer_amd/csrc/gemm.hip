@@ -660,10 +660,6 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
 #pragma unroll
     for (int im = 0; im < TM; ++im) {
       if (ROPE && rope && !M32) {
-        if (im > 0) {
-          rope_table(rpos[2 * im], tq[0]);
-          rope_table(rpos[2 * im + 1], tq[1]);
-        }
         // pair (x, y) at frequency f: x' = x cos - y sin, y' = x sin + y cos
         auto rot = [](f32x4 &a, f32x4 &b, int j, float c, float sn) {
           const float x = a[j], y = b[j];
@@ -691,6 +687,12 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
               rot(acc[2 * hh][xb], acc[2 * hh + 1][xb], 3, t[0][1].z, t[0][1].w);
             }
           }
+        }
+        // the next block's (cos, sin) entries, in flight under this block's
+        // staging and stores
+        if (im + 1 < TM) {
+          rope_table(rpos[2 * im + 2], tq[0]);
+          rope_table(rpos[2 * im + 3], tq[1]);
         }
       }
       if constexpr (M32) {
