@@ -58,6 +58,7 @@ struct GemmParams {
   const float *rope_cs;    // QKV_ROPE: [W][half][2] cos, sin of p * theta^(-2j/d_head)
   int rope_cols;           // QKV_ROPE: columns [0, rope_cols) hold q and k
   int half;                // QKV_ROPE: d_head / 2
+  float rope_log2_theta;   // QKV_ROPE: log2 of the RoPE base
   int a_panel_rows;        // 0: A is [rows][K]; else A is in 32-k panels [K/32][a_panel_rows][32]
   int c_panel_rows;        // bf16 store epilogues: 0 = C is [rows][ldc]; else 32-column panels
   int gm;                  // m-tiles per group of the tile order (see "Tile order")
@@ -472,13 +473,31 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   // (cos, sin) of frequencies f .. f + 3 at position pos, f = 16 q + 4 (lane / 16)
   // (q = 0, and q = 1 for d_head = 64), for each 16-row half of a 32-row block
   float4 tq[ROPE ? 2 : 1][2][2];
+  // computed, not loaded: frequency f turns theta^(-f / half) / (2 pi)
+  // revolutions per position; the hardware sine and cosine take revolutions
+  float frev[ROPE ? 2 : 1][4];
+  if (ROPE) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = 16 * q + 4 * (lane >> 4) + i;
+        frev[q][i] = __builtin_amdgcn_exp2f(-(float)f / (float)P.half * P.rope_log2_theta) * 0.15915494309189535f;
+      }
+  }
   auto rope_table = [&](int pos, float4 (&t)[2][2]) {
-    const float *cs = P.rope_cs + (size_t)pos * P.half * 2 + 8 * (lane >> 4);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       if (q == 0 || P.half == 32) {
-        t[q][0] = *reinterpret_cast<const float4 *>(cs + 32 * q);
-        t[q][1] = *reinterpret_cast<const float4 *>(cs + 32 * q + 4);
+        float c[4], sn[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float r = __builtin_amdgcn_fractf((float)pos * frev[q][i]);
+          c[i] = __builtin_amdgcn_cosf(r);
+          sn[i] = __builtin_amdgcn_sinf(r);
+        }
+        t[q][0] = make_float4(c[0], sn[0], c[1], sn[1]);
+        t[q][1] = make_float4(c[2], sn[2], c[3], sn[3]);
       }
     }
   };
@@ -1276,6 +1295,7 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.rope_cs = ws.rope_cs;
   P.rope_cols = a.rope_cols;
   P.half = p.d_head / 2;
+  P.rope_log2_theta = p.cfg.rope_theta > 0.f ? log2f(p.cfg.rope_theta) : 0.f;
   P.a_panel_rows = a.a_panel_rows;
   P.c_panel_rows = a.c_panel_rows;
   P.gm = (EPI == EPI_SWIGLU ? 2 * a.N : a.N) >= 8192 ? GM_WIDE : GM_OTHER;
