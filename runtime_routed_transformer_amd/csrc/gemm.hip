@@ -486,6 +486,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
       }
   }
   auto rope_table = [&](int pos, float4 (&t)[2][2]) {
+    // (the fraction of the position's revolutions, exact to about 2^-24 W)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       if (q == 0 || P.half == 32) {
@@ -660,8 +661,8 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
     };
     const int rr = lane_e / LPR, cc = (lane_e % LPR) * 2;   // read-back row in pass, first slot
     const int col_base = nt * out_cols + wn * NC;
-    // RoPE: window positions of this lane's rows and the (cos, sin) table
-    // entries of its first 32-row block
+    // RoPE: window positions of this lane's rows and the (cos, sin) values
+    // of its first 32-row block
     const bool rope = ROPE && col_base < P.rope_cols;
     if (ROPE && rope && !M32) {
 #pragma unroll
@@ -707,8 +708,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
             }
           }
         }
-        // the next block's (cos, sin) entries, in flight under this block's
-        // staging and stores
+        // the next block's (cos, sin) values
         if (im + 1 < TM) {
           rope_table(rpos[2 * im + 2], tq[0]);
           rope_table(rpos[2 * im + 3], tq[1]);
