@@ -152,7 +152,7 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 // ranges (workgroup i runs on XCD i mod 8), so that tiles sharing an A or B
 // slice run close together in time on one XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int TN = 2;                   // 32 x 32 blocks per wave along N: 64 output columns
+constexpr int TN = 2;                   // 32-wide units per wave along N (64 output columns)
 constexpr int BK = 32;
 // m-tiles per group: 4 for the wide projections (8,192 weight rows and
 // more: gate/up, the vocabulary readout), 2 for the others (same-box A/B at
@@ -181,7 +181,7 @@ constexpr int GM_WIDE = 4, GM_OTHER = 2;
 // tile per CU, where a stage's matrix work (256 clocks per wave) is far
 // shorter than a load's latency and only a deep ring keeps it fed.
 template <int WM, int WN, int TMV = 4, int NSV = 0> struct Shape {
-  static constexpr int TM = TMV;                         // 32 x 32 blocks per wave along M
+  static constexpr int TM = TMV;                         // 32-row units per wave along M
   static constexpr int NW = WM * WN;                     // waves
   static constexpr int BMT = 32 * TM * WM;               // rows of A per tile
   static constexpr int BNT = 32 * TN * WN;               // weight rows per tile
