@@ -115,6 +115,17 @@ def test_parity_edge_cases(cfg):
     _report(parity.run(parity.prepare(cfg)))
 
 
+def test_parity_short_k_shapes():
+    """K = 512 with every expert's row count a multiple of 256 (d = d_ffn =
+    512, full 256-token windows, no shift): QKV (with RoPE) and gate/up run
+    on two 256 x 128 workgroups per CU, the shape chosen for 16 stages of K
+    or fewer; compared on the first and last documents."""
+    cfg = CoreConfig("short_k_2x2", batch=8, n=2048, d=512, n_heads=8, d_ffn=512, L=4, D=2,
+                     W=256, S=0, mlp="swiglu", dtype="bf16", seed=44)
+    print(f"[parity] {cfg.name}", flush=True)
+    _report(parity.run(parity.prepare(cfg), rows=[0, cfg.batch - 1], n_tokens=3 * cfg.W + cfg.W // 2))
+
+
 def test_parity_many_experts_clear_margins():
     """Free routing over 32 experts with every route clear of the near-tie
     threshold: W_r drawn with std 1.0 instead of 0.02 makes the router's
