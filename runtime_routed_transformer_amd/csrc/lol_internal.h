@@ -92,13 +92,17 @@ struct LaunchEvents {
 extern thread_local LaunchEvents g_launch_ev;
 
 // Every kernel of the library is launched through this, with the timing
-// events (if any) attached to its dispatch packet.
+// events (if any) attached to its dispatch packet; without events it is a
+// plain launch.
 template <typename F, typename... Args>
 inline void lol_launch(F kernel, const dim3 &grid, const dim3 &block, uint32_t shmem, hipStream_t st,
                        Args... args) {
   hipEvent_t a = g_launch_ev.start;
   g_launch_ev.start = nullptr;
-  hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, a, g_launch_ev.stop, 0u, args...);
+  if (!a && !g_launch_ev.stop)
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+  else
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, a, g_launch_ev.stop, 0u, args...);
 }
 
 size_t workspace_layout(const Plan &p, char *base, Workspace *ws);
