@@ -56,6 +56,15 @@ def test_parity_full_size_sampled(name):
     _report(parity.run(inp, rows=[0, cfg.batch - 1], n_tokens=min(cfg.n, 3 * cfg.W + cfg.W // 2)))
 
 
+def test_parity_bench_workload_complete():
+    """The benchmark's workload (mid_bf16: 4 documents of 4,096 tokens, 8
+    experts, 8 depths) compared with the oracle on every token of every
+    document, not on a sample."""
+    cfg = CONFIG_BY_NAME["mid_bf16"]
+    print(f"[parity-complete] {cfg.name}", flush=True)
+    _report(parity.run(parity.prepare(cfg)))
+
+
 EDGE = [
     CoreConfig("edge_fp32_ragged", batch=2, n=37, d=64, n_heads=2, d_ffn=128, L=3, D=4, W=5, S=3,
                mlp="swiglu", dtype="fp32", seed=21),
