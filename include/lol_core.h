@@ -99,6 +99,14 @@ typedef struct {
  *                          every forward rearranges W_o into its workspace
  *                          first; given, the forward reads it and does not.
  *                          Must hold the panels of the same wo.
+ *   weight_panels          NULL, or wqkv, w_gu and w_down already
+ *                          rearranged by lol_prepare_weight_panels (see
+ *                          there; bf16 only).  Given, the forward's grouped
+ *                          QKV, gate/up and down GEMMs read their weights
+ *                          from it and not from wqkv, w_gu, w_down (which
+ *                          must still be set: the decode kernels read
+ *                          them).  Must hold the panels of the same
+ *                          matrices.
  * Callers that build this struct must set every member (NULL / 0 where not
  * used). */
 typedef struct {
@@ -107,6 +115,7 @@ typedef struct {
   const float *film_gamma, *film_beta;
   int32_t film_per_expert;
   const void *wo_panels;
+  const void *weight_panels;
 } lol_library;
 
 /* The router (DEVICE, fp32):
@@ -250,6 +259,27 @@ lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
 size_t lol_prepare_wo_panels_size(const lol_core_config *cfg);
 lol_status lol_prepare_wo_panels(const lol_core_config *cfg, const void *wo, void *wo_panels,
                                  void *stream);
+
+/* The experts' block matrices (paper "Library of Layers (LoL)", App. A:
+ * the library of transformer blocks) do not change between forwards either.
+ * The grouped QKV, gate/up and down GEMMs read an expert's weights 32
+ * columns of k at a time.  Row-major, such a step takes 64 bytes from each
+ * weight row: half of a 128-byte line, the other half a step later.  In
+ * 32-k panels, [L][K/32][N_w][32] for a matrix [L][N_w][K] (panel p of
+ * expert e holds W[e][j][32 p .. 32 p + 31] for every row j in order), a
+ * step of a tile is one contiguous block of whole lines.  The buffer holds
+ * the panels of wqkv (N_w = 3d, K = d), then of w_gu (N_w = 2 d_ffn for
+ * SwiGLU, d_ffn for GELU; K = d), then of w_down (N_w = d, K = d_ffn), back
+ * to back; pass it as lol_library.weight_panels.
+ * lol_prepare_weight_panels_size: bytes of that buffer for cfg (the sum of
+ * the three matrices' sizes), or 0 for fp32 or an invalid cfg.  HOST, pure.
+ * lol_prepare_weight_panels: lib->wqkv, lib->w_gu, lib->w_down (DEVICE,
+ * bf16) -> weight_panels (DEVICE, the size above, 16-byte aligned; must not
+ * overlap them).  Asynchronous on stream.  LOL_EUNSUPPORTED when the size
+ * above is 0, LOL_EINVAL for NULL or misaligned pointers. */
+size_t lol_prepare_weight_panels_size(const lol_core_config *cfg);
+lol_status lol_prepare_weight_panels(const lol_core_config *cfg, const lol_library *lib,
+                                     void *weight_panels, void *stream);
 
 /* ---- Expert bucketing of the last routed depth --------------------------
  * A forward groups every depth's windows by chosen expert (the grouped

@@ -39,7 +39,7 @@ class lol_core_config(ctypes.Structure):
 class lol_library(ctypes.Structure):
     _fields_ = [(name, c_void_p) for name in
                 ("wqkv", "wo", "w_gu", "w_down", "g_attn", "g_ffn", "film_gamma", "film_beta")] + \
-               [("film_per_expert", c_int32), ("wo_panels", c_void_p)]
+               [("film_per_expert", c_int32), ("wo_panels", c_void_p), ("weight_panels", c_void_p)]
 
 
 class lol_router(ctypes.Structure):
@@ -68,6 +68,9 @@ _SIGNATURES.update({
                                           c_void_p, c_void_p, POINTER(lol_path), c_void_p]),
     "lol_prepare_wo_panels_size": (c_size_t, [POINTER(lol_core_config)]),
     "lol_prepare_wo_panels": (c_int32, [POINTER(lol_core_config), c_void_p, c_void_p, c_void_p]),
+    "lol_prepare_weight_panels_size": (c_size_t, [POINTER(lol_core_config)]),
+    "lol_prepare_weight_panels": (c_int32, [POINTER(lol_core_config), POINTER(lol_library), c_void_p,
+                                            c_void_p]),
     "lol_core_buckets_size": (c_size_t, [POINTER(lol_core_config)]),
     "lol_core_read_buckets": (c_int32, [POINTER(lol_core_config), c_void_p, c_size_t, c_void_p,
                                         c_void_p]),
@@ -182,6 +185,15 @@ def lol_prepare_wo_panels_size(cfg: lol_core_config) -> int:
 
 def lol_prepare_wo_panels(cfg, wo, wo_panels, stream) -> int:
     return load().lol_prepare_wo_panels(ctypes.byref(cfg), wo, wo_panels, stream)
+
+
+def lol_prepare_weight_panels_size(cfg: lol_core_config) -> int:
+    return load().lol_prepare_weight_panels_size(ctypes.byref(cfg))
+
+
+def lol_prepare_weight_panels(cfg, lib, weight_panels, stream) -> int:
+    return load().lol_prepare_weight_panels(ctypes.byref(cfg), None if lib is None else ctypes.byref(lib),
+                                            weight_panels, stream)
 
 
 def lol_core_buckets_size(cfg: lol_core_config) -> int:

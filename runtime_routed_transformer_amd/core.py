@@ -68,6 +68,17 @@ class DeviceCore:
             film_gamma=_ptr(self.film_gamma), film_beta=_ptr(self.film_beta),
             film_per_expert=1 if self.cfg.film_mode == "depth_expert" else 0,
             wo_panels=_ptr(self.wo_panels))
+        # the QKV, gate/up and down weights in 32-k panels (bf16), likewise
+        # rearranged once
+        self.weight_panels = None
+        panel_bytes = B.lol_prepare_weight_panels_size(self.ccfg)
+        if panel_bytes:
+            self.weight_panels = torch.empty(panel_bytes, dtype=torch.uint8, device=dev)
+            status = B.lol_prepare_weight_panels(self.ccfg, self.lib, _ptr(self.weight_panels),
+                                                 torch.cuda.current_stream(dev).cuda_stream)
+            if status != B.LOL_OK:
+                raise B.LolError(status, "lol_prepare_weight_panels")
+            self.lib.weight_panels = _ptr(self.weight_panels)
         self.rt = B.lol_router(w_r=_ptr(self.w_r), b_r=_ptr(self.b_r), e_depth=_ptr(self.e_depth),
                                expert_bias=_ptr(self.expert_bias),
                                per_depth=1 if self.cfg.router == "per_depth" else 0)

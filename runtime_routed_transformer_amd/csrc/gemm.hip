@@ -60,6 +60,7 @@ struct GemmParams {
   int half;                // QKV_ROPE: d_head / 2
   float rope_log2_theta;   // QKV_ROPE: log2 of the RoPE base
   int a_panel_rows;        // 0: A is [rows][K]; else A is in 32-k panels [K/32][a_panel_rows][32]
+  int b_panel_rows;        // 0: an expert's weights are [N_w][K]; else 32-k panels [K/32][N_w][32]
   int c_panel_rows;        // bf16 store epilogues: 0 = C is [rows][ldc]; else 32-column panels
   int gm;                  // m-tiles per group of the tile order (see "Tile order")
 };
@@ -327,6 +328,8 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   // the tile is then one contiguous block of whole lines)
   const int a_rs = P.a_panel_rows ? BK : K;
   const size_t a_ks = P.a_panel_rows ? (size_t)P.a_panel_rows * BK : BK;
+  const int b_rs = P.b_panel_rows ? BK : K;
+  const int b_ks = P.b_panel_rows ? P.b_panel_rows * BK : BK;
   auto set_src = [&](int e_, int row0_, int row_end_, int nt_) {
     a_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(A + (size_t)row0_ * a_rs), 0, -1,
                                                kBufferFlags);
@@ -352,13 +355,13 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
       } else {
         wrow = nt_ * BNT + r;
       }
-      soff[LAQ + i] = ((uint32_t)wrow * K + ((lchunk ^ swz(r)) << 3)) * 2;   // bytes
+      soff[LAQ + i] = ((uint32_t)wrow * b_rs + ((lchunk ^ swz(r)) << 3)) * 2;   // bytes
     }
   };
   set_src(e, row0, row_end, nt);
   auto issue_l = [&](int stage, int slot) {
     char *base = smem + slot * STAGE_BYTES;
-    const int a_so = (int)(stage * a_ks * 2), b_so = stage * BK * 2;   // bytes
+    const int a_so = (int)(stage * a_ks * 2), b_so = stage * b_ks * 2;   // bytes
 #pragma unroll
     for (int i = 0; i < LAQ; ++i) lds_dma16_buf(a_rsrc, soff[i], a_so, base + (wave % LW + LW * i) * 1024);
 #pragma unroll
@@ -910,21 +913,25 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
 // 4 whole rows: h = s_in[t] + y, one wave reduction of h^2, u = FiLM(g_e h /
 // rms) in bf16 and s[t] = s_in[t] + gate y, all as contiguous row accesses.
 // ---------------------------------------------------------------------------
-// W [L][d][d] (row n, contiguous k) -> Wp [L][d/16][d][16]: the 16-k
-// panel p of expert e holds W[e][n][16 p .. 16 p + 16) for every n, in n
-// order.  One thread per 16-byte piece, numbered in Wp order, so the
-// stores are contiguous.
+// W [L][rows][K] (row n, contiguous k) -> Wp [L][K/PW][rows][PW]: the
+// PW-k panel p of expert e holds W[e][n][PW p .. PW p + PW) for every n, in
+// n order, so that one PW-column step of an expert's weights is one
+// contiguous block of whole lines.  One thread per 16-byte piece, numbered
+// in Wp order, so the stores are contiguous.  PW = 16 for the fused output
+// projection's W_o, 32 for the grouped GEMMs' stages.
+template <int PW>
 __global__ void __launch_bounds__(256) k_pack_panels(const bf16_t *__restrict__ W, bf16_t *__restrict__ Wp,
-                                                     int d, long long pieces) {
+                                                     int rows, int K, long long pieces) {
+  constexpr int PPR = PW / 8;                  // 16-byte pieces per panel row
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= pieces) return;
-  const int half = (int)(i & 1);
-  const long long nn = i >> 1;                 // (e, panel, n) in Wp order
-  const int n = (int)(nn % d);
-  const long long ep = nn / d;                 // e * (d / 16) + panel
-  const int panel = (int)(ep % (d / 16));
-  const long long e = ep / (d / 16);
-  const uint4 v = *reinterpret_cast<const uint4 *>(W + ((size_t)e * d + n) * d + panel * 16 + half * 8);
+  const int q = (int)(i % PPR);
+  const long long nn = i / PPR;                // (e, panel, n) in Wp order
+  const int n = (int)(nn % rows);
+  const long long ep = nn / rows;              // e * (K / PW) + panel
+  const int panel = (int)(ep % (K / PW));
+  const long long e = ep / (K / PW);
+  const uint4 v = *reinterpret_cast<const uint4 *>(W + ((size_t)e * rows + n) * K + panel * PW + q * 8);
   *reinterpret_cast<uint4 *>(Wp + (size_t)i * 8) = v;
 }
 
@@ -1298,8 +1305,10 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.rope_log2_theta = p.cfg.rope_theta > 0.f ? log2f(p.cfg.rope_theta) : 0.f;
   P.a_panel_rows = a.a_panel_rows;
   P.c_panel_rows = a.c_panel_rows;
+  P.b_panel_rows = a.b_panel_rows;
   P.gm = (EPI == EPI_SWIGLU ? 2 * a.N : a.N) >= 8192 ? GM_WIDE : GM_OTHER;
-  if ((a.a_panel_rows || a.c_panel_rows) && p.cfg.dtype != LOL_BF16) return hipErrorInvalidValue;
+  if ((a.a_panel_rows || a.b_panel_rows || a.c_panel_rows) && p.cfg.dtype != LOL_BF16)
+    return hipErrorInvalidValue;
   if (a.c_panel_rows && (EPI == EPI_RESID || EPI == EPI_BLEND || EPI == EPI_ACCUM)) return hipErrorInvalidValue;
   if (EPI == EPI_QKV_ROPE && (p.cfg.dtype != LOL_BF16 || (p.d_head != 32 && p.d_head != 64)))
     return hipErrorInvalidValue;  // fp32 mode rotates inside its attention kernel
@@ -1416,13 +1425,21 @@ hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws,
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_pack_wo(const lol_core_config &c, const void *wo, void *wo_p, hipStream_t st) {
-  if (!wo || !wo_p) return hipErrorInvalidValue;
-  const int d = c.d;
-  const long long pieces = (long long)c.L * d * d / 8;   // 16-byte pieces
-  lol_launch(k_pack_panels, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const bf16_t *>(wo), reinterpret_cast<bf16_t *>(wo_p), d, pieces);
+hipError_t launch_pack_panels(const void *w, void *wp, int L, int rows, int K, int pw, hipStream_t st) {
+  if (!w || !wp || (pw != 16 && pw != 32) || K % pw != 0) return hipErrorInvalidValue;
+  const long long pieces = (long long)L * rows * K / 8;   // 16-byte pieces
+  const dim3 grid((unsigned)((pieces + 255) / 256));
+  const bf16_t *src = reinterpret_cast<const bf16_t *>(w);
+  bf16_t *dst = reinterpret_cast<bf16_t *>(wp);
+  if (pw == 16)
+    lol_launch(k_pack_panels<16>, grid, dim3(256), 0, st, src, dst, rows, K, pieces);
+  else
+    lol_launch(k_pack_panels<32>, grid, dim3(256), 0, st, src, dst, rows, K, pieces);
   return hipGetLastError();
+}
+
+hipError_t launch_pack_wo(const lol_core_config &c, const void *wo, void *wo_p, hipStream_t st) {
+  return launch_pack_panels(wo, wo_p, c.L, c.d, c.d, 16, st);
 }
 
 hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st) {

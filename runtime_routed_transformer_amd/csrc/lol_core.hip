@@ -253,6 +253,17 @@ lol_status lol_core_forward_docs(const lol_core_config *cfg, int64_t n_tokens,
 
 namespace lol {
 namespace {
+// Byte offsets of the three matrices inside lol_prepare_weight_panels'
+// buffer (wqkv's panels start at 0); returns the buffer's size.
+size_t weight_panel_layout(const lol_core_config &c, size_t *off_gu, size_t *off_down) {
+  const size_t L = c.L, d = c.d, f = c.d_ffn;
+  const size_t n_gu = c.mlp == LOL_MLP_SWIGLU ? 2 * f : f;
+  const size_t qkv = L * 3 * d * d * 2, gu = L * n_gu * d * 2, down = L * d * f * 2;
+  if (off_gu) *off_gu = qkv;
+  if (off_down) *off_down = qkv + gu;
+  return qkv + gu + down;
+}
+
 // The routed-core forward behind every entry point.  allow_timing = false
 // leaves the timing instrumentation off for this call (it creates HIP
 // events on first use).
@@ -272,6 +283,9 @@ lol_status forward_impl(const lol_core_config *cfg, int64_t n_tokens, const int3
   if ((lib->film_gamma == nullptr) != (lib->film_beta == nullptr)) return LOL_EINVAL;
   if (!rt->w_r || !rt->e_depth) return LOL_EINVAL;
   if ((rt->per_depth != 0 && rt->per_depth != 1) || (lib->film_per_expert != 0 && lib->film_per_expert != 1))
+    return LOL_EINVAL;
+  if (lib->weight_panels &&
+      (cfg->dtype != LOL_BF16 || (reinterpret_cast<uintptr_t>(lib->weight_panels) & 15)))
     return LOL_EINVAL;
   Plan p = make_plan(cfg);
   p.doc_start = doc_start;
@@ -318,6 +332,11 @@ lol_status forward_impl(const lol_core_config *cfg, int64_t n_tokens, const int3
   // W_o in 16-k panels for the fused output projection, unless the caller
   // prepared them once (lol_prepare_wo_panels)
   if (fused_o && !lib->wo_panels) LOL_TRY(KK_SETUP, launch_pack_wo(c, lib->wo, ws.wo_p, st));
+  // the experts' QKV, gate/up and down weights in 32-k panels, when the
+  // caller prepared them (lol_prepare_weight_panels)
+  const char *wpan = static_cast<const char *>(lib->weight_panels);
+  size_t wpan_gu = 0, wpan_down = 0;
+  weight_panel_layout(c, &wpan_gu, &wpan_down);
   for (int l = 0; l < c.D; ++l) {
     cur_depth = l;
     const float *s = l == 0 ? s0 : s_out;   // depth input
@@ -344,6 +363,10 @@ lol_status forward_impl(const lol_core_config *cfg, int64_t n_tokens, const int3
     a.rope_cols = rope_in_gemm ? 2 * c.d : 0;
     a.C = ws.qkv;
     a.a_panel_rows = qkv_panels ? p.T : 0;
+    if (wpan) {
+      a.Wt = wpan;
+      a.b_panel_rows = 3 * c.d;
+    }
     LOL_TRY(KK_GEMM_QKV, launch_gemm(p, ws, a, st));
     LOL_TRY(KK_ATTN, launch_attention(p, g, ws, st));
     if (fused_o) {
@@ -375,6 +398,10 @@ lol_status forward_impl(const lol_core_config *cfg, int64_t n_tokens, const int3
     // the fused O kernel leaves u in 32-k panels: whole-line loads per stage
     a.a_panel_rows = fused_o ? p.T : 0;
     a.c_panel_rows = down_panels ? p.T : 0;
+    if (wpan) {
+      a.Wt = wpan + wpan_gu;
+      a.b_panel_rows = (glu ? 2 : 1) * c.d_ffn;
+    }
     LOL_TRY(KK_GEMM_GATE_UP, launch_gemm(p, ws, a, st));
     a = GemmArgs{};
     a.len_gcd = g.len_gcd;
@@ -393,6 +420,10 @@ lol_status forward_impl(const lol_core_config *cfg, int64_t n_tokens, const int3
       a.h = ws.h;
     }
     a.s = s_out;
+    if (wpan) {
+      a.Wt = wpan + wpan_down;
+      a.b_panel_rows = c.d;
+    }
     LOL_TRY(KK_GEMM_DOWN, launch_gemm(p, ws, a, st));
   }
 #undef LOL_TRY
@@ -567,6 +598,38 @@ lol_status lol_prepare_wo_panels(const lol_core_config *cfg, const void *wo, voi
   const uintptr_t a = reinterpret_cast<uintptr_t>(wo), b = reinterpret_cast<uintptr_t>(wo_panels);
   if (a < b + bytes && b < a + bytes) return LOL_EINVAL;   // overlapping buffers
   if (launch_pack_wo(*cfg, wo, wo_panels, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LOL_EHIP;
+  return LOL_OK;
+}
+
+size_t lol_prepare_weight_panels_size(const lol_core_config *cfg) {
+  if (validate(cfg) != LOL_OK || cfg->dtype != LOL_BF16) return 0;
+  return weight_panel_layout(*cfg, nullptr, nullptr);
+}
+
+lol_status lol_prepare_weight_panels(const lol_core_config *cfg, const lol_library *lib,
+                                     void *weight_panels, void *stream) {
+  const lol_status vs = validate(cfg);
+  if (vs != LOL_OK) return vs;
+  if (cfg->dtype != LOL_BF16) return LOL_EUNSUPPORTED;
+  if (!lib || !weight_panels || (reinterpret_cast<uintptr_t>(weight_panels) & 15)) return LOL_EINVAL;
+  const void *src[3] = {lib->wqkv, lib->w_gu, lib->w_down};
+  size_t off[3] = {0, 0, 0};
+  const size_t bytes = weight_panel_layout(*cfg, &off[1], &off[2]);
+  const size_t len[3] = {off[1], off[2] - off[1], bytes - off[2]};
+  const uintptr_t b = reinterpret_cast<uintptr_t>(weight_panels);
+  for (int i = 0; i < 3; ++i) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src[i]);
+    if (!src[i] || (a & 15)) return LOL_EINVAL;
+    if (a < b + bytes && b < a + len[i]) return LOL_EINVAL;   // overlapping buffers
+  }
+  const int d = cfg->d, f = cfg->d_ffn, L = cfg->L;
+  const int n_gu = cfg->mlp == LOL_MLP_SWIGLU ? 2 * f : f;
+  char *dst = static_cast<char *>(weight_panels);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (launch_pack_panels(lib->wqkv, dst, L, 3 * d, d, 32, st) != hipSuccess ||
+      launch_pack_panels(lib->w_gu, dst + off[1], L, n_gu, d, 32, st) != hipSuccess ||
+      launch_pack_panels(lib->w_down, dst + off[2], L, d, f, 32, st) != hipSuccess)
     return LOL_EHIP;
   return LOL_OK;
 }

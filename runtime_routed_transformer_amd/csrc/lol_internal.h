@@ -155,6 +155,8 @@ struct GemmArgs {
   int rope_cols;        // QKV_ROPE: columns [0, rope_cols) are rotated (2 d; 0 = no RoPE)
   int len_gcd;          // gcd of the depth's window lengths: every expert's row count is a multiple
   int a_panel_rows;     // 0: A is [T][K]; else 32-k panels [K/32][a_panel_rows][32] (bf16 only)
+  int b_panel_rows;     // 0: each expert's weights are [N_w][K]; else 32-k panels
+                        // [K/32][b_panel_rows][32] per expert, b_panel_rows = N_w (bf16 only)
   int c_panel_rows;     // SwiGLU / GELU / STORE (bf16): 0 = C is [T][N]; else 32-column panels
 };
 hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st);
@@ -170,6 +172,8 @@ bool o_norm_fused(const Plan &p);                  // eligible and the device's 
 // W_o [L][d][d] -> 16-k panels [L][d/16][d][16]: one 16-k stage of all d
 // rows of an expert becomes one contiguous block
 hipError_t launch_pack_wo(const lol_core_config &c, const void *wo, void *wo_p, hipStream_t st);
+// w [L][rows][K] bf16 -> wp [L][K/pw][rows][pw] (pw = 16 or 32)
+hipError_t launch_pack_panels(const void *w, void *wp, int L, int rows, int K, int pw, hipStream_t st);
 // u_panel_rows > 0 writes u in 32-k panels [d/32][u_panel_rows][32] (the
 // A layout the next GEMM reads with GemmArgs::a_panel_rows)
 hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws, const float *s_in,

@@ -213,6 +213,43 @@ def test_prepared_wo_panels_sizes_and_rejections(lib):
     assert B.lol_prepare_wo_panels(bad, 4096, 1 << 40, None) == B.LOL_EINVAL
 
 
+def test_prepared_weight_panels_sizes_and_rejections(lib):
+    """lol_prepare_weight_panels: the three GEMM matrices' bytes in bf16 mode,
+    nothing in fp32 mode; bad arguments are refused before anything is
+    launched, and a forward refuses weight panels in fp32 mode or
+    misaligned."""
+    for cfg in CONFIGS:
+        c = make_config(cfg)
+        n_gu = (2 if cfg.mlp == "swiglu" else 1) * cfg.d_ffn
+        want = (cfg.L * (3 * cfg.d * cfg.d + n_gu * cfg.d + cfg.d * cfg.d_ffn) * 2
+                if cfg.dtype == "bf16" else 0)
+        assert B.lol_prepare_weight_panels_size(c) == want, cfg.name
+    tiny = make_config(CONFIG_BY_NAME["tiny_fp32"])
+    libw = B.lol_library(wqkv=4096, wo=4096, w_gu=1 << 36, w_down=1 << 37, g_attn=16, g_ffn=16)
+    assert B.lol_prepare_weight_panels(tiny, libw, 1 << 40, None) == B.LOL_EUNSUPPORTED
+    mid = make_config(CONFIG_BY_NAME["mid_bf16"])
+    size = B.lol_prepare_weight_panels_size(mid)
+    assert B.lol_prepare_weight_panels(mid, None, 1 << 40, None) == B.LOL_EINVAL
+    assert B.lol_prepare_weight_panels(mid, libw, None, None) == B.LOL_EINVAL
+    assert B.lol_prepare_weight_panels(mid, libw, (1 << 40) + 8, None) == B.LOL_EINVAL  # misaligned
+    assert B.lol_prepare_weight_panels(mid, libw, 4096 + 16, None) == B.LOL_EINVAL  # overlaps wqkv
+    assert B.lol_prepare_weight_panels(mid, libw, (1 << 37) - size + 16, None) == B.LOL_EINVAL  # w_down
+    libm = B.lol_library(wqkv=4096, wo=4096, w_gu=None, w_down=1 << 37, g_attn=16, g_ffn=16)
+    assert B.lol_prepare_weight_panels(mid, libm, 1 << 40, None) == B.LOL_EINVAL
+    bad = make_config(CONFIG_BY_NAME["mid_bf16"]); bad.W = 0
+    assert B.lol_prepare_weight_panels_size(bad) == 0
+    assert B.lol_prepare_weight_panels(bad, libw, 1 << 40, None) == B.LOL_EINVAL
+    # a forward with weight panels: fp32 mode and misaligned panels are
+    # refused (before the workspace check, which a one-byte-short workspace
+    # would fail: nothing can be launched)
+    rt = B.lol_router(w_r=16, e_depth=16)
+    for cfg, panels in ((CONFIG_BY_NAME["tiny_fp32"], 1 << 40), (CONFIG_BY_NAME["mid_bf16"], (1 << 40) + 8)):
+        c = make_config(cfg)
+        lw = B.lol_library(wqkv=16, wo=16, w_gu=16, w_down=16, g_attn=16, g_ffn=16, weight_panels=panels)
+        ws = B.lol_core_workspace_size(c)
+        assert B.lol_core_forward(c, 16, lw, rt, None, None, 16, None, 256, ws - 1, None) == B.LOL_EINVAL
+
+
 def test_buckets_size_matches_the_documented_layout(lib):
     """counts [L], row_off [L + 1], win_row0 [batch K_max], n_tiles [2],
     tiles128 [ceil(T / 128) + L][2], tiles256 [ceil(T / 256) + L][2]."""

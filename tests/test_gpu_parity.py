@@ -174,6 +174,28 @@ def test_gate_zero_identity_and_determinism_and_inplace():
     assert torch.equal(s, a), "in-place run differs"
 
 
+@pytest.mark.parametrize("name", ["mid_bf16", "small_bf16", "tiny_bf16_gelu"])
+def test_prepared_weight_panels_give_the_row_major_result(name):
+    """The grouped GEMMs reading wqkv, w_gu and w_down from the 32-k panels of
+    lol_prepare_weight_panels compute bit for bit what they compute from the
+    row-major matrices (only addresses differ), at every tile shape the
+    workload's depths use, for SwiGLU and GELU."""
+    import torch
+    from runtime_routed_transformer_amd.core import DeviceCore
+    if name == "tiny_bf16_gelu":
+        cfg = CONFIG_BY_NAME["tiny_fp32"].with_(name=name, dtype="bf16", d=128, d_ffn=256)
+    else:
+        cfg = CONFIG_BY_NAME[name]
+    inp = parity.prepare(cfg)
+    core = DeviceCore(inp)
+    assert core.weight_panels is not None and core.lib.weight_panels
+    with_panels = core.forward().clone()
+    core.lib.weight_panels = None
+    row_major = core.forward().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(with_panels, row_major)
+
+
 def test_forced_own_path_and_bad_forced_id_flag():
     import torch
     from runtime_routed_transformer_amd import binding
