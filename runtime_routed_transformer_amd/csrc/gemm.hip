@@ -1319,11 +1319,13 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
     // 256 x 256 tiles (persistent) when every expert's row count is a
     // multiple of 256 and such tiles fill the CUs; otherwise tiles from the
     // 128-row table, which leave no partial tile when rows come in multiples
-    // of 128: 128 x 512 (persistent) for long K (the down projection) when N
-    // allows and they fill the CUs, else 128 x 256 (measured: 128 x 512 is
-    // faster at K = 4096, slower at K = 1024, where the larger tile's
-    // prologue and epilogue weigh more; gate/up measured faster with
-    // 256 x 256 either way);
+    // of 128: 128 x 512 (persistent) when N allows and they fill the CUs,
+    // for long K (the down projection) or with the weights in 32-k panels,
+    // else 128 x 256 (measured: with row-major weights 128 x 512 is faster
+    // at K = 4096 and slower at K = 1024, where its 512 weight rows per
+    // stage are 1,024 half-line requests; in panels it is faster at K =
+    // 1,024 too, QKV at the shifted depths of mid_bf16 112 -> 101 us;
+    // gate/up measured faster with 256 x 256 either way);
     // 256 x 128 when N is not a multiple of 256
     const int n_w = EPI == EPI_SWIGLU ? 2 * a.N : a.N;   // weight rows
     if (n_w % 256 == 0) {
@@ -1346,7 +1348,7 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
       // mid_bf16_packed down 284 -> 240 us)
       if (!rows128 && tiles256 >= ncu) return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
       const long long tiles512 = (long long)(p.T / kTileM) * (n_w / 512);
-      if (a.K >= 2048 && n_w % 512 == 0 && tiles512 >= ncu)
+      if ((a.K >= 2048 || a.b_panel_rows) && n_w % 512 == 0 && tiles512 >= ncu)
         return launch_shape<EPI, 1, 8>(P, ws, n_w, st);
       // a small problem whose 128 x 256 tiles would not fill the workgroup
       // slots (two per CU) in one round: 128 x 128 tiles of four 64 x 64
