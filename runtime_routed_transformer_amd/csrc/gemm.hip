@@ -155,11 +155,14 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 // ---------------------------------------------------------------------------
 constexpr int TN = 2;                   // 32-wide units per wave along N (64 output columns)
 constexpr int BK = 32;
-// m-tiles per group: 4 for the wide projections (8,192 weight rows and
-// more: gate/up, the vocabulary readout), 2 for the others (same-box A/B at
-// mid_bf16: QKV 124 vs 127 us with 2 rather than 4, gate/up equal in time
-// but with 819 instead of 659 MB of L2-miss traffic; 1 and 8 slower)
-constexpr int GM_WIDE = 4, GM_OTHER = 2;
+// m-tiles per group: 2 for every projection.  With row-major weights 4 was
+// as fast for the wide ones (8,192 weight rows and more) and moved less
+// L2-miss traffic; with the weights in 32-k panels 2 is faster there too
+// (same-box A/B at mid_bf16, two runs each: 3.493 / 3.493 M tokens/s
+// against 3.482 / 3.485 with 4 for gate/up and 3.485 / 3.491 with 8;
+// gate/up at the unshifted depths 205-210 against 209-218 us with 4; 4 for
+// every projection 3.473, and 1 for the narrow ones 3.482)
+constexpr int GM = 2;
 // Four shapes of workgroup, WM x WN waves:
 //   2 x 2: 256 x 128 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
 //   2 x 4: 256 x 256 tile, 8 waves, 4-stage ring of 128 KiB, one per CU
@@ -1306,7 +1309,7 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.a_panel_rows = a.a_panel_rows;
   P.c_panel_rows = a.c_panel_rows;
   P.b_panel_rows = a.b_panel_rows;
-  P.gm = (EPI == EPI_SWIGLU ? 2 * a.N : a.N) >= 8192 ? GM_WIDE : GM_OTHER;
+  P.gm = GM;
   if ((a.a_panel_rows || a.b_panel_rows || a.c_panel_rows) && p.cfg.dtype != LOL_BF16)
     return hipErrorInvalidValue;
   if (a.c_panel_rows && (EPI == EPI_RESID || EPI == EPI_BLEND || EPI == EPI_ACCUM)) return hipErrorInvalidValue;
