@@ -286,7 +286,7 @@ __global__ void __launch_bounds__(256, 3) k_attn_mfma(const bf16_t *__restrict__
                                                       const int32_t *__restrict__ win_exp,
                                                       const int32_t *__restrict__ win_row0,
                                                       const int32_t *__restrict__ win_len, int d,
-                                                      float qscale) {
+                                                      float qscale, int o_panel_rows) {
   using LY = AttnLds<DH>;
   constexpr int CH = 256;            // keys / queries per chunk
   constexpr int RB = LY::RB, NCK = LY::NCK, RPI = LY::RPI;
@@ -457,7 +457,6 @@ __global__ void __launch_bounds__(256, 3) k_attn_mfma(const bf16_t *__restrict__
     const int q = q_begin + qblk[b] * 32 + col;
     if (q >= len) continue;
     const float il = 1.0f / l_run[b];
-    bf16_t *op = o + (size_t)(base + q) * d + h * DH;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -465,7 +464,11 @@ __global__ void __launch_bounds__(256, 3) k_attn_mfma(const bf16_t *__restrict__
         uint2 pk;
         pk.x = (uint32_t)f2bf(acc[b][db][4 * g] * il) | ((uint32_t)f2bf(acc[b][db][4 * g + 1] * il) << 16);
         pk.y = (uint32_t)f2bf(acc[b][db][4 * g + 2] * il) | ((uint32_t)f2bf(acc[b][db][4 * g + 3] * il) << 16);
-        *reinterpret_cast<uint2 *>(op + db * 32 + g * 8 + 4 * hl) = pk;
+        // 4 consecutive columns, inside one 16-column panel when o is in panels
+        const int col = h * DH + db * 32 + g * 8 + 4 * hl;
+        bf16_t *op = o_panel_rows ? o + ((size_t)(col >> 4) * o_panel_rows + base + q) * 16 + (col & 15)
+                                  : o + (size_t)(base + q) * d + col;
+        *reinterpret_cast<uint2 *>(op) = pk;
       }
   }
 }
@@ -524,13 +527,14 @@ hipError_t attn_typed(const Plan &p, const DepthGeom &g, const Workspace &ws, hi
 }
 
 template <int DH>
-hipError_t attn_mfma(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {
+hipError_t attn_mfma(const Plan &p, const DepthGeom &g, const Workspace &ws, int o_panel_rows,
+                     hipStream_t st) {
   dim3 grid(p.n_slots, p.cfg.n_heads, (p.cfg.W + 255) / 256);
   // scores come out in log2 units: softmax uses exp2
   const float qscale = 1.4426950408889634f / sqrtf((float)DH);
   lol_launch((k_attn_mfma<DH>), grid, dim3(256), 0, st,
                      reinterpret_cast<const bf16_t *>(ws.qkv), reinterpret_cast<bf16_t *>(ws.o),
-                     ws.win_exp, ws.win_row0, ws.win_len, p.cfg.d, qscale);
+                     ws.win_exp, ws.win_row0, ws.win_len, p.cfg.d, qscale, o_panel_rows);
   return hipGetLastError();
 }
 
@@ -544,9 +548,12 @@ hipError_t launch_norm(const Plan &p, const DepthGeom &g, int which, const float
   return norm_typed<float>(p, which, s, lib, ws, g.depth, g.delta, 0, st);
 }
 
-hipError_t launch_attention(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st) {
+hipError_t launch_attention(const Plan &p, const DepthGeom &g, const Workspace &ws, int o_panel_rows,
+                            hipStream_t st) {
   if (p.cfg.dtype == LOL_BF16)
-    return p.d_head == 64 ? attn_mfma<64>(p, g, ws, st) : attn_mfma<32>(p, g, ws, st);
+    return p.d_head == 64 ? attn_mfma<64>(p, g, ws, o_panel_rows, st)
+                          : attn_mfma<32>(p, g, ws, o_panel_rows, st);
+  if (o_panel_rows) return hipErrorInvalidValue;   // fp32 mode keeps o row-major
   return p.d_head == 64 ? attn_typed<float, 64>(p, g, ws, st) : attn_typed<float, 32>(p, g, ws, st);
 }
 

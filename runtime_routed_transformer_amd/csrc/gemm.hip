@@ -939,7 +939,8 @@ __global__ void __launch_bounds__(256) k_pack_panels(const bf16_t *__restrict__ 
 }
 
 struct ONormParams {
-  const bf16_t *A;         // o, [T][d]
+  const bf16_t *A;         // o in 16-k panels, [d/16][a_panel_rows][16]
+  int a_panel_rows;        // rows of each panel of o (T)
   const bf16_t *Wp;        // W_o in 16-k panels, [L][d/16][d][16]
   const int32_t *mtile;    // 128-row tile table: (expert, first row)
   const int32_t *mcount;
@@ -1004,14 +1005,16 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
 
   // ---- load sources.  Activations: wave w fetches rows 8 w .. 8 w + 7, 4
   // bytes per lane (lane -> row 8 w + lane / 8, dword lane % 8 of the row's
-  // 32 bytes).  Weights: instruction q of wave w fetches rows (w + 8 q) 32 +
-  // lane / 2, 16 bytes per lane (physical chunk lane % 2).
+  // 32 bytes); o is in 16-k panels, so a stage of the tile's 64 rows is one
+  // contiguous 2 KiB block.  Weights: instruction q of wave w fetches rows
+  // (w + 8 q) 32 + lane / 2, 16 bytes per lane (physical chunk lane % 2).
   const int last = row_end - 1 - row0;
   const int ar = wave * 8 + (lane >> 3);
   const int a_chunk = ((lane >> 2) & 1) ^ ((ar >> 3) & 1);
-  const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(P.A + (size_t)row0 * D), 0, -1, kBufferFlags);
-  const uint32_t a_off = ((uint32_t)min(ar, last) * D + a_chunk * 8 + (lane & 3) * 2) * 2;   // bytes
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(P.A + (size_t)row0 * kONormBK), 0, -1, kBufferFlags);
+  const uint32_t a_off = ((uint32_t)min(ar, last) * kONormBK + a_chunk * 8 + (lane & 3) * 2) * 2;   // bytes
+  const int a_step = P.a_panel_rows * kONormBK * 2;   // bytes from one 16-k panel to the next
   // weights in 16-k panels: stage k0 / 16 of expert e is the contiguous
   // block Wp[e][k0 / 16][0 .. d)[0 .. 16), so every request is a whole line
   const __amdgpu_buffer_rsrc_t b_rsrc =
@@ -1024,7 +1027,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
   }
   auto issue = [&](int stage, int slot) {
     char *base = smem + slot * STAGE;
-    lds_dma4_buf(a_rsrc, a_off, stage * kONormBK * 2, base + wave * 256);
+    lds_dma4_buf(a_rsrc, a_off, stage * a_step, base + wave * 256);
     const int b_so = stage * (D * kONormBK) * 2;
 #pragma unroll
     for (int q = 0; q < TN; ++q) lds_dma16_buf(b_rsrc, boff[q], b_so, base + A_STAGE + (wave + 8 * q) * 1024);
@@ -1390,6 +1393,9 @@ bool o_norm_eligible(const lol_core_config &c) {
 bool o_norm_fused(const Plan &p) {
   const int d = p.cfg.d;
   if (!o_norm_eligible(p.cfg)) return false;
+  // o and u are read and written in panels whose per-stage steps are 32-bit
+  // byte offsets
+  if (!panels_addressable(p, d)) return false;
   int dev = 0, lds = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return false;
@@ -1402,6 +1408,7 @@ hipError_t launch_o_norm(const Plan &p, const DepthGeom &g, const Workspace &ws,
   const int d = p.cfg.d;
   ONormParams P;
   P.A = reinterpret_cast<const bf16_t *>(ws.o);
+  P.a_panel_rows = p.T;   // the attention kernel wrote o in 16-k panels
   // W_o in panels: the caller's (prepared once) or the forward's own copy
   P.Wp = lib.wo_panels ? reinterpret_cast<const bf16_t *>(lib.wo_panels) : ws.wo_p;
   P.mtile = ws.mtile;

@@ -326,8 +326,8 @@ lol_status forward_impl(const lol_core_config *cfg, int64_t n_tokens, const int3
   // bf16 GEMM inputs written by this library's own kernels go in 32-k
   // panels: a stage of an A tile is then one block of whole lines
   const bool bf16 = c.dtype == LOL_BF16;
-  const bool qkv_panels = bf16;    // u from the attention norm
-  const bool down_panels = bf16;   // hid from the gate/up epilogue
+  const bool qkv_panels = bf16 && panels_addressable(p, c.d);        // u from the attention norm
+  const bool down_panels = bf16 && panels_addressable(p, c.d_ffn);   // hid from the gate/up epilogue
   LOL_TRY(KK_SETUP, launch_setup(p, ws, st));
   // W_o in 16-k panels for the fused output projection, unless the caller
   // prepared them once (lol_prepare_wo_panels)
@@ -368,7 +368,7 @@ lol_status forward_impl(const lol_core_config *cfg, int64_t n_tokens, const int3
       a.b_panel_rows = 3 * c.d;
     }
     LOL_TRY(KK_GEMM_QKV, launch_gemm(p, ws, a, st));
-    LOL_TRY(KK_ATTN, launch_attention(p, g, ws, st));
+    LOL_TRY(KK_ATTN, launch_attention(p, g, ws, fused_o ? p.T : 0, st));
     if (fused_o) {
       LOL_TRY(KK_GEMM_O, launch_o_norm(p, g, ws, s, s_out, *lib, p.T, st));
     } else {

@@ -126,7 +126,10 @@ hipError_t launch_setup(const Plan &p, const Workspace &ws, hipStream_t st);
 // panel_rows > 0 (bf16) writes u in 32-column panels [d/32][panel_rows][32].
 hipError_t launch_norm(const Plan &p, const DepthGeom &g, int which, const float *s,
                        const lol_library &lib, const Workspace &ws, int panel_rows, hipStream_t st);
-hipError_t launch_attention(const Plan &p, const DepthGeom &g, const Workspace &ws, hipStream_t st);
+// o_panel_rows > 0 (bf16): o is written in 16-k panels [d/16][o_panel_rows][16]
+// (the fused output projection reads it so); 0: o is [T][d]
+hipError_t launch_attention(const Plan &p, const DepthGeom &g, const Workspace &ws, int o_panel_rows,
+                            hipStream_t st);
 
 enum GemmEpilogue {
   EPI_STORE = 0,    // C (act) = acc
@@ -168,6 +171,12 @@ hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hi
 // so that the down projection finishes the gated blend with EPI_ACCUM.
 // h is never stored.  s may equal s_in.
 bool o_norm_eligible(const lol_core_config &c);   // bf16, d a multiple of 256 up to 1024
+// An activation buffer of T rows and `cols` bf16 columns can be kept in k
+// panels: the GEMMs step from one panel to the next with a 32-bit byte
+// offset, so the whole buffer must stay under 2 GiB.
+inline bool panels_addressable(const Plan &p, int cols) {
+  return (long long)p.T * cols * 2 <= 0x7FFFFFFFLL;
+}
 bool o_norm_fused(const Plan &p);                  // eligible and the device's LDS holds the ring
 // W_o [L][d][d] -> 16-k panels [L][d/16][d][16]: one 16-k stage of all d
 // rows of an expert becomes one contiguous block

@@ -135,6 +135,18 @@ def test_parity_short_k_shapes():
     _report(parity.run(parity.prepare(cfg), rows=[0, cfg.batch - 1], n_tokens=3 * cfg.W + cfg.W // 2))
 
 
+def test_parity_activations_beyond_2_gib():
+    """T x d_ffn bf16 values above 2 GiB (131,200 tokens, d_ffn 8,192): the
+    gate/up output and the down projection's input stay row-major, because
+    the GEMMs step through k panels with 32-bit offsets; compared on the
+    first and last documents."""
+    cfg = CoreConfig("acts_beyond_2gib", batch=2, n=65600, d=128, n_heads=2, d_ffn=8192, L=2, D=2,
+                     W=64, S=32, mlp="swiglu", dtype="bf16", seed=46)
+    assert cfg.tokens * cfg.d_ffn * 2 > 2 ** 31
+    print(f"[parity] {cfg.name}", flush=True)
+    _report(parity.run(parity.prepare(cfg), rows=[0, cfg.batch - 1], n_tokens=3 * cfg.W + cfg.W // 2))
+
+
 def test_parity_many_experts_clear_margins():
     """Free routing over 32 experts with every route clear of the near-tie
     threshold: W_r drawn with std 1.0 instead of 0.02 makes the router's
