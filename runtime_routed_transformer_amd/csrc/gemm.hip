@@ -152,6 +152,20 @@ __device__ __forceinline__ void store_glu4(const GemmParams &P, int row, int col
 // (n-tile major inside a group) and dealt to the 8 XCDs in contiguous
 // ranges (workgroup i runs on XCD i mod 8), so that tiles sharing an A or B
 // slice run close together in time on one XCD's L2.
+//
+// Mixed tiles (2 x 4 shape, gate/up): where every expert's row count is a
+// multiple of 128 but not of 256, an expert's last 256-row m-tile holds 128
+// rows, and a 256 x 256 tile of it leaves one wave row idle: such tiles
+// formed a partial extra round.  The mixed variant runs the full m-tiles as
+// 256 x 256 tiles and each half-filled one as "wide" 128 x 512 tiles, both
+// wave rows on its 128 activation rows and each on its own 256 weight rows
+// (n-tiles 2 nt and 2 nt + 1): the same MACs per tile, so the number of
+// rounds is that of the aligned depths.  A stage slot holds 128 + 512 rows
+// (40 KiB): pieces 0-7 are A rows 0-127, 8-15 A rows 128-255 or B rows
+// 0-127, 16-31 B rows 0-255 or 128-383, 32-39 (wide only) B rows 384-511;
+// every loading wave issues ten pieces per stage either way, a 256 x 256
+// tile's last two through a buffer resource with no records (nothing is
+// read), so the stage wait counts are the same for both kinds.
 // ---------------------------------------------------------------------------
 constexpr int TN = 2;                   // 32-wide units per wave along N (64 output columns)
 constexpr int BK = 32;
@@ -166,7 +180,8 @@ constexpr int GM = 2;
 // Four shapes of workgroup, WM x WN waves:
 //   2 x 2: 256 x 128 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
 //   2 x 4: 256 x 256 tile, 8 waves, 4-stage ring of 128 KiB, one per CU
-//          (persistent);
+//          (persistent); its mixed variant also runs 128 x 512 tiles, with
+//          a 4-stage ring of 160 KiB (see "Mixed tiles");
 //   1 x 4: 128 x 256 tile, 4 waves, 3-stage ring of 72 KiB, two per CU;
 //   1 x 8: 128 x 512 tile, 8 waves, 4-stage ring of 160 KiB (all of the
 //          LDS), one per CU (persistent);
@@ -184,13 +199,18 @@ constexpr int GM = 2;
 // the 128 x 128 shape with an 8-stage ring for problems with at most one
 // tile per CU, where a stage's matrix work (256 clocks per wave) is far
 // shorter than a load's latency and only a deep ring keeps it fed.
-template <int WM, int WN, int TMV = 4, int NSV = 0> struct Shape {
+// MXV != 0: the 2 x 4 shape that also runs "wide" tiles, 128 x 512: both
+// wave rows on the same 128 activation rows, each on its own 256 weight rows
+// (see "Mixed tiles"); its stage slots hold 128 + 512 rows (40 KiB).
+template <int WM, int WN, int TMV = 4, int NSV = 0, int MXV = 0> struct Shape {
   static constexpr int TM = TMV;                         // 32-row units per wave along M
   static constexpr int NW = WM * WN;                     // waves
   static constexpr int BMT = 32 * TM * WM;               // rows of A per tile
   static constexpr int BNT = 32 * TN * WN;               // weight rows per tile
   static constexpr int NSTAGE = NSV ? NSV : (NW == 8 ? 4 : 3);
-  static constexpr int STAGE_BYTES = (BMT + BNT) * BK * 2;
+  static constexpr bool MIX = MXV != 0;
+  static_assert(!MIX || (WM == 2 && WN == 4 && TMV == 4 && NSV == 0), "mixed tiles: the 2 x 4 shape");
+  static constexpr int STAGE_BYTES = MIX ? (kTileM + 2 * BNT) * BK * 2 : (BMT + BNT) * BK * 2;
   static constexpr int LDS = NSTAGE * STAGE_BYTES;
   static constexpr int PER_CU = NSV ? 1 : NW == 8 ? 1 : (TM == 2 ? 3 : 2);
   // one workgroup per CU walks a range of tiles (see "Persistent tiles")
@@ -265,9 +285,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int EPI, int WM, int WN, int TMV, int NSV>
-__global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU)) k_gemm_bf16(GemmParams P) {
-  using S = Shape<WM, WN, TMV, NSV>;
+template <int EPI, int WM, int WN, int TMV, int NSV, int MXV>
+__global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV, MXV>::PER_CU)) k_gemm_bf16(GemmParams P) {
+  using S = Shape<WM, WN, TMV, NSV, MXV>;
+  constexpr bool MIX = S::MIX;
   constexpr int TM = S::TM;
   constexpr int NW = S::NW, BMT = S::BMT, BNT = S::BNT, NSTAGE = S::NSTAGE;
   constexpr int STAGE_BYTES = S::STAGE_BYTES;
@@ -278,23 +299,38 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   constexpr bool PERSIST = S::PERSIST;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  // ---- tiles of this workgroup (see "Tile order"): number u of its XCD's
-  // range; a persistent workgroup then steps by the workgroups per XCD
-  const int n_mt = P.mcount[0];
+  // ---- tiles of this workgroup (see "Tile order"): unit u of its XCD's
+  // range; a persistent workgroup then steps by the workgroups per XCD.
+  // Mixed tiles: units [0, nf) are 256 x 256 tiles of the full m-tiles,
+  // [nf, nf + nw) wide tiles (n-tiles 2 nt and 2 nt + 1 of a half-filled
+  // m-tile), spread evenly over the XCDs.
+  const int n_mt = MIX ? P.mcount[1] : P.mcount[0];   // m-tiles run as 256 x 256
   const int n_nt = P.n_tiles_n;
   const int R = n_mt * n_nt;
-  const int per = (R + 7) >> 3;
+  const int RW = MIX ? (P.mcount[0] - n_mt) * (n_nt >> 1) : 0;
+  const int per = (R + 7) >> 3, perw = (RW + 7) >> 3;
   const int xcd = blockIdx.x & 7;
+  const int nf = max(0, min(per, R - xcd * per));
+  const int nw = max(0, min(perw, RW - xcd * perw));
   const int ustep = gridDim.x >> 3;
   int u = blockIdx.x >> 3;
-  auto locate = [&](int uu, int &mt_, int &nt_, int &e_, int &row0_, int &row_end_) -> bool {
-    const int t = xcd * per + uu;
-    if (uu >= per || t >= R) return false;
-    const int GM = P.gm;
-    const int grp = t / (GM * n_nt), within = t - grp * (GM * n_nt);
-    const int gm = min(GM, n_mt - grp * GM);
-    mt_ = grp * GM + within % gm;
-    nt_ = within / gm;
+  auto locate = [&](int uu, int &mt_, int &nt_, int &e_, int &row0_, int &row_end_, bool &wide_) -> bool {
+    wide_ = false;
+    if (uu < nf) {
+      const int t = xcd * per + uu;
+      const int GM = P.gm;
+      const int grp = t / (GM * n_nt), within = t - grp * (GM * n_nt);
+      const int gm = min(GM, n_mt - grp * GM);
+      mt_ = grp * GM + within % gm;
+      nt_ = within / gm;
+    } else if (MIX && uu - nf < nw) {
+      const int h = xcd * perw + uu - nf;
+      mt_ = n_mt + h / (n_nt >> 1);
+      nt_ = h % (n_nt >> 1);
+      wide_ = true;
+    } else {
+      return false;
+    }
     e_ = P.mtile[2 * mt_];
     if (e_ < 0) return false;
     row0_ = P.mtile[2 * mt_ + 1];
@@ -302,7 +338,8 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
     return true;
   };
   int mt, nt, e, row0, row_end;
-  if (!locate(u, mt, nt, e, row0, row_end)) return;
+  bool wide;
+  if (!locate(u, mt, nt, e, row0, row_end, wide)) return;
   const int K = P.K;
   const bf16_t *A = reinterpret_cast<const bf16_t *>(P.A);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -324,22 +361,58 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   // (measured 1-2% faster).
   constexpr bool LB = PERSIST && TM == 4;
   constexpr int LW = LB ? NW / 2 : NW;
-  constexpr int LAQ = LB ? 2 * AQ : AQ, LBQ = LB ? 2 * BQ : BQ, LNQ = LAQ + LBQ;
+  constexpr int LAQ = LB ? 2 * AQ : AQ, LBQ = LB ? 2 * BQ : BQ;
+  // mixed tiles: ten 1 KiB pieces per loading wave and stage, piece
+  // p = wave + 4 i of the 40 KiB slot (see "Mixed tiles")
+  constexpr int LNQ = MIX ? 10 : LAQ + LBQ;
   const bool loader = !LB || wave < LW;
   uint32_t soff[LNQ];
+  bool ld_wide = false;   // the tile whose stages are being loaded is wide
+  __amdgpu_buffer_rsrc_t z_rsrc;   // no records: every access out of range, nothing read
+  if (MIX) z_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(P.Wt), 0, 0, kBufferFlags);
   // A row stride and per-stage step: row-major, or 32-k panels (a stage of
   // the tile is then one contiguous block of whole lines)
   const int a_rs = P.a_panel_rows ? BK : K;
   const size_t a_ks = P.a_panel_rows ? (size_t)P.a_panel_rows * BK : BK;
   const int b_rs = P.b_panel_rows ? BK : K;
   const int b_ks = P.b_panel_rows ? P.b_panel_rows * BK : BK;
-  auto set_src = [&](int e_, int row0_, int row_end_, int nt_) {
+  // weight row of row r (< BNT) of n-tile nt_'s B tile
+  auto wrow_of = [&](int nt_, int r) -> int {
+    if (EPI == EPI_SWIGLU) {
+      // each wave column's 64 B rows: 32 gate rows, then the 32 up rows of
+      // the same hidden columns
+      const int wc = r >> 6, in_wc = r & 63;
+      const int hidden = nt_ * (BNT / 2) + wc * 32 + (in_wc & 31);
+      return (in_wc < 32 ? 0 : P.glu_offset) + hidden;
+    }
+    return nt_ * BNT + r;
+  };
+  auto set_src = [&](int e_, int row0_, int row_end_, int nt_, bool wide_) {
     a_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(A + (size_t)row0_ * a_rs), 0, -1,
                                                kBufferFlags);
     b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16_t *>(reinterpret_cast<const bf16_t *>(P.Wt) + (size_t)e_ * P.w_stride), 0, -1,
         kBufferFlags);
     const int last = row_end_ - 1 - row0_;                   // last valid row of the A tile
+    if constexpr (MIX) {
+      // pieces 0-7: A rows 0-127; 8-15: A rows 128-255 (256 x 256) or B
+      // rows 0-127 (wide); 16-31: B rows 0-255 (256 x 256) or 128-383
+      // (wide); 32-39: B rows 384-511 (wide; nothing otherwise)
+      ld_wide = wide_;
+#pragma unroll
+      for (int i = 0; i < LNQ; ++i) {
+        const int pc = wave % LW + LW * i;
+        if (i < 2 || (i < 4 && !wide_)) {
+          const int r = pc * 16 + lrow;
+          soff[i] = ((uint32_t)min(r, last) * a_rs + ((lchunk ^ swz(r)) << 3)) * 2;
+        } else {
+          const int r = (pc - (wide_ ? 8 : 16)) * 16 + lrow;   // row of the 512 (or 256) B rows
+          const int wrow = wrow_of(wide_ ? 2 * nt_ + (r >> 8) : nt_, r & (BNT - 1));
+          soff[i] = ((uint32_t)wrow * b_rs + ((lchunk ^ swz(r)) << 3)) * 2;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < LAQ; ++i) {
       const int r = (wave % LW + LW * i) * 16 + lrow;        // row inside the A tile
@@ -348,23 +421,30 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
 #pragma unroll
     for (int i = 0; i < LBQ; ++i) {
       const int r = (wave % LW + LW * i) * 16 + lrow;        // row inside the B tile
-      int wrow;
-      if (EPI == EPI_SWIGLU) {
-        // each wave column's 64 B rows: 32 gate rows, then the 32 up rows of
-        // the same hidden columns
-        const int wc = r >> 6, in_wc = r & 63;
-        const int hidden = nt_ * (BNT / 2) + wc * 32 + (in_wc & 31);
-        wrow = (in_wc < 32 ? 0 : P.glu_offset) + hidden;
-      } else {
-        wrow = nt_ * BNT + r;
-      }
-      soff[LAQ + i] = ((uint32_t)wrow * b_rs + ((lchunk ^ swz(r)) << 3)) * 2;   // bytes
+      soff[LAQ + i] = ((uint32_t)wrow_of(nt_, r) * b_rs + ((lchunk ^ swz(r)) << 3)) * 2;   // bytes
     }
   };
-  set_src(e, row0, row_end, nt);
+  set_src(e, row0, row_end, nt, wide);
   auto issue_l = [&](int stage, int slot) {
     char *base = smem + slot * STAGE_BYTES;
     const int a_so = (int)(stage * a_ks * 2), b_so = stage * b_ks * 2;   // bytes
+    if constexpr (MIX) {
+      const __amdgpu_buffer_rsrc_t r23 = ld_wide ? b_rsrc : a_rsrc, r89 = ld_wide ? b_rsrc : z_rsrc;
+      const int so23 = ld_wide ? b_so : a_so;
+#pragma unroll
+      for (int i = 0; i < LNQ; ++i) {
+        char *dst = base + (wave % LW + LW * i) * 1024;
+        if (i < 2)
+          lds_dma16_buf(a_rsrc, soff[i], a_so, dst);
+        else if (i < 4)
+          lds_dma16_buf(r23, soff[i], so23, dst);
+        else if (i < 8)
+          lds_dma16_buf(b_rsrc, soff[i], b_so, dst);
+        else
+          lds_dma16_buf(r89, soff[i], b_so, dst);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < LAQ; ++i) lds_dma16_buf(a_rsrc, soff[i], a_so, base + (wave % LW + LW * i) * 1024);
 #pragma unroll
@@ -396,8 +476,16 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
   // lanes l and l + 16 sit at 16-byte slots whose XOR has even parity
   const int kq = (lane >> 5) ^ (((lane >> 4) & 1) * 3);
   const int coff = (kq ^ swz(frow)) << 4;                    // swz of every row of the block
-  const int a_frag = (wm * NXB * 16 + frow) * 64 + coff;    // byte offset inside the A part
-  const int b_frag = A_BYTES + (wn * NWB * 16 + frow) * 64 + coff;   // inside the B part
+  // byte offsets in a stage slot: this wave's activation rows, then its
+  // weight rows (a wide tile: A rows 0-127 for both wave rows, and wave row
+  // wm's 256 weight rows from 8 KiB + 256 wm rows on)
+  int a_frag, b_frag;
+  auto set_frags = [&](bool wide_) {
+    const bool wd = MIX && wide_;
+    a_frag = ((wd ? 0 : wm * NXB * 16) + frow) * 64 + coff;
+    b_frag = (wd ? kTileM * BK * 2 : A_BYTES) + ((wd ? wm * BNT : 0) + wn * NWB * 16 + frow) * 64 + coff;
+  };
+  set_frags(wide);
 
   f32x4 acc[NWB][NXB];
 
@@ -526,7 +614,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
     // A wave whose 128 rows all lie past the expert's last row (the second
     // wave row of a partial tile with at most 128 rows) skips its fragment
     // reads and MFMAs and only keeps the barriers and its share of the loads.
-    const bool active = wm * 32 * TM < row_end - row0;
+    const bool active = (MIX && wide) || wm * 32 * TM < row_end - row0;
     auto main_loop = [&](auto act_tag, auto ldr_tag) {
       constexpr bool ACT = decltype(act_tag)::value;
       constexpr bool LDR = decltype(ldr_tag)::value;
@@ -635,10 +723,11 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
     // next tile (persistent): its stages 0 .. NSTAGE-3 go into the ring now,
     // under this tile's epilogue, which stages through the other two slots
     int mt2 = 0, nt2 = 0, e2 = 0, r02 = 0, re2 = 0;
-    const bool more = PERSIST && locate(u + ustep, mt2, nt2, e2, r02, re2);
+    bool wide2 = false;
+    const bool more = PERSIST && locate(u + ustep, mt2, nt2, e2, r02, re2, wide2);
     const int gb2 = (int)((unsigned)(gb + nk) % NSTAGE);
     if (PERSIST && more) {
-      set_src(e2, r02, re2, nt2);
+      set_src(e2, r02, re2, nt2, wide2);
 #pragma unroll
       for (int st = 0; st < NSTAGE - 2; ++st)
         if (st < nk) issue(st, (gb2 + st) % NSTAGE);
@@ -666,14 +755,17 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
       return r * SLOTS + (c ^ (SLOTS == 16 ? (r & 15) : ((r >> 1) & 7)));
     };
     const int rr = lane_e / LPR, cc = (lane_e % LPR) * 2;   // read-back row in pass, first slot
-    const int col_base = nt * out_cols + wn * NC;
+    // this wave's first row in the tile and its n-tile (a wide tile: rows
+    // 0-127 for both wave rows, n-tile 2 nt + wm)
+    const int wrow0 = (MIX && wide) ? 0 : wm * TM * 32;
+    const int col_base = ((MIX && wide) ? 2 * nt + wm : nt) * out_cols + wn * NC;
     // RoPE: window positions of this lane's rows and the (cos, sin) values
     // of its first 32-row block
     const bool rope = ROPE && col_base < P.rope_cols;
     if (ROPE && rope && !M32) {
 #pragma unroll
       for (int xb = 0; xb < NXB; ++xb)
-        rpos[xb] = P.row_pos[min(row0 + wm * NXB * 16 + xb * 16 + (lane_e & 15), row_end - 1)];
+        rpos[xb] = P.row_pos[min(row0 + wrow0 + xb * 16 + (lane_e & 15), row_end - 1)];
       rope_table(rpos[0], tq[0]);
       rope_table(rpos[1], tq[1]);
     }
@@ -809,7 +901,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
         const int r = rr + pass * RPP;
         v0[pass] = *reinterpret_cast<const float4 *>(stage_f + sslot(r, cc) * 4);
         v1[pass] = *reinterpret_cast<const float4 *>(stage_f + sslot(r, cc + 1) * 4);
-        const int rw = row0 + wm * TM * 32 + im * 32 + r;
+        const int rw = row0 + wrow0 + im * 32 + r;
         ok[pass] = rw < row_end;
         row[pass] = ok[pass] ? rw : row_end - 1;   // rows past the expert: read a valid row, store nothing
       }
@@ -890,6 +982,10 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV>::PER_CU
     stage_barrier<63, 0>();
     u += ustep;
     mt = mt2; nt = nt2; e = e2; row0 = r02; row_end = re2; gb = gb2;
+    if (MIX) {
+      wide = wide2;
+      set_frags(wide);
+    }
     if (NSTAGE - 2 < nk) issue(NSTAGE - 2, slot(NSTAGE - 2));
   }  // tiles
 }
@@ -1263,14 +1359,14 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmParams P) {
 }
 
 
-template <int EPI, int WM, int WN, int TMV = 4, int NSV = 0>
+template <int EPI, int WM, int WN, int TMV = 4, int NSV = 0, int MXV = 0>
 hipError_t launch_shape(GemmParams P, const Workspace &ws, int n_w, hipStream_t st) {
-  using S = Shape<WM, WN, TMV, NSV>;
+  using S = Shape<WM, WN, TMV, NSV, MXV>;
   const bool tall = S::BMT == kTileM2;
   P.mtile = tall ? ws.mtile2 : ws.mtile;
   P.mcount = tall ? ws.mcount + 1 : ws.mcount;
   P.n_tiles_n = n_w / S::BNT;
-  const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, WM, WN, TMV, NSV>,
+  const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_bf16<EPI, WM, WN, TMV, NSV, MXV>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
   if (e != hipSuccess) return e;
   int grid = (((tall ? ws.max_mtiles2 : ws.max_mtiles) * P.n_tiles_n + 7) / 8) * 8;
@@ -1281,7 +1377,7 @@ hipError_t launch_shape(GemmParams P, const Workspace &ws, int n_w, hipStream_t 
     if (ec != hipSuccess) return ec;
     grid = min(grid, max(8, ncu / 8 * 8));
   }
-  lol_launch((k_gemm_bf16<EPI, WM, WN, TMV, NSV>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
+  lol_launch((k_gemm_bf16<EPI, WM, WN, TMV, NSV, MXV>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
   return hipGetLastError();
 }
 
@@ -1346,6 +1442,19 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
       // beat the persistent 256 x 256 tile (small_bf16, K = 512: gate/up
       // 49.2 -> 45.4 us, QKV 27.8 -> 26.6 us, same box)
       if (a.K <= 16 * BK && rows256 && tiles256 >= ncu) return launch_shape<EPI, 2, 2>(P, ws, n_w, st);
+      // mixed tiles (gate/up): expert rows in multiples of 128 but not of
+      // 256 (the depths shifted by half a window) and the weights in panels
+      // (a wide tile reads 512 weight rows per stage): 256 x 256 tiles for
+      // the full m-tiles and 128 x 512 for the half-filled ones, which then
+      // add no partial round of tiles (mid_bf16, same box: gate/up at the
+      // shifted depths 241-252 -> 228-235 us, forward 3.335 -> 3.352 M
+      // tokens/s; QKV measured slower so than with 128 x 512 tiles at those
+      // depths: 117 against 98-108 us)
+      if constexpr (EPI == EPI_SWIGLU) {
+        if (rows128 && a.len_gcd % kTileM2 != 0 && a.b_panel_rows && (n_w / 256) % 2 == 0 &&
+            tiles256 >= ncu)
+          return launch_shape<EPI, 2, 4, 4, 0, 1>(P, ws, n_w, st);
+      }
       if (rows256 && tiles256 >= ncu) return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
       // expert rows that leave partial tiles in either table (windows whose
       // lengths are not multiples of 128, packed documents): the persistent

@@ -184,7 +184,7 @@ size_t workspace_layout(const Plan &p, char *base, Workspace *ws) {
   w.toff = (int32_t *)carve((size_t)(c.L + 1) * 4);
   w.mtile = (int32_t *)carve((size_t)max_mtiles * 8);
   w.mtile2 = (int32_t *)carve((size_t)max_mtiles2 * 8);
-  w.mcount = (int32_t *)carve(2 * 4);
+  w.mcount = (int32_t *)carve(3 * 4);
   w.row_tok = (int32_t *)carve(T * 4);
   w.row_pos = (int32_t *)carve(T * 4);
   w.row_exp = (int32_t *)carve(T * 4);

@@ -56,7 +56,7 @@ struct Workspace {
   int32_t *toff;       // [L+1]              grouped-row offset of each expert
   int32_t *mtile;      // [max_mtiles][2]    (expert, first row) per kTileM-row tile, -1 = idle
   int32_t *mtile2;     // [max_mtiles2][2]   the same for kTileM2-row tiles
-  int32_t *mcount;     // [2]                tiles in use in mtile, mtile2
+  int32_t *mcount;     // [3]                tiles in use in mtile, mtile2; full tiles in mtile2
   int32_t *row_tok;    // [T]                token (b*n + i) of each grouped row
   int32_t *row_pos;    // [T]                window-local position
   int32_t *row_exp;    // [T]

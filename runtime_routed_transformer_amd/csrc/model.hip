@@ -90,6 +90,7 @@ __global__ void k_dense_tiles(int32_t *__restrict__ mtile, int max1, int32_t *__
   if (i == 0) {
     mcount[0] = (T + kTileM - 1) / kTileM;
     mcount[1] = (T + kTileM2 - 1) / kTileM2;
+    mcount[2] = T / kTileM2;   // full 256-row tiles
     toff[0] = 0;
     toff[1] = T;
   }
@@ -111,7 +112,7 @@ size_t head_layout(int T, int d, int dtype, char *base, Workspace *ws) {
   w.u = carve((size_t)T * d * ab);
   w.mtile = (int32_t *)carve((size_t)max1 * 8);
   w.mtile2 = (int32_t *)carve((size_t)max2 * 8);
-  w.mcount = (int32_t *)carve(8);
+  w.mcount = (int32_t *)carve(12);
   w.toff = (int32_t *)carve(8);
   w.max_mtiles = max1;
   w.max_mtiles2 = max2;

@@ -330,6 +330,7 @@ __global__ void __launch_bounds__(1024) k_route_all(
     ecount[L] = w;
     mcount[0] = f + q;
     mcount[1] = f2 + q2;
+    mcount[2] = f2;   // full 256-row tiles (the table's first entries)
   }
   __syncthreads();
   for (int e = tid; e <= L; e += blockDim.x) toff_out[e] = toff[e];
