@@ -37,6 +37,9 @@ SCALED = [
     CONFIG_BY_NAME["tiny_fp32"],
     CONFIG_BY_NAME["small_bf16"].scaled(2, 384),
     CONFIG_BY_NAME["mid_bf16"].scaled(2, 640),
+    # 2,048 tokens: enough 256 x 256 gate/up tiles to fill the CUs, so the
+    # shifted depths (half windows at the document edges) run mixed tiles
+    CONFIG_BY_NAME["mid_bf16"].scaled(2, 1024),
     CONFIG_BY_NAME["sparse_bf16"].scaled(2, 640),
     CONFIG_BY_NAME["forced_bf16"].scaled(3, 224),
 ]
