@@ -63,6 +63,8 @@ struct GemmParams {
   int b_panel_rows;        // 0: an expert's weights are [N_w][K]; else 32-k panels [K/32][N_w][32]
   int c_panel_rows;        // bf16 store epilogues: 0 = C is [rows][ldc]; else 32-column panels
   int gm;                  // m-tiles per group of the tile order (see "Tile order")
+  float *part;             // K-split tail (EPI_ACCUM, 256 x 256): fp32 partial tiles [part_slots][256][256]
+  int part_slots;          // 0: tail tiles are not split
 };
 
 // Writes 4 consecutive logical columns [col, col+4) of grouped row `row`.
@@ -285,6 +287,50 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// ---- K-split tail (persistent 256 x 256 tiles, the down projection's
+// EPI_ACCUM).  A persistent launch runs each XCD's tiles in rounds of one
+// tile per workgroup.  Ragged expert row counts (packed documents, windows
+// whose lengths are not multiples of 256) add a few partial m-tiles and so
+// a short last round that costs nearly a whole tile's time on a handful of
+// CUs.  When that round holds at most half the XCD's workgroups, its tiles
+// are cut along K into `split` pieces that run side by side: each piece
+// stores its fp32 partial tile into a slot of P.part, and k_split_accum then
+// sums a tile's pieces in piece order (a fixed order: the result does not
+// depend on timing) and applies the epilogue.
+constexpr int kSplitMax = 8, kSplitMin = 2;
+struct TailSplit {
+  int per, nf;      // tiles per XCD range; tiles of this XCD
+  int full, tail;   // tiles run whole; tail tiles (the short last round)
+  int split, spx;   // pieces per tail tile (1: none); partial slots per XCD
+};
+__host__ __device__ inline TailSplit tail_split(int R, int xcd, int ustep, int nk, int part_slots) {
+  TailSplit t;
+  t.per = (R + 7) >> 3;
+  const int rest = R - xcd * t.per;
+  t.nf = rest < 0 ? 0 : (rest < t.per ? rest : t.per);
+  t.tail = t.nf % ustep;
+  t.full = t.nf - t.tail;
+  t.spx = part_slots >> 3;
+  t.split = 1;
+  if (t.tail > 0) {
+    int sp = ustep / t.tail;
+    if (t.spx / t.tail < sp) sp = t.spx / t.tail;
+    if (kSplitMax < sp) sp = kSplitMax;
+    // whole groups of 4 stages per piece
+    while (sp > 1 && (nk % sp != 0 || (nk / sp) % 4 != 0)) --sp;
+    t.split = sp < kSplitMin ? 1 : sp;
+  }
+  if (t.split == 1) t.full = t.nf;
+  return t;
+}
+// m-tile and n-tile of tile t of the tile order (see "Tile order")
+__device__ __forceinline__ void tile_mn(int t, int n_mt, int n_nt, int GM_, int &mt, int &nt) {
+  const int grp = t / (GM_ * n_nt), within = t - grp * (GM_ * n_nt);
+  const int gm = min(GM_, n_mt - grp * GM_);
+  mt = grp * GM_ + within % gm;
+  nt = within / gm;
+}
+
 template <int EPI, int WM, int WN, int TMV, int NSV, int MXV>
 __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV, MXV>::PER_CU)) k_gemm_bf16(GemmParams P) {
   using S = Shape<WM, WN, TMV, NSV, MXV>;
@@ -314,15 +360,26 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV, MXV>::P
   const int nw = max(0, min(perw, RW - xcd * perw));
   const int ustep = gridDim.x >> 3;
   int u = blockIdx.x >> 3;
-  auto locate = [&](int uu, int &mt_, int &nt_, int &e_, int &row0_, int &row_end_, bool &wide_) -> bool {
+  // K-split tail: units [ts.full, ts.full + ts.tail * ts.split) are pieces,
+  // piece q = kc * tail + j of tail tile j, in partial slot xcd * spx + q
+  constexpr bool SPLIT = EPI == EPI_ACCUM && PERSIST && !MIX && BMT == kTileM2 && BNT == 256;
+  const int nk_all = P.K / BK;
+  TailSplit ts{};
+  ts.full = nf;
+  ts.split = 1;
+  if constexpr (SPLIT) ts = tail_split(R, xcd, ustep, nk_all, P.part_slots);
+  auto locate = [&](int uu, int &mt_, int &nt_, int &e_, int &row0_, int &row_end_, bool &wide_, int &kc_,
+                    int &slot_) -> bool {
     wide_ = false;
-    if (uu < nf) {
-      const int t = xcd * per + uu;
-      const int GM = P.gm;
-      const int grp = t / (GM * n_nt), within = t - grp * (GM * n_nt);
-      const int gm = min(GM, n_mt - grp * GM);
-      mt_ = grp * GM + within % gm;
-      nt_ = within / gm;
+    kc_ = -1;
+    slot_ = 0;
+    if (uu < ts.full) {
+      tile_mn(xcd * per + uu, n_mt, n_nt, P.gm, mt_, nt_);
+    } else if (SPLIT && ts.split > 1 && uu - ts.full < ts.tail * ts.split) {
+      const int q = uu - ts.full;
+      tile_mn(xcd * per + ts.full + q % ts.tail, n_mt, n_nt, P.gm, mt_, nt_);
+      kc_ = q / ts.tail;
+      slot_ = xcd * ts.spx + q;
     } else if (MIX && uu - nf < nw) {
       const int h = xcd * perw + uu - nf;
       mt_ = n_mt + h / (n_nt >> 1);
@@ -331,15 +388,21 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV, MXV>::P
     } else {
       return false;
     }
+    // uniform across the wave (the compiler loses track of it through the
+    // tail arithmetic and would take the tile's buffer resources as divergent)
+    mt_ = __builtin_amdgcn_readfirstlane(mt_);
+    nt_ = __builtin_amdgcn_readfirstlane(nt_);
     e_ = P.mtile[2 * mt_];
     if (e_ < 0) return false;
     row0_ = P.mtile[2 * mt_ + 1];
     row_end_ = P.toff[e_ + 1];
     return true;
   };
-  int mt, nt, e, row0, row_end;
+  int mt, nt, e, row0, row_end, kc, pslot;
   bool wide;
-  if (!locate(u, mt, nt, e, row0, row_end, wide)) return;
+  if (!locate(u, mt, nt, e, row0, row_end, wide, kc, pslot)) return;
+  // stages of the tile (a piece: its share of K, from stage kc * nk)
+  auto tile_nk = [&](int kc_) { return kc_ >= 0 ? nk_all / ts.split : nk_all; };
   const int K = P.K;
   const bf16_t *A = reinterpret_cast<const bf16_t *>(P.A);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -387,12 +450,13 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV, MXV>::P
     }
     return nt_ * BNT + r;
   };
-  auto set_src = [&](int e_, int row0_, int row_end_, int nt_, bool wide_) {
-    a_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(A + (size_t)row0_ * a_rs), 0, -1,
-                                               kBufferFlags);
+  auto set_src = [&](int e_, int row0_, int row_end_, int nt_, bool wide_, int kc_) {
+    const size_t kst0 = kc_ >= 0 ? (size_t)kc_ * tile_nk(kc_) : 0;   // first stage of a piece
+    a_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(A + (size_t)row0_ * a_rs + kst0 * a_ks), 0,
+                                               -1, kBufferFlags);
     b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(reinterpret_cast<const bf16_t *>(P.Wt) + (size_t)e_ * P.w_stride), 0, -1,
-        kBufferFlags);
+        const_cast<bf16_t *>(reinterpret_cast<const bf16_t *>(P.Wt) + (size_t)e_ * P.w_stride + kst0 * b_ks), 0,
+        -1, kBufferFlags);
     const int last = row_end_ - 1 - row0_;                   // last valid row of the A tile
     if constexpr (MIX) {
       // pieces 0-7: A rows 0-127; 8-15: A rows 128-255 (256 x 256) or B
@@ -424,7 +488,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV, MXV>::P
       soff[LAQ + i] = ((uint32_t)wrow_of(nt_, r) * b_rs + ((lchunk ^ swz(r)) << 3)) * 2;   // bytes
     }
   };
-  set_src(e, row0, row_end, nt, wide);
+  set_src(e, row0, row_end, nt, wide, kc);
   auto issue_l = [&](int stage, int slot) {
     char *base = smem + slot * STAGE_BYTES;
     const int a_so = (int)(stage * a_ks * 2), b_so = stage * b_ks * 2;   // bytes
@@ -555,7 +619,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV, MXV>::P
   // measured no faster.)  The explicit LDS waits sit where the reads have
   // had an MFMA block to arrive, so the compiler needs none of its own in
   // front of the MFMAs.
-  const int nk = K / BK;
+  int nk = tile_nk(kc);
   int gb = 0;   // ring slot of the tile's stage 0 (rotates from tile to tile)
   auto slot = [&](int st) { return (int)((unsigned)(gb + st) % NSTAGE); };
 #pragma unroll
@@ -722,15 +786,16 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV, MXV>::P
 
     // next tile (persistent): its stages 0 .. NSTAGE-3 go into the ring now,
     // under this tile's epilogue, which stages through the other two slots
-    int mt2 = 0, nt2 = 0, e2 = 0, r02 = 0, re2 = 0;
+    int mt2 = 0, nt2 = 0, e2 = 0, r02 = 0, re2 = 0, kc2 = -1, pslot2 = 0;
     bool wide2 = false;
-    const bool more = PERSIST && locate(u + ustep, mt2, nt2, e2, r02, re2, wide2);
+    const bool more = PERSIST && locate(u + ustep, mt2, nt2, e2, r02, re2, wide2, kc2, pslot2);
     const int gb2 = (int)((unsigned)(gb + nk) % NSTAGE);
+    const int nk2 = tile_nk(kc2);
     if (PERSIST && more) {
-      set_src(e2, r02, re2, nt2, wide2);
+      set_src(e2, r02, re2, nt2, wide2, kc2);
 #pragma unroll
       for (int st = 0; st < NSTAGE - 2; ++st)
-        if (st < nk) issue(st, (gb2 + st) % NSTAGE);
+        if (st < nk2) issue(st, (gb2 + st) % NSTAGE);
     }
 
     // ---- epilogue.  acc[jn][xb] holds C[m = xb*16 + lane%16][n = jn*16 +
@@ -905,7 +970,18 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV, MXV>::P
         ok[pass] = rw < row_end;
         row[pass] = ok[pass] ? rw : row_end - 1;   // rows past the expert: read a valid row, store nothing
       }
-      if (EPI == EPI_RESID || EPI == EPI_BLEND || EPI == EPI_ACCUM) {
+      if (SPLIT && kc >= 0) {
+        // a piece of a K-split tail tile: its fp32 partial, row-major 256 x 256
+        float *pp = P.part + (size_t)pslot * (kTileM2 * 256);
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+          if (!ok[pass]) continue;
+          float4 *q = reinterpret_cast<float4 *>(pp + (size_t)(wrow0 + im * 32 + rr + pass * RPP) * 256 +
+                                                 (col - nt * BNT));
+          q[0] = v0[pass];
+          q[1] = v1[pass];
+        }
+      } else if (EPI == EPI_RESID || EPI == EPI_BLEND || EPI == EPI_ACCUM) {
         // every load of the block first (token ids, then the residual rows),
         // then the arithmetic and the stores: the loads overlap each other
         const float *__restrict__ sres = P.s_in;
@@ -982,6 +1058,7 @@ __global__ void __launch_bounds__(64 * WM * WN, (Shape<WM, WN, TMV, NSV, MXV>::P
     stage_barrier<63, 0>();
     u += ustep;
     mt = mt2; nt = nt2; e = e2; row0 = r02; row_end = re2; gb = gb2;
+    kc = kc2; pslot = pslot2; nk = nk2;
     if (MIX) {
       wide = wide2;
       set_frags(wide);
@@ -1359,8 +1436,56 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmParams P) {
 }
 
 
+// Finishes the K-split tail tiles of a persistent EPI_ACCUM launch of
+// gemm_grid workgroups: each tail tile's pieces summed in piece order, then
+// s[t] = s_in[t] + g y for its rows, the epilogue the whole tile would have
+// applied.  Block (8 j + xcd, rg): tail tile j of XCD xcd, rows 16 rg ..
+// 16 rg + 15 of the tile (small blocks: the sums spread over many CUs;
+// 64-row blocks measured 4% slower on packed documents); blocks past the tail (or past the expert's rows)
+// do nothing (the host cannot tell how many there are: the tile counts are
+// the router's).
+__global__ void __launch_bounds__(256) k_split_accum(GemmParams P, int gemm_grid) {
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int n_mt = P.mcount[0], n_nt = P.n_tiles_n;
+  const TailSplit ts = tail_split(n_mt * n_nt, xcd, gemm_grid >> 3, P.K / BK, P.part_slots);
+  if (ts.split < 2 || j >= ts.tail) return;
+  int mt, nt;
+  tile_mn(xcd * ts.per + ts.full + j, n_mt, n_nt, P.gm, mt, nt);
+  const int e = P.mtile[2 * mt];
+  if (e < 0) return;
+  const int r0 = P.mtile[2 * mt + 1] + blockIdx.y * 16, row_end = P.toff[e + 1];
+  if (r0 >= row_end) return;
+  constexpr size_t SLOT = (size_t)kTileM2 * 256;
+  // piece kc of tail tile j sits in slot xcd * spx + kc * tail + j
+  const float *part = P.part + (size_t)(xcd * ts.spx + j) * SLOT + (size_t)blockIdx.y * 16 * 256;
+  const size_t pstep = (size_t)ts.tail * SLOT;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = threadIdx.x + 256 * i;   // 16 rows x 64 float4
+    const int r = idx >> 6, c = (idx & 63) * 4;
+    const int row = r0 + r;
+    if (row >= row_end) continue;
+    float4 y = *reinterpret_cast<const float4 *>(part + (size_t)r * 256 + c);
+    for (int kc = 1; kc < ts.split; ++kc) {
+      const float4 q = *reinterpret_cast<const float4 *>(part + kc * pstep + (size_t)r * 256 + c);
+      y.x += q.x;
+      y.y += q.y;
+      y.z += q.z;
+      y.w += q.w;
+    }
+    const size_t tok = (size_t)P.row_tok[row];
+    const float g = P.row_gate[row];
+    const int col = nt * 256 + c;
+    const float4 x = *reinterpret_cast<const float4 *>(P.s_in + tok * P.ldc + col);
+    *reinterpret_cast<float4 *>(P.s + tok * P.ldc + col) =
+        make_float4(x.x + g * y.x, x.y + g * y.y, x.z + g * y.z, x.w + g * y.w);
+  }
+}
+
+// exact_mt: the number of 256-row m-tiles when the host knows it (every
+// expert's row count a multiple of 256), else -1
 template <int EPI, int WM, int WN, int TMV = 4, int NSV = 0, int MXV = 0>
-hipError_t launch_shape(GemmParams P, const Workspace &ws, int n_w, hipStream_t st) {
+hipError_t launch_shape(GemmParams P, const Workspace &ws, int n_w, hipStream_t st, int exact_mt = -1) {
   using S = Shape<WM, WN, TMV, NSV, MXV>;
   const bool tall = S::BMT == kTileM2;
   P.mtile = tall ? ws.mtile2 : ws.mtile;
@@ -1377,7 +1502,26 @@ hipError_t launch_shape(GemmParams P, const Workspace &ws, int n_w, hipStream_t 
     if (ec != hipSuccess) return ec;
     grid = min(grid, max(8, ncu / 8 * 8));
   }
+  // K-split tail: on when the partial slots allow two pieces per XCD and
+  // the tiles may leave a short last round (always possible when the host
+  // does not know the tile count; when it does, only if some XCD splits)
+  bool split = false;
+  if constexpr (EPI == EPI_ACCUM && S::PERSIST && !S::MIX && S::BMT == kTileM2 && S::BNT == 256) {
+    split = P.part && P.part_slots >= 16;
+    if (split && exact_mt >= 0) {
+      split = false;
+      for (int x = 0; x < 8; ++x)
+        if (tail_split(exact_mt * P.n_tiles_n, x, grid >> 3, P.K / BK, P.part_slots).split > 1) split = true;
+    }
+  }
+  if (!split) P.part_slots = 0;
   lol_launch((k_gemm_bf16<EPI, WM, WN, TMV, NSV, MXV>), dim3(grid), dim3(64 * S::NW), S::LDS, st, P);
+  if (split) {
+    const hipError_t e1 = hipGetLastError();
+    if (e1 != hipSuccess) return e1;
+    const int max_tail = (grid >> 3) / kSplitMin;   // a longer tail is not split
+    lol_launch(k_split_accum, dim3(8 * (max_tail > 0 ? max_tail : 1), kTileM2 / 16), dim3(256), 0, st, P, grid);
+  }
   return hipGetLastError();
 }
 
@@ -1409,6 +1553,8 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
   P.c_panel_rows = a.c_panel_rows;
   P.b_panel_rows = a.b_panel_rows;
   P.gm = GM;
+  P.part = a.part;
+  P.part_slots = EPI == EPI_ACCUM && a.part ? a.part_slots : 0;
   if ((a.a_panel_rows || a.b_panel_rows || a.c_panel_rows) && p.cfg.dtype != LOL_BF16)
     return hipErrorInvalidValue;
   if (a.c_panel_rows && (EPI == EPI_RESID || EPI == EPI_BLEND || EPI == EPI_ACCUM)) return hipErrorInvalidValue;
@@ -1455,7 +1601,8 @@ hipError_t launch_typed(const Plan &p, const Workspace &ws, const GemmArgs &a, h
             tiles256 >= ncu)
           return launch_shape<EPI, 2, 4, 4, 0, 1>(P, ws, n_w, st);
       }
-      if (rows256 && tiles256 >= ncu) return launch_shape<EPI, 2, 4>(P, ws, n_w, st);
+      if (rows256 && tiles256 >= ncu)
+        return launch_shape<EPI, 2, 4>(P, ws, n_w, st, a.len_gcd % kTileM2 == 0 ? p.T / kTileM2 : -1);
       // expert rows that leave partial tiles in either table (windows whose
       // lengths are not multiples of 128, packed documents): the persistent
       // 256 x 256 shape, whose waves skip the MFMAs of rows past the expert

@@ -414,6 +414,9 @@ lol_status forward_impl(const lol_core_config *cfg, int64_t n_tokens, const int3
     if (fused_o) {
       a.epi = EPI_ACCUM;
       a.s_in = s_out;
+      // h is not used on this path: it holds the K-split tail's partial tiles
+      a.part = ws.h;
+      a.part_slots = (int)((long long)p.T * c.d / (kTileM2 * 256));
     } else {
       a.epi = EPI_BLEND;
       a.s_in = s;

@@ -161,6 +161,8 @@ struct GemmArgs {
   int b_panel_rows;     // 0: each expert's weights are [N_w][K]; else 32-k panels
                         // [K/32][b_panel_rows][32] per expert, b_panel_rows = N_w (bf16 only)
   int c_panel_rows;     // SwiGLU / GELU / STORE (bf16): 0 = C is [T][N]; else 32-column panels
+  float *part;          // ACCUM (bf16): room for the K-split tail's fp32 partial tiles, part_slots
+  int part_slots;       // of 256 x 256 floats each (none: nullptr, 0)
 };
 hipError_t launch_gemm(const Plan &p, const Workspace &ws, const GemmArgs &a, hipStream_t st);
 

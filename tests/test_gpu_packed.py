@@ -77,6 +77,18 @@ def test_packed_mid_full_size_sampled():
     _report(parity.run_docs(packed, docs=docs, prefix=3 * cfg.core.W + cfg.core.W // 2))
 
 
+def test_packed_mid_full_size_every_document():
+    """The same 16,384-token stream compared on every token of every
+    document.  Its ragged expert row counts leave the down projection's
+    persistent 256 x 256 tiles a short last round, which runs cut along K
+    into pieces summed by a second kernel; the rows of those tiles are
+    compared here like every other."""
+    cfg = PACKED_BY_NAME["mid_bf16_packed"]
+    packed = _prepare(cfg)
+    print(f"[packed-full-all] {cfg.name} docs={packed.core.cfg.batch}", flush=True)
+    _report(parity.run_docs(packed))
+
+
 def test_rows_as_documents_equal_the_row_layout_and_bad_tables_raise_a_flag():
     """A table naming the rows of the [batch][n] layout reproduces
     lol_core_forward bit for bit; a table with overlapping documents or a
