@@ -89,6 +89,27 @@ def test_packed_mid_full_size_every_document():
     _report(parity.run_docs(packed))
 
 
+def test_packed_mid_full_size_repeats_bit_for_bit():
+    """Two forwards of the 16,384-token packed stream give the same bits:
+    the K-split tail's pieces are summed in a fixed order, whatever order
+    the workgroups that made them finished in."""
+    import torch
+    from runtime_routed_transformer_amd.core import DeviceCore
+    packed = _prepare(PACKED_BY_NAME["mid_bf16_packed"])
+    core = DeviceCore(packed.core)
+    s_in = torch.from_numpy(packed.stream()).to(core.device)
+    d_start = torch.from_numpy(packed.start).to(core.device)
+    d_len = torch.from_numpy(packed.length).to(core.device)
+    outs = []
+    for _ in range(3):
+        s_out = torch.empty_like(s_in)
+        core.forward_docs(s_in, s_out, d_start, d_len)
+        outs.append(s_out)
+    torch.cuda.synchronize(core.device)
+    assert core.flags() == 0
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2]), "packed forwards differ"
+
+
 def test_rows_as_documents_equal_the_row_layout_and_bad_tables_raise_a_flag():
     """A table naming the rows of the [batch][n] layout reproduces
     lol_core_forward bit for bit; a table with overlapping documents or a
