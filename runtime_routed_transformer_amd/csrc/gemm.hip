@@ -1128,6 +1128,7 @@ struct ONormParams {
   bf16_t *u;
   int u_panel_rows;        // 0: u is [T][d]; else u is in 32-k panels [d/32][u_panel_rows][32]
   float eps;
+  int cpx;                 // CUs per XCD (0: no tail sub-units)
 };
 
 constexpr int kONormRows = 64;
@@ -1165,12 +1166,28 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
   const int n_t = 2 * P.mcount[0];
   const int per = (n_t + 7) >> 3;
   const int u_ = blockIdx.x >> 3;
-  const int t = (blockIdx.x & 7) * per + u_;
-  if (u_ >= per || t >= n_t) return;
+  // Tail sub-units: ragged expert rows (packed documents) add a few units,
+  // which would run as a second round of whole units on a few CUs of each
+  // XCD.  When the overrun is at most half the XCD's CUs (and the grid has
+  // the room), each overrun unit runs instead as two 32-row sub-units,
+  // whose workgroups skip the MFMAs of the missing half.
+  const int tail = per - P.cpx;
+  const bool subs = P.cpx > 0 && tail > 0 && P.cpx + 2 * tail <= (int)(gridDim.x >> 3);
+  int t, sub = -1;
+  if (!subs || u_ < P.cpx) {
+    t = (blockIdx.x & 7) * per + u_;
+    if (u_ >= per || t >= n_t) return;
+  } else {
+    const int q = u_ - P.cpx;
+    if (q >= 2 * tail) return;
+    t = (blockIdx.x & 7) * per + P.cpx + (q >> 1);
+    if (t >= n_t) return;
+    sub = q & 1;
+  }
   const int e = P.mtile[2 * (t >> 1)];
   if (e < 0) return;
-  const int row0 = P.mtile[2 * (t >> 1) + 1] + (t & 1) * kONormRows;
-  const int row_end = P.toff[e + 1];
+  const int row0 = P.mtile[2 * (t >> 1) + 1] + (t & 1) * kONormRows + (sub > 0 ? kONormRows / 2 : 0);
+  const int row_end = sub >= 0 ? min(P.toff[e + 1], row0 + kONormRows / 2) : P.toff[e + 1];
   if (row0 >= row_end) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1240,23 +1257,31 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
   // (The barrier's own lgkmcnt(0) covers this wave's reads of stage kt; an
   // extra explicit wait in front of it made the compiler add another one
   // between the MFMAs.)
-  auto step = [&](int kt, auto cur_tag) {
-    constexpr int cur = decltype(cur_tag)::value;
-    stage_barrier<NQ * 2, 0>();
-    issue(min(kt + NS, nk - 1), (int)((unsigned)kt % NS));
-    read_frags(cur ^ 1, (int)((unsigned)(kt + 1) % NS));
+  // (a sub-unit: IM = 1, the MFMAs of the first 32-row block only)
+  auto main_loop = [&](auto im_tag) {
+    constexpr int IM = decltype(im_tag)::value;
+    auto step = [&](int kt, auto cur_tag) {
+      constexpr int cur = decltype(cur_tag)::value;
+      stage_barrier<NQ * 2, 0>();
+      issue(min(kt + NS, nk - 1), (int)((unsigned)kt % NS));
+      read_frags(cur ^ 1, (int)((unsigned)(kt + 1) % NS));
 #pragma unroll
-    for (int in = 0; in < TN; ++in)
+      for (int in = 0; in < TN; ++in)
 #pragma unroll
-      for (int im = 0; im < 2; ++im)
-        acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][in], fx[cur][im], acc[in][im], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, TN + 2, 0);   // the fragment reads
-    mfma_load_groups<NQ, 2 * TN>();                           // MFMAs, stage loads among them
+        for (int im = 0; im < IM; ++im)
+          acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][in], fx[cur][im], acc[in][im], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, TN + 2, 0);   // the fragment reads
+      mfma_load_groups<NQ, IM * TN>();                          // MFMAs, stage loads among them
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(kt, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
+    }
   };
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, std::integral_constant<int, 0>{});
-    step(kt + 1, std::integral_constant<int, 1>{});
-  }
+  if (sub >= 0)
+    main_loop(std::integral_constant<int, 1>{});
+  else
+    main_loop(std::integral_constant<int, 2>{});
   stage_barrier<0, 0>();   // every wave is done with the ring: the epilogue reuses it
 
   // ---- epilogue.  acc[in][im] holds y[m = im*32 + lane%32][n = wave*32*TN +
@@ -1281,6 +1306,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_o_norm(ONormParams P) {
   }
 #pragma unroll
   for (int im = 0; im < 2; ++im) {
+    if (im && sub >= 0) break;        // a sub-unit's rows are all in the first block
     if (im) stage_barrier<63, 0>();   // every wave is done reading the first half
     {
       const int r = lane_e & 31;
@@ -1635,8 +1661,17 @@ hipError_t launch_o_norm_tn(const ONormParams &P, const Workspace &ws, hipStream
   const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_o_norm<TN>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
-  const int grid = ((2 * ws.max_mtiles + 7) / 8) * 8;   // 64-row halves of the 128-row table
-  lol_launch((k_gemm_o_norm<TN>), dim3(grid), dim3(512), LDS, st, P);
+  // 64-row halves of the 128-row table, per XCD; room for the tail's
+  // sub-units when the halves can overrun the XCD's CUs by at most half
+  int ncu = 0;
+  const hipError_t ec = cu_count(&ncu);
+  if (ec != hipSuccess) return ec;
+  ONormParams Q = P;
+  Q.cpx = ncu / 8;
+  const int per_max = (2 * ws.max_mtiles + 7) / 8;
+  const int tail_max = per_max - Q.cpx;
+  const int slots = tail_max > 0 && 2 * tail_max <= Q.cpx ? Q.cpx + 2 * tail_max : per_max;
+  lol_launch((k_gemm_o_norm<TN>), dim3(8 * slots), dim3(512), LDS, st, Q);
   return hipGetLastError();
 }
 
